@@ -1,0 +1,169 @@
+"""Plain fp64 CPU oracle for the fused transformer feed-forward path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The GPU
+library never imports it, shares no code with it, and must never fall back to it.
+
+Every function computes the plain definition the pages give, in float64, on the
+caller's (bf16-valued) inputs, with no rounding of any intermediate and no
+blocking, fusion or reordering beyond a library matmul.  Fusion on the GPU
+changes launches and memory traffic, never the mathematics (ainews.cool
+"PyTorch fused MLP efficiency", section "technical deep dive": the fused form
+loads X once and computes the same W1*X+b1 -> activation -> W2*(.)+b2 chain;
+"Profiling in PyTorch (Part 2): From nn.Linear to a Fused MLP", section "The
+fused Triton kernel": the fused kernel computes gelu(g)*u exactly as eager does).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  * GELU formulas: the pages name ``F.gelu(g, approximate="tanh")`` and plain
+    "GELU" but print no formula; we take PyTorch's documented definitions
+    (Hendrycks & Gimpel): exact  z*Phi(z) = z/2 * erfc(-z/sqrt 2)  and tanh
+    z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+  * Intermediates (h, g, u, m) are NOT rounded: the oracle is the plain
+    definition; the GPU's bf16 rounding of h/m is absorbed by the tolerance.
+  * MoE: y[t] = sum_j gate_w[t, j] * geglu_{expert_ids[t, j]}(x[t]); duplicate
+    expert ids within a token simply add.
+
+Pins: tests/test_oracle_pins.py checks every function here against brute-force
+loops, library routines, closed forms, a printed worked example and invariants.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erfc as _erfc
+
+__all__ = [
+    "ACTS",
+    "gelu_erf",
+    "gelu_tanh",
+    "activation",
+    "linear",
+    "mlp2",
+    "geglu",
+    "moe_geglu",
+]
+
+ACTS = ("none", "gelu_erf", "gelu_tanh")
+
+_SQRT_HALF = np.sqrt(0.5)
+_SQRT_2_OVER_PI = np.sqrt(2.0 / np.pi)
+_GELU_TANH_CUBIC = 0.044715
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def gelu_erf(z):
+    """Exact GELU, z * Phi(z), with Phi the standard normal CDF.
+
+    The ainews.cool article ("technical deep dive" / "benchmark data") names a
+    plain "GELU" activation for its 4096-wide MLP; PyTorch's default GELU is the
+    exact one.  Phi(z) = erfc(-z/sqrt(2)) / 2, which keeps full relative accuracy
+    in the negative tail where 1 + erf(.) would cancel.
+    """
+    z = _f64(z)
+    return 0.5 * z * _erfc(-z * _SQRT_HALF)
+
+
+def gelu_tanh(z):
+    """Tanh-approximated GELU, as named by ``F.gelu(g, approximate="tanh")``.
+
+    "Profiling in PyTorch (Part 2)", section "Stacking three Linears: the MLP"
+    (the SimpleGeGLUMLP forward).  Formula: PyTorch's documented definition,
+    z/2 * (1 + tanh(sqrt(2/pi) * (z + 0.044715 z^3))).
+    """
+    z = _f64(z)
+    inner = _SQRT_2_OVER_PI * (z + _GELU_TANH_CUBIC * z * z * z)
+    return 0.5 * z * (1.0 + np.tanh(inner))
+
+
+def activation(z, act: str):
+    """The epilogue activation selected by name: none, gelu_erf or gelu_tanh.
+
+    "Profiling in PyTorch (Part 2)", section "Why are there no separate mul and
+    add kernels?": applying an activation is a classic GEMM epilogue.
+    """
+    if act == "none":
+        return _f64(z)
+    if act == "gelu_erf":
+        return gelu_erf(z)
+    if act == "gelu_tanh":
+        return gelu_tanh(z)
+    raise ValueError(f"unknown activation {act!r}; expected one of {ACTS}")
+
+
+def linear(x, W, b=None, act: str = "none"):
+    """y = act(x @ W^T + b), W stored [out, in] as nn.Linear stores it.
+
+    "Profiling in PyTorch (Part 2)", section "From matmul-add to Linear"
+    (y = x @ w.T + b) and section "Why are there no separate mul and add
+    kernels?" (addmm: out = x @ weight.T + bias; bias/activation are the
+    epilogue).  x is [M, K], W is [N, K], b is [N] or None; returns [M, N].
+    """
+    x = _f64(x)
+    W = _f64(W)
+    if x.ndim != 2 or W.ndim != 2 or x.shape[1] != W.shape[1]:
+        raise ValueError(f"shape mismatch: x{x.shape} W{W.shape}")
+    z = x @ W.T
+    if b is not None:
+        b = _f64(b)
+        if b.shape != (W.shape[0],):
+            raise ValueError(f"bias shape {b.shape} != ({W.shape[0]},)")
+        z = z + b[None, :]
+    return activation(z, act)
+
+
+def mlp2(x, W1, b1, W2, b2, act: str):
+    """Two-layer MLP: y = act(x W1^T + b1) W2^T + b2 (activation between layers only).
+
+    ainews.cool "PyTorch fused MLP efficiency", section "technical deep dive":
+    launch 1 computes W1*X+b1, launch 2 applies the activation, launch 3
+    computes W2*(act(W1*X+b1))+b2; the fused form does the same chain in one
+    launch.  x [M,K], W1 [H,K], b1 [H]|None, W2 [N,H], b2 [N]|None.
+    """
+    h = linear(x, W1, b1, act)
+    return linear(h, W2, b2, "none")
+
+
+def geglu(x, Wg, Wu, Wd):
+    """GeGLU feed-forward: y = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T, no biases.
+
+    "Profiling in PyTorch (Part 2)", section "Stacking three Linears: the MLP"
+    (SimpleGeGLUMLP: gate_proj, up_proj, down_proj all bias=False;
+    g = gate(x), u = up(x), h = gelu(g, tanh), m = h * u, y = down(m)).
+    x [M,D], Wg/Wu [H,D], Wd [D,H].
+    """
+    g = linear(x, Wg)
+    u = linear(x, Wu)
+    m = gelu_tanh(g) * u
+    return linear(m, Wd)
+
+
+def moe_geglu(x, expert_ids, gate_w, expert_weights):
+    """Top-k routed mixture of GeGLU experts with a weighted combine.
+
+    ainews.cool "PyTorch fused MLP efficiency", section "architectural impact":
+    an MoE layer routes each token to several experts, each expert being an
+    MLP.  Here each expert is the GeGLU block above and
+        y[t] = sum_j gate_w[t, j] * geglu_{expert_ids[t, j]}(x[t]).
+
+    x [T,D]; expert_ids int [T,k]; gate_w [T,k];
+    expert_weights: a sequence (or callable e -> (Wg, Wu, Wd)) of per-expert
+    weights, fetched one expert at a time so only one expert's fp64 copy is
+    resident.  Experts that receive no token are never fetched.
+    """
+    x = _f64(x)
+    ids = np.asarray(expert_ids)
+    w = _f64(gate_w)
+    if ids.shape != w.shape or ids.ndim != 2 or ids.shape[0] != x.shape[0]:
+        raise ValueError(f"routes shape mismatch: ids{ids.shape} w{w.shape} x{x.shape}")
+    get = expert_weights if callable(expert_weights) else (lambda e: expert_weights[e])
+    # A GeGLU expert maps dim -> dim, so y has x's shape.
+    y = np.zeros_like(x)
+    for e in np.unique(ids):
+        tok, slot = np.nonzero(ids == e)
+        Wg, Wu, Wd = get(int(e))
+        ye = geglu(x[tok], Wg, Wu, Wd)
+        # np.add.at: a token routed twice to the same expert adds both terms.
+        np.add.at(y, tok, w[tok, slot][:, None] * ye)
+    return y

@@ -1,0 +1,330 @@
+"""Pins that tie the fp64 oracle to something other than itself.
+
+Each ``check_*`` takes the oracle module ``o`` and raises AssertionError when the
+oracle disagrees with:
+  * brute force: pure-Python loops on tiny shapes, using libm's math.erf /
+    math.tanh (not the oracle's scipy/numpy path);
+  * library routines the pages name: ``F.gelu(..., approximate="tanh")`` and the
+    exact ``F.gelu`` (torch, float64, CPU);
+  * closed forms and identities (Phi(1), gelu(x) - gelu(-x) = x, ...);
+  * the page's printed strides-and-views example (tests/golden/transpose_view.json);
+  * invariants (fusion does not change the math; MoE linearity / permutation).
+
+The same checks are run against planted mistakes in test_oracle_mutants.py to
+show that each plausible mistake is caught.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# brute force (pure Python, libm)
+# ---------------------------------------------------------------------------
+def _bf_act(z: float, act: str) -> float:
+    if act == "none":
+        return z
+    if act == "gelu_erf":
+        return 0.5 * z * (1.0 + math.erf(z / math.sqrt(2.0)))
+    if act == "gelu_tanh":
+        c = math.sqrt(2.0 / math.pi)
+        return 0.5 * z * (1.0 + math.tanh(c * (z + 0.044715 * z ** 3)))
+    raise ValueError(act)
+
+
+def bf_linear(x, W, b, act):
+    M, K = len(x), len(x[0])
+    N = len(W)
+    y = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            s = 0.0
+            for k in range(K):
+                s += float(x[m][k]) * float(W[n][k])
+            if b is not None:
+                s += float(b[n])
+            y[m][n] = _bf_act(s, act)
+    return y
+
+
+def bf_geglu(x, Wg, Wu, Wd):
+    g = bf_linear(x, Wg, None, "none")
+    u = bf_linear(x, Wu, None, "none")
+    m = [[_bf_act(g[i][j], "gelu_tanh") * u[i][j] for j in range(len(g[0]))] for i in range(len(g))]
+    return bf_linear(m, Wd, None, "none")
+
+
+def bf_moe(x, ids, gw, experts):
+    T, D = len(x), len(x[0])
+    y = [[0.0] * D for _ in range(T)]
+    for t in range(T):
+        for j in range(len(ids[t])):
+            Wg, Wu, Wd = experts[int(ids[t][j])]
+            yt = bf_geglu([x[t]], Wg, Wu, Wd)[0]
+            for d in range(D):
+                y[t][d] += float(gw[t][j]) * yt[d]
+    return y
+
+
+def _close(a, b, rtol=1e-12, atol=1e-13, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} != {b.shape}"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    scale = max(np.max(np.abs(b)) if b.size else 0.0, 1.0)
+    assert err <= rtol * scale + atol, f"{what}: max err {err:.3e} (scale {scale:.3e})"
+
+
+def _bf16ish(rng, shape, scale=1.0):
+    """Random values exactly representable in bf16 (8 significant bits)."""
+    a = rng.standard_normal(shape) * scale
+    e = np.floor(np.log2(np.maximum(np.abs(a), 1e-30)))
+    return np.round(a / 2.0 ** (e - 7)) * 2.0 ** (e - 7)
+
+
+# ---------------------------------------------------------------------------
+# checks
+# ---------------------------------------------------------------------------
+def check_linear_bruteforce(o):
+    rng = np.random.default_rng(1234)
+    for (M, K, N) in [(1, 1, 1), (2, 3, 5), (3, 8, 2), (5, 16, 8), (8, 8, 8), (16, 2, 3)]:
+        x = _bf16ish(rng, (M, K))
+        W = _bf16ish(rng, (N, K), 0.5)
+        b = _bf16ish(rng, (N,), 0.5)
+        for act in ("none", "gelu_erf", "gelu_tanh"):
+            for bias in (None, b):
+                ref = bf_linear(x.tolist(), W.tolist(), None if bias is None else bias.tolist(), act)
+                _close(o.linear(x, W, bias, act), ref, what=f"linear {M}x{K}x{N} {act} bias={bias is not None}")
+
+
+def check_mlp2_bruteforce(o):
+    rng = np.random.default_rng(99)
+    for (M, K, H, N) in [(1, 4, 6, 3), (3, 8, 5, 2), (4, 2, 8, 8)]:
+        x = _bf16ish(rng, (M, K))
+        W1 = _bf16ish(rng, (H, K), 0.5)
+        b1 = _bf16ish(rng, (H,), 0.5)
+        W2 = _bf16ish(rng, (N, H), 0.5)
+        b2 = _bf16ish(rng, (N,), 0.5)
+        for act in ("gelu_erf", "gelu_tanh", "none"):
+            h = bf_linear(x.tolist(), W1.tolist(), b1.tolist(), act)
+            ref = bf_linear(h, W2.tolist(), b2.tolist(), "none")
+            _close(o.mlp2(x, W1, b1, W2, b2, act), ref, what=f"mlp2 {act}")
+
+
+def check_geglu_bruteforce(o):
+    rng = np.random.default_rng(7)
+    for (M, D, H) in [(1, 3, 4), (2, 5, 7), (4, 8, 6)]:
+        x = _bf16ish(rng, (M, D))
+        Wg = _bf16ish(rng, (H, D), 0.7)
+        Wu = _bf16ish(rng, (H, D), 0.7)
+        Wd = _bf16ish(rng, (D, H), 0.7)
+        ref = bf_geglu(x.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist())
+        _close(o.geglu(x, Wg, Wu, Wd), ref, what=f"geglu {M}x{D}x{H}")
+
+
+def check_moe_bruteforce(o):
+    rng = np.random.default_rng(5)
+    T, D, H, E, k = 6, 4, 5, 3, 2
+    x = _bf16ish(rng, (T, D))
+    experts = [(_bf16ish(rng, (H, D), 0.7), _bf16ish(rng, (H, D), 0.7), _bf16ish(rng, (D, H), 0.7))
+               for _ in range(E)]
+    ids = np.array([[0, 1], [2, 0], [1, 2], [2, 1], [0, 2], [1, 1]], dtype=np.int32)  # last: duplicate id
+    gw = rng.random((T, k))
+    ref = bf_moe(x.tolist(), ids.tolist(), gw.tolist(),
+                 [(a.tolist(), b.tolist(), c.tolist()) for a, b, c in experts])
+    _close(o.moe_geglu(x, ids, gw, experts), ref, what="moe brute force")
+
+
+def check_gelu_library(o):
+    """The pages name torch's F.gelu (exact) and F.gelu(approximate="tanh")."""
+    import torch
+    import torch.nn.functional as F
+
+    z = np.concatenate([np.linspace(-12, 12, 4801), [-1e-3, 1e-3, 0.0, 3.0, -3.0]])
+    t = torch.from_numpy(z)
+    _close(o.gelu_erf(z), F.gelu(t).numpy(), rtol=1e-14, atol=1e-15, what="gelu_erf vs F.gelu")
+    _close(o.gelu_tanh(z), F.gelu(t, approximate="tanh").numpy(), rtol=1e-14, atol=1e-15,
+           what="gelu_tanh vs F.gelu(tanh)")
+    # activation() dispatches by name
+    _close(o.activation(z, "gelu_erf"), F.gelu(t).numpy(), rtol=1e-14, atol=1e-15, what="act erf")
+    _close(o.activation(z, "gelu_tanh"), F.gelu(t, approximate="tanh").numpy(), rtol=1e-14,
+           atol=1e-15, what="act tanh")
+    _close(o.activation(z, "none"), z, what="act none")
+
+
+def check_gelu_closed_forms(o):
+    # Phi(1) and Phi(-1): standard normal table values.
+    assert abs(float(o.gelu_erf(1.0)) - 0.8413447460685429) < 1e-15
+    assert abs(float(o.gelu_erf(-1.0)) + 0.15865525393145707) < 1e-15
+    # libm erf, scalar, at a spread of points (incl. the negative tail).
+    for v in (-6.0, -4.0, -2.5, -0.3, 0.7, 2.0, 5.0):
+        ref = 0.5 * v * math.erfc(-v / math.sqrt(2.0))
+        assert abs(float(o.gelu_erf(v)) - ref) <= 1e-15 * max(1.0, abs(ref)), v
+    for g in (o.gelu_erf, o.gelu_tanh):
+        assert float(g(0.0)) == 0.0
+        assert float(g(10.0)) == 10.0           # gelu(x) -> x for x >> 0
+        assert -1e-20 <= float(g(-10.0)) <= 0.0  # gelu(x) -> 0- for x << 0
+        # odd-part identity: gelu(x) - gelu(-x) = x (Phi(x) + Phi(-x) = 1; tanh odd)
+        x = np.linspace(-6, 6, 1201)
+        _close(g(x) - g(-x), x, rtol=1e-14, atol=1e-14, what="odd-part identity")
+        # derivative 1/2 at 0
+        h = 1e-6
+        d = (float(g(h)) - float(g(-h))) / (2 * h)
+        assert abs(d - 0.5) < 1e-9, d
+    # the two variants differ, by at most ~4.73e-4, attained near |x| ~ 2.70
+    # (their difference is even in x, a consequence of the odd-part identity)
+    x = np.linspace(-8, 8, 160001)
+    diff = np.abs(o.gelu_erf(x) - o.gelu_tanh(x))
+    assert 4.70e-4 < diff.max() < 4.76e-4, diff.max()
+    assert 2.6 < abs(x[diff.argmax()]) < 2.8
+
+
+def check_transpose_worked_example(o):
+    """The page's strides-and-views example: with W = M ([out=3, in=2]) and
+    x = I_2, nn.Linear's y = x @ W.T is exactly the printed M.t()."""
+    g = _load("transpose_view.json")
+    M = np.array(g["M"], dtype=np.float64)
+    assert list(M.shape) == g["M_shape"]
+    y = o.linear(np.eye(2), M, None, "none")
+    assert y.tolist() == g["Mt"], y.tolist()
+    assert y.flatten().tolist() == g["Mt_flatten"]
+    # a single input row e_k picks out column k of W, i.e. row k of M.t()
+    for k in range(2):
+        e = np.zeros((1, 2))
+        e[0, k] = 1.0
+        assert o.linear(e, M, None, "none")[0].tolist() == g["Mt"][k]
+
+
+def check_linear_special_cases(o):
+    rng = np.random.default_rng(11)
+    x = _bf16ish(rng, (7, 16))
+    # identity weight, no bias, no activation -> y == x bitwise
+    y = o.linear(x, np.eye(16), None, "none")
+    assert np.array_equal(y, x)
+    # W = 0 -> y = act(b) exactly
+    b = _bf16ish(rng, (5,))
+    for act in ("none", "gelu_erf", "gelu_tanh"):
+        y = o.linear(x, np.zeros((5, 16)), b, act)
+        ref = np.array([[_bf_act(float(v), act) for v in b]] * 7)
+        _close(y, ref, rtol=1e-15, atol=1e-16, what=f"W=0 {act}")
+    # one-hot rows: W[n] = e_{p(n)} -> y[:, n] = x[:, p(n)]
+    p = np.array([3, 0, 15, 7, 7, 2])
+    W = np.zeros((6, 16))
+    W[np.arange(6), p] = 1.0
+    assert np.array_equal(o.linear(x, W, None, "none"), x[:, p])
+    # bias adds (not subtracts), per output column
+    b6 = np.arange(1, 7, dtype=np.float64)
+    assert np.array_equal(o.linear(x, W, b6, "none"), x[:, p] + b6[None, :])
+
+
+def check_mlp2_bias_pins(o):
+    rng = np.random.default_rng(3)
+    x = _bf16ish(rng, (4, 8))
+    b1 = _bf16ish(rng, (8,))
+    # W1 = 0 -> h = act(b1); W2 = I, b2 = 0 -> y = act(b1) for every row
+    for act in ("gelu_erf", "gelu_tanh"):
+        y = o.mlp2(x, np.zeros((8, 8)), b1, np.eye(8), np.zeros(8), act)
+        ref = np.array([[_bf_act(float(v), act) for v in b1]] * 4)
+        _close(y, ref, rtol=1e-15, atol=1e-16, what="mlp2 W1=0")
+    # the activation sits between the layers only: W1 = I, b1 = 0, W2 = -I, b2 = c
+    c = _bf16ish(rng, (8,))
+    y = o.mlp2(x, np.eye(8), None, -np.eye(8), c, "gelu_tanh")
+    ref = -np.vectorize(lambda v: _bf_act(v, "gelu_tanh"))(x) + c[None, :]
+    _close(y, ref, what="mlp2 act placement")
+
+
+def check_geglu_special_cases(o):
+    rng = np.random.default_rng(13)
+    x = _bf16ish(rng, (5, 6))
+    I = np.eye(6)
+    # Wg = Wu = Wd = I -> y = gelu_tanh(x) * x
+    ref = np.vectorize(lambda v: _bf_act(v, "gelu_tanh") * v)(x)
+    _close(o.geglu(x, I, I, I), ref, what="geglu identity")
+    W = _bf16ish(rng, (9, 6))
+    Wd = _bf16ish(rng, (6, 9))
+    assert np.array_equal(o.geglu(x, W, np.zeros((9, 6)), Wd), np.zeros((5, 6)))   # Wu = 0
+    assert np.array_equal(o.geglu(x, W, W, np.zeros((6, 9))), np.zeros((5, 6)))    # Wd = 0
+    # the gate goes through gelu, the up projection does not
+    Wg = _bf16ish(rng, (9, 6))
+    Wu = _bf16ish(rng, (9, 6))
+    a = o.geglu(x, Wg, Wu, Wd)
+    b = o.geglu(x, Wu, Wg, Wd)
+    assert np.max(np.abs(a - b)) > 1e-3
+    # gate = identity path: Wg = I, Wu = I (dim=hidden), Wd = I: elementwise gelu(x)*x
+    # (already covered); up only linear: doubling Wu doubles y
+    _close(o.geglu(x, Wg, 2 * Wu, Wd), 2 * a, what="geglu linear in up")
+
+
+def check_fused_equals_unfused(o):
+    """Fusion changes launches and traffic, not the mathematics: the one-call
+    forms equal their compositions of Linears."""
+    rng = np.random.default_rng(17)
+    x = _bf16ish(rng, (6, 8))
+    W1, b1 = _bf16ish(rng, (12, 8), 0.4), _bf16ish(rng, (12,), 0.4)
+    W2, b2 = _bf16ish(rng, (5, 12), 0.4), _bf16ish(rng, (5,), 0.4)
+    for act in ("gelu_erf", "gelu_tanh"):
+        _close(o.mlp2(x, W1, b1, W2, b2, act),
+               o.linear(o.linear(x, W1, b1, act), W2, b2, "none"), what="mlp2 == 2 linears")
+    Wg, Wu, Wd = _bf16ish(rng, (12, 8), 0.4), _bf16ish(rng, (12, 8), 0.4), _bf16ish(rng, (8, 12), 0.4)
+    m = o.linear(x, Wg, None, "gelu_tanh") * o.linear(x, Wu, None, "none")
+    _close(o.geglu(x, Wg, Wu, Wd), o.linear(m, Wd, None, "none"), what="geglu == composition")
+
+
+def check_moe_invariants(o):
+    rng = np.random.default_rng(21)
+    T, D, H, E = 9, 6, 7, 4
+    x = _bf16ish(rng, (T, D))
+    experts = [(_bf16ish(rng, (H, D), 0.6), _bf16ish(rng, (H, D), 0.6), _bf16ish(rng, (D, H), 0.6))
+               for _ in range(E)]
+    # top_k = 1, every token to expert e with weight 1 -> dense geglu of expert e
+    for e in range(E):
+        ids = np.full((T, 1), e, dtype=np.int32)
+        _close(o.moe_geglu(x, ids, np.ones((T, 1)), experts), o.geglu(x, *experts[e]),
+               what=f"moe top1 expert {e}")
+    # weights (w, 1-w) on the same expert twice -> dense expert (linearity)
+    w = rng.random(T)
+    ids = np.full((T, 2), 2, dtype=np.int32)
+    _close(o.moe_geglu(x, ids, np.stack([w, 1 - w], 1), experts), o.geglu(x, *experts[2]),
+           what="moe split weight")
+    # permuting tokens permutes output rows
+    ids = rng.integers(0, E, size=(T, 2)).astype(np.int32)
+    gw = rng.random((T, 2))
+    y = o.moe_geglu(x, ids, gw, experts)
+    p = rng.permutation(T)
+    _close(o.moe_geglu(x[p], ids[p], gw[p], experts), y[p], what="moe permutation")
+    # swapping the two slots of a token changes nothing
+    _close(o.moe_geglu(x, ids[:, ::-1], gw[:, ::-1], experts), y, what="moe slot order")
+    # zero gate weight removes an expert's contribution
+    gw0 = gw.copy()
+    gw0[:, 1] = 0.0
+    y1 = o.moe_geglu(x, ids[:, :1], gw[:, :1], experts)
+    _close(o.moe_geglu(x, ids, gw0, experts), y1, what="moe zero weight")
+    # an expert fetched lazily through a callable gives the same result
+    _close(o.moe_geglu(x, ids, gw, lambda e: experts[e]), y, what="moe callable")
+
+
+ALL_CHECKS = [
+    check_linear_bruteforce,
+    check_mlp2_bruteforce,
+    check_geglu_bruteforce,
+    check_moe_bruteforce,
+    check_gelu_library,
+    check_gelu_closed_forms,
+    check_transpose_worked_example,
+    check_linear_special_cases,
+    check_mlp2_bias_pins,
+    check_geglu_special_cases,
+    check_fused_equals_unfused,
+    check_moe_invariants,
+]

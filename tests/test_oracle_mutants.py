@@ -1,0 +1,139 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and confirm that at least
+one pin catches each.  This is what makes the pins worth trusting: a dropped
+term, a wrong sign or index, a transposed operand, a swapped gate/up, or the
+wrong GELU variant must all fail."""
+import numpy as np
+import pytest
+from scipy.special import erfc
+
+import oracle.fmlp_oracle as fo
+from oracle_pins import ALL_CHECKS
+
+_orig_linear = fo.linear
+_orig_activation = fo.activation
+_orig_gelu_erf = fo.gelu_erf
+_orig_gelu_tanh = fo.gelu_tanh
+_orig_moe = fo.moe_geglu
+
+
+def _linear_no_bias(x, W, b=None, act="none"):
+    return _orig_linear(x, W, None, act)
+
+
+def _linear_bias_sub(x, W, b=None, act="none"):
+    z = np.asarray(x, float) @ np.asarray(W, float).T
+    if b is not None:
+        z = z - np.asarray(b, float)[None, :]
+    return fo.activation(z, act)
+
+
+def _linear_square_transposed(x, W, b=None, act="none"):
+    x = np.asarray(x, float)
+    W = np.asarray(W, float)
+    z = x @ W if W.shape[0] == W.shape[1] else x @ W.T
+    if b is not None:
+        z = z + np.asarray(b, float)[None, :]
+    return fo.activation(z, act)
+
+
+def _linear_act_before_bias(x, W, b=None, act="none"):
+    z = fo.activation(np.asarray(x, float) @ np.asarray(W, float).T, act)
+    if b is not None:
+        z = z + np.asarray(b, float)[None, :]
+    return z
+
+
+def _gelu_erf_sign(z):
+    z = np.asarray(z, float)
+    return 0.5 * z * erfc(z * np.sqrt(0.5))
+
+
+def _gelu_tanh_no_cubic(z):
+    z = np.asarray(z, float)
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(2 / np.pi) * z))
+
+
+def _gelu_tanh_wrong_const(z):
+    z = np.asarray(z, float)
+    return 0.5 * z * (1.0 + np.tanh(np.sqrt(1 / np.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _act_names_swapped(z, act):
+    return _orig_activation(z, {"gelu_erf": "gelu_tanh", "gelu_tanh": "gelu_erf"}.get(act, act))
+
+
+def _geglu_swapped(x, Wg, Wu, Wd):
+    return _orig_linear(fo.gelu_tanh(_orig_linear(x, Wu)) * _orig_linear(x, Wg), Wd)
+
+
+def _geglu_no_gelu(x, Wg, Wu, Wd):
+    return _orig_linear(_orig_linear(x, Wg) * _orig_linear(x, Wu), Wd)
+
+
+def _geglu_wrong_act(x, Wg, Wu, Wd):
+    return _orig_linear(fo.gelu_erf(_orig_linear(x, Wg)) * _orig_linear(x, Wu), Wd)
+
+
+def _mlp2_act_twice(x, W1, b1, W2, b2, act):
+    return _orig_linear(_orig_linear(x, W1, b1, act), W2, b2, act)
+
+
+def _mlp2_drop_b2(x, W1, b1, W2, b2, act):
+    return _orig_linear(_orig_linear(x, W1, b1, act), W2, None, "none")
+
+
+def _moe_unweighted(x, ids, gw, ew):
+    return _orig_moe(x, ids, np.ones_like(np.asarray(gw, float)), ew)
+
+
+def _moe_first_slot(x, ids, gw, ew):
+    ids = np.asarray(ids)
+    return _orig_moe(x, ids[:, :1], np.asarray(gw, float)[:, :1], ew)
+
+
+def _moe_dedup(x, ids, gw, ew):
+    # overwrites instead of accumulating a token routed twice to one expert
+    x = np.asarray(x, float)
+    ids = np.asarray(ids)
+    gw = np.asarray(gw, float)
+    get = ew if callable(ew) else (lambda e: ew[e])
+    y = np.zeros_like(x)
+    for e in np.unique(ids):
+        tok, slot = np.nonzero(ids == e)
+        y[tok] += gw[tok, slot][:, None] * fo.geglu(x[tok], *get(int(e)))
+    return y
+
+
+MUTANTS = {
+    "linear_drops_bias": ("linear", _linear_no_bias),
+    "linear_subtracts_bias": ("linear", _linear_bias_sub),
+    "linear_square_W_not_transposed": ("linear", _linear_square_transposed),
+    "linear_act_before_bias": ("linear", _linear_act_before_bias),
+    "gelu_erf_wrong_sign": ("gelu_erf", _gelu_erf_sign),
+    "gelu_tanh_is_erf": ("gelu_tanh", _orig_gelu_erf),
+    "gelu_erf_is_tanh": ("gelu_erf", _orig_gelu_tanh),
+    "gelu_tanh_no_cubic": ("gelu_tanh", _gelu_tanh_no_cubic),
+    "gelu_tanh_wrong_const": ("gelu_tanh", _gelu_tanh_wrong_const),
+    "activation_names_swapped": ("activation", _act_names_swapped),
+    "geglu_gate_up_swapped": ("geglu", _geglu_swapped),
+    "geglu_no_gelu": ("geglu", _geglu_no_gelu),
+    "geglu_erf_gelu": ("geglu", _geglu_wrong_act),
+    "mlp2_act_after_both": ("mlp2", _mlp2_act_twice),
+    "mlp2_drops_b2": ("mlp2", _mlp2_drop_b2),
+    "moe_ignores_gate_w": ("moe_geglu", _moe_unweighted),
+    "moe_first_slot_only": ("moe_geglu", _moe_first_slot),
+    "moe_overwrites_duplicates": ("moe_geglu", _moe_dedup),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(fo, attr, fn)
+    caught = []
+    for check in ALL_CHECKS:
+        try:
+            check(fo)
+        except Exception as e:  # AssertionError or a shape error
+            caught.append(f"{check.__name__}: {type(e).__name__}")
+    assert caught, f"planted mistake {name!r} passed every pin"
