@@ -1,0 +1,283 @@
+"""Fused transformer feed-forward kernels for AMD MI355X (gfx950).
+
+Thin Python binding of the C-ABI library ``libfmlp.so`` (declared in
+``include/fmlp.h``).  It only marshals arguments: it checks tensor dtypes and
+devices, flattens leading dims (M = batch * seq), allocates outputs and
+workspaces with torch, and passes raw device pointers plus the current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback of any kind: if the library is not built, every call
+raises.
+
+    fmlp_linear(x, W, b=None, act="none")          y = act(x W^T + b)
+    fmlp_mlp2(x, W1, b1, W2, b2, act)               y = act(x W1^T + b1) W2^T + b2
+    fmlp_geglu(x, Wg, Wu, Wd)                       y = (gelu_tanh(x Wg^T) * x Wu^T) Wd^T
+    fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd)
+                                                    y[t] = sum_j w[t,j] geglu_{e[t,j]}(x[t])
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "FmlpError",
+    "ACT",
+    "library_path",
+    "lib",
+    "fmlp_linear",
+    "fmlp_mlp2",
+    "fmlp_geglu",
+    "fmlp_moe_geglu",
+    "fmlp_mlp2_workspace_size",
+    "fmlp_geglu_workspace_size",
+    "fmlp_moe_workspace_size",
+    "force_path",
+    "workspace_for",
+    "barrier_timeouts",
+    "moe_invalid_ids",
+    "linear",
+    "mlp2",
+    "geglu",
+    "moe_geglu",
+]
+
+ACT = {"none": 0, "gelu_erf": 1, "gelu_tanh": 2}
+PATHS = {"auto": 0, "decode": 1, "gemm": 2, "small": 3}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libfmlp.so")
+
+
+class FmlpError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"fmlp status {status}: {detail}")
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfmlp.so (built in-tree).  Raises if it is missing."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise FmlpError(-1, f"{path} is not built; run gemm_epilogue_bf16_amd.build.build() "
+                                "(there is no non-HIP fallback)")
+        L = ctypes.CDLL(path)
+        L.fmlp_linear.argtypes = [_p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
+        L.fmlp_mlp2.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _sz, _p]
+        L.fmlp_geglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p]
+        L.fmlp_moe_geglu.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int32,
+                                     ctypes.c_int32, _p, _p, _sz, _p]
+        for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_moe_geglu", "fmlp_set_path"):
+            getattr(L, f).restype = ctypes.c_int
+        L.fmlp_set_path.argtypes = [ctypes.c_int]
+        L.fmlp_mlp2_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
+        L.fmlp_mlp2_workspace_size.restype = _sz
+        L.fmlp_geglu_workspace_size.argtypes = [_i64, _i64, _i64]
+        L.fmlp_geglu_workspace_size.restype = _sz
+        L.fmlp_moe_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_int32]
+        L.fmlp_moe_workspace_size.restype = _sz
+        L.fmlp_moe_error_offset.argtypes = []
+        L.fmlp_moe_error_offset.restype = _sz
+        L.fmlp_status_string.argtypes = [ctypes.c_int]
+        L.fmlp_status_string.restype = ctypes.c_char_p
+        L.fmlp_last_error.argtypes = []
+        L.fmlp_last_error.restype = ctypes.c_char_p
+        L.fmlp_version.argtypes = []
+        L.fmlp_version.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise FmlpError(status, f"{L.fmlp_status_string(status).decode()} -- {L.fmlp_last_error().decode()}")
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtype=torch.bfloat16) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_ws_cache: dict = {}
+_ws_lock = threading.Lock()
+
+
+def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per (device,
+    stream).  Its 256-byte header must start zeroed; every call leaves it so."""
+    if nbytes <= 0:
+        return None
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+@contextlib.contextmanager
+def force_path(path: str):
+    """Force the calling thread's mlp2/geglu path: "auto", "decode", "gemm", "small"."""
+    L = lib()
+    _check(L.fmlp_set_path(PATHS[path]))
+    try:
+        yield
+    finally:
+        L.fmlp_set_path(0)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def fmlp_linear(x, W, b=None, act: str = "none", out=None):
+    """y = act(x W^T + b); x [..., K], W [N, K], b [N] or None -> y [..., N]."""
+    _dev_tensor("x", x)
+    _dev_tensor("W", W)
+    if b is not None:
+        _dev_tensor("b", b)
+    K = x.shape[-1]
+    N = W.shape[0]
+    if W.dim() != 2 or W.shape[1] != K:
+        raise ValueError(f"W must be [N, {K}], got {tuple(W.shape)}")
+    M = x.numel() // K if K else 0
+    y = out if out is not None else torch.empty(*x.shape[:-1], N, dtype=torch.bfloat16, device=x.device)
+    _dev_tensor("out", y)
+    with torch.cuda.device(x.device):
+        _check(lib().fmlp_linear(_ptr(x), _ptr(W), _ptr(b), ACT[act], M, K, N, _ptr(y), _stream(x.device)))
+    return y
+
+
+def fmlp_mlp2_workspace_size(M, K, H, N) -> int:
+    return int(lib().fmlp_mlp2_workspace_size(M, K, H, N))
+
+
+def fmlp_mlp2(x, W1, b1, W2, b2, act: str = "gelu_erf", out=None, workspace=None):
+    """y = act(x W1^T + b1) W2^T + b2; W1 [H, K], W2 [N, H]; biases may be None."""
+    for n, t in (("x", x), ("W1", W1), ("W2", W2)):
+        _dev_tensor(n, t)
+    for n, t in (("b1", b1), ("b2", b2)):
+        if t is not None:
+            _dev_tensor(n, t)
+    K = x.shape[-1]
+    H, N = W1.shape[0], W2.shape[0]
+    if W1.shape[1] != K or W2.shape[1] != H:
+        raise ValueError(f"shape mismatch: x[...,{K}] W1{tuple(W1.shape)} W2{tuple(W2.shape)}")
+    M = x.numel() // K
+    y = out if out is not None else torch.empty(*x.shape[:-1], N, dtype=torch.bfloat16, device=x.device)
+    L = lib()
+    need = int(L.fmlp_mlp2_workspace_size(M, K, H, N))
+    ws = workspace if workspace is not None else workspace_for(x.device, need)
+    with torch.cuda.device(x.device):
+        _check(L.fmlp_mlp2(_ptr(x), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), ACT[act], M, K, H, N,
+                           _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device)))
+    return y
+
+
+def fmlp_geglu_workspace_size(M, D, H) -> int:
+    return int(lib().fmlp_geglu_workspace_size(M, D, H))
+
+
+def fmlp_geglu(x, Wg, Wu, Wd, out=None, workspace=None):
+    """y = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T; Wg, Wu [H, D], Wd [D, H]."""
+    for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
+        _dev_tensor(n, t)
+    D = x.shape[-1]
+    H = Wg.shape[0]
+    if Wg.shape != (H, D) or Wu.shape != (H, D) or Wd.shape != (D, H):
+        raise ValueError(f"shape mismatch: x[...,{D}] Wg{tuple(Wg.shape)} Wu{tuple(Wu.shape)} Wd{tuple(Wd.shape)}")
+    M = x.numel() // D
+    y = out if out is not None else torch.empty_like(x)
+    L = lib()
+    need = int(L.fmlp_geglu_workspace_size(M, D, H))
+    ws = workspace if workspace is not None else workspace_for(x.device, need)
+    with torch.cuda.device(x.device):
+        _check(L.fmlp_geglu(_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), M, D, H, _ptr(y), _ptr(ws),
+                            ws.numel(), _stream(x.device)))
+    return y
+
+
+def fmlp_moe_workspace_size(T, D, H, E, top_k) -> int:
+    return int(lib().fmlp_moe_workspace_size(T, D, H, E, top_k))
+
+
+def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
+    """Top-k MoE of GeGLU experts.  x [T, D]; expert_ids int32 [T, k];
+    gate_w fp32 [T, k]; Wg, Wu [E, H, D]; Wd [E, D, H]."""
+    for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
+        _dev_tensor(n, t)
+    _dev_tensor("expert_ids", expert_ids, torch.int32)
+    _dev_tensor("gate_w", gate_w, torch.float32)
+    T, D = x.shape
+    E, H = Wg.shape[0], Wg.shape[1]
+    k = expert_ids.shape[1]
+    if Wg.shape != (E, H, D) or Wu.shape != (E, H, D) or Wd.shape != (E, D, H):
+        raise ValueError("expert weight shapes must be Wg,Wu [E,H,D] and Wd [E,D,H]")
+    if expert_ids.shape != (T, k) or gate_w.shape != (T, k):
+        raise ValueError("routes must be [T, top_k]")
+    y = out if out is not None else torch.empty_like(x)
+    L = lib()
+    need = int(L.fmlp_moe_workspace_size(T, D, H, E, k))
+    ws = workspace if workspace is not None else workspace_for(x.device, need)
+    with torch.cuda.device(x.device):
+        _check(L.fmlp_moe_geglu(_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu), _ptr(Wd),
+                                T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)))
+    return y
+
+
+# ---------------------------------------------------------------------------
+# diagnostics (read after a sync)
+# ---------------------------------------------------------------------------
+def barrier_timeouts(workspace: torch.Tensor) -> int:
+    """Times the persistent decode kernel's device-wide barrier gave up waiting."""
+    return int(workspace[8:12].view(torch.int32).item())
+
+
+def moe_invalid_ids(workspace: torch.Tensor) -> int:
+    """Invalid expert ids seen by the last fmlp_moe_geglu call on this workspace."""
+    off = int(lib().fmlp_moe_error_offset())
+    return int(workspace[off:off + 4].view(torch.int32).item())
+
+
+linear = fmlp_linear
+mlp2 = fmlp_mlp2
+geglu = fmlp_geglu
+moe_geglu = fmlp_moe_geglu

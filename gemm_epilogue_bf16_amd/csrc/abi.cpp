@@ -1,0 +1,402 @@
+// C ABI of the fused feed-forward library: argument validation (always before
+// anything is enqueued), device check, path choice, workspace layout and
+// launches on the caller's stream.  See include/fmlp.h for the contract.
+#include "../../include/fmlp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "kernels.h"
+
+using namespace fmlp;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local int g_path = 0;   // 0 auto, 1 decode, 2 two-GEMM, 3 small fused
+
+constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3;
+constexpr int64_t kDecodeMaxM = 16;
+constexpr int64_t kSmallMaxDim = 128;
+constexpr int64_t kMaxDim = int64_t(1) << 31;   // bound on any single dimension
+constexpr size_t kHeader = 256;                 // barrier / error words
+
+fmlp_status fail(fmlp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+fmlp_status ok() {
+  g_last_error.clear();
+  return FMLP_OK;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                      \
+  do {                                                                      \
+    if ((p) == nullptr) return fail(FMLP_E_NULL, "%s is NULL", #p);         \
+    if (!aligned16(p)) return fail(FMLP_E_ALIGN, "%s is not 16-byte aligned", #p); \
+  } while (0)
+
+#define OPTIONAL_PTR(p)                                                     \
+  do {                                                                      \
+    if ((p) != nullptr && !aligned16(p))                                    \
+      return fail(FMLP_E_ALIGN, "%s is not 16-byte aligned", #p);           \
+  } while (0)
+
+fmlp_status check_rows(const char* name, int64_t v) {
+  if (v < 0 || v >= kMaxDim) return fail(FMLP_E_SHAPE, "%s=%lld is out of range", name, (long long)v);
+  return FMLP_OK;
+}
+
+fmlp_status check_inner(const char* name, int64_t v) {
+  if (v <= 0 || v >= kMaxDim) return fail(FMLP_E_SHAPE, "%s=%lld must be positive", name, (long long)v);
+  if (v % 8 != 0) return fail(FMLP_E_ALIGN, "%s=%lld is not a multiple of 8", name, (long long)v);
+  return FMLP_OK;
+}
+
+fmlp_status check_act(int act) {
+  if (act != FMLP_ACT_NONE && act != FMLP_ACT_GELU_ERF && act != FMLP_ACT_GELU_TANH)
+    return fail(FMLP_E_ARG, "act=%d is not an fmlp_act", act);
+  return FMLP_OK;
+}
+
+#define TRY(expr)                              \
+  do {                                         \
+    fmlp_status s_ = (expr);                   \
+    if (s_ != FMLP_OK) return s_;              \
+  } while (0)
+
+// ---- device check (cached per device) ---------------------------------------
+struct DevInfo {
+  bool probed = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+DevInfo g_dev[64];
+
+fmlp_status check_device(int* cus_out = nullptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(FMLP_E_DEVICE, "no current HIP device (%s)", hipGetErrorString(e));
+  if (dev >= 64) return fail(FMLP_E_DEVICE, "device index %d unsupported", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo& d = g_dev[dev];
+  if (!d.probed) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(FMLP_E_DEVICE, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    d.gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.probed = true;
+    if (!d.gfx950) {
+      d.probed = true;
+      return fail(FMLP_E_DEVICE, "device %d is %s; this library is built for gfx950 only", dev, prop.gcnArchName);
+    }
+  }
+  if (!d.gfx950) return fail(FMLP_E_DEVICE, "current device is not gfx950");
+  if (cus_out) *cus_out = d.cus;
+  return FMLP_OK;
+}
+
+fmlp_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FMLP_E_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- tile choice --------------------------------------------------------------
+int choose_tile(int64_t M, int64_t out_cols_per_256_tile_n, int cus) {
+  // Big tiles when they alone fill the chip at least once.
+  const int64_t tiles256 = ((M + 255) / 256) * out_cols_per_256_tile_n;
+  return tiles256 >= cus ? TILE_256x256 : TILE_128x128;
+}
+
+GemmParams dense_params(const uint16_t* A, int64_t lda, const uint16_t* B0, const uint16_t* B1,
+                        const uint16_t* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                        int act) {
+  GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.A = A;
+  p.lda = lda;
+  p.B0 = B0;
+  p.B1 = B1;
+  p.bias = bias;
+  p.C = C;
+  p.ldc = ldc;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.act = act;
+  return p;
+}
+
+hipError_t gemm_linear(const uint16_t* x, const uint16_t* W, const uint16_t* b, int act, int64_t M,
+                       int64_t K, int64_t N, uint16_t* y, int cus, hipStream_t s) {
+  const int tile = choose_tile(M, (N + 255) / 256, cus);
+  return launch_gemm(GEMM_OUT_BF16, false, false, tile, dense_params(x, K, W, nullptr, b, y, N, M, N, K, act), s);
+}
+
+hipError_t gemm_geglu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int64_t M,
+                             int64_t D, int64_t H, uint16_t* m, int cus, hipStream_t s) {
+  const int tile = choose_tile(M, (H + 127) / 128, cus);
+  return launch_gemm(GEMM_OUT_GEGLU, false, false, tile, dense_params(x, D, Wg, Wu, nullptr, m, H, M, H, D, 0), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fmlp_version(void) { return 100; }
+
+const char* fmlp_status_string(fmlp_status s) {
+  switch (s) {
+    case FMLP_OK: return "FMLP_OK";
+    case FMLP_E_NULL: return "FMLP_E_NULL: a required pointer is NULL";
+    case FMLP_E_SHAPE: return "FMLP_E_SHAPE: a dimension is out of range";
+    case FMLP_E_ALIGN: return "FMLP_E_ALIGN: inner dimension not a multiple of 8 or pointer not 16-byte aligned";
+    case FMLP_E_ARG: return "FMLP_E_ARG: invalid argument";
+    case FMLP_E_WORKSPACE: return "FMLP_E_WORKSPACE: workspace missing or too small";
+    case FMLP_E_DEVICE: return "FMLP_E_DEVICE: no usable gfx950 device";
+    case FMLP_E_HIP: return "FMLP_E_HIP: HIP launch failed";
+  }
+  return "unknown fmlp_status";
+}
+
+const char* fmlp_last_error(void) { return g_last_error.c_str(); }
+
+fmlp_status fmlp_set_path(int path) {
+  if (path < kPathAuto || path > kPathSmall) return fail(FMLP_E_ARG, "path=%d is not 0..3", path);
+  g_path = path;
+  return ok();
+}
+
+// ---------------------------------------------------------------------------
+fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16* b, int act,
+                        int64_t M, int64_t K, int64_t N, fmlp_bf16* y, fmlp_stream stream) {
+  TRY(check_rows("M", M));
+  TRY(check_inner("K", K));
+  TRY(check_inner("N", N));
+  TRY(check_act(act));
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(W);
+  OPTIONAL_PTR(b);
+  REQUIRE_PTR(y);
+  if (M == 0) return ok();
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= kDecodeMaxM) {
+    GemvLayer L{x, W, nullptr, b, y, K, N, act, 0};
+    return launched(launch_gemv(L, (int)M, s), "linear (decode) launch");
+  }
+  return launched(gemm_linear(x, W, b, act, M, K, N, y, cus, s), "linear launch");
+}
+
+size_t fmlp_mlp2_workspace_size(int64_t M, int64_t K, int64_t H, int64_t N) {
+  (void)K;
+  (void)N;
+  if (M < 0 || H <= 0) return 0;
+  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+}
+
+fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* b1,
+                      const fmlp_bf16* W2, const fmlp_bf16* b2, int act, int64_t M, int64_t K,
+                      int64_t H, int64_t N, fmlp_bf16* y, void* workspace, size_t workspace_bytes,
+                      fmlp_stream stream) {
+  TRY(check_rows("M", M));
+  TRY(check_inner("K", K));
+  TRY(check_inner("H", H));
+  TRY(check_inner("N", N));
+  TRY(check_act(act));
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(W1);
+  OPTIONAL_PTR(b1);
+  REQUIRE_PTR(W2);
+  OPTIONAL_PTR(b2);
+  REQUIRE_PTR(y);
+  const bool small_ok = K <= kSmallMaxDim && H <= kSmallMaxDim && N <= kSmallMaxDim;
+  int path = g_path;
+  if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : (small_ok ? kPathSmall : kPathGemm);
+  if (path == kPathDecode && M > kDecodeMaxM)
+    return fail(FMLP_E_ARG, "decode path needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
+  if (path == kPathSmall && !small_ok)
+    return fail(FMLP_E_ARG, "small fused path needs K, H, N <= %lld", (long long)kSmallMaxDim);
+  const size_t need = (path == kPathSmall) ? 0 : fmlp_mlp2_workspace_size(M, K, H, N);
+  if (need > 0) {
+    if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FMLP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  }
+  if (M == 0) return ok();
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
+  if (path == kPathSmall)
+    return launched(launch_small_mlp2(x, W1, b1, W2, b2, act, M, (int)K, (int)H, (int)N, y, s),
+                    "mlp2 (small fused) launch");
+  if (path == kPathDecode) {
+    GemvLayer L1{x, W1, nullptr, b1, h, K, H, act, 0};
+    GemvLayer L2{h, W2, nullptr, b2, y, H, N, FMLP_ACT_NONE, 0};
+    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
+                    "mlp2 (decode, persistent) launch");
+  }
+  hipError_t e = gemm_linear(x, W1, b1, act, M, K, H, h, cus, s);
+  if (e != hipSuccess) return launched(e, "mlp2 layer-1 launch");
+  return launched(gemm_linear(h, W2, b2, FMLP_ACT_NONE, M, H, N, y, cus, s), "mlp2 layer-2 launch");
+}
+
+size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H) {
+  (void)D;
+  if (M < 0 || H <= 0) return 0;
+  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+}
+
+fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
+                       const fmlp_bf16* Wd, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
+                       void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_rows("M", M));
+  TRY(check_inner("D", D));
+  TRY(check_inner("H", H));
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(Wg);
+  REQUIRE_PTR(Wu);
+  REQUIRE_PTR(Wd);
+  REQUIRE_PTR(y);
+  int path = g_path;
+  if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : kPathGemm;
+  if (path == kPathSmall) return fail(FMLP_E_ARG, "the small fused path is mlp2-only");
+  if (path == kPathDecode && M > kDecodeMaxM)
+    return fail(FMLP_E_ARG, "decode path needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
+  const size_t need = fmlp_geglu_workspace_size(M, D, H);
+  if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FMLP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  if (M == 0) return ok();
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* m = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
+  if (path == kPathDecode) {
+    GemvLayer L1{x, Wg, Wu, nullptr, m, D, H, FMLP_ACT_NONE, 1};
+    GemvLayer L2{m, Wd, nullptr, nullptr, y, H, D, FMLP_ACT_NONE, 0};
+    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
+                    "geglu (decode, persistent) launch");
+  }
+  hipError_t e = gemm_geglu_gateup(x, Wg, Wu, M, D, H, m, cus, s);
+  if (e != hipSuccess) return launched(e, "geglu gate+up launch");
+  return launched(gemm_linear(m, Wd, nullptr, FMLP_ACT_NONE, M, H, D, y, cus, s), "geglu down launch");
+}
+
+// ---- mixture of experts --------------------------------------------------------
+namespace {
+struct MoeLayout {
+  size_t tok_of, scale_of, pos_of, group_off, tile_off, m, ytilde, total;
+};
+MoeLayout moe_layout(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k) {
+  MoeLayout L;
+  const size_t P = (size_t)T * (size_t)top_k;
+  size_t o = kHeader;
+  L.tok_of = o;    o += round_up(P * 4, 256);
+  L.scale_of = o;  o += round_up(P * 4, 256);
+  L.pos_of = o;    o += round_up(P * 4, 256);
+  L.group_off = o; o += round_up(((size_t)E + 1) * 4, 256);
+  L.tile_off = o;  o += round_up(((size_t)E + 1) * 4, 256);
+  L.m = o;         o += round_up(P * (size_t)H * 2, 256);
+  L.ytilde = o;    o += round_up(P * (size_t)D * 4, 256);
+  L.total = o;
+  return L;
+}
+constexpr int kMoeTile = TILE_256x256;
+}  // namespace
+
+size_t fmlp_moe_workspace_size(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k) {
+  if (T < 0 || D <= 0 || H <= 0 || E <= 0 || top_k <= 0) return 0;
+  return moe_layout(T, D, H, E, top_k).total;
+}
+
+size_t fmlp_moe_error_offset(void) { return 16; }
+
+fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
+                           const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int64_t T,
+                           int64_t D, int64_t H, int32_t E, int32_t top_k, fmlp_bf16* y,
+                           void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_rows("T", T));
+  TRY(check_inner("D", D));
+  TRY(check_inner("H", H));
+  if (E < 1 || E > 1024) return fail(FMLP_E_ARG, "E=%d must be in [1, 1024]", E);
+  if (top_k < 1 || top_k > 8) return fail(FMLP_E_ARG, "top_k=%d must be in [1, 8]", top_k);
+  if ((int64_t)T * top_k >= (int64_t(1) << 31))
+    return fail(FMLP_E_SHAPE, "T*top_k=%lld is too large", (long long)T * top_k);
+  REQUIRE_PTR(x);
+  if (expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
+  if (gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
+  REQUIRE_PTR(Wg);
+  REQUIRE_PTR(Wu);
+  REQUIRE_PTR(Wd);
+  REQUIRE_PTR(y);
+  const MoeLayout L = moe_layout(T, D, H, E, top_k);
+  if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(FMLP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  if (T == 0) return ok();
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  MoeRouteOut r;
+  r.tok_of = reinterpret_cast<int32_t*>(ws + L.tok_of);
+  r.scale_of = reinterpret_cast<float*>(ws + L.scale_of);
+  r.pos_of = reinterpret_cast<int32_t*>(ws + L.pos_of);
+  r.group_off = reinterpret_cast<int32_t*>(ws + L.group_off);
+  r.tile_off = reinterpret_cast<int32_t*>(ws + L.tile_off);
+  r.err = reinterpret_cast<int32_t*>(ws + fmlp_moe_error_offset());
+  uint16_t* m = reinterpret_cast<uint16_t*>(ws + L.m);
+  float* ytilde = reinterpret_cast<float*>(ws + L.ytilde);
+  const int bm = gemm_tile_bm(kMoeTile);
+  const int64_t P = T * top_k;
+
+  hipError_t e = launch_moe_route(expert_ids, gate_w, T, top_k, E, bm, r, s);
+  if (e != hipSuccess) return launched(e, "moe route launch");
+
+  GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, 0);
+  g.a_rows = r.tok_of;
+  g.group_off = r.group_off;
+  g.tile_off = r.tile_off;
+  g.groups = E;
+  g.strideB = H * D;
+  g.tiles_m = (int)((P + bm - 1) / bm + E);
+  e = launch_gemm(GEMM_OUT_GEGLU, true, true, kMoeTile, g, s);
+  if (e != hipSuccess) return launched(e, "moe gate+up launch");
+
+  GemmParams d = dense_params(m, H, Wd, nullptr, nullptr, ytilde, D, P, D, H, 0);
+  d.group_off = r.group_off;
+  d.tile_off = r.tile_off;
+  d.groups = E;
+  d.strideB = D * H;
+  d.row_scale = r.scale_of;
+  d.tiles_m = (int)((P + bm - 1) / bm + E);
+  e = launch_gemm(GEMM_OUT_F32_SCALED, false, true, kMoeTile, d, s);
+  if (e != hipSuccess) return launched(e, "moe down launch");
+
+  return launched(launch_moe_combine(ytilde, r.pos_of, T, top_k, D, y, s), "moe combine launch");
+}
+
+}  // extern "C"

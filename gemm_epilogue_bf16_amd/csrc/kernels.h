@@ -1,0 +1,102 @@
+// Internal launch interface between the C ABI (abi.cpp) and the gfx950
+// kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmlp {
+
+// ---------------------------------------------------------------------------
+// Tiled MFMA GEMM:  C[rows, N] = epilogue(A[rows, K] . B[N, K]^T)
+// ---------------------------------------------------------------------------
+enum GemmOut : int {
+  GEMM_OUT_BF16 = 0,        // C bf16 = act(acc + bias)
+  GEMM_OUT_GEGLU = 1,       // B0 = Wg, B1 = Wu; C bf16 [rows, N] = gelu_tanh(g) * u
+  GEMM_OUT_F32_SCALED = 2,  // C fp32 = acc * row_scale[row]
+};
+
+struct GemmParams {
+  const uint16_t* A;       // activations, row stride lda (elements)
+  int64_t lda;
+  const uint16_t* B0;      // weights [N, K] (row stride K)
+  const uint16_t* B1;      // second weight set for GEMM_OUT_GEGLU
+  int64_t strideB;         // elements between consecutive groups' weights (grouped mode)
+  const uint16_t* bias;    // [N] or nullptr (GEMM_OUT_BF16 only)
+  void* C;                 // output, row stride ldc (elements)
+  int64_t ldc;
+  int64_t M, N, K;         // M: rows (dense mode)
+  int act;                 // Act, GEMM_OUT_BF16 only
+  // gather / grouped (mixture of experts)
+  const int32_t* a_rows;     // gather: A row of each logical row, or nullptr
+  const int32_t* group_off;  // grouped: [groups+1] logical row offsets
+  const int32_t* tile_off;   // grouped: [groups+1] prefix of m-tiles per group
+  int groups;
+  const float* row_scale;    // GEMM_OUT_F32_SCALED: per logical row
+  // launch geometry, filled by launch_gemm
+  int tiles_m, tiles_n, group_m;
+};
+
+// Tile configurations compiled in.
+enum GemmTile : int {
+  TILE_128x128 = 0,   // 4 waves, 64x64 per wave
+  TILE_256x256 = 1,   // 8 waves, 128x64 per wave
+  TILE_COUNT
+};
+
+int gemm_tile_bm(int tile);
+int gemm_tile_bn(int tile);
+// Launch one GEMM.  For grouped mode p.tiles_m must be an upper bound on the
+// number of m tiles over all groups (extra blocks exit at once).
+hipError_t launch_gemm(int out_kind, bool gather, bool grouped, int tile, GemmParams p,
+                       hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Skinny-M (decode) path: M <= 16 rows, weights streamed once with 16-byte
+// loads, fp32 MFMA accumulation, fixed-order cross-wave reduction.
+// ---------------------------------------------------------------------------
+struct GemvLayer {
+  const uint16_t* x;     // [M, K]
+  const uint16_t* W0;    // [N, K]
+  const uint16_t* W1;    // [N, K] (GeGLU up) or nullptr
+  const uint16_t* bias;  // [N] or nullptr
+  uint16_t* y;           // [M, N]
+  int64_t K, N;
+  int act;               // Act; ignored for GeGLU layers
+  int geglu;             // 1: y = gelu_tanh(x W0^T) * (x W1^T)
+};
+
+// One layer, one launch.
+hipError_t launch_gemv(const GemvLayer& L, int M, hipStream_t s);
+// Two dependent layers in one persistent (cooperative) launch with a device-wide
+// barrier between them.  bar points at 3 zeroed uint32 words (count,
+// generation, timeout count) that the kernel leaves consistent.
+hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M,
+                                   uint32_t* bar, hipStream_t s);
+// Largest grid the persistent kernel can have resident at once (0 = unknown).
+int gemv2_persistent_max_blocks();
+
+// ---------------------------------------------------------------------------
+// Small fused MLP: K, H, N <= 128, any M; one launch.
+// ---------------------------------------------------------------------------
+hipError_t launch_small_mlp2(const uint16_t* x, const uint16_t* W1, const uint16_t* b1,
+                             const uint16_t* W2, const uint16_t* b2, int act, int64_t M,
+                             int K, int H, int N, uint16_t* y, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Mixture of experts: routing buckets and weighted combine.
+// ---------------------------------------------------------------------------
+struct MoeRouteOut {
+  int32_t* tok_of;      // [P] token of each sorted pair position
+  float* scale_of;      // [P] gate weight of each sorted pair position
+  int32_t* pos_of;      // [P] sorted position of pair p (-1: invalid id)
+  int32_t* group_off;   // [E+1]
+  int32_t* tile_off;    // [E+1] prefix of ceil(count/BM)
+  int32_t* err;         // invalid-id count
+};
+hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, int top_k, int E,
+                            int bm, const MoeRouteOut& o, hipStream_t s);
+hipError_t launch_moe_combine(const float* ytilde, const int32_t* pos_of, int64_t T, int top_k,
+                              int64_t D, uint16_t* y, hipStream_t s);
+
+}  // namespace fmlp

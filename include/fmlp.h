@@ -1,0 +1,157 @@
+/*
+ * fmlp.h -- C ABI of the fused transformer feed-forward library for AMD
+ * MI355X (CDNA4, gfx950).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  Data:       all matrices are dense, row-major and contiguous.  Weights are
+ *              stored [out, in] as nn.Linear stores them, and are read as
+ *              stored: the GEMM walks both operands along K, so no transpose
+ *              copy ever runs ("Profiling in PyTorch (Part 2): From nn.Linear
+ *              to a Fused MLP", section "Where did the transpose go? Kernel
+ *              layouts and pre-ops": a transpose only rewrites strides and the
+ *              GEMM variant that reads the weight in transposed order is picked).
+ *              Leading dims of activations are flattened by the caller:
+ *              M = batch * seq (same page, section "Why are there two kinds of
+ *              GEMM kernels?").
+ *  Types:      activations, weights, biases and outputs are bf16, passed as raw
+ *              16-bit patterns (fmlp_bf16).  Accumulation is fp32; the output is
+ *              rounded to bf16 round-to-nearest-even.  Hidden activations that
+ *              feed a second GEMM (h, m) are rounded to bf16 once.
+ *  Pointers:   device pointers (hipMalloc / torch CUDA tensors) on the current
+ *              HIP device, 16-byte aligned.  The caller owns every buffer,
+ *              including outputs and workspaces; the library never allocates
+ *              on a call and keeps no pointer after it returns.  Outputs must
+ *              not alias inputs.
+ *  Shapes:     every inner dimension (K, H, N, D) must be a positive multiple
+ *              of 8 (16-byte rows), the analogue of the "align8" GEMM variants
+ *              named on the page above; the token count M (or T) may be any
+ *              value >= 0 (M == 0 is a no-op).
+ *  Streams:    fmlp_stream is a hipStream_t (NULL = the null stream).  Every
+ *              call only enqueues work on that stream and returns; FMLP_OK means
+ *              "enqueued".  Device faults surface at the caller's next sync.
+ *  Errors:     a call validates every argument before it enqueues anything; on
+ *              an error nothing is enqueued and the outputs are untouched.  A
+ *              failed launch returns FMLP_E_HIP.  fmlp_last_error() gives a
+ *              thread-local detail string for the last failing call.
+ *  Threads:    calls are thread-safe.  Calls that share a workspace must be
+ *              ordered on one stream.
+ */
+#ifndef FMLP_H_
+#define FMLP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t fmlp_bf16;  /* raw bf16 bit pattern */
+typedef void* fmlp_stream;   /* a hipStream_t */
+
+typedef enum {
+  FMLP_ACT_NONE = 0,
+  FMLP_ACT_GELU_ERF = 1,   /* exact GELU  z*Phi(z) */
+  FMLP_ACT_GELU_TANH = 2   /* z/2 * (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+} fmlp_act;
+
+typedef enum {
+  FMLP_OK = 0,
+  FMLP_E_NULL = 1,       /* a required pointer is NULL */
+  FMLP_E_SHAPE = 2,      /* a dimension is negative/zero or too large */
+  FMLP_E_ALIGN = 3,      /* an inner dim is not a multiple of 8, or a pointer is not 16-B aligned */
+  FMLP_E_ARG = 4,        /* bad enum / top_k / expert count / path */
+  FMLP_E_WORKSPACE = 5,  /* workspace NULL or smaller than the *_workspace_size() value */
+  FMLP_E_DEVICE = 6,     /* no usable gfx950 device current */
+  FMLP_E_HIP = 7         /* a HIP launch failed; see fmlp_last_error() */
+} fmlp_status;
+
+/*
+ * y[M,N] = act(x[M,K] . W[N,K]^T + b[N])
+ *
+ * One nn.Linear forward with its epilogue: bias add and activation run on the
+ * fp32 accumulator in registers, and only the final tile is written to HBM
+ * ("Profiling in PyTorch (Part 2)", sections "From matmul-add to Linear" and
+ * "Why are there no separate mul and add kernels?").  b may be NULL (no bias;
+ * the page's bias-free Linears).  act is an fmlp_act.  Exactly one kernel
+ * launch.  No workspace.
+ */
+fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16* b, int act,
+                        int64_t M, int64_t K, int64_t N, fmlp_bf16* y, fmlp_stream stream);
+
+/*
+ * y[M,N] = act(x[M,K] . W1[H,K]^T + b1[H]) . W2[N,H]^T + b2[N]
+ *
+ * The two-layer MLP with the activation between the layers only (ainews.cool
+ * "PyTorch fused MLP efficiency", section "technical deep dive": W1*X+b1,
+ * activation, W2*(.)+b2).  b1 and/or b2 may be NULL.  The hidden activation h
+ * is rounded to bf16 once before the second GEMM.
+ * Paths (chosen from the shape): M <= 16: one persistent decode launch;
+ * K, H, N <= 128: one fused small-MLP launch; otherwise two GEMM launches with
+ * h in the workspace.  workspace must hold fmlp_mlp2_workspace_size(M,K,H,N)
+ * bytes (it may be NULL when that size is 0) and its first 256 bytes must be
+ * zero before the first call that uses it; every call leaves them zero again.
+ */
+fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* b1,
+                      const fmlp_bf16* W2, const fmlp_bf16* b2, int act,
+                      int64_t M, int64_t K, int64_t H, int64_t N,
+                      fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_mlp2_workspace_size(int64_t M, int64_t K, int64_t H, int64_t N);
+
+/*
+ * y[M,D] = (gelu_tanh(x[M,D] . Wg[H,D]^T) * (x . Wu[H,D]^T)) . Wd[D,H]^T
+ *
+ * The GeGLU feed-forward block, all projections bias-free ("Profiling in
+ * PyTorch (Part 2)", section "Stacking three Linears: the MLP").  The gate and
+ * up projections share each x tile and apply gelu(g)*u in registers, so g and
+ * u never reach HBM; m is rounded to bf16 once.  Paths: M <= 16: one
+ * persistent decode launch; otherwise a fused gate+up launch writing m to the
+ * workspace and a down-projection launch.  Workspace rules as fmlp_mlp2.
+ */
+fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
+                       const fmlp_bf16* Wd, int64_t M, int64_t D, int64_t H,
+                       fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H);
+
+/*
+ * y[t,:] = sum_{j<top_k} gate_w[t,j] * geglu_{expert_ids[t,j]}(x[t,:])
+ *
+ * Mixture of GeGLU experts (ainews.cool "PyTorch fused MLP efficiency",
+ * section "architectural impact": tokens are routed to several experts, each an
+ * MLP).  x [T,D]; expert_ids int32 [T,top_k] and gate_w fp32 [T,top_k] are
+ * device arrays; Wg, Wu are stacked [E,H,D] and Wd is [E,D,H].  1 <= top_k <= 8,
+ * 1 <= E <= 1024.  Routed pairs are bucketed per expert (stable in token
+ * order), each expert runs the fused gate+up and down GEMMs over its rows, and
+ * the weighted combine sums the top_k contributions of a token in slot order in
+ * fp32 (deterministic; no atomics).  An expert id outside [0,E) contributes
+ * nothing and is counted in the workspace error word (fmlp_moe_error_count
+ * documents where).  Workspace: fmlp_moe_workspace_size(T,D,H,E,top_k) bytes.
+ */
+fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
+                           const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd,
+                           int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k,
+                           fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_moe_workspace_size(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k);
+/* Byte offset, inside the MoE workspace, of the int32 count of invalid expert ids
+ * seen by the last call (read it after a stream sync). */
+size_t fmlp_moe_error_offset(void);
+
+/*
+ * Path override for tests and benchmarks (thread-local; applies to the calling
+ * thread's later fmlp_mlp2 / fmlp_geglu calls):
+ *   0 = automatic (default), 1 = force the decode path (needs M <= 16),
+ *   2 = force the two-GEMM path, 3 = force the fused small-MLP path (mlp2 only).
+ * A forced path that does not apply to a call makes it return FMLP_E_ARG.
+ */
+fmlp_status fmlp_set_path(int path);
+
+const char* fmlp_status_string(fmlp_status s);
+const char* fmlp_last_error(void);
+int fmlp_version(void);  /* major*10000 + minor*100 + patch */
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* FMLP_H_ */

@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads without a GPU, exports every function
+include/fmlp.h declares, and rejects bad arguments with the documented status
+before touching any device.  No call here reaches a kernel launch: every call
+either fails validation or is an M == 0 no-op, so the suite is safe anywhere."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fmlp.h")
+LIBPATH = os.path.join(ROOT, "gemm_epilogue_bf16_amd", "libfmlp.so")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_ARG, E_WS, E_DEV, E_HIP = range(8)
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fmlp_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIBPATH):
+        from gemm_epilogue_bf16_amd.build import build
+
+        build()
+    import gemm_epilogue_bf16_amd as F
+
+    return F.lib()
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_moe_geglu"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+    assert L.fmlp_version() >= 100
+
+
+def test_status_strings(L):
+    for s in range(8):
+        assert L.fmlp_status_string(s).decode().startswith("FMLP_")
+
+
+# fake, 16-byte aligned, never dereferenced
+X, W, B, Y, WS = 0x10000, 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def _err(L):
+    return L.fmlp_last_error().decode()
+
+
+@pytest.mark.parametrize("args,status,msg", [
+    ((X, W, None, 0, 4, 30, 8, Y, None), E_ALIGN, "K=30"),
+    ((X, W, None, 0, 4, 32, 12, Y, None), E_ALIGN, "N=12"),
+    ((X, W, None, 0, 4, 0, 8, Y, None), E_SHAPE, "K=0"),
+    ((X, W, None, 0, -1, 32, 8, Y, None), E_SHAPE, "M=-1"),
+    ((X, W, None, 7, 4, 32, 8, Y, None), E_ARG, "act=7"),
+    ((None, W, None, 0, 4, 32, 8, Y, None), E_NULL, "x is NULL"),
+    ((X, None, None, 0, 4, 32, 8, Y, None), E_NULL, "W is NULL"),
+    ((X, W, None, 0, 4, 32, 8, None, None), E_NULL, "y is NULL"),
+    ((X + 2, W, None, 0, 4, 32, 8, Y, None), E_ALIGN, "x is not 16-byte aligned"),
+    ((X, W, B + 8, 0, 4, 32, 8, Y, None), E_ALIGN, "b is not 16-byte aligned"),
+])
+def test_linear_validation(L, args, status, msg):
+    assert L.fmlp_linear(*args) == status
+    assert msg in _err(L)
+
+
+def test_linear_zero_rows_is_a_noop(L):
+    assert L.fmlp_linear(X, W, None, 0, 0, 32, 8, Y, None) == OK
+
+
+def test_mlp2_validation(L):
+    need = L.fmlp_mlp2_workspace_size(4, 32, 64, 32)
+    assert need == 256 + 512  # header + 4*64 bf16 rounded to 256
+    # workspace NULL / too small
+    assert L.fmlp_mlp2(X, W, B, W, B, 1, 20, 256, 256, 256, Y, None, 0, None) == E_WS
+    assert L.fmlp_mlp2(X, W, B, W, B, 1, 20, 256, 256, 256, Y, WS, 100, None) == E_WS
+    assert "needs" in _err(L)
+    # the small fused path needs no workspace; a forced wrong path is rejected
+    assert L.fmlp_set_path(1) == OK
+    try:
+        assert L.fmlp_mlp2(X, W, B, W, B, 1, 17, 32, 64, 32, Y, WS, 1 << 20, None) == E_ARG
+        assert "M <= 16" in _err(L)
+    finally:
+        L.fmlp_set_path(0)
+    assert L.fmlp_set_path(3) == OK
+    try:
+        assert L.fmlp_mlp2(X, W, B, W, B, 1, 17, 256, 64, 32, Y, WS, 1 << 20, None) == E_ARG
+    finally:
+        L.fmlp_set_path(0)
+    assert L.fmlp_set_path(9) == E_ARG
+    assert L.fmlp_mlp2(X, W, B, W, B, 5, 4, 32, 64, 32, Y, WS, 1 << 20, None) == E_ARG
+    assert L.fmlp_mlp2(X, W, B, W, B, 1, 4, 32, 60, 32, Y, WS, 1 << 20, None) == E_ALIGN
+    assert L.fmlp_mlp2(X, W, B, None, B, 1, 4, 32, 64, 32, Y, WS, 1 << 20, None) == E_NULL
+
+
+def test_geglu_validation(L):
+    need = L.fmlp_geglu_workspace_size(8192, 768, 3072)
+    assert need == 256 + 8192 * 3072 * 2
+    assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, None, 0, None) == E_WS
+    assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, WS + 8, 1 << 20, None) == E_ALIGN
+    assert L.fmlp_geglu(X, W, None, W, 16, 64, 128, Y, WS, 1 << 20, None) == E_NULL
+    assert L.fmlp_geglu(X, W, W, W, 16, 60, 128, Y, WS, 1 << 20, None) == E_ALIGN
+    assert L.fmlp_set_path(3) == OK
+    try:
+        assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, WS, 1 << 20, None) == E_ARG
+    finally:
+        L.fmlp_set_path(0)
+    assert L.fmlp_geglu(X, W, W, W, 0, 64, 128, Y, WS, 1 << 20, None) == OK
+
+
+def test_moe_validation(L):
+    T, D, H, E, k = 4096, 4096, 14336, 8, 2
+    P = T * k
+    need = L.fmlp_moe_workspace_size(T, D, H, E, k)
+    assert need >= 256 + 3 * P * 4 + P * H * 2 + P * D * 4
+    ids, gw = 0x60000, 0x70000
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, 0, k, Y, WS, need, None) == E_ARG
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, E, 9, Y, WS, need, None) == E_ARG
+    assert L.fmlp_moe_geglu(X, None, gw, W, W, W, T, D, H, E, k, Y, WS, need, None) == E_NULL
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, E, k, Y, WS, need - 1, None) == E_WS
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, 4092, H, E, k, Y, WS, need, None) == E_ALIGN
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, 0, D, H, E, k, Y, WS, need, None) == OK
+    assert L.fmlp_moe_error_offset() < 256
+
+
+def test_no_fallback_without_library(tmp_path, monkeypatch):
+    """The binding raises when the library is missing: there is no CPU path."""
+    import gemm_epilogue_bf16_amd as F
+
+    monkeypatch.setattr(F, "_lib", None)
+    monkeypatch.setattr(F, "library_path", lambda: str(tmp_path / "absent.so"))
+    with pytest.raises(F.FmlpError, match="not built"):
+        F.lib()

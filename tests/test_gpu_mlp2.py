@@ -1,0 +1,143 @@
+"""fmlp_mlp2 on the GPU against the fp64 oracle, on every path (persistent
+decode, single-launch small MLP, two GEMMs), at the tiny and decode workloads'
+full sizes and on random ragged shapes; plus fused == unfused and the bias pins."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import gemm_epilogue_bf16_amd as F
+import oracle
+from gpu_util import DEV, assert_parity, bf16_ulp, bits_of, f64_of, f64_of_bits, rand_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_inputs(t):
+    return {k: to_dev(v) for k, v in t.items()}
+
+
+def _oracle(t, act):
+    g = lambda k: None if k not in t else f64_of_bits(t[k])  # noqa: E731
+    return oracle.mlp2(g("x"), g("W1"), g("b1"), g("W2"), g("b2"), act)
+
+
+def _run(d, act, path="auto", ws=None):
+    with F.force_path(path):
+        y = F.fmlp_mlp2(d["x"], d["W1"], d.get("b1"), d["W2"], d.get("b2"), act, workspace=ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("path", ["auto", "small", "gemm"])
+def test_tiny_workload_full(path):
+    w = datagen.workload("tiny")
+    t = datagen.make_inputs(w, seed=0)
+    print(f"case {w.name} path={path}", flush=True)
+    y = _run(_dev_inputs(t), w.act, path)
+    assert_parity(y, _oracle(t, w.act), f"{w.name} {path}")
+
+
+@pytest.mark.parametrize("name", ["decode1", "decode16"])
+@pytest.mark.parametrize("path", ["auto", "gemm"])
+def test_decode_workload_full(name, path):
+    w = datagen.workload(name)
+    t = datagen.make_inputs(w, seed=0)
+    d = _dev_inputs(t)
+    ws = F.workspace_for(DEV, F.fmlp_mlp2_workspace_size(w.M, w.K, w.H, w.N))
+    print(f"case {w.name} path={path}", flush=True)
+    y = _run(d, w.act, path, ws)
+    assert_parity(y, _oracle(t, w.act), f"{w.name} {path}")
+    assert F.barrier_timeouts(ws) == 0
+
+
+SHAPES = [
+    # (M, K, H, N)
+    (1, 8, 8, 8), (1, 64, 200, 40), (3, 136, 520, 264), (16, 512, 256, 1024), (16, 1024, 4096, 64),
+    (9, 4096, 1024, 4096), (17, 32, 64, 32), (40, 128, 128, 128), (100, 96, 40, 120),
+    (257, 256, 512, 136), (600, 768, 1024, 392),
+]
+
+
+@pytest.mark.parametrize("M,K,H,N", SHAPES)
+@pytest.mark.parametrize("act", ["gelu_erf", "gelu_tanh"])
+def test_mlp2_random(M, K, H, N, act):
+    rng = np.random.default_rng(M * 7919 + K * 31 + H * 3 + N)
+    t = {"x": rand_bf16(rng, (M, K)),
+         "W1": rand_bf16(rng, (H, K), K ** -0.5, "uniform"), "b1": rand_bf16(rng, (H,), 0.3, "uniform"),
+         "W2": rand_bf16(rng, (N, H), H ** -0.5, "uniform"), "b2": rand_bf16(rng, (N,), 0.3, "uniform")}
+    d = _dev_inputs(t)
+    ref = _oracle(t, act)
+    paths = ["auto", "gemm"]
+    if M <= 16:
+        paths.append("decode")
+    if max(K, H, N) <= 128:
+        paths.append("small")
+    for p in paths:
+        print(f"case mlp2 M={M} K={K} H={H} N={N} act={act} path={p}", flush=True)
+        assert_parity(_run(d, act, p), ref, f"mlp2 {M}x{K}x{H}x{N} {p}")
+
+
+@pytest.mark.parametrize("M,path", [(1, "decode"), (16, "decode"), (64, "small"), (300, "gemm")])
+def test_mlp2_no_biases(M, path):
+    rng = np.random.default_rng(M)
+    K, H, N = 64, 128, 96
+    t = {"x": rand_bf16(rng, (M, K)), "W1": rand_bf16(rng, (H, K), 0.125, "uniform"),
+         "W2": rand_bf16(rng, (N, H), 0.09, "uniform")}
+    print(f"case mlp2 no-bias M={M} path={path}", flush=True)
+    assert_parity(_run(_dev_inputs(t), "gelu_tanh", path), _oracle(t, "gelu_tanh"), f"no-bias {path}")
+
+
+@pytest.mark.parametrize("M,path", [(1, "decode"), (16, "decode"), (64, "small"), (300, "gemm")])
+def test_mlp2_bias_pins(M, path):
+    """W1 = 0 -> h = act(b1); W2 = I, b2 = 0 -> y = bf16(act(b1)) for every row."""
+    rng = np.random.default_rng(M + 1)
+    K = H = N = 64
+    b1 = rand_bf16(rng, (H,), 2.0, "uniform")
+    t = {"x": rand_bf16(rng, (M, K)), "W1": np.zeros((H, K), np.uint16), "b1": b1,
+         "W2": datagen.rne_bf16(np.eye(N, H, dtype=np.float32)), "b2": np.zeros(N, np.uint16)}
+    for act in ("gelu_erf", "gelu_tanh"):
+        print(f"case mlp2 bias pin M={M} path={path} act={act}", flush=True)
+        y = f64_of(_run(_dev_inputs(t), act, path))
+        want = oracle.activation(f64_of_bits(b1), act)
+        assert np.all(np.abs(y - want[None, :]) <= bf16_ulp(want)[None, :])
+
+
+@pytest.mark.parametrize("M,path", [(1, "decode"), (16, "decode"), (300, "gemm"), (512, "small")])
+def test_fused_equals_unfused(M, path):
+    """One fused call == fmlp_linear(act) then fmlp_linear: both round h to
+    bf16 once, at the same place."""
+    rng = np.random.default_rng(M + 2)
+    K, H, N = (128, 128, 64) if path == "small" else (512, 1024, 256)
+    t = {"x": rand_bf16(rng, (M, K)),
+         "W1": rand_bf16(rng, (H, K), K ** -0.5, "uniform"), "b1": rand_bf16(rng, (H,), 0.3, "uniform"),
+         "W2": rand_bf16(rng, (N, H), H ** -0.5, "uniform"), "b2": rand_bf16(rng, (N,), 0.3, "uniform")}
+    d = _dev_inputs(t)
+    print(f"case fused==unfused M={M} path={path}", flush=True)
+    fused = _run(d, "gelu_erf", path)
+    h = F.fmlp_linear(d["x"], d["W1"], d["b1"], "gelu_erf")
+    unfused = F.fmlp_linear(h, d["W2"], d["b2"], "none")
+    torch.cuda.synchronize()
+    a, b = f64_of(fused), f64_of(unfused)
+    if path == "gemm":
+        assert np.array_equal(bits_of(fused), bits_of(unfused))
+    else:
+        # different accumulation order: agree to the final rounding
+        assert np.max(np.abs(a - b)) <= 2 * bf16_ulp(np.max(np.abs(b)))
+
+
+def test_decode_determinism_and_repeat():
+    """The persistent kernel is bitwise reproducible and its barrier words stay
+    consistent over many back-to-back calls on one workspace."""
+    w = datagen.workload("decode1")
+    t = datagen.make_inputs(w, seed=0)
+    d = _dev_inputs(t)
+    ws = F.workspace_for(DEV, F.fmlp_mlp2_workspace_size(16, 4096, 4096, 4096))
+    print("case decode repeat x50", flush=True)
+    first = bits_of(_run(d, w.act, "decode", ws))
+    for _ in range(50):
+        y = F.fmlp_mlp2(d["x"], d["W1"], d["b1"], d["W2"], d["b2"], w.act, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(y), first)
+    hdr = ws[:12].view(torch.int32).cpu().numpy()
+    assert hdr[0] == 0 and hdr[2] == 0, hdr   # count back to 0, no timeouts

@@ -1,0 +1,126 @@
+"""fmlp_moe_geglu on the GPU against the fp64 oracle: small random routings
+(ragged and empty experts, duplicate ids, top_k 1..3), reductions to the dense
+GeGLU, invalid-id accounting, and the 8-expert 4096-token workload on sampled
+tokens."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import gemm_epilogue_bf16_amd as F
+import oracle
+from gpu_util import DEV, assert_parity, bits_of, f64_of, f64_of_bits, rand_bf16, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _experts(rng, E, D, H):
+    Wg = np.stack([rand_bf16(rng, (H, D), D ** -0.5, "uniform") for _ in range(E)])
+    Wu = np.stack([rand_bf16(rng, (H, D), D ** -0.5, "uniform") for _ in range(E)])
+    Wd = np.stack([rand_bf16(rng, (D, H), H ** -0.5, "uniform") for _ in range(E)])
+    return Wg, Wu, Wd
+
+
+def _oracle(x, ids, gw, Wg, Wu, Wd):
+    return oracle.moe_geglu(f64_of_bits(x), ids, gw.astype(np.float64),
+                            lambda e: (f64_of_bits(Wg[e]), f64_of_bits(Wu[e]), f64_of_bits(Wd[e])))
+
+
+def _run(x, ids, gw, Wg, Wu, Wd, ws=None):
+    y = F.fmlp_moe_geglu(to_dev(x), to_dev(ids, torch.int32), to_dev(gw, torch.float32),
+                         to_dev(Wg), to_dev(Wu), to_dev(Wd), workspace=ws)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("T,D,H,E,k", [
+    (1, 64, 64, 2, 1), (5, 64, 128, 4, 2), (37, 128, 96, 4, 2), (300, 256, 512, 8, 2),
+    (129, 64, 200, 3, 3), (1000, 128, 256, 16, 2), (64, 96, 64, 1, 1),
+])
+def test_moe_random(T, D, H, E, k):
+    rng = np.random.default_rng(T * 17 + D + H + E + k)
+    x = rand_bf16(rng, (T, D))
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    gw = rng.random((T, k)).astype(np.float32)
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    print(f"case moe T={T} D={D} H={H} E={E} k={k}", flush=True)
+    assert_parity(_run(x, ids, gw, Wg, Wu, Wd), _oracle(x, ids, gw, Wg, Wu, Wd), f"moe {T}x{D}x{H} E{E} k{k}")
+
+
+def test_moe_skewed_and_empty_experts():
+    rng = np.random.default_rng(1)
+    T, D, H, E, k = 700, 128, 256, 8, 2
+    x = rand_bf16(rng, (T, D))
+    ids = np.where(rng.random((T, k)) < 0.9, 5, 2).astype(np.int32)   # experts 5 and 2 only
+    ids[:3] = [[0, 7], [7, 7], [0, 0]]                                # duplicates
+    gw = rng.random((T, k)).astype(np.float32)
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    print("case moe skewed/empty experts", flush=True)
+    assert_parity(_run(x, ids, gw, Wg, Wu, Wd), _oracle(x, ids, gw, Wg, Wu, Wd), "moe skewed")
+
+
+def test_moe_top1_equals_dense_geglu():
+    rng = np.random.default_rng(2)
+    T, D, H, E = 250, 256, 512, 4
+    x = rand_bf16(rng, (T, D))
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    dense = F.fmlp_geglu(to_dev(x), to_dev(Wg[3]), to_dev(Wu[3]), to_dev(Wd[3]))
+    ids = np.full((T, 1), 3, np.int32)
+    gw = np.ones((T, 1), np.float32)
+    print("case moe top1 == dense", flush=True)
+    y = _run(x, ids, gw, Wg, Wu, Wd)
+    # same m rounding; y differs only by the fp32 -> bf16 round of the combine
+    assert np.max(np.abs(f64_of(y) - f64_of(dense))) <= 1e-2 * np.max(np.abs(f64_of(dense))) + 1e-3
+
+
+def test_moe_invalid_ids_counted_and_skipped():
+    rng = np.random.default_rng(3)
+    T, D, H, E, k = 50, 64, 64, 4, 2
+    x = rand_bf16(rng, (T, D))
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    ids[4, 1] = 9
+    ids[10, 0] = -1
+    gw = rng.random((T, k)).astype(np.float32)
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    ws = F.workspace_for(DEV, F.fmlp_moe_workspace_size(T, D, H, E, k))
+    print("case moe invalid ids", flush=True)
+    y = _run(x, ids, gw, Wg, Wu, Wd, ws)
+    assert F.moe_invalid_ids(ws) == 2
+    ok_ids = ids.copy()
+    gw0 = gw.copy()
+    bad = (ids < 0) | (ids >= E)
+    ok_ids[bad] = 0
+    gw0[bad] = 0.0          # an invalid pair contributes nothing
+    assert_parity(y, _oracle(x, ok_ids, gw0, Wg, Wu, Wd), "moe invalid ids")
+
+
+def test_moe_determinism():
+    rng = np.random.default_rng(4)
+    T, D, H, E, k = 513, 256, 384, 8, 2
+    x = rand_bf16(rng, (T, D))
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    gw = rng.random((T, k)).astype(np.float32)
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    print("case moe determinism", flush=True)
+    assert np.array_equal(bits_of(_run(x, ids, gw, Wg, Wu, Wd)), bits_of(_run(x, ids, gw, Wg, Wu, Wd)))
+
+
+@pytest.mark.slow
+def test_moe_workload_sampled_tokens():
+    """The 8 x (4096/14336) top-2 workload at 4096 tokens, checked on a token
+    sample (tokens are independent)."""
+    w = datagen.workload("moe")
+    x = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
+    ids, gw = datagen.make_routes(w.M, w.E, w.top_k, seed=0)
+    experts = [datagen.expert_weights(w, e, seed=0) for e in range(w.E)]
+    Wg = torch.stack([to_dev(e[0]) for e in experts])
+    Wu = torch.stack([to_dev(e[1]) for e in experts])
+    Wd = torch.stack([to_dev(e[2]) for e in experts])
+    print(f"case {w.name} (sampled tokens)", flush=True)
+    y = F.fmlp_moe_geglu(to_dev(x), to_dev(ids, torch.int32), to_dev(gw, torch.float32), Wg, Wu, Wd)
+    torch.cuda.synchronize()
+    toks = np.array([0, 1, 2, 511, 1024, 2047, 3000, 4095])
+    ref = oracle.moe_geglu(f64_of_bits(x[toks]), ids[toks], gw[toks].astype(np.float64),
+                           lambda e: tuple(f64_of_bits(a) for a in experts[e]))
+    assert_parity(y[torch.from_numpy(toks).to(DEV)], ref, f"{w.name} tokens")
+    assert np.isfinite(f64_of(y)).all()
