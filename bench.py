@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Throughput of the fused feed-forward path on one MI355X (gfx950).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward of the workload's whole feed-forward block through the
+C ABI (one fmlp_* call) on synthetic seeded bf16 inputs already resident in
+HBM.  Default workload: the decode two-layer MLP 4096 -> 4096 -> 4096 with exact
+GELU and biases at 1 token (the 4096-wide GELU MLP at batch 1 of ainews.cool
+"PyTorch fused MLP efficiency", section "benchmark data").  Its 64 MiB of
+weights fit the 256 MB Infinity Cache, so by default steps rotate through
+enough weight copies (>= 1 GiB) that every step reads its weights from HBM.
+
+Prints ONE JSON line: metric/value (TFLOP/s), ms_per_step, the roofline of the
+dominant kernel (HIP-event time over the timed region) and the fp64 CPU
+oracle timed on a bounded sample on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-MLP TFLOP/s & µs/forward (bf16) + % of MFMA or HBM roofline, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+COLD_BYTES = 1 << 30           # rotate weight copies until this many bytes (4x the 256 MB MALL)
+# the page's fused 4096-wide GELU MLP at batch 1 on H100: 8.1 us (context only)
+PAGE_H100_FUSED_US = 8.1
+
+KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "decode.hip", "small_mlp.hip", "moe.hip"]
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gemm_epilogue_bf16_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workload set-up: returns a Case with bound launches (one per weight copy)
+# ---------------------------------------------------------------------------
+class Case:
+    def __init__(self, w, calls, kernel, launches, path, copies, oracle_fn, oracle_sample):
+        self.w = w
+        self.calls = calls
+        self.kernel = kernel          # dominant kernel (symbol prefix in traces)
+        self.launches = launches      # kernel launches per step
+        self.path = path
+        self.copies = copies
+        self.oracle_fn = oracle_fn    # () -> None, runs the oracle on the sample
+        self.oracle_sample = oracle_sample  # (description, fraction of one step's flops)
+
+
+def _dev(bits, torch, dev, dtype=None):
+    import torch as _t
+    if dtype is None:
+        return _t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(_t.bfloat16).to(dev)
+    return _t.from_numpy(np.ascontiguousarray(bits)).to(dev)
+
+
+def _copies_for(weight_bytes: int, cold: bool) -> int:
+    if not cold:
+        return 1
+    return max(1, -(-COLD_BYTES // weight_bytes))
+
+
+def setup_case(name: str, cold: bool, dev, path: str):
+    import torch
+
+    import datagen
+    import gemm_epilogue_bf16_amd as F
+
+    w = datagen.workload(name)
+    f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)  # noqa: E731
+    R = _copies_for(w.weight_bytes, cold)
+
+    if w.op in ("mlp2", "geglu"):
+        t = datagen.make_inputs(w, seed=0)
+        x = _dev(t["x"], torch, dev)
+        base = {k: _dev(v, torch, dev) for k, v in t.items() if k != "x"}
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+        y = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+        calls = []
+        if w.op == "mlp2":
+            ws = F.workspace_for(dev, F.fmlp_mlp2_workspace_size(w.M, w.K, w.H, w.N))
+            for s in sets:
+                calls.append(F.bind_mlp2(x, s["W1"], s.get("b1"), s["W2"], s.get("b2"), w.act, out=y, workspace=ws))
+            if w.M <= 16:
+                kernel, launches, p = "gemv2_onetile_kernel", 1, "persistent decode (1 launch)"
+            elif max(w.K, w.H, w.N) <= 128:
+                kernel, launches, p = "small_mlp2_kernel", 1, "small fused MLP (1 launch)"
+            else:
+                kernel, launches, p = "gemm_bf16_kernel", 2, "two tiled GEMMs"
+            rows = min(w.M, 256)
+            import oracle
+
+            cache = {}
+
+            def fn():
+                if not cache:   # input decoding (bf16 bits -> float64), once, before timing
+                    cache.update({k: f64(v) for k, v in t.items()})
+                c = cache
+                return oracle.mlp2(c["x"][:rows], c["W1"], c.get("b1"), c["W2"], c.get("b2"), w.act)
+            sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
+        else:
+            ws = F.workspace_for(dev, F.fmlp_geglu_workspace_size(w.M, w.K, w.H))
+            for s in sets:
+                calls.append(F.bind_geglu(x, s["Wg"], s["Wu"], s["Wd"], out=y, workspace=ws))
+            if w.M <= 16:
+                kernel, launches, p = "gemv2_persistent_kernel", 1, "persistent decode (1 launch)"
+            else:
+                kernel, launches, p = "gemm_bf16_kernel", 2, "fused gate+up GEMM + down GEMM (2 launches)"
+            import oracle
+
+            rows = min(w.M, 64 if w.K * w.H > 1e8 else 1024)
+            cache = {}
+
+            def fn():
+                if not cache:   # input decoding (bf16 bits -> float64), once, before timing
+                    cache.update({k: f64(v) for k, v in t.items()})
+                c = cache
+                return oracle.geglu(c["x"][:rows], c["Wg"], c["Wu"], c["Wd"])
+            sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
+        return Case(w, calls, kernel, launches, p, R, fn, sample)
+
+    # mixture of experts
+    x_bits = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
+    ids, gw = datagen.make_routes(w.M, w.E, w.top_k, seed=0)
+    experts = [datagen.expert_weights(w, e, seed=0) for e in range(w.E)]
+    x = _dev(x_bits, torch, dev)
+    Wg = torch.stack([_dev(e[0], torch, dev) for e in experts])
+    Wu = torch.stack([_dev(e[1], torch, dev) for e in experts])
+    Wd = torch.stack([_dev(e[2], torch, dev) for e in experts])
+    ids_d = torch.from_numpy(ids).to(dev)
+    gw_d = torch.from_numpy(gw).to(dev)
+    y = torch.empty_like(x)
+    ws = F.workspace_for(dev, F.fmlp_moe_workspace_size(w.M, w.K, w.H, w.E, w.top_k))
+    calls = [F.bind_moe_geglu(x, ids_d, gw_d, Wg, Wu, Wd, out=y, workspace=ws)]
+    import oracle
+
+    toks = 32
+    xs = datagen.bf16_to_f32(x_bits[:toks]).astype(np.float64)
+    f64e = {}
+
+    def get(e):
+        if e not in f64e:
+            f64e[e] = tuple(datagen.bf16_to_f32(a).astype(np.float64) for a in experts[e])
+        return f64e[e]
+
+    fn = lambda: oracle.moe_geglu(xs, ids[:toks], gw[:toks], get)  # noqa: E731
+    return Case(w, calls, "gemm_bf16_kernel", 4, "route + grouped gate+up + grouped down + combine",
+                1, fn, (f"{toks} of {w.M} tokens (their experts' weights pre-converted)", toks / w.M))
+
+
+def copy_calibration(dev, nbytes: int, reps: int):
+    """A plain elementwise copy of known size (one read + one write of nbytes),
+    run so that rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE can be scaled."""
+    import torch
+
+    src = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+# ---------------------------------------------------------------------------
+def time_oracle(case: Case, seconds: float):
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    case.oracle_fn()  # warm (BLAS init, page-in)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        case.oracle_fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per_call = el / n
+    flops = case.w.flops * case.oracle_sample[1]
+    return {
+        "value": round(flops / per_call / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{case.oracle_sample[0]}; {n} oracle calls in {el:.1f} s (fp64 numpy/OpenBLAS)",
+        "us_per_forward_equiv": round(per_call / case.oracle_sample[1] * 1e6, 1),
+        "cpu": platform.processor() or platform.machine(),
+    }
+
+
+def read_traffic(case: Case):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{case.w.name}.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode1",
+                    choices=["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe"])
+    ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
+                    help="only run a plain copy of this many MiB (for PMC scaling) and exit")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the feed-forward path shards by tokens or by hidden columns; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import gemm_epilogue_bf16_amd as F
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        copy_calibration(dev, args.copy_calibration << 20, 10)
+        return 0
+
+    case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path)
+    w = case.w
+    est_us = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
+              "large16": 250, "large4096": 4000, "moe": 2500}[args.workload]
+    K = args.steps if args.steps is not None else max(20, int(1.5e6 / est_us))
+    W = args.warmup if args.warmup is not None else max(5, K // 10)
+    R = len(case.calls)
+    calls = case.calls
+    stream = torch.cuda.current_stream(dev)
+
+    with F.force_path(args.path):
+        for i in range(W):
+            calls[i % R]()
+        torch.cuda.synchronize()
+
+        # ---- timed region: K steps, synchronize on both sides -------------
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(K):
+            calls[i % R]()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        wall_s = (t1 - t0) / K
+        dev_s = ev0.elapsed_time(ev1) * 1e-3 / K
+
+        # ---- per-launch events (same stream) for the kernel duration ------
+        n_ev = min(K, 200)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        torch.cuda.synchronize()
+        for i in range(n_ev):
+            starts[i].record(stream)
+            calls[i % R]()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        per_launch_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+
+    # one step = one forward; value = algorithmic TFLOP/s of the whole job
+    value = w.flops / wall_s / 1e12
+    memory_bound = w.flops / w.bytes < 300.0
+    # HIP-event time per step over the timed region: for a one-launch step this
+    # is the average launch duration (incl. the dispatch gap to the next launch)
+    kernel_s = dev_s
+    if memory_bound:
+        achieved = w.bytes / kernel_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        achieved = w.flops / kernel_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = read_traffic(case)
+    roof["kernel"] = case.kernel
+    roof["launches_per_step"] = case.launches
+    roof["algorithmic_flops"] = w.flops
+    roof["algorithmic_bytes"] = w.bytes
+    roof["us_per_step_events"] = round(kernel_s * 1e6, 3)
+    roof["us_per_launch_bracketed"] = round(per_launch_s * 1e6, 3)
+
+    vs = None
+    if w.name.startswith("decode_mlp2_4096x4096x4096_M1"):
+        vs = round(value / (w.flops / (PAGE_H100_FUSED_US * 1e-6) / 1e12), 4)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(wall_s * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": vs,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "op": w.op,
+            "tokens": w.M,
+            "dims": {"in": w.K, "hidden": w.H, "out": w.N, **({"experts": w.E, "top_k": w.top_k} if w.op == "moe" else {})},
+            "act": w.act if w.op == "mlp2" else "gelu_tanh (GeGLU)",
+            "bias": w.bias,
+            "weights": (f"cold: {case.copies} rotated copies ({case.copies * w.weight_bytes / 2**20:.0f} MiB)"
+                        if case.copies > 1 else "single copy"),
+            "path": case.path,
+            "parallelism": "single GPU",
+        },
+        "us_per_forward": round(wall_s * 1e6, 3),
+        "us_per_forward_device": round(dev_s * 1e6, 3),
+        "roofline": roof,
+        "baseline_note": ("vs_baseline = value / the page's H100 fused figure (8.1 us, same workload); "
+                          "another machine, context only") if vs is not None else None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = time_oracle(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

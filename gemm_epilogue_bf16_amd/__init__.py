@@ -39,6 +39,11 @@ __all__ = [
     "workspace_for",
     "barrier_timeouts",
     "moe_invalid_ids",
+    "BoundCall",
+    "bind_mlp2",
+    "bind_geglu",
+    "bind_moe_geglu",
+    "bind_linear",
     "linear",
     "mlp2",
     "geglu",
@@ -142,7 +147,8 @@ _ws_lock = threading.Lock()
 
 def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
     """A zero-initialised workspace of at least nbytes, cached per (device,
-    stream).  Its 256-byte header must start zeroed; every call leaves it so."""
+    stream).  Its 8 KB header (barrier words) must start zeroed; calls keep it
+    consistent."""
     if nbytes <= 0:
         return None
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
@@ -168,8 +174,28 @@ def force_path(path: str):
 # ---------------------------------------------------------------------------
 # entry points (same names as the C ABI)
 # ---------------------------------------------------------------------------
-def fmlp_linear(x, W, b=None, act: str = "none", out=None):
-    """y = act(x W^T + b); x [..., K], W [N, K], b [N] or None -> y [..., N]."""
+class BoundCall:
+    """One C-ABI call with its arguments marshalled once (device pointers,
+    sizes, workspace, stream).  Calling it re-enqueues the same launch with a
+    single foreign call: for tight decode loops, where per-call Python
+    marshalling would cost more than the kernel itself."""
+
+    __slots__ = ("_fn", "_args", "out", "_keep")
+
+    def __init__(self, fn, args, out, keep=()):
+        self._fn = fn
+        self._args = tuple(args)
+        self.out = out
+        self._keep = tuple(keep)   # the tensors whose pointers args hold
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st:
+            _check(st)
+        return self.out
+
+
+def _linear_call(x, W, b, act, out):
     _dev_tensor("x", x)
     _dev_tensor("W", W)
     if b is not None:
@@ -181,17 +207,26 @@ def fmlp_linear(x, W, b=None, act: str = "none", out=None):
     M = x.numel() // K if K else 0
     y = out if out is not None else torch.empty(*x.shape[:-1], N, dtype=torch.bfloat16, device=x.device)
     _dev_tensor("out", y)
+    return BoundCall(lib().fmlp_linear, (_ptr(x), _ptr(W), _ptr(b), ACT[act], M, K, N, _ptr(y),
+                                         _stream(x.device)), y, (x, W, b))
+
+
+def fmlp_linear(x, W, b=None, act: str = "none", out=None):
+    """y = act(x W^T + b); x [..., K], W [N, K], b [N] or None -> y [..., N]."""
     with torch.cuda.device(x.device):
-        _check(lib().fmlp_linear(_ptr(x), _ptr(W), _ptr(b), ACT[act], M, K, N, _ptr(y), _stream(x.device)))
-    return y
+        return _linear_call(x, W, b, act, out)()
+
+
+def bind_linear(x, W, b=None, act: str = "none", out=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _linear_call(x, W, b, act, out)
 
 
 def fmlp_mlp2_workspace_size(M, K, H, N) -> int:
     return int(lib().fmlp_mlp2_workspace_size(M, K, H, N))
 
 
-def fmlp_mlp2(x, W1, b1, W2, b2, act: str = "gelu_erf", out=None, workspace=None):
-    """y = act(x W1^T + b1) W2^T + b2; W1 [H, K], W2 [N, H]; biases may be None."""
+def _mlp2_call(x, W1, b1, W2, b2, act, out, workspace):
     for n, t in (("x", x), ("W1", W1), ("W2", W2)):
         _dev_tensor(n, t)
     for n, t in (("b1", b1), ("b2", b2)):
@@ -206,18 +241,27 @@ def fmlp_mlp2(x, W1, b1, W2, b2, act: str = "gelu_erf", out=None, workspace=None
     L = lib()
     need = int(L.fmlp_mlp2_workspace_size(M, K, H, N))
     ws = workspace if workspace is not None else workspace_for(x.device, need)
+    return BoundCall(L.fmlp_mlp2, (_ptr(x), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), ACT[act], M, K, H,
+                                   N, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(x.device)), y, (x, W1, b1, W2, b2, ws))
+
+
+def fmlp_mlp2(x, W1, b1, W2, b2, act: str = "gelu_erf", out=None, workspace=None):
+    """y = act(x W1^T + b1) W2^T + b2; W1 [H, K], W2 [N, H]; biases may be None."""
     with torch.cuda.device(x.device):
-        _check(L.fmlp_mlp2(_ptr(x), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), ACT[act], M, K, H, N,
-                           _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device)))
-    return y
+        return _mlp2_call(x, W1, b1, W2, b2, act, out, workspace)()
+
+
+def bind_mlp2(x, W1, b1, W2, b2, act: str = "gelu_erf", out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _mlp2_call(x, W1, b1, W2, b2, act, out, workspace)
 
 
 def fmlp_geglu_workspace_size(M, D, H) -> int:
     return int(lib().fmlp_geglu_workspace_size(M, D, H))
 
 
-def fmlp_geglu(x, Wg, Wu, Wd, out=None, workspace=None):
-    """y = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T; Wg, Wu [H, D], Wd [D, H]."""
+def _geglu_call(x, Wg, Wu, Wd, out, workspace):
     for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
         _dev_tensor(n, t)
     D = x.shape[-1]
@@ -229,19 +273,26 @@ def fmlp_geglu(x, Wg, Wu, Wd, out=None, workspace=None):
     L = lib()
     need = int(L.fmlp_geglu_workspace_size(M, D, H))
     ws = workspace if workspace is not None else workspace_for(x.device, need)
+    return BoundCall(L.fmlp_geglu, (_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), M, D, H, _ptr(y), _ptr(ws),
+                                    ws.numel(), _stream(x.device)), y, (x, Wg, Wu, Wd, ws))
+
+
+def fmlp_geglu(x, Wg, Wu, Wd, out=None, workspace=None):
+    """y = (gelu_tanh(x Wg^T) * (x Wu^T)) Wd^T; Wg, Wu [H, D], Wd [D, H]."""
     with torch.cuda.device(x.device):
-        _check(L.fmlp_geglu(_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), M, D, H, _ptr(y), _ptr(ws),
-                            ws.numel(), _stream(x.device)))
-    return y
+        return _geglu_call(x, Wg, Wu, Wd, out, workspace)()
+
+
+def bind_geglu(x, Wg, Wu, Wd, out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _geglu_call(x, Wg, Wu, Wd, out, workspace)
 
 
 def fmlp_moe_workspace_size(T, D, H, E, top_k) -> int:
     return int(lib().fmlp_moe_workspace_size(T, D, H, E, top_k))
 
 
-def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
-    """Top-k MoE of GeGLU experts.  x [T, D]; expert_ids int32 [T, k];
-    gate_w fp32 [T, k]; Wg, Wu [E, H, D]; Wd [E, D, H]."""
+def _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace):
     for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
         _dev_tensor(n, t)
     _dev_tensor("expert_ids", expert_ids, torch.int32)
@@ -257,10 +308,22 @@ def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
     L = lib()
     need = int(L.fmlp_moe_workspace_size(T, D, H, E, k))
     ws = workspace if workspace is not None else workspace_for(x.device, need)
+    return BoundCall(L.fmlp_moe_geglu, (_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu),
+                                        _ptr(Wd), T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(),
+                                        _stream(x.device)), y,
+                     (x, expert_ids, gate_w, Wg, Wu, Wd, ws))
+
+
+def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
+    """Top-k MoE of GeGLU experts.  x [T, D]; expert_ids int32 [T, k];
+    gate_w fp32 [T, k]; Wg, Wu [E, H, D]; Wd [E, D, H]."""
     with torch.cuda.device(x.device):
-        _check(L.fmlp_moe_geglu(_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu), _ptr(Wd),
-                                T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(), _stream(x.device)))
-    return y
+        return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace)()
+
+
+def bind_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace)
 
 
 # ---------------------------------------------------------------------------

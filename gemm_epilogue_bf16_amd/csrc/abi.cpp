@@ -24,7 +24,7 @@ constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3;
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kSmallMaxDim = 128;
 constexpr int64_t kMaxDim = int64_t(1) << 31;   // bound on any single dimension
-constexpr size_t kHeader = 256;                 // barrier / error words
+constexpr size_t kHeader = kWorkspaceHeaderBytes;  // barrier / error words
 
 fmlp_status fail(fmlp_status s, const char* fmt, ...) {
   char buf[512];

@@ -68,13 +68,23 @@ struct GemvLayer {
 
 // One layer, one launch.
 hipError_t launch_gemv(const GemvLayer& L, int M, hipStream_t s);
-// Two dependent layers in one persistent (cooperative) launch with a device-wide
-// barrier between them.  bar points at 3 zeroed uint32 words (count,
-// generation, timeout count) that the kernel leaves consistent.
+
+// Workspace header shared by the two-layer decode kernel: 32-bit words.
+// Word kSyncGenWord holds the barrier generation, kSyncTimeoutWord counts waits
+// that gave up, and words kSyncFlagWord0 + b are block b's arrival flags.  The
+// header must be zero before its first use; the kernel only ever moves the
+// generation forward, so it stays valid across calls and grid sizes.
+constexpr int kWorkspaceHeaderBytes = 8192;
+constexpr int kSyncGenWord = 0;
+constexpr int kSyncTimeoutWord = 2;
+constexpr int kSyncFlagWord0 = 64;
+constexpr int kDecodeMaxBlocks = kWorkspaceHeaderBytes / 4 - kSyncFlagWord0;
+
+// Two dependent layers in ONE launch: every block is resident at once, layer-1
+// outputs are published through device-coherent stores and a flag barrier,
+// layer-2 weights stream across the barrier.  sync = the workspace header.
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M,
-                                   uint32_t* bar, hipStream_t s);
-// Largest grid the persistent kernel can have resident at once (0 = unknown).
-int gemv2_persistent_max_blocks();
+                                   uint32_t* sync, hipStream_t s);
 
 // ---------------------------------------------------------------------------
 // Small fused MLP: K, H, N <= 128, any M; one launch.

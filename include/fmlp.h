@@ -90,8 +90,9 @@ fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16*
  * Paths (chosen from the shape): M <= 16: one persistent decode launch;
  * K, H, N <= 128: one fused small-MLP launch; otherwise two GEMM launches with
  * h in the workspace.  workspace must hold fmlp_mlp2_workspace_size(M,K,H,N)
- * bytes (it may be NULL when that size is 0) and its first 256 bytes must be
- * zero before the first call that uses it; every call leaves them zero again.
+ * bytes (it may be NULL when that size is 0) and its first 8192 bytes (the
+ * decode kernel's barrier words) must be zero before the first call that uses
+ * it; later calls keep them consistent, whatever their shapes.
  */
 fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* b1,
                       const fmlp_bf16* W2, const fmlp_bf16* b2, int act,

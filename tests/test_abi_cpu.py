@@ -80,7 +80,7 @@ def test_linear_zero_rows_is_a_noop(L):
 
 def test_mlp2_validation(L):
     need = L.fmlp_mlp2_workspace_size(4, 32, 64, 32)
-    assert need == 256 + 512  # header + 4*64 bf16 rounded to 256
+    assert need == 8192 + 512  # 8 KB header + 4*64 bf16 rounded to 256
     # workspace NULL / too small
     assert L.fmlp_mlp2(X, W, B, W, B, 1, 20, 256, 256, 256, Y, None, 0, None) == E_WS
     assert L.fmlp_mlp2(X, W, B, W, B, 1, 20, 256, 256, 256, Y, WS, 100, None) == E_WS
@@ -105,7 +105,7 @@ def test_mlp2_validation(L):
 
 def test_geglu_validation(L):
     need = L.fmlp_geglu_workspace_size(8192, 768, 3072)
-    assert need == 256 + 8192 * 3072 * 2
+    assert need == 8192 + 8192 * 3072 * 2
     assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, None, 0, None) == E_WS
     assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, WS + 8, 1 << 20, None) == E_ALIGN
     assert L.fmlp_geglu(X, W, None, W, 16, 64, 128, Y, WS, 1 << 20, None) == E_NULL
@@ -122,7 +122,7 @@ def test_moe_validation(L):
     T, D, H, E, k = 4096, 4096, 14336, 8, 2
     P = T * k
     need = L.fmlp_moe_workspace_size(T, D, H, E, k)
-    assert need >= 256 + 3 * P * 4 + P * H * 2 + P * D * 4
+    assert need >= 8192 + 3 * P * 4 + P * H * 2 + P * D * 4
     ids, gw = 0x60000, 0x70000
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, 0, k, Y, WS, need, None) == E_ARG
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, E, 9, Y, WS, need, None) == E_ARG
@@ -130,7 +130,7 @@ def test_moe_validation(L):
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, E, k, Y, WS, need - 1, None) == E_WS
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, 4092, H, E, k, Y, WS, need, None) == E_ALIGN
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, 0, D, H, E, k, Y, WS, need, None) == OK
-    assert L.fmlp_moe_error_offset() < 256
+    assert L.fmlp_moe_error_offset() < 8192
 
 
 def test_no_fallback_without_library(tmp_path, monkeypatch):

@@ -135,9 +135,48 @@ def test_decode_determinism_and_repeat():
     ws = F.workspace_for(DEV, F.fmlp_mlp2_workspace_size(16, 4096, 4096, 4096))
     print("case decode repeat x50", flush=True)
     first = bits_of(_run(d, w.act, "decode", ws))
+    gen0 = int(ws[:4].view(torch.int32).item())
     for _ in range(50):
         y = F.fmlp_mlp2(d["x"], d["W1"], d["b1"], d["W2"], d["b2"], w.act, workspace=ws)
     torch.cuda.synchronize()
     assert np.array_equal(bits_of(y), first)
     hdr = ws[:12].view(torch.int32).cpu().numpy()
-    assert hdr[0] == 0 and hdr[2] == 0, hdr   # count back to 0, no timeouts
+    assert hdr[0] == gen0 + 50, hdr          # one barrier generation per call
+    assert hdr[2] == 0, hdr                  # no wait gave up
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_no_stale_hidden_vector(M):
+    """Back-to-back persistent calls on alternating inputs into one output
+    buffer: if a block read another XCD's h before it was visible (or a stale
+    copy from the previous call), the result would carry the other input's h."""
+    rng = np.random.default_rng(77 + M)
+    K, H, N = 1024, 4096, 2048
+    W1 = rand_bf16(rng, (H, K), K ** -0.5, "uniform")
+    b1 = rand_bf16(rng, (H,), 0.2, "uniform")
+    W2 = rand_bf16(rng, (N, H), H ** -0.5, "uniform")
+    b2 = rand_bf16(rng, (N,), 0.2, "uniform")
+    xs = [rand_bf16(rng, (M, K)), rand_bf16(rng, (M, K))]
+    dW = {k: to_dev(v) for k, v in (("W1", W1), ("b1", b1), ("W2", W2), ("b2", b2))}
+    dx = [to_dev(x) for x in xs]
+    ws = F.workspace_for(DEV, F.fmlp_mlp2_workspace_size(M, K, H, N))
+    outs = [torch.empty(M, N, dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    print(f"case decode alternating inputs M={M}", flush=True)
+    with F.force_path("decode"):
+        want = []
+        for i in range(2):
+            F.fmlp_mlp2(dx[i], dW["W1"], dW["b1"], dW["W2"], dW["b2"], "gelu_erf", out=outs[i], workspace=ws)
+            torch.cuda.synchronize()
+            want.append(bits_of(outs[i]))
+            ref = oracle.mlp2(f64_of_bits(xs[i]), f64_of_bits(W1), f64_of_bits(b1), f64_of_bits(W2),
+                              f64_of_bits(b2), "gelu_erf")
+            assert_parity(outs[i], ref, f"alternating input {i}")
+        assert not np.array_equal(want[0], want[1])
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+        for it in range(200):
+            F.fmlp_mlp2(dx[it % 2], dW["W1"], dW["b1"], dW["W2"], dW["b2"], "gelu_erf", out=y, workspace=ws)
+            if it % 20 == 19 or it < 4:
+                torch.cuda.synchronize()
+                assert np.array_equal(bits_of(y), want[it % 2]), f"iteration {it}"
+    torch.cuda.synchronize()
+    assert F.barrier_timeouts(ws) == 0
