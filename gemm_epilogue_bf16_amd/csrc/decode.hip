@@ -7,35 +7,43 @@
 // loads X once and writes only the final output).  The two-layer forms run as
 // ONE launch.
 //
+// Roles.  A block has 7 worker waves and 1 control wave.  The workers stream
+// weights and run the MFMAs; the control wave never loads a weight, so its
+// waits cover only its own few accesses: it sums the workers' partial tiles,
+// runs the epilogue, stores the result, and (two-layer form) publishes and
+// awaits the hidden vector h.
+//
 // Work unit.  A block owns 16 output rows of a layer (one MFMA row tile) and
-// walks K in stages of kSK = 1024: one stage is the 16 x 1024 bf16 slab of the
-// weight (32 KB, one contiguous 2 KB piece per row).  Each thread loads 4
-// 16-byte chunks per stage so that every wave instruction reads 1 KB of one
+// walks K in stages of kSK = 896: one stage is the 16 x 896 bf16 slab of the
+// weight (28 KB, one contiguous 1792-byte piece per row).  Each worker thread
+// loads 4 16-byte chunks per stage, so a wave instruction reads 1 KB of one
 // weight row (fully coalesced), into a register ring: three stages (two when
 // the gate and up weights stream together) are in flight per block while the
-// oldest is written to a double-buffered LDS slab and consumed.  The LDS slab is swizzled (chunk c of row r sits at
-// c ^ (r & 15) within its 16-chunk group) so the MFMA fragment reads of 16 rows
-// are bank-conflict free.  Wave w takes k-steps of 32 from its 16-chunk group
-// of every stage; v_mfma_f32_16x16x32_bf16 gets the weight rows as the row
-// operand and the <= 16 activation rows as the column operand (zero for
-// columns >= M).  Per-wave fp32 partial tiles are summed in a fixed order
-// through LDS (bitwise deterministic), then the epilogue (bias + activation, or
-// gelu_tanh(g) * u) runs in fp32 and rounds once to bf16.
+// oldest is written to a double-buffered LDS slab and consumed.  The slab is
+// swizzled (chunk c of row r sits at c ^ (r & 15) within its 16-chunk group)
+// so the MFMA fragment reads of 16 rows are bank-conflict free.  Worker w takes
+// 4 k-steps of 32 from its 16-chunk group of every stage;
+// v_mfma_f32_16x16x32_bf16 gets the weight rows as the row operand and the
+// <= 16 activation rows as the column operand (zero for columns >= M).  The
+// control wave sums the 7 fp32 partial tiles in a fixed order (bitwise
+// deterministic) and applies the epilogue (bias + activation, or
+// gelu_tanh(g) * u) in fp32 with one rounding to bf16.
 //
 // One stream, two layers.  The stages of layer 2 follow those of layer 1 in
-// the same ring, so layer-2 weights are already in flight while layer 1
-// finishes and while the block waits at the device-wide barrier that makes the
-// hidden vector h visible.  h is written and read with device-coherent (agent
-// scope) 32-bit atomic accesses, and the barrier is a set of per-block arrival
-// flags polled by block 0, so no L2 write-back / invalidate is needed.  Every
-// wait is bounded: a wait that gives up is counted in the workspace and the
-// kernel still exits.
+// the same ring, so layer-2 weights are in flight while layer 1 finishes and
+// while the block waits for h.  The control wave stores h with device-coherent
+// (agent scope) stores, waits for its own stores, and raises the block's
+// arrival flag; every control wave then polls all flags (one hop, no L2
+// write-back or invalidate) and releases its workers, which read h with plain
+// loads: no h line is touched before every block has published, so no stale
+// copy can sit in an L2.  Every wait is bounded: a wait that gives up is
+// counted in the workspace and the kernel still exits.
 //
-// All loads are buffer loads whose out-of-range offsets return 0 without a
-// memory access: ragged tiles, the k tail, stages past the end of the stream
+// All worker loads are buffer loads whose out-of-range offsets return 0 without
+// a memory access: ragged tiles, the k tail, stages past the end of the stream
 // and h fragments requested before the barrier are masked by the offset, with
-// no branch around a load, so the compiler can count loads in flight and only
-// waits for the ring slot it is about to consume.
+// no branch around a load, so the compiler counts the loads in flight and waits
+// only for the ring slot it is about to consume.
 #include <algorithm>
 #include <mutex>
 
@@ -46,13 +54,15 @@ namespace fmlp {
 
 namespace {
 
-constexpr int kNW = 8;                      // waves per block
-constexpr int kThreads = kNW * 64;
-constexpr int kSK = 1024;                   // k per stage
-constexpr int kCH = kSK / 8;                // 16-byte chunks per row per stage (128)
-constexpr int kLoads = 16 * kCH / kThreads; // chunks per thread per stage (4)
-constexpr int kKS = kSK / 32 / kNW;         // MFMA k-steps per wave per stage (4)
-constexpr uint32_t kSpinLimit = 1u << 20;   // bounded waits
+constexpr int kWorkers = 7;                    // streaming + MFMA waves
+constexpr int kThreads = (kWorkers + 1) * 64;  // + the control wave
+constexpr int kWT = kWorkers * 64;             // worker threads
+constexpr int kSK = kWorkers * 128;            // k per stage: 128 per worker wave
+constexpr int kCH = kSK / 8;                   // 16-byte chunks per row per stage (112)
+constexpr int kLoads = 16 * kCH / kWT;         // chunks per worker thread per stage (4)
+constexpr int kKS = 4;                         // MFMA k-steps per worker wave per stage
+constexpr uint32_t kSpinLimit = 1u << 20;      // bounded waits
+static_assert(16 * kCH == kLoads * kWT, "stage tiling");
 
 __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -69,22 +79,23 @@ __device__ __forceinline__ void wait_vm_all() {
 }
 
 // Buffer resources: loads through them return 0 for offsets past the end
-// without touching memory, which masks ragged tiles, the k tail and stages
-// past the end of the stream without a branch around the load.
+// without touching memory.
 constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+// Every descriptor here is wave-uniform by construction (it depends only on
+// the stage, the layer and the block); readfirstlane puts it in SGPRs so the
+// load needs no per-lane loop.  readfirstlane returns a signed int: each half
+// is widened through uint32_t, never sign-extended into the other half.
+__device__ __forceinline__ uint32_t uniform32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
-// plain 16-byte load
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t ua = ((uint64_t)uniform32((uint32_t)(a >> 32)) << 32) | (uint64_t)uniform32((uint32_t)a);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ua), (short)0,
+                                           (int)uniform32(bytes), 0x00020000);
+}
 __device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-// device-coherent (agent scope, sc1) 16-byte load: sees h stored by other XCDs
-__device__ __forceinline__ u32x4_t bload_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16));
 }
 
 struct Stream {
@@ -97,13 +108,13 @@ struct Stream {
 template <bool TWO>
 __device__ __forceinline__ Stream make_stream(const GemvLayer& L1, const GemvLayer& L2) {
   Stream st;
-  const int64_t G = gridDim.x, b = blockIdx.x;
-  const int64_t tiles1 = (L1.N + 15) / 16;
-  st.nt[0] = b < tiles1 ? (int)((tiles1 - 1 - b) / G + 1) : 0;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int tiles1 = (int)((L1.N + 15) / 16);
+  st.nt[0] = b < tiles1 ? (tiles1 - 1 - b) / G + 1 : 0;
   st.S[0] = (int)((L1.K + kSK - 1) / kSK);
   if (TWO) {
-    const int64_t tiles2 = (L2.N + 15) / 16;
-    st.nt[1] = b < tiles2 ? (int)((tiles2 - 1 - b) / G + 1) : 0;
+    const int tiles2 = (int)((L2.N + 15) / 16);
+    st.nt[1] = b < tiles2 ? (tiles2 - 1 - b) / G + 1 : 0;
     st.S[1] = (int)((L2.K + kSK - 1) / kSK);
   } else {
     st.nt[1] = 0;
@@ -137,14 +148,16 @@ template <bool DUAL1, bool TWO>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   constexpr int kSets = DUAL1 ? 2 : 1;   // layer 1 of GeGLU streams Wg and Wu together
-  // stages in flight: 3 x 32 KB per block, or 2 x 64 KB when two weights stream
+  // stages in flight: 3 x 28 KB per block, or 2 x 56 KB when two weights stream
   constexpr int kRing = DUAL1 ? 2 : 3;
   __shared__ u32x4_t slab[2][kSets][16 * kCH];
-  __shared__ float4 red[kSets][kNW * 64];
+  __shared__ float4 red[kSets][kWorkers * 64];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int li = lane & 15, lg = lane >> 4;
+  const bool worker = wave < kWorkers;
   const Stream st = make_stream<TWO>(L1, L2);
 
   uint32_t target = 0;
@@ -152,22 +165,18 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
 
   u32x4_t wreg[kRing][kSets][kLoads];
   u32x4_t xreg[kRing][kKS];
-  uint2 breg[kRing];                      // bias of the tile ending at that stage
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 
-  // weight chunks of stage g: thread tid loads chunks tid + i*kThreads; a wave
-  // instruction covers 64 consecutive chunks (1 KB) of one weight row.  A stage
-  // past the end of the stream, or one held back (live == false), loads nothing.
-  auto issue_w = [&](int g, bool live, u32x4_t (&dst)[kSets][kLoads], uint2& bias) {
-    const bool in = live && g < st.total;
+  // ---- worker side ---------------------------------------------------------
+  // The control wave executes the same ring loads with every offset out of
+  // range (no memory access), so all waves issue the same sequence of loads
+  // and the compiler's count of loads in flight stays exact on every path.
+  // weight chunks of stage g: worker thread tid loads chunks tid + i*kWT; a
+  // wave instruction covers 64 consecutive chunks (1 KB) of one weight row.
+  auto issue_w = [&](int g, u32x4_t (&dst)[kSets][kLoads]) {
+    const bool in = worker && g < st.total;
     const StageId id = stage_id(st, in ? g : 0);
     const GemvLayer& L = id.phase ? L2 : L1;
-    {   // the tile's bias, fetched with its last stage so the epilogue never waits
-      const bool want = in && id.last && L.bias != nullptr;
-      const int64_t n = id.n0 + 4 * lg;
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(want ? L.bias : L.W0, want ? (uint32_t)(L.N * 2) : 0u);
-      bias = bload8(rb, n < L.N ? (uint32_t)(n * 2) : kOutOfRange);
-    }
     const int64_t left = L.N - id.n0;
     const int64_t rows = in ? (left < 16 ? left : 16) : 0;
     const uint32_t nrec = (uint32_t)(rows * L.K * 2);
@@ -177,7 +186,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       const __amdgpu_buffer_rsrc_t r = make_rsrc(W + id.n0 * L.K, (set && id.phase == 1) ? 0u : nrec);
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int q = tid + i * kThreads;
+        const int q = tid + i * kWT;
         const int row = q / kCH, c = q % kCH;
         const int64_t k = id.k0 + c * 8;
         const uint32_t off = k < L.K ? (uint32_t)((row * L.K + k) * 2) : kOutOfRange;
@@ -185,10 +194,11 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       }
     }
   };
-  // activation fragments of stage g: rows >= M fall past the end of x and read
-  // 0.  Loaded device-coherent in both layers (layer 2 reads h).
+  // activation fragments of stage g (x, or h after the barrier); rows >= M
+  // fall past the end of the activation buffer and read 0.  live == false
+  // (h before the barrier) loads nothing.
   auto issue_x = [&](int g, bool live, u32x4_t (&dst)[kKS]) {
-    const bool in = live && g < st.total;
+    const bool in = worker && live && g < st.total;
     const StageId id = stage_id(st, in ? g : 0);
     const GemvLayer& L = id.phase ? L2 : L1;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(L.x, in ? (uint32_t)((int64_t)M * L.K * 2) : 0u);
@@ -196,13 +206,13 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
     for (int j = 0; j < kKS; ++j) {
       const int64_t k = id.k0 + (int64_t)(wave * 16 + j * 4 + lg) * 8;
       const uint32_t off = k < L.K ? (uint32_t)(((int64_t)li * L.K + k) * 2) : kOutOfRange;
-      dst[j] = bload_coherent(r, off);
+      dst[j] = bload(r, off);
     }
   };
   auto write_slab = [&](int buf, int phase, const u32x4_t (&src)[kSets][kLoads]) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int q = tid + i * kThreads;
+      const int q = tid + i * kWT;
       const int row = q / kCH, c = q % kCH;
       const int slot = row * kCH + ((c & ~15) | ((c & 15) ^ row));
 #pragma unroll
@@ -221,88 +231,96 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       if (DUAL1 && phase == 0) acc1 = mfma_16x16x32(slab[buf][kSets - 1][slot], x[j], acc1);
     }
   };
-  // end of a tile: fixed-order sum of the wave partials, epilogue, store
-  auto finish_tile = [&](const StageId& id, const uint2 bias) {
-    const bool dual = DUAL1 && id.phase == 0;
+  auto post_partials = [&](int phase) {
     red[0][wave * 64 + lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-    if (dual) red[kSets - 1][wave * 64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+    if (DUAL1 && phase == 0)
+      red[kSets - 1][wave * 64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
     acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
     acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    if (wave == 0) {
-      const GemvLayer& L = id.phase ? L2 : L1;
-      float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int w = 0; w < kNW; ++w) {
-        const float4 t = red[0][w * 64 + lane];
-        g[0] += t.x; g[1] += t.y; g[2] += t.z; g[3] += t.w;
-        if (dual) {
-          const float4 v = red[kSets - 1][w * 64 + lane];
-          u[0] += v.x; u[1] += v.y; u[2] += v.z; u[3] += v.w;
-        }
+  };
+
+  // ---- control side --------------------------------------------------------
+  // bias of the control wave's next tile, requested one tile ahead
+  int ctile = 0;
+  uint2 cbias = make_uint2(0u, 0u);
+  auto ctrl_fetch_bias = [&](int t) {
+    const int ntiles = st.nt[0] + st.nt[1];
+    const int p = t < st.nt[0] ? 0 : 1;
+    const GemvLayer& L = p ? L2 : L1;
+    const int i = p ? t - st.nt[0] : t;
+    const int64_t n = ((int64_t)blockIdx.x + (int64_t)i * gridDim.x) * 16 + 4 * lg;
+    const bool want = t < ntiles && L.bias != nullptr;          // wave-uniform
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(want ? L.bias : L.W0, want ? (uint32_t)(L.N * 2) : 0u);
+    const uint32_t off = n < L.N ? (uint32_t)(n * 2) : kOutOfRange;   // per lane
+    cbias = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0));
+  };
+  auto ctrl_epilogue = [&](const StageId& id) {
+    const bool dual = DUAL1 && id.phase == 0;
+    const GemvLayer& L = id.phase ? L2 : L1;
+    float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kWorkers; ++w) {
+      const float4 t = red[0][w * 64 + lane];
+      g[0] += t.x; g[1] += t.y; g[2] += t.z; g[3] += t.w;
+      if (dual) {
+        const float4 v = red[kSets - 1][w * 64 + lane];
+        u[0] += v.x; u[1] += v.y; u[2] += v.z; u[3] += v.w;
       }
-      const int m = li;
-      const int64_t n = id.n0 + 4 * lg;   // this lane's 4 consecutive outputs
-      if (m < M && n < L.N) {
-        float v[4];
-        const float b[4] = {bf16_lo(bias.x), bf16_hi(bias.x), bf16_lo(bias.y), bf16_hi(bias.y)};
+    }
+    const uint2 bias = cbias;
+    ctrl_fetch_bias(++ctile);
+    const int m = li;
+    const int64_t n = id.n0 + 4 * lg;   // this lane's 4 consecutive outputs
+    if (m < M && n < L.N) {
+      float v[4];
+      const float b[4] = {bf16_lo(bias.x), bf16_hi(bias.x), bf16_lo(bias.y), bf16_hi(bias.y)};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (dual) {
-            v[r] = gelu_tanh(g[r]) * u[r];
-          } else {
-            v[r] = apply_act(g[r] + b[r], L.act);   // b = 0 without a bias
-          }
-        }
-        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(L.y + (int64_t)m * L.N + n);
-        if (TWO && id.phase == 0) {   // h: read by every block after the barrier
-          st_coherent(dst, lo);
-          st_coherent(dst + 1, hi);
-        } else {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-        }
+      for (int r = 0; r < 4; ++r)
+        v[r] = dual ? gelu_tanh(g[r]) * u[r] : apply_act(g[r] + b[r], L.act);   // b = 0 without a bias
+      const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(L.y + (int64_t)m * L.N + n);
+      if (TWO && id.phase == 0) {   // h: read by every block after the barrier
+        st_coherent(dst, lo);
+        st_coherent(dst + 1, hi);
+      } else {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
       }
     }
   };
-  // this block's h is complete once wave 0's stores are: publish the flag
-  auto arrive = [&]() {
-    if (wave == 0) {
-      wait_vm_all();
-      if (lane == 0) st_coherent(sync + kSyncFlagWord0 + blockIdx.x, target);
-    }
+  // this block's h is complete once the control wave's stores are: raise the flag
+  auto ctrl_arrive = [&]() {
+    wait_vm_all();
+    if (lane == 0) st_coherent(sync + kSyncFlagWord0 + blockIdx.x, target);
   };
-  auto bounded_wait = [&](const uint32_t* p) {
-    uint32_t spins = 0;
-    while (ld_coherent(p) != target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
+  // every control wave polls every block's flag (one hop)
+  auto ctrl_wait_all = [&]() {
+    for (int b = lane; b < (int)gridDim.x; b += 64) {
+      uint32_t spins = 0;
+      while (ld_coherent(sync + kSyncFlagWord0 + b) != target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
       }
     }
+    if (blockIdx.x == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
   };
-  // block 0 waits for every flag, then opens the generation every block waits on
-  auto wait_all = [&]() {
-    if (blockIdx.x == 0) {
-      for (int b = tid; b < (int)gridDim.x; b += kThreads) bounded_wait(sync + kSyncFlagWord0 + b);
-      __syncthreads();
-      if (tid == 0) st_coherent(sync + kSyncGenWord, target);
-    } else {
-      if (tid == 0) bounded_wait(sync + kSyncGenWord);
-      __syncthreads();
-    }
-  };
-  // Layer-2 stages issued before the barrier get their h fragments after it.
+
+  // An h fragment may be requested only once the barrier has passed, i.e. from
+  // iteration first2 on (its wait runs at the start of that iteration); the
+  // ones requested earlier are re-requested right after the barrier.
   auto x_live = [&](int gx, int g) { return !(TWO && gx >= st.first2 && g < st.first2); };
 
-  // a block with no layer-1 tile has nothing to publish
-  if (TWO && st.first2 == 0) arrive();
-
-  // ---- prologue: fill the ring ------------------------------------------------
+  if (!worker) {
+    ctrl_fetch_bias(0);
+    if (TWO && st.first2 == 0) ctrl_arrive();   // no layer-1 tile: nothing to publish
+  }
+  // the prologue runs before iteration 0, i.e. before any barrier (g = -1):
+  // touching h here would also pull not-yet-published lines into the L2
 #pragma unroll
   for (int d = 0; d < kRing; ++d) {
-    issue_w(d, true, wreg[d], breg[d]);
-    issue_x(d, x_live(d, 0), xreg[d]);
+    issue_w(d, wreg[d]);
+    issue_x(d, x_live(d, -1), xreg[d]);
   }
 
   // ---- main loop, unrolled by the ring size so ring slots are static --------
@@ -312,20 +330,24 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       const int g = g0 + d;
       const bool valid = g < st.total;
       const StageId id = stage_id(st, valid ? g : 0);
-      const uint2 bias_g = breg[d];   // slot d is refilled below, before the epilogue
       if (TWO && valid && g == st.first2) {   // entering layer 2: h must be complete
-        wait_all();
+        if (!worker) ctrl_wait_all();
+        __syncthreads();
 #pragma unroll
         for (int e = 0; e < kRing; ++e) issue_x(g + e, true, xreg[(d + e) % kRing]);
       }
-      if (valid) write_slab(g & 1, id.phase, wreg[d]);
+      if (worker && valid) write_slab(g & 1, id.phase, wreg[d]);
       __syncthreads();
-      issue_w(g + kRing, true, wreg[d], breg[d]);
-      if (valid) compute(g & 1, id.phase, xreg[d]);
+      issue_w(g + kRing, wreg[d]);
+      if (worker && valid) compute(g & 1, id.phase, xreg[d]);
       issue_x(g + kRing, x_live(g + kRing, g), xreg[d]);
+      if (worker && valid && id.last) post_partials(id.phase);
       if (valid && id.last) {
-        finish_tile(id, bias_g);
-        if (TWO && g == st.first2 - 1) arrive();
+        __syncthreads();
+        if (!worker) {
+          ctrl_epilogue(id);
+          if (TWO && g == st.first2 - 1) ctrl_arrive();
+        }
       }
     }
   }
