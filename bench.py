@@ -99,7 +99,7 @@ def setup_case(name: str, cold: bool, dev, path: str):
             for s in sets:
                 calls.append(F.bind_mlp2(x, s["W1"], s.get("b1"), s["W2"], s.get("b2"), w.act, out=y, workspace=ws))
             if w.M <= 16:
-                kernel, launches, p = "gemv2_onetile_kernel", 1, "persistent decode (1 launch)"
+                kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             elif max(w.K, w.H, w.N) <= 128:
                 kernel, launches, p = "small_mlp2_kernel", 1, "small fused MLP (1 launch)"
             else:
@@ -120,7 +120,7 @@ def setup_case(name: str, cold: bool, dev, path: str):
             for s in sets:
                 calls.append(F.bind_geglu(x, s["Wg"], s["Wu"], s["Wd"], out=y, workspace=ws))
             if w.M <= 16:
-                kernel, launches, p = "gemv2_persistent_kernel", 1, "persistent decode (1 launch)"
+                kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             else:
                 kernel, launches, p = "gemm_bf16_kernel", 2, "fused gate+up GEMM + down GEMM (2 launches)"
             import oracle
@@ -210,7 +210,7 @@ def time_oracle(case: Case, seconds: float):
 def read_traffic(case: Case):
     """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
     were taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{case.w.name}.json")
+    p = os.path.join(ROOT, "profiles", f"{case.kernel}__{case.w.name}__traffic.json")
     if not os.path.exists(p):
         return None
     try:
