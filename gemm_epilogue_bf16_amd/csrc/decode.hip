@@ -7,43 +7,45 @@
 // loads X once and writes only the final output).  The two-layer forms run as
 // ONE launch.
 //
-// Roles.  A block has 7 worker waves and 1 control wave.  The workers stream
-// weights and run the MFMAs; the control wave never loads a weight, so its
-// waits cover only its own few accesses: it sums the workers' partial tiles,
-// runs the epilogue, stores the result, and (two-layer form) publishes and
-// awaits the hidden vector h.
+// Streaming.  Weights and activation slices go from memory straight into an
+// LDS ring with buffer loads that write LDS (no register staging): one block
+// per CU keeps R - 1 stages in flight (112 KB of weights per CU at one token,
+// 48 KB at 16), which is what HBM latency times bandwidth asks for.  A stage is
+// 16 weight rows x 512 k (one 1 KB piece per row), or 2 x 16 rows x 256 k when
+// the gate and up weights of GeGLU stream together, plus the same k range of
+// the <= 16 activation rows.  Each 1 KB load instruction writes 1 KB of LDS
+// contiguously, lane by lane; a lane picks the global 16-byte chunk whose
+// swizzled home is its own LDS slot (chunk c of row r lives at c ^ (r & 15)
+// within its group of 16), so loads stay fully coalesced and the MFMA fragment
+// reads of 16 rows are bank-conflict free.  The streaming loop is rolled (a
+// ring slot is a runtime offset), so its few dozen instructions stay in the
+// instruction cache.
 //
-// Work unit.  A block owns 16 output rows of a layer (one MFMA row tile) and
-// walks K in stages of kSK = 896: one stage is the 16 x 896 bf16 slab of the
-// weight (28 KB, one contiguous 1792-byte piece per row).  Each worker thread
-// loads 4 16-byte chunks per stage, so a wave instruction reads 1 KB of one
-// weight row (fully coalesced), into a register ring: three stages (two when
-// the gate and up weights stream together) are in flight per block while the
-// oldest is written to a double-buffered LDS slab and consumed.  The slab is
-// swizzled (chunk c of row r sits at c ^ (r & 15) within its 16-chunk group)
-// so the MFMA fragment reads of 16 rows are bank-conflict free.  Worker w takes
-// 4 k-steps of 32 from its 16-chunk group of every stage;
-// v_mfma_f32_16x16x32_bf16 gets the weight rows as the row operand and the
-// <= 16 activation rows as the column operand (zero for columns >= M).  The
-// control wave sums the 7 fp32 partial tiles in a fixed order (bitwise
-// deterministic) and applies the epilogue (bias + activation, or
-// gelu_tanh(g) * u) in fp32 with one rounding to bf16.
+// Roles.  A block has 8 worker waves and 1 control wave.  Every worker issues
+// the same number of loads per stage, so a wave waits only for the stage it
+// is about to consume, and one workgroup barrier per stage publishes it to all
+// waves.  Worker w owns 1/8 of every stage's k range and runs
+// v_mfma_f32_16x16x32_bf16 with the weight rows as the row operand and the
+// activation rows as the column operand (zero for columns >= M).  The control
+// wave never loads a weight: it sums the 8 partial tiles in a fixed order
+// (bitwise deterministic), applies the epilogue (bias + activation, or
+// gelu_tanh(g) * u) in fp32 with one rounding to bf16, stores the result and,
+// in the two-layer form, publishes h and awaits every block's h.
 //
-// One stream, two layers.  The stages of layer 2 follow those of layer 1 in
-// the same ring, so layer-2 weights are in flight while layer 1 finishes and
-// while the block waits for h.  The control wave stores h with device-coherent
-// (agent scope) stores, waits for its own stores, and raises the block's
-// arrival flag; every control wave then polls all flags (one hop, no L2
-// write-back or invalidate) and releases its workers, which read h with plain
-// loads: no h line is touched before every block has published, so no stale
-// copy can sit in an L2.  Every wait is bounded: a wait that gives up is
-// counted in the workspace and the kernel still exits.
+// One stream, two layers.  Layer-2 stages follow layer-1 stages in the same
+// ring, so layer-2 weights are in flight while the block waits for h.  The
+// control wave stores h with device-coherent stores, waits for its own
+// stores, raises the block's flag, then reads every block's flag (one hop, no
+// L2 write-back or invalidate).  Workers read h only after that: the h slices
+// of the layer-2 stages issued before the barrier are requested empty and
+// re-requested after it, so no h line is touched before every block has
+// published and no stale copy can sit in an L2.  Every wait is bounded; a wait
+// that gives up is counted in the workspace and the kernel still exits.
 //
-// All worker loads are buffer loads whose out-of-range offsets return 0 without
-// a memory access: ragged tiles, the k tail, stages past the end of the stream
-// and h fragments requested before the barrier are masked by the offset, with
-// no branch around a load, so the compiler counts the loads in flight and waits
-// only for the ring slot it is about to consume.
+// Out-of-range rows, the k tail and stages past the end of the stream are
+// masked by buffer offsets (loads past the end return 0 without a memory
+// access), never by a branch around a load; fragments past K are also zeroed
+// at the read, so stale LDS never meets the MFMA.
 #include <algorithm>
 #include <mutex>
 
@@ -54,15 +56,28 @@ namespace fmlp {
 
 namespace {
 
-constexpr int kWorkers = 7;                    // streaming + MFMA waves
+constexpr int kWorkers = 8;                    // streaming + MFMA waves
 constexpr int kThreads = (kWorkers + 1) * 64;  // + the control wave
-constexpr int kWT = kWorkers * 64;             // worker threads
-constexpr int kSK = kWorkers * 128;            // k per stage: 128 per worker wave
-constexpr int kCH = kSK / 8;                   // 16-byte chunks per row per stage (112)
-constexpr int kLoads = 16 * kCH / kWT;         // chunks per worker thread per stage (4)
-constexpr int kKS = 4;                         // MFMA k-steps per worker wave per stage
+constexpr int kWChunks = 1024;                 // 16-byte weight chunks per stage (16 KB)
+constexpr int kSK1 = 512;                      // k per stage, one weight matrix
+constexpr int kSK2 = 256;                      // k per stage, gate + up together
 constexpr uint32_t kSpinLimit = 1u << 20;      // bounded waits
-static_assert(16 * kCH == kLoads * kWT, "stage tiling");
+constexpr uint32_t kOutOfRange = 0x80000000u;  // offset past any descriptor's end
+constexpr int kLdsBudget = 160 * 1024;
+
+// Activation rows held per stage (a class of M) and the ring depth it leaves.
+template <int MC, bool DUAL1>
+struct RingShape {
+  static constexpr int kXChunks = MC * 64;                        // MC rows x 1 KB
+  static constexpr int kSlotBytes = (kWChunks + kXChunks) * 16;
+  static constexpr int kRedBytes = (DUAL1 ? 2 : 1) * kWorkers * 64 * 16;
+  static constexpr int kFixed = kRedBytes + 2 * 64 * 4 + 1024;    // partials, bias, sink
+  static constexpr int R = (kLdsBudget - kFixed) / kSlotBytes;
+  static constexpr int XI = MC > 8 ? 2 : 1;                       // activation loads per wave and stage
+  static constexpr int kLoads = 2 + XI;                           // loads per wave and stage
+  static_assert(R >= 3 && R * kSlotBytes + kFixed <= kLdsBudget, "ring does not fit");
+  static_assert(kLoads * (R - 2) < 64, "vmcnt range");
+};
 
 __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -71,20 +86,30 @@ __device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-// wait until every vector memory access this wave issued has completed
-__device__ __forceinline__ void wait_vm_all() {
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
   compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt not waited
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  compiler_fence();
+}
+// Workgroup barrier for LDS hand-off: this wave's LDS accesses are complete,
+// then all waves meet.  No vector-memory wait: loads into LDS are waited for
+// explicitly, per stage, before it.
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
   compiler_fence();
 }
 
-// Buffer resources: loads through them return 0 for offsets past the end
-// without touching memory.
-constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
 // Every descriptor here is wave-uniform by construction (it depends only on
-// the stage, the layer and the block); readfirstlane puts it in SGPRs so the
-// load needs no per-lane loop.  readfirstlane returns a signed int: each half
-// is widened through uint32_t, never sign-extended into the other half.
+// the stage, the layer, the block and the wave); readfirstlane puts it in
+// SGPRs so no load needs a per-lane loop.  readfirstlane returns a signed int:
+// each half is widened through uint32_t, never sign-extended into the other.
 __device__ __forceinline__ uint32_t uniform32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
 }
@@ -94,191 +119,437 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ua), (short)0,
                                            (int)uniform32(bytes), 0x00020000);
 }
-__device__ __forceinline__ u32x4_t bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// ---- worker-side loads ------------------------------------------------------
+// The streaming loop issues its loads into LDS through inline assembly and
+// places every wait itself: the compiler's own bookkeeping would treat each
+// LDS read as dependent on every load into LDS still in flight and drain the
+// ring before each stage.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// raw buffer descriptor in SGPRs: base, stride 0, num_records = bytes
+__device__ __forceinline__ i32x4_t make_desc(uint64_t base, uint32_t bytes) {
+  i32x4_t d;
+  d[0] = (int)uniform32((uint32_t)base);
+  d[1] = (int)(uniform32((uint32_t)(base >> 32)) & 0xFFFFu);
+  d[2] = (int)uniform32(bytes);
+  d[3] = 0x00020000;
+  return d;
 }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uniform32((uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane into LDS at lds + 16 * lane (lds wave-uniform)
+__device__ __forceinline__ void asm_load_lds(const i32x4_t& d, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :: "v"(off), "s"(d), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// c ? a : b on values: a conditional between two lvalues would select their
+// addresses and load, which keeps the operands in private memory.
+template <class T>
+__device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
+
+// A kernel-argument field as an opaque scalar register value: a later choice
+// between two layers' fields then stays a register select.
+template <class T>
+__device__ __forceinline__ T in_sgpr(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32/64-bit scalars");
+  asm volatile("" : "+s"(v));
+  return v;
+}
+
+// position of 16-byte chunk c of stage row r inside the row (an involution)
+__device__ __forceinline__ int swz(int c, int r) { return (c & ~15) | ((c ^ r) & 15); }
 
 struct Stream {
   int nt[2];        // tiles this block owns in each layer
   int S[2];         // stages per tile in each layer
-  int first2;       // index of the first layer-2 stage (= nt[0] * S[0])
+  int first2;       // end of the layer-1 stages (= nt[0] * S[0])
   int total;        // stages of this block
 };
 
-template <bool TWO>
+template <bool DUAL1, bool TWO>
 __device__ __forceinline__ Stream make_stream(const GemvLayer& L1, const GemvLayer& L2) {
   Stream st;
   const int G = gridDim.x, b = blockIdx.x;
   const int tiles1 = (int)((L1.N + 15) / 16);
+  const int sk1 = DUAL1 ? kSK2 : kSK1;
   st.nt[0] = b < tiles1 ? (tiles1 - 1 - b) / G + 1 : 0;
-  st.S[0] = (int)((L1.K + kSK - 1) / kSK);
+  st.S[0] = (int)((L1.K + sk1 - 1) / sk1);
+  st.first2 = st.nt[0] * st.S[0];
   if (TWO) {
     const int tiles2 = (int)((L2.N + 15) / 16);
     st.nt[1] = b < tiles2 ? (tiles2 - 1 - b) / G + 1 : 0;
-    st.S[1] = (int)((L2.K + kSK - 1) / kSK);
+    st.S[1] = (int)((L2.K + kSK1 - 1) / kSK1);
   } else {
     st.nt[1] = 0;
     st.S[1] = 1;
   }
-  st.first2 = st.nt[0] * st.S[0];
   st.total = st.first2 + st.nt[1] * st.S[1];
   return st;
 }
 
-struct StageId {
-  int phase;        // 0: layer 1, 1: layer 2
-  int64_t n0;       // first output row of the tile
-  int64_t k0;       // first k of the stage
-  bool last;        // last stage of its tile
+// The block's stage stream as a run of segments: each layer-1 tile (S[0]
+// stages), each layer-2 tile (S[1] stages), then an endless run of empty
+// stages.  A walker moves one stage at a time; only entering a new segment
+// costs more than a decrement.
+enum SegKind : int { SEG_L1 = 0, SEG_L2 = 1, SEG_END = 2 };
+
+struct Seg {
+  int kind;
+  int tile;   // tile index within its layer
+  int left;   // stages left in the segment, the current one included
 };
 
-__device__ __forceinline__ StageId stage_id(const Stream& st, int g) {
-  StageId id;
-  const int p = g < st.first2 ? 0 : 1;
-  const int r = p ? g - st.first2 : g;
-  const int i = r / st.S[p], s = r - i * st.S[p];
-  id.phase = p;
-  id.n0 = ((int64_t)blockIdx.x + (int64_t)i * gridDim.x) * 16;
-  id.k0 = (int64_t)s * kSK;
-  id.last = (s == st.S[p] - 1);
-  return id;
+template <bool TWO>
+__device__ __forceinline__ void seg_next(const Stream& st, Seg& q) {
+  if (q.kind == SEG_L1 && q.tile + 1 < st.nt[0]) {
+    ++q.tile;
+    q.left = st.S[0];
+  } else if (q.kind == SEG_L1 && TWO && st.nt[1] > 0) {
+    q.kind = SEG_L2;
+    q.tile = 0;
+    q.left = st.S[1];
+  } else if (q.kind == SEG_L2 && q.tile + 1 < st.nt[1]) {
+    ++q.tile;
+    q.left = st.S[1];
+  } else {
+    q.kind = SEG_END;
+    q.left = 1 << 30;
+  }
 }
 
-template <bool DUAL1, bool TWO>
+template <bool TWO>
+__device__ __forceinline__ Seg seg_first(const Stream& st) {
+  Seg q{SEG_L1, 0, st.S[0]};
+  if (st.nt[0] == 0) {   // no layer-1 tile
+    q.tile = st.nt[0];
+    seg_next<TWO>(st, q);
+  }
+  return q;
+}
+
+template <bool DUAL1, bool TWO, int MC>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
-  constexpr int kSets = DUAL1 ? 2 : 1;   // layer 1 of GeGLU streams Wg and Wu together
-  // stages in flight: 3 x 28 KB per block, or 2 x 56 KB when two weights stream
-  constexpr int kRing = DUAL1 ? 2 : 3;
-  __shared__ u32x4_t slab[2][kSets][16 * kCH];
+  using RS = RingShape<MC, DUAL1>;
+  constexpr int R = RS::R, XI = RS::XI;
+  constexpr int kSets = DUAL1 ? 2 : 1;
+  constexpr uint32_t kSlot = (uint32_t)RS::kSlotBytes;
+  __shared__ u32x4_t ring[R][kWChunks + RS::kXChunks];
   __shared__ float4 red[kSets][kWorkers * 64];
+  __shared__ uint32_t bias_lds[2][64];         // bias of the control wave's current and next tile
+  __shared__ u32x4_t sink[64];                 // destination of activation loads with no row
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int li = lane & 15, lg = lane >> 4;
-  const bool worker = wave < kWorkers;
-  const Stream st = make_stream<TWO>(L1, L2);
+  const Stream st = make_stream<DUAL1, TWO>(L1, L2);
+  const int G = (int)gridDim.x, blk = (int)blockIdx.x;
 
   uint32_t target = 0;
   if (TWO) target = ld_coherent(sync + kSyncGenWord) + 1u;
 
-  u32x4_t wreg[kRing][kSets][kLoads];
-  u32x4_t xreg[kRing][kKS];
-  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (wave < kWorkers) {
+    // ======================= worker waves =====================================
+    const int w = wave;
+    const int K0 = in_sgpr((int)L1.K), K1 = in_sgpr((int)L2.K);
+    const int N0 = in_sgpr((int)L1.N), N1 = in_sgpr((int)L2.N);
+    const uint64_t Wa0 = in_sgpr(reinterpret_cast<uint64_t>(L1.W0));
+    const uint64_t Wb0 = in_sgpr(reinterpret_cast<uint64_t>(DUAL1 ? L1.W1 : L1.W0));
+    const uint64_t Wa1 = in_sgpr(reinterpret_cast<uint64_t>(L2.W0));
+    const uint64_t X0 = in_sgpr(reinterpret_cast<uint64_t>(L1.x));
+    const uint64_t X1 = in_sgpr(reinterpret_cast<uint64_t>(L2.x));
 
-  // ---- worker side ---------------------------------------------------------
-  // The control wave executes the same ring loads with every offset out of
-  // range (no memory access), so all waves issue the same sequence of loads
-  // and the compiler's count of loads in flight stays exact on every path.
-  // weight chunks of stage g: worker thread tid loads chunks tid + i*kWT; a
-  // wave instruction covers 64 consecutive chunks (1 KB) of one weight row.
-  auto issue_w = [&](int g, u32x4_t (&dst)[kSets][kLoads]) {
-    const bool in = worker && g < st.total;
-    const StageId id = stage_id(st, in ? g : 0);
-    const GemvLayer& L = id.phase ? L2 : L1;
-    const int64_t left = L.N - id.n0;
-    const int64_t rows = in ? (left < 16 ? left : 16) : 0;
-    const uint32_t nrec = (uint32_t)(rows * L.K * 2);
+    // Per-lane byte offsets, fixed for a whole layer: weight load i of this
+    // wave (stage row r, global chunk c of the row: chunk c of row r sits at
+    // LDS position c ^ (r & 15)), and activation load j (one 1 KB piece: one
+    // row, or two rows of 512 B for gate + up).  The *t variants are a tile's
+    // last stage, whose chunks past K go out of range.
+    uint32_t woff[2][2], wofft[2][2], xoff[2][XI], xofft[2][XI];
 #pragma unroll
-    for (int set = 0; set < kSets; ++set) {
-      const uint16_t* W = (set && id.phase == 0) ? L.W1 : L.W0;
-      const __amdgpu_buffer_rsrc_t r = make_rsrc(W + id.n0 * L.K, (set && id.phase == 1) ? 0u : nrec);
+    for (int p = 0; p < 2; ++p) {
+      const bool dual = DUAL1 && p == 0;
+      const int K = pick(p != 0, K1, K0);
+      const int sk = dual ? kSK2 : kSK1;
+      const int klast = ((K + sk - 1) / sk - 1) * sk;   // k0 of a tile's last stage
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int q = tid + i * kWT;
-        const int row = q / kCH, c = q % kCH;
-        const int64_t k = id.k0 + c * 8;
-        const uint32_t off = k < L.K ? (uint32_t)((row * L.K + k) * 2) : kOutOfRange;
-        dst[set][i] = bload(r, off);
+      for (int i = 0; i < 2; ++i) {
+        const int inst = 2 * w + i;
+        int r, c;
+        if (dual) {
+          const int sr = 2 * inst + (lane >> 5);   // stage row 0..31: gate 0-15, up 16-31
+          r = sr & 15;
+          c = swz(lane & 31, sr);
+        } else {
+          r = inst;
+          c = swz(lane, inst);
+        }
+        woff[p][i] = (uint32_t)(r * K + c * 8) * 2u;
+        wofft[p][i] = klast + c * 8 < K ? woff[p][i] : kOutOfRange;
+      }
+#pragma unroll
+      for (int j = 0; j < XI; ++j) {
+        int r, c;
+        if (dual) {
+          r = 2 * w + (lane >> 5);               // one load: rows 2w, 2w+1
+          c = swz(lane & 31, r);
+        } else {
+          r = w + 8 * j;
+          c = swz(lane, r);
+        }
+        const bool has = dual ? j == 0 : true;
+        xoff[p][j] = has ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
+        xofft[p][j] = klast + c * 8 < K ? xoff[p][j] : kOutOfRange;
       }
     }
-  };
-  // activation fragments of stage g (x, or h after the barrier); rows >= M
-  // fall past the end of the activation buffer and read 0.  live == false
-  // (h before the barrier) loads nothing.
-  auto issue_x = [&](int g, bool live, u32x4_t (&dst)[kKS]) {
-    const bool in = worker && live && g < st.total;
-    const StageId id = stage_id(st, in ? g : 0);
-    const GemvLayer& L = id.phase ? L2 : L1;
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(L.x, in ? (uint32_t)((int64_t)M * L.K * 2) : 0u);
+    // LDS: this wave's 1 KB weight pieces of a slot, its activation pieces
+    // (or the sink), and this lane's fragment positions
+    const uint32_t ring0 = lds_addr(&ring[0][0]);
+    const uint32_t lds_w = ring0 + (uint32_t)(2 * w) * 1024u;
+    const uint32_t sink_lds = lds_addr(&sink[0]);
+    uint32_t lds_x[2][XI];   // [layer][load]: offset inside a slot, or the sink (bit 31)
 #pragma unroll
-    for (int j = 0; j < kKS; ++j) {
-      const int64_t k = id.k0 + (int64_t)(wave * 16 + j * 4 + lg) * 8;
-      const uint32_t off = k < L.K ? (uint32_t)(((int64_t)li * L.K + k) * 2) : kOutOfRange;
-      dst[j] = bload(r, off);
-    }
-  };
-  auto write_slab = [&](int buf, int phase, const u32x4_t (&src)[kSets][kLoads]) {
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int q = tid + i * kWT;
-      const int row = q / kCH, c = q % kCH;
-      const int slot = row * kCH + ((c & ~15) | ((c & 15) ^ row));
-#pragma unroll
-      for (int set = 0; set < kSets; ++set) {
-        if (set == 1 && phase == 1) break;
-        slab[buf][set][slot] = src[set][i];
+      for (int j = 0; j < XI; ++j) {
+        const bool dual = DUAL1 && p == 0;
+        const int piece = dual ? w : w + 8 * j;        // which 1 KB piece of the slot's activation area
+        const bool fits = dual ? (j == 0 && 2 * w < MC) : (w + 8 * j < MC);
+        lds_x[p][j] = fits ? (uint32_t)(kWChunks * 16 + piece * 1024) : 0x80000000u;
       }
     }
-  };
-  auto compute = [&](int buf, int phase, const u32x4_t (&x)[kKS]) {
+    uint32_t apos[2], bpos[2];
 #pragma unroll
-    for (int j = 0; j < kKS; ++j) {
-      const int c = wave * 16 + j * 4 + lg;
-      const int slot = li * kCH + ((c & ~15) | ((c & 15) ^ li));
-      acc0 = mfma_16x16x32(slab[buf][0][slot], x[j], acc0);
-      if (DUAL1 && phase == 0) acc1 = mfma_16x16x32(slab[buf][kSets - 1][slot], x[j], acc1);
+    for (int t = 0; t < 2; ++t) {
+      const int c = 8 * w + 4 * t + lg;
+      apos[t] = (uint32_t)(li * 64 + swz(c, li)) * 16u;
+      bpos[t] = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * 64 + swz(c, li)) * 16u;
     }
-  };
-  auto post_partials = [&](int phase) {
-    red[0][wave * 64 + lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
-    if (DUAL1 && phase == 0)
-      red[kSets - 1][wave * 64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
-    acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
+    const int cd = 4 * w + lg;   // gate + up: one k-step per stage
+    const uint32_t gpos = (uint32_t)(li * 32 + swz(cd, li)) * 16u;
+    const uint32_t bdpos = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * 32 + swz(cd, li)) * 16u;
+    const bool bcol = li < M;    // this lane's activation row exists
+    bool aok[2][2];              // weight fragment inside K at a tile's last stage
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool dual = DUAL1 && p == 0;
+      const int K = pick(p != 0, K1, K0);
+      const int sk = dual ? kSK2 : kSK1;
+      const int klast = ((K + sk - 1) / sk - 1) * sk;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) aok[p][t] = klast + (dual ? cd : 8 * w + 4 * t + lg) * 8 < K;
+    }
 
-  // ---- control side --------------------------------------------------------
-  // bias of the control wave's next tile, requested one tile ahead
-  int ctile = 0;
-  uint2 cbias = make_uint2(0u, 0u);
-  auto ctrl_fetch_bias = [&](int t) {
-    const int ntiles = st.nt[0] + st.nt[1];
-    const int p = t < st.nt[0] ? 0 : 1;
-    const GemvLayer& L = p ? L2 : L1;
-    const int i = p ? t - st.nt[0] : t;
-    const int64_t n = ((int64_t)blockIdx.x + (int64_t)i * gridDim.x) * 16 + 4 * lg;
-    const bool want = t < ntiles && L.bias != nullptr;          // wave-uniform
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(want ? L.bias : L.W0, want ? (uint32_t)(L.N * 2) : 0u);
-    const uint32_t off = n < L.N ? (uint32_t)(n * 2) : kOutOfRange;   // per lane
-    cbias = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0));
+    f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- issue side: the next stage to load ---------------------------------
+    Seg is = seg_first<TWO>(st);
+    bool h_ok = false;         // h may be read (the barrier has passed)
+    uint64_t wbase = 0, xbase = 0;
+    uint32_t wrec = 0, xrec = 0, step_bytes = kSK1 * 2;
+    bool i_l2 = false, i_tailk = false;
+    auto issue_enter = [&]() {   // issue state for the segment `is` begins
+      i_l2 = TWO && is.kind == SEG_L2;
+      const bool real = is.kind != SEG_END;
+      const bool dual = DUAL1 && is.kind == SEG_L1;
+      const int K = pick(i_l2, K1, K0);
+      const int N = pick(i_l2, N1, N0);
+      const int sk = dual ? kSK2 : kSK1;
+      step_bytes = (uint32_t)sk * 2u;
+      i_tailk = K % sk != 0;
+      const int n0 = (blk + is.tile * G) * 16;
+      const int left = N - n0;
+      const int rows = real ? (left < 16 ? left : 16) : 0;
+      const uint64_t W = pick(i_l2, Wa1, (dual && w >= 4) ? Wb0 : Wa0);   // loads 8-15: up rows
+      wbase = rows ? W + (uint64_t)((int64_t)n0 * K) * 2u : W;
+      wrec = (uint32_t)(rows * K) * 2u;
+      xbase = pick(i_l2, X1, X0);
+      xrec = real ? (uint32_t)(M * K) * 2u : 0u;
+    };
+    // all loads of one stage into ring slot `slot`: 2 weight pieces, then XI
+    // activation pieces (h only once the barrier has passed)
+    int inext = 0;             // stream index of the next stage to load
+    auto issue = [&](uint32_t slot) {
+      if (inext >= st.total) return;   // past the end: nothing to load
+      ++inext;
+      if (is.left == 0) {
+        seg_next<TWO>(st, is);
+        issue_enter();
+      }
+      const bool tail = i_tailk && is.left == 1;
+      const i32x4_t wd = make_desc(wbase, wrec);
+      const uint32_t slot_lds = ring0 + slot * kSlot;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t off = pick(tail, pick(i_l2, wofft[1][i], wofft[0][i]), pick(i_l2, woff[1][i], woff[0][i]));
+        asm_load_lds(wd, lds_w + slot * kSlot + (uint32_t)i * 1024u, off);
+      }
+      const i32x4_t xd = make_desc(xbase, (i_l2 && !h_ok) ? 0u : xrec);
+#pragma unroll
+      for (int j = 0; j < XI; ++j) {
+        const uint32_t off = pick(tail, pick(i_l2, xofft[1][j], xofft[0][j]), pick(i_l2, xoff[1][j], xoff[0][j]));
+        const uint32_t where = pick(i_l2, lds_x[1][j], lds_x[0][j]);
+        asm_load_lds(xd, (where & 0x80000000u) ? sink_lds : slot_lds + where, off);
+      }
+      --is.left;
+      wbase += step_bytes;
+      wrec = wrec > step_bytes ? wrec - step_bytes : 0u;
+      xbase += step_bytes;
+      xrec = xrec > step_bytes ? xrec - step_bytes : 0u;
+    };
+
+    // ---- consume side: the stage in ring slot `slot` ------------------------
+    // Once every stage has been requested (stream index >= quiet_from), the
+    // first step waits for all loads and meets the other waves once; the
+    // rest read resident stages with no wait and no barrier.
+    Seg cs = seg_first<TWO>(st);
+    const int quiet_from = st.total - (R - 1) > 0 ? st.total - (R - 1) : 0;
+    int gidx = 0;              // stream index of the stage being consumed
+    auto step = [&](uint32_t slot) {
+      if (cs.left == 0) seg_next<TWO>(st, cs);
+      if (gidx < quiet_from) {
+        wait_vm<RS::kLoads * (R - 2)>();   // this wave's loads of the stage
+        lds_barrier();                     // the stage is in LDS for every wave; the slot before it is free
+        issue(slot == 0 ? R - 1 : slot - 1);
+      } else if (gidx == quiet_from) {
+        wait_vm<0>();                      // every load of the stream has landed ...
+        lds_barrier();                     // ... for every wave
+      }
+      ++gidx;
+      const bool real = cs.kind != SEG_END;
+      const bool last = real && cs.left == 1;
+      if (real) {
+        const bool c_l2 = TWO && cs.kind == SEG_L2;
+        const bool tail = last && (pick(c_l2, K1, K0) % ((DUAL1 && !c_l2) ? kSK2 : kSK1) != 0);
+        const char* sp = reinterpret_cast<const char*>(&ring[0][0]) + slot * kSlot;
+        if (DUAL1 && !c_l2) {
+          u32x4_t g = *reinterpret_cast<const u32x4_t*>(sp + gpos);
+          u32x4_t u = *reinterpret_cast<const u32x4_t*>(sp + gpos + 16 * 32 * 16);
+          u32x4_t x = zero4();               // lanes of absent rows read nothing
+          if (bcol) x = *reinterpret_cast<const u32x4_t*>(sp + bdpos);
+          if (tail && !aok[0][0]) g = u = zero4();
+          acc0 = mfma_16x16x32(g, x, acc0);
+          acc1 = mfma_16x16x32(u, x, acc1);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            u32x4_t a = *reinterpret_cast<const u32x4_t*>(sp + apos[t]);
+            u32x4_t x = zero4();
+            if (bcol) x = *reinterpret_cast<const u32x4_t*>(sp + bpos[t]);
+            if (tail && !pick(c_l2, aok[1][t], aok[0][t])) a = zero4();
+            acc0 = mfma_16x16x32(a, x, acc0);
+          }
+        }
+      }
+      if (last) {                        // partial tile of this wave -> control wave
+        red[0][w * 64 + lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
+        if (DUAL1 && cs.kind == SEG_L1)
+          red[kSets - 1][w * 64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
+        acc0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        lds_barrier();
+      }
+      --cs.left;
+    };
+
+    // prologue: stages 0 .. R-2.  It runs before any barrier: touching h here
+    // would also pull unpublished lines into an L2.
+    issue_enter();
+    for (uint32_t d = 0; d < (uint32_t)R - 1; ++d) issue(d);
+    uint32_t slot = 0;
+    for (int g = 0; g < st.first2; ++g) {
+      step(slot);
+      slot = slot + 1 == (uint32_t)R ? 0 : slot + 1;
+    }
+    if (TWO && st.total > st.first2) {
+      lds_barrier();   // the control wave has seen every block's h
+      h_ok = true;
+      // h slices of the layer-2 stages already in flight, re-requested now
+      // that h is complete (in order after the empty ones: they land later)
+      const uint32_t hrec = (uint32_t)(M * K1) * 2u;
+      const bool htailk = K1 % kSK1 != 0;
+      Seg hq = cs;
+      uint32_t hs = slot;
+      for (int e = 0; e < R - 1; ++e) {
+        if (hq.left == 0) seg_next<TWO>(st, hq);
+        if (hq.kind != SEG_L2) break;      // the rest was never requested
+        const bool in = true;
+        const uint32_t k0b = (uint32_t)((st.S[1] - hq.left) * kSK1) * 2u;   // k0 of the stage, in bytes
+        const i32x4_t hd = make_desc(X1 + (in ? k0b : 0u), in ? hrec - k0b : 0u);
+        const bool tail = in && htailk && hq.left == 1;
+#pragma unroll
+        for (int j = 0; j < XI; ++j) {
+          const uint32_t where = lds_x[1][j];
+          asm_load_lds(hd, (where & 0x80000000u) ? sink_lds : ring0 + hs * kSlot + where,
+                       pick(tail, xofft[1][j], xoff[1][j]));
+        }
+        --hq.left;
+        hs = hs + 1 == (uint32_t)R ? 0 : hs + 1;
+      }
+      wait_vm<0>();    // the steps below then wait as in steady state (their
+      lds_barrier();   // counts only over-estimate what is younger); h is in LDS for every wave
+      for (int g = st.first2; g < st.total; ++g) {
+        step(slot);
+        slot = slot + 1 == (uint32_t)R ? 0 : slot + 1;
+      }
+    }
+    wait_vm<0>();      // nothing is left in flight into LDS at exit
+    return;
+  }
+
+  // ========================= control wave =====================================
+  const uint16_t* const bias1 = in_sgpr(L1.bias);
+  const uint16_t* const bias2 = in_sgpr(L2.bias);
+  uint16_t* const y1 = in_sgpr(L1.y);
+  uint16_t* const y2 = in_sgpr(L2.y);
+  const int N1 = in_sgpr((int)L1.N), N2 = in_sgpr((int)L2.N);
+  const int act1 = in_sgpr(L1.act), act2 = in_sgpr(L2.act);
+  // The bias of the next tile is requested one tile ahead, straight into LDS.
+  auto ctrl_fetch_bias = [&](int bslot, const Seg& q) {
+    const bool l2 = TWO && q.kind == SEG_L2;
+    const bool real = q.kind != SEG_END;
+    const uint16_t* bias = pick(l2, bias2, bias1);
+    const int N = pick(l2, N2, N1);
+    const int n = (blk + q.tile * G) * 16 + 2 * lane;   // 2 outputs per lane
+    const bool want = real && bias != nullptr;          // wave-uniform
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(pick<const uint16_t*>(want, bias, y1), want ? (uint32_t)N * 2u : 0u);
+    const uint32_t off = (lane < 8 && n < N) ? (uint32_t)n * 2u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)&bias_lds[bslot][0], 4, off, 0, 0, 0);
   };
-  auto ctrl_epilogue = [&](const StageId& id) {
-    const bool dual = DUAL1 && id.phase == 0;
-    const GemvLayer& L = id.phase ? L2 : L1;
+  auto ctrl_epilogue = [&](const Seg& q, int bslot) {
+    const bool l2 = TWO && q.kind == SEG_L2;
+    const bool dual = DUAL1 && q.kind == SEG_L1;
+    const int N = pick(l2, N2, N1);
+    const int act = pick(l2, act2, act1);
+    uint16_t* const y = pick(l2, y2, y1);
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int w = 0; w < kWorkers; ++w) {
-      const float4 t = red[0][w * 64 + lane];
+    for (int v = 0; v < kWorkers; ++v) {
+      const float4 t = red[0][v * 64 + lane];
       g[0] += t.x; g[1] += t.y; g[2] += t.z; g[3] += t.w;
       if (dual) {
-        const float4 v = red[kSets - 1][w * 64 + lane];
-        u[0] += v.x; u[1] += v.y; u[2] += v.z; u[3] += v.w;
+        const float4 r = red[kSets - 1][v * 64 + lane];
+        u[0] += r.x; u[1] += r.y; u[2] += r.z; u[3] += r.w;
       }
     }
-    const uint2 bias = cbias;
-    ctrl_fetch_bias(++ctile);
+    wait_vm<0>();   // this tile's bias (and the control wave's earlier stores)
+    const uint2 bias = *reinterpret_cast<const uint2*>(&bias_lds[bslot][2 * lg]);
     const int m = li;
-    const int64_t n = id.n0 + 4 * lg;   // this lane's 4 consecutive outputs
-    if (m < M && n < L.N) {
+    const int n = (blk + q.tile * G) * 16 + 4 * lg;   // this lane's 4 consecutive outputs
+    if (m < M && n < N) {
       float v[4];
       const float b[4] = {bf16_lo(bias.x), bf16_hi(bias.x), bf16_lo(bias.y), bf16_hi(bias.y)};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        v[r] = dual ? gelu_tanh(g[r]) * u[r] : apply_act(g[r] + b[r], L.act);   // b = 0 without a bias
+        v[r] = dual ? gelu_tanh(g[r]) * u[r] : apply_act(g[r] + b[r], act);   // b = 0 without a bias
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(L.y + (int64_t)m * L.N + n);
-      if (TWO && id.phase == 0) {   // h: read by every block after the barrier
+      uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)m * N + n);
+      if (TWO && !l2) {   // h: read by every block after the barrier
         st_coherent(dst, lo);
         st_coherent(dst + 1, hi);
       } else {
@@ -288,85 +559,81 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   };
   // this block's h is complete once the control wave's stores are: raise the flag
   auto ctrl_arrive = [&]() {
-    wait_vm_all();
-    if (lane == 0) st_coherent(sync + kSyncFlagWord0 + blockIdx.x, target);
+    wait_vm<0>();
+    if (lane == 0) st_coherent(sync + kSyncFlagWord0 + blk, target);
   };
-  // every control wave polls every block's flag (one hop)
+  // Every control wave reads every block's flag: 4 flags per lane in one
+  // 16-byte device-coherent load, so one round trip checks 256 blocks.
   auto ctrl_wait_all = [&]() {
-    for (int b = lane; b < (int)gridDim.x; b += 64) {
-      uint32_t spins = 0;
-      while (ld_coherent(sync + kSyncFlagWord0 + b) != target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > kSpinLimit) {
-          __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // whole 16-byte groups (the header's flag area holds a multiple of 4
+    // words); flags past the grid are ignored below
+    const __amdgpu_buffer_rsrc_t rf = make_rsrc(sync + kSyncFlagWord0, ((uint32_t)G + 3u) / 4u * 16u);
+    for (int b0 = 0; b0 < G; b0 += 256) {
+      const int f0 = b0 + 4 * lane;
+      for (uint32_t spins = 0;; ++spins) {
+        const u32x4_t v = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rf, (uint32_t)f0 * 4u, 0, 16 /* sc1 */));
+        bool ok = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ok = ok && (f0 + j >= G || v[j] == target);
+        if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+        if (spins >= kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
+        __builtin_amdgcn_s_sleep(1);
       }
     }
-    if (blockIdx.x == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
+    if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
+  };
+  // the control wave meets the workers at each of their barriers
+  Seg cs = seg_first<TWO>(st);
+  Seg bq = cs;                // the tile whose bias is requested next
+  int bslot = 0;
+  ctrl_fetch_bias(0, bq);
+  const int quiet_from = st.total - (R - 1) > 0 ? st.total - (R - 1) : 0;
+  int gidx = 0;
+  auto ctrl_step = [&]() {
+    if (cs.left == 0) seg_next<TWO>(st, cs);
+    if (gidx <= quiet_from) lds_barrier();
+    ++gidx;
+    if (cs.kind != SEG_END && cs.left == 1) {
+      lds_barrier();                 // the workers' partial tiles are in LDS
+      const Seg q = cs;
+      seg_next<TWO>(st, bq);         // request the next tile's bias
+      ctrl_epilogue(q, bslot);
+      ctrl_fetch_bias(bslot ^ 1, bq);
+      bslot ^= 1;
+      if (TWO && q.kind == SEG_L1 && q.tile == st.nt[0] - 1) ctrl_arrive();
+    }
+    --cs.left;
   };
 
-  // An h fragment may be requested only once the barrier has passed, i.e. from
-  // iteration first2 on (its wait runs at the start of that iteration); the
-  // ones requested earlier are re-requested right after the barrier.
-  auto x_live = [&](int gx, int g) { return !(TWO && gx >= st.first2 && g < st.first2); };
-
-  if (!worker) {
-    ctrl_fetch_bias(0);
-    if (TWO && st.first2 == 0) ctrl_arrive();   // no layer-1 tile: nothing to publish
+  if (TWO && st.first2 == 0) ctrl_arrive();   // no layer-1 tile: nothing to publish
+  for (int g = 0; g < st.first2; ++g) ctrl_step();
+  if (TWO && st.total > st.first2) {
+    ctrl_wait_all();                 // entering layer 2: every block's h is complete
+    lds_barrier();
+    lds_barrier();                   // the workers' h slices are in LDS
+    for (int g = st.first2; g < st.total; ++g) ctrl_step();
   }
-  // the prologue runs before iteration 0, i.e. before any barrier (g = -1):
-  // touching h here would also pull not-yet-published lines into the L2
-#pragma unroll
-  for (int d = 0; d < kRing; ++d) {
-    issue_w(d, wreg[d]);
-    issue_x(d, x_live(d, -1), xreg[d]);
-  }
-
-  // ---- main loop, unrolled by the ring size so ring slots are static --------
-  for (int g0 = 0; g0 < st.total; g0 += kRing) {
-#pragma unroll
-    for (int d = 0; d < kRing; ++d) {
-      const int g = g0 + d;
-      const bool valid = g < st.total;
-      const StageId id = stage_id(st, valid ? g : 0);
-      if (TWO && valid && g == st.first2) {   // entering layer 2: h must be complete
-        if (!worker) ctrl_wait_all();
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < kRing; ++e) issue_x(g + e, true, xreg[(d + e) % kRing]);
-      }
-      if (worker && valid) write_slab(g & 1, id.phase, wreg[d]);
-      __syncthreads();
-      issue_w(g + kRing, wreg[d]);
-      if (worker && valid) compute(g & 1, id.phase, xreg[d]);
-      issue_x(g + kRing, x_live(g + kRing, g), xreg[d]);
-      if (worker && valid && id.last) post_partials(id.phase);
-      if (valid && id.last) {
-        __syncthreads();
-        if (!worker) {
-          ctrl_epilogue(id);
-          if (TWO && g == st.first2 - 1) ctrl_arrive();
-        }
-      }
-    }
-  }
+  wait_vm<0>();
 }
 
 struct Occ {
   bool probed = false;
   bool ok = false;
   int cus = 0;
-  int one = 0;      // blocks per CU, one-layer kernel
-  int two = 0;      // blocks per CU, two-layer kernel
-  int two_dual = 0; // blocks per CU, GeGLU two-layer kernel
+  int per_cu = 0;   // blocks per CU (the LDS ring admits one)
 };
 
 std::mutex g_occ_mu;
 Occ g_occ[64];
 
 // Residency of the decode kernels on the current device, queried once per
-// device with the runtime's occupancy calculator and cached.
+// device with the runtime's occupancy calculator (for the largest-LDS
+// variant) and cached.
 Occ occ() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return Occ{};
@@ -377,16 +644,25 @@ Occ occ() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return o;
     o.cus = prop.multiProcessorCount;
-    bool ok = true;
-    ok &= hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &o.one, reinterpret_cast<const void*>(&decode_kernel<false, false>), kThreads, 0) == hipSuccess;
-    ok &= hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &o.two, reinterpret_cast<const void*>(&decode_kernel<false, true>), kThreads, 0) == hipSuccess;
-    ok &= hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &o.two_dual, reinterpret_cast<const void*>(&decode_kernel<true, true>), kThreads, 0) == hipSuccess;
-    o.ok = ok && o.cus > 0 && o.one > 0 && o.two > 0 && o.two_dual > 0;
+    const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                        &o.per_cu, reinterpret_cast<const void*>(&decode_kernel<true, true, 1>), kThreads,
+                        0) == hipSuccess;
+    o.ok = ok && o.cus > 0 && o.per_cu > 0;
   }
   return o;
+}
+
+// activation-row class of M: the rows an LDS stage holds
+template <bool DUAL1, bool TWO>
+hipError_t launch_mc(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
+                     hipStream_t s) {
+  if (M <= 1)
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+  else if (M <= 4)
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 4>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+  else
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 16>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -395,30 +671,27 @@ hipError_t launch_gemv(const GemvLayer& L, int M, hipStream_t s) {
   if (L.geglu) return hipErrorInvalidValue;   // gate+up runs only in the two-layer kernel
   const int64_t tiles = (L.N + 15) / 16;
   if (tiles <= 0 || M <= 0) return hipSuccess;
+  if (M > 16) return hipErrorInvalidValue;
   const Occ o = occ();
   if (!o.ok) return hipErrorInvalidDevice;
   // one layer has no barrier: cap the grid at one resident round of blocks
-  const unsigned grid = (unsigned)std::min<int64_t>(tiles, (int64_t)o.cus * o.one);
-  hipLaunchKernelGGL((decode_kernel<false, false>), dim3(grid), dim3(kThreads), 0, s, L, L, M,
-                     static_cast<uint32_t*>(nullptr));
-  return hipGetLastError();
+  const unsigned grid = (unsigned)std::min<int64_t>(tiles, (int64_t)o.cus * o.per_cu);
+  return launch_mc<false, false>(grid, L, L, M, nullptr, s);
 }
 
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
                                    hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (M > 16) return hipErrorInvalidValue;
   const Occ o = occ();
   if (!o.ok) return hipErrorInvalidDevice;
-  const bool dual = L1.geglu != 0;
   const int64_t tiles1 = (L1.N + 15) / 16, tiles2 = (L2.N + 15) / 16;
   // every block must be resident at once: the barrier waits for all of them
-  const int64_t cap = std::min<int64_t>((int64_t)o.cus * (dual ? o.two_dual : o.two), kDecodeMaxBlocks);
+  const int64_t cap = std::min<int64_t>((int64_t)o.cus * o.per_cu, kDecodeMaxBlocks);
   const unsigned grid = (unsigned)std::min<int64_t>(cap, std::max(tiles1, tiles2));
   if (grid == 0) return hipSuccess;
-  if (dual)
-    hipLaunchKernelGGL((decode_kernel<true, true>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  else
-    hipLaunchKernelGGL((decode_kernel<false, true>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  return hipGetLastError();
+  if (L1.geglu) return launch_mc<true, true>(grid, L1, L2, M, sync, s);
+  return launch_mc<false, true>(grid, L1, L2, M, sync, s);
 }
 
 }  // namespace fmlp

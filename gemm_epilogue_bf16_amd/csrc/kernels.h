@@ -79,6 +79,7 @@ constexpr int kSyncGenWord = 0;
 constexpr int kSyncTimeoutWord = 2;
 constexpr int kSyncFlagWord0 = 64;
 constexpr int kDecodeMaxBlocks = kWorkspaceHeaderBytes / 4 - kSyncFlagWord0;
+static_assert(kDecodeMaxBlocks % 4 == 0, "flags are read 4 at a time");
 
 // Two dependent layers in ONE launch: every block is resident at once, layer-1
 // outputs are published through device-coherent stores and a flag barrier,
