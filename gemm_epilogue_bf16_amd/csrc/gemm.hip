@@ -18,8 +18,8 @@
 // K advances in stages of 64; each stage of A and B is copied HBM -> registers
 // -> LDS (double buffered, one barrier per stage, the next stage's global loads
 // in flight while the current stage feeds the MFMAs).  LDS rows are 128 bytes
-// (8 chunks of 16 B) with chunk c of row r stored at slot c ^ (r & 7), so the
-// 16-byte fragment reads of 8 consecutive rows hit 8 distinct slots.
+// (8 chunks of 16 B), each chunk at an XOR-permuted slot chosen so the 16-byte
+// fragment reads of 16 rows are bank-conflict free (swz_a, swz_b below).
 // v_mfma_f32_16x16x32_bf16 is fed with the weight as the row operand and the
 // activation as the column operand; the weight rows of a fragment pair are
 // interleaved so each lane ends with 8 consecutive output columns of one row,
@@ -32,6 +32,14 @@ namespace fmlp {
 namespace {
 
 constexpr int kBK = 64;  // k per LDS stage
+
+// LDS rows are 128 bytes (8 chunks of 16 B).  With 64 four-byte banks, two
+// rows share a bank line, so a 16-lane fragment read is conflict free when
+// (row & 1, slot of the chunk) differs across its 16 rows.  Activation
+// fragments read 16 consecutive rows; weight fragments read rows interleaved
+// in groups of 4 (8*(l/4) + (l%4)).  Each gets its own chunk permutation.
+__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_b(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT, bool GATHER, bool GROUPED>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
@@ -98,7 +106,7 @@ gemm_bf16_kernel(GemmParams p) {
     if (lr >= row_end) lr = row_end - 1;
     const int64_t src = GATHER ? (int64_t)p.a_rows[lr] : lr;
     a_src[i] = p.A + src * p.lda + ck;
-    a_slot[i] = r * 8 + ((tid & 7) ^ (r & 7));
+    a_slot[i] = r * 8 + ((tid & 7) ^ swz_a(r));
   }
 #pragma unroll
   for (int i = 0; i < B_IT; ++i) {
@@ -111,7 +119,7 @@ gemm_bf16_kernel(GemmParams p) {
     }
     if (n >= N) n = N - 1;
     b_src[i] = base + n * K + ck;
-    b_slot[i] = r * 8 + ((tid & 7) ^ (r & 7));
+    b_slot[i] = r * 8 + ((tid & 7) ^ swz_b(r));
   }
 
   u32x4_t ra[A_IT], rb[B_IT];
@@ -152,29 +160,42 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Software pipeline: the fragments of the next k-step are read from LDS
+  // while the MFMAs of the current one run, and the second k-step's MFMAs
+  // straddle the stage barrier (they read registers only), so every phase
+  // pairs LDS traffic with MFMA work.
+  u32x4_t xf[2][FM], wf[2][FN];
+  auto read_frags = [&](int buf, int ks, int set) {
+    const int chunk = ks * 4 + lg;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) xf[set][f] = sA[buf][x_row[f] * 8 + (chunk ^ swz_a(x_row[f]))];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) wf[set][f] = sB[buf][w_row[f] * 8 + (chunk ^ swz_b(w_row[f]))];
+  };
+  auto mfmas = [&](int set, int i0, int i1) {
+#pragma unroll
+    for (int i = i0; i < i1; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(wf[set][j], xf[set][i], acc[i][j]);
+  };
+
   const int nk = (int)((K + kBK - 1) / kBK);
   gload(0);
   swrite(0);
   __syncthreads();
+  read_frags(0, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = ks * 4 + lg;
-      u32x4_t xf[FM], wf[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) xf[f] = sA[cur][x_row[f] * 8 + (chunk ^ (x_row[f] & 7))];
-#pragma unroll
-      for (int f = 0; f < FN; ++f) wf[f] = sB[cur][w_row[f] * 8 + (chunk ^ (w_row[f] & 7))];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(wf[j], xf[i], acc[i][j]);
-    }
-    if (kt + 1 < nk) swrite(cur ^ 1);
+    const bool more = kt + 1 < nk;
+    if (more) gload(kt + 1);
+    read_frags(cur, 1, 1);
+    mfmas(0, 0, FM);                 // k-step 0 of this stage
+    mfmas(1, 0, FM / 2);             // first half of k-step 1
+    if (more) swrite(cur ^ 1);
     __syncthreads();
+    if (more) read_frags(cur ^ 1, 0, 0);
+    mfmas(1, FM / 2, FM);            // second half of k-step 1
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -253,7 +274,7 @@ template <int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   switch (tile) {
     case TILE_128x128: return launch_cfg<128, 128, 2, 2, OUT, GATHER, GROUPED>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 4, OUT, GATHER, GROUPED>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 2, OUT, GATHER, GROUPED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
