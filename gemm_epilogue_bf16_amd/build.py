@@ -20,6 +20,13 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfmlp.so")
 SOURCES = ["abi.cpp", "gemm.hip", "decode.hip", "small_mlp.hip", "moe.hip"]
 ARCH = "gfx950"
+# Per-source flags.  The GEMM main loop is written in issue order (fragment
+# reads of the next stage ahead of the MFMAs they hide behind); the pre-RA
+# machine scheduler reorders it so that the 256 fp32 accumulators of a wave no
+# longer fit in AGPRs next to the fragments, and the register allocator then
+# shuffles them between register files on every MFMA.  Keeping the source
+# order keeps them in place.
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-enable-misched=0"]}
 
 
 def hipcc() -> str:
@@ -45,7 +52,8 @@ def common_flags() -> list[str]:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -23,7 +23,9 @@ thread_local int g_path = 0;   // 0 auto, 1 decode, 2 two-GEMM, 3 small fused
 constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3;
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kSmallMaxDim = 128;
-constexpr int64_t kMaxDim = int64_t(1) << 31;   // bound on any single dimension
+constexpr int64_t kMaxDim = int64_t(1) << 31;   // bound on a token count
+constexpr int64_t kMaxInner = int64_t(1) << 22; // bound on an inner dimension: a 256-row
+                                                // operand tile spans < 2^31 bytes
 constexpr size_t kHeader = kWorkspaceHeaderBytes;  // barrier / error words
 
 fmlp_status fail(fmlp_status s, const char* fmt, ...) {
@@ -63,7 +65,8 @@ fmlp_status check_rows(const char* name, int64_t v) {
 }
 
 fmlp_status check_inner(const char* name, int64_t v) {
-  if (v <= 0 || v >= kMaxDim) return fail(FMLP_E_SHAPE, "%s=%lld must be positive", name, (long long)v);
+  if (v <= 0 || v >= kMaxInner)
+    return fail(FMLP_E_SHAPE, "%s=%lld must be in [8, 2^22)", name, (long long)v);
   if (v % 8 != 0) return fail(FMLP_E_ALIGN, "%s=%lld is not a multiple of 8", name, (long long)v);
   return FMLP_OK;
 }
@@ -344,6 +347,8 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
   if (top_k < 1 || top_k > 8) return fail(FMLP_E_ARG, "top_k=%d must be in [1, 8]", top_k);
   if ((int64_t)T * top_k >= (int64_t(1) << 31))
     return fail(FMLP_E_SHAPE, "T*top_k=%lld is too large", (long long)T * top_k);
+  if (T * D >= (int64_t(1) << 30))
+    return fail(FMLP_E_SHAPE, "T*D=%lld must be below 2^30", (long long)(T * D));
   REQUIRE_PTR(x);
   if (expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
   if (gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
@@ -378,6 +383,7 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
 
   GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, 0);
   g.a_rows = r.tok_of;
+  g.a_src_rows = T;
   g.group_off = r.group_off;
   g.tile_off = r.tile_off;
   g.groups = E;

@@ -51,6 +51,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace fmlp {
 
@@ -62,7 +63,6 @@ constexpr int kWChunks = 1024;                 // 16-byte weight chunks per stag
 constexpr int kSK1 = 512;                      // k per stage, one weight matrix
 constexpr int kSK2 = 256;                      // k per stage, gate + up together
 constexpr uint32_t kSpinLimit = 1u << 20;      // bounded waits
-constexpr uint32_t kOutOfRange = 0x80000000u;  // offset past any descriptor's end
 constexpr int kLdsBudget = 160 * 1024;
 
 // Activation rows held per stage (a class of M) and the ring depth it leaves.
@@ -85,34 +85,6 @@ __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
 __device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-  compiler_fence();
-}
-// Workgroup barrier for LDS hand-off: this wave's LDS accesses are complete,
-// then all waves meet.  No vector-memory wait: loads into LDS are waited for
-// explicitly, per stage, before it.
-__device__ __forceinline__ void lds_barrier() {
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-}
-
-// Every descriptor here is wave-uniform by construction (it depends only on
-// the stage, the layer, the block and the wave); readfirstlane puts it in
-// SGPRs so no load needs a per-lane loop.  readfirstlane returns a signed int:
-// each half is widened through uint32_t, never sign-extended into the other.
-__device__ __forceinline__ uint32_t uniform32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
-}
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   const uint64_t ua = ((uint64_t)uniform32((uint32_t)(a >> 32)) << 32) | (uint64_t)uniform32((uint32_t)a);
@@ -120,33 +92,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            (int)uniform32(bytes), 0x00020000);
 }
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// ---- worker-side loads ------------------------------------------------------
-// The streaming loop issues its loads into LDS through inline assembly and
-// places every wait itself: the compiler's own bookkeeping would treat each
-// LDS read as dependent on every load into LDS still in flight and drain the
-// ring before each stage.
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
-// raw buffer descriptor in SGPRs: base, stride 0, num_records = bytes
-__device__ __forceinline__ i32x4_t make_desc(uint64_t base, uint32_t bytes) {
-  i32x4_t d;
-  d[0] = (int)uniform32((uint32_t)base);
-  d[1] = (int)(uniform32((uint32_t)(base >> 32)) & 0xFFFFu);
-  d[2] = (int)uniform32(bytes);
-  d[3] = 0x00020000;
-  return d;
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return uniform32((uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p));
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 16 bytes per lane into LDS at lds + 16 * lane (lds wave-uniform)
-__device__ __forceinline__ void asm_load_lds(const i32x4_t& d, uint32_t lds, uint32_t off) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-               :: "v"(off), "s"(d), "s"(lds) : "memory", "m0");
-}
-#pragma clang diagnostic pop
 
 // c ? a : b on values: a conditional between two lvalues would select their
 // addresses and load, which keeps the operands in private memory.

@@ -15,56 +15,66 @@
 //   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights)
 //
 // Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves.
-// K advances in stages of 64; each stage of A and B is copied HBM -> registers
-// -> LDS (double buffered, one barrier per stage, the next stage's global loads
-// in flight while the current stage feeds the MFMAs).  LDS rows are 128 bytes
-// (8 chunks of 16 B), each chunk at an XOR-permuted slot chosen so the 16-byte
-// fragment reads of 16 rows are bank-conflict free (swz_a, swz_b below).
+// K advances in stages of 32 (one MFMA k-step).  Stages stream from memory
+// straight into a ring of R LDS slots with buffer loads that write LDS, R - 1
+// stages ahead of the MFMAs and with no register staging; each wave waits
+// only for its own loads of the stage it is about to read, and one workgroup
+// barrier per stage publishes the stage and frees the slot the next load
+// goes to.  LDS rows are 64 bytes (4 chunks of 16 B); each 1 KB load
+// instruction fills 16 rows, a lane fetching the global chunk whose permuted
+// home (swz_a, swz_b below) is its own LDS position, so the 16-byte fragment
+// reads of 16 rows are bank-conflict free.  Rows past the tile's end and
+// chunks past K are requested out of range and arrive as zeros.
 // v_mfma_f32_16x16x32_bf16 is fed with the weight as the row operand and the
 // activation as the column operand; the weight rows of a fragment pair are
 // interleaved so each lane ends with 8 consecutive output columns of one row,
 // stored as one 16-byte write.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace fmlp {
 
 namespace {
 
-constexpr int kBK = 64;  // k per LDS stage
+constexpr int kBK = 32;  // k per LDS stage
 
-// LDS rows are 128 bytes (8 chunks of 16 B).  With 64 four-byte banks, two
+// LDS rows are 64 bytes (4 chunks of 16 B).  With 64 four-byte banks, four
 // rows share a bank line, so a 16-lane fragment read is conflict free when
-// (row & 1, slot of the chunk) differs across its 16 rows.  Activation
+// (row & 3, slot of the chunk) differs across its 16 rows.  Activation
 // fragments read 16 consecutive rows; weight fragments read rows interleaved
 // in groups of 4 (8*(l/4) + (l%4)).  Each gets its own chunk permutation.
-__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int swz_b(int r) { return ((r >> 1) & 1) | ((r >> 2) & 6); }
+__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
+__device__ __forceinline__ int swz_b(int r) { return (r >> 3) & 3; }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int OUT, bool GATHER, bool GROUPED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int R, int OUT, bool GATHER, bool GROUPED>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
-  constexpr int NT = WAVES_M * WAVES_N * 64;
+  constexpr int NW = WAVES_M * WAVES_N;
   constexpr int TM = BM / WAVES_M;   // wave tile rows (activation rows)
   constexpr int TN = BN / WAVES_N;   // wave tile width in B-tile rows
   constexpr int FM = TM / 16;
   constexpr int FN = TN / 16;
   constexpr bool DUAL = (OUT == GEMM_OUT_GEGLU);
   constexpr int HALF = FN / 2;       // DUAL: gate fragments [0,HALF), up [HALF,FN)
-  constexpr int ROWS_PER_PASS = NT / 8;
-  constexpr int A_IT = BM / ROWS_PER_PASS;
-  constexpr int B_IT = BN / ROWS_PER_PASS;
+  constexpr int A_INS = BM / (16 * NW);   // 1 KB load instructions per wave and stage
+  constexpr int B_INS = BN / (16 * NW);
+  constexpr int LOADS = A_INS + B_INS;
+  constexpr int SLOT = (BM + BN) * 4;     // 16-byte chunks per ring slot
   constexpr int OUT_N = DUAL ? BN / 2 : BN;   // output columns per block
-  static_assert(BM % ROWS_PER_PASS == 0 && BN % ROWS_PER_PASS == 0, "load mapping");
-  static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile");
+  static_assert(A_INS >= 1 && B_INS >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "load mapping");
+  static_assert(!DUAL || (BN / 2) % (16 * NW) == 0, "a load instruction stays in one weight set");
+  static_assert(TM % 16 == 0 && TN % 16 == 0 && FM % 2 == 0, "wave tile");
   static_assert(DUAL ? (HALF % 2 == 0) : (FN % 2 == 0), "fragment pairs");
+  static_assert(R >= 3 && LOADS * (R - 2) < 64, "ring depth");
 
-  __shared__ u32x4_t sA[2][BM * 8];
-  __shared__ u32x4_t sB[2][BN * 8];
+  __shared__ u32x4_t ring[R * SLOT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
@@ -94,56 +104,83 @@ gemm_bf16_kernel(GemmParams p) {
   const int64_t n0 = (int64_t)tn * OUT_N;
   const int64_t K = p.K, N = p.N;
 
-  // ---- per-thread global source rows (clamped; k chunk fixed per thread) --
-  const int ck = (tid & 7) * 8;           // k offset of this thread's chunk in a stage
-  const uint16_t* a_src[A_IT];
-  const uint16_t* b_src[B_IT];
-  int a_slot[A_IT], b_slot[B_IT];
+  // ---- load descriptors and per-lane offsets -------------------------------
+  // Load instruction i of this wave fills tile rows 16 * (i * NW + wave) +
+  // lane / 4; the lane's LDS position in its row is lane % 4 and it fetches
+  // the chunk that belongs there.  Byte spans fit 31 bits (checked by the
+  // caller), so kOutOfRange is past every descriptor's end.
+  const int jr = lane >> 2, jp = lane & 3;
+  const int64_t a_rows_here = row_end - row_begin;
+  const i32x4_t da = GATHER
+      ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
+      : make_desc(reinterpret_cast<uint64_t>(p.A + row_begin * p.lda), (uint32_t)(a_rows_here * p.lda * 2));
+  const int64_t n_here = min((int64_t)OUT_N, N - n0);   // weight rows of each set in this tile
+  const i32x4_t db0 = make_desc(reinterpret_cast<uint64_t>(B0 + n0 * K), (uint32_t)(n_here * K * 2));
+  const i32x4_t db1 = DUAL ? make_desc(reinterpret_cast<uint64_t>(B1 + n0 * K), (uint32_t)(n_here * K * 2)) : db0;
+  uint32_t a_off[A_INS], b_off[B_INS];
+  int a_k[A_INS], b_k[B_INS];   // k offset of the lane's chunk within a stage
 #pragma unroll
-  for (int i = 0; i < A_IT; ++i) {
-    const int r = (tid >> 3) + i * ROWS_PER_PASS;
-    int64_t lr = row_begin + r;
-    if (lr >= row_end) lr = row_end - 1;
-    const int64_t src = GATHER ? (int64_t)p.a_rows[lr] : lr;
-    a_src[i] = p.A + src * p.lda + ck;
-    a_slot[i] = r * 8 + ((tid & 7) ^ swz_a(r));
-  }
-#pragma unroll
-  for (int i = 0; i < B_IT; ++i) {
-    const int r = (tid >> 3) + i * ROWS_PER_PASS;
-    const uint16_t* base = B0;
-    int64_t n = n0 + r;
-    if (DUAL && r >= BN / 2) {
-      base = B1;
-      n = n0 + (r - BN / 2);
+  for (int i = 0; i < A_INS; ++i) {
+    const int r = 16 * (i * NW + wave) + jr;
+    const int c = jp ^ swz_a(r);
+    a_k[i] = 8 * c;
+    if (r < a_rows_here) {
+      const int64_t src = GATHER ? (int64_t)p.a_rows[row_begin + r] : (int64_t)r;
+      a_off[i] = (uint32_t)(src * p.lda * 2 + c * 16);
+    } else {
+      a_off[i] = kOutOfRange;
     }
-    if (n >= N) n = N - 1;
-    b_src[i] = base + n * K + ck;
-    b_slot[i] = r * 8 + ((tid & 7) ^ swz_b(r));
   }
+#pragma unroll
+  for (int i = 0; i < B_INS; ++i) {
+    const int r = 16 * (i * NW + wave) + jr;
+    const int c = jp ^ swz_b(r);
+    const int n = DUAL ? r % (BN / 2) : r;
+    b_k[i] = 8 * c;
+    b_off[i] = n < n_here ? (uint32_t)(n * K * 2 + c * 16) : kOutOfRange;
+  }
+  const uint32_t ring_lds = lds_addr(&ring[0]);
+  // Stages run in pairs (the fragment register sets alternate within a
+  // pair); an odd count gets one all-zero stage more, which adds nothing.
+  const int nk = (int)((K + kBK - 1) / kBK);
+  const int NS = (nk + 1) & ~1;
+  const int full = (int)(K / kBK);   // stages with no chunk past K
 
-  u32x4_t ra[A_IT], rb[B_IT];
-  auto gload = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
-    const bool ok = (k0 + ck) < K;
+  // stage s into ring slot `slot`
+  auto issue = [&](int s, int slot) {
+    const uint32_t kb = (uint32_t)s * (kBK * 2);
+    const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16) + (uint32_t)wave * 1024u;
+    if (s < full) {
 #pragma unroll
-    for (int i = 0; i < A_IT; ++i) ra[i] = ok ? ld16(a_src[i] + k0) : zero4();
+      for (int i = 0; i < A_INS; ++i) asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, a_off[i], kb);
 #pragma unroll
-    for (int i = 0; i < B_IT; ++i) rb[i] = ok ? ld16(b_src[i] + k0) : zero4();
-  };
-  auto swrite = [&](int buf) {
+      for (int i = 0; i < B_INS; ++i) {
+        const bool up = DUAL && 16 * (i * NW) >= BN / 2;   // compile-time per i
+        asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + i * NW * 1024), b_off[i], kb);
+      }
+    } else {   // the k tail, or the padding stage: chunks past K arrive as zeros
+      const int k0 = s * kBK;
 #pragma unroll
-    for (int i = 0; i < A_IT; ++i) sA[buf][a_slot[i]] = ra[i];
+      for (int i = 0; i < A_INS; ++i)
+        asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, k0 + a_k[i] < K ? a_off[i] : kOutOfRange, kb);
 #pragma unroll
-    for (int i = 0; i < B_IT; ++i) sB[buf][b_slot[i]] = rb[i];
+      for (int i = 0; i < B_INS; ++i) {
+        const bool up = DUAL && 16 * (i * NW) >= BN / 2;
+        asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + i * NW * 1024),
+                     k0 + b_k[i] < K ? b_off[i] : kOutOfRange, kb);
+      }
+    }
   };
 
-  // ---- LDS fragment rows --------------------------------------------------
+  // ---- LDS fragment positions (chunk index within a slot) --------------------
   const int li = lane & 15;   // fragment row (weight) / column (activation)
   const int lg = lane >> 4;   // k group: 8 consecutive k
-  int x_row[FM], w_row[FN];
+  int x_pos[FM], w_pos[FN];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) x_row[f] = wm * TM + f * 16 + li;
+  for (int f = 0; f < FM; ++f) {
+    const int r = wm * TM + f * 16 + li;
+    x_pos[f] = r * 4 + (lg ^ swz_a(r));
+  }
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     // interleave the rows of a fragment pair: lane group g ends up holding
@@ -151,7 +188,8 @@ gemm_bf16_kernel(GemmParams p) {
     const int set = DUAL ? f / HALF : 0;
     const int fl = DUAL ? f % HALF : f;
     const int base = set * (BN / 2) + wn * (DUAL ? TN / 2 : TN) + (fl >> 1) * 32;
-    w_row[f] = base + 8 * (li >> 2) + 4 * (fl & 1) + (li & 3);
+    const int r = base + 8 * (li >> 2) + 4 * (fl & 1) + (li & 3);
+    w_pos[f] = BM * 4 + r * 4 + (lg ^ swz_b(r));
   }
 
   f32x4_t acc[FM][FN];
@@ -160,42 +198,62 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Software pipeline: the fragments of the next k-step are read from LDS
-  // while the MFMAs of the current one run, and the second k-step's MFMAs
-  // straddle the stage barrier (they read registers only), so every phase
-  // pairs LDS traffic with MFMA work.
   u32x4_t xf[2][FM], wf[2][FN];
-  auto read_frags = [&](int buf, int ks, int set) {
-    const int chunk = ks * 4 + lg;
+  auto read_frags = [&](int slot, auto set_c) {
+    constexpr int set = decltype(set_c)::value;
+    const u32x4_t* sl = ring + slot * SLOT;
 #pragma unroll
-    for (int f = 0; f < FM; ++f) xf[set][f] = sA[buf][x_row[f] * 8 + (chunk ^ swz_a(x_row[f]))];
+    for (int f = 0; f < FM; ++f) xf[set][f] = sl[x_pos[f]];
 #pragma unroll
-    for (int f = 0; f < FN; ++f) wf[set][f] = sB[buf][w_row[f] * 8 + (chunk ^ swz_b(w_row[f]))];
+    for (int f = 0; f < FN; ++f) wf[set][f] = sl[w_pos[f]];
   };
-  auto mfmas = [&](int set, int i0, int i1) {
+  auto mfmas = [&](auto set_c, int i0, int i1) {
+    constexpr int set = decltype(set_c)::value;
 #pragma unroll
     for (int i = i0; i < i1; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(wf[set][j], xf[set][i], acc[i][j]);
   };
+  // Hand-off to stage s+1 (slot `next`), run after this wave's reads of stage
+  // s (slot `cur`) have been issued: wait for this wave's loads of stage s+1;
+  // barrier (stage s+1 is in LDS for every wave and every wave has finished
+  // reading slot `cur`); stage s+R goes to slot `cur`.  vmcnt cannot tell
+  // stages apart, so near the end, with fewer stages in flight, it drains.
+  auto hand_off = [&](int s, int cur) {
+    if (s + R - 1 < NS) wait_vm<LOADS * (R - 2)>(); else wait_vm<0>();
+    lds_barrier();
+    if (s + R < NS) issue(s + R, cur);
+  };
+  using Set0 = std::integral_constant<int, 0>;
+  using Set1 = std::integral_constant<int, 1>;
 
-  const int nk = (int)((K + kBK - 1) / kBK);
-  gload(0);
-  swrite(0);
-  __syncthreads();
-  read_frags(0, 0, 0);
+  // Prologue: stages 0 .. R-2 in flight, stage 0 published, R-1 issued.
+#pragma unroll
+  for (int s = 0; s < R - 1; ++s)
+    if (s < NS) issue(s, s);
+  if (R - 1 <= NS) wait_vm<LOADS * (R - 2)>(); else wait_vm<0>();
+  lds_barrier();
+  if (R - 1 < NS) issue(R - 1, R - 1);
+  read_frags(0, Set0{});
 
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
-    read_frags(cur, 1, 1);
-    mfmas(0, 0, FM);                 // k-step 0 of this stage
-    mfmas(1, 0, FM / 2);             // first half of k-step 1
-    if (more) swrite(cur ^ 1);
-    __syncthreads();
-    if (more) read_frags(cur ^ 1, 0, 0);
-    mfmas(1, FM / 2, FM);            // second half of k-step 1
+  // Stage s lives in slot s % R.  The second half of each stage's MFMAs runs
+  // after the next stage's fragment reads are issued, so LDS latency hides
+  // behind MFMA work; the first half runs before the barrier, from registers.
+  int slot = 0;
+  for (int g = 0; g < NS; g += 2) {
+    const int s1 = slot + 1 == R ? 0 : slot + 1;
+    const int s2 = s1 + 1 == R ? 0 : s1 + 1;
+    mfmas(Set0{}, 0, FM / 2);
+    hand_off(g, slot);
+    read_frags(s1, Set1{});
+    mfmas(Set0{}, FM / 2, FM);
+    mfmas(Set1{}, 0, FM / 2);
+    if (g + 2 < NS) {
+      hand_off(g + 1, s1);
+      read_frags(s2, Set0{});
+    }
+    mfmas(Set1{}, FM / 2, FM);
+    slot = s2;
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -256,7 +314,7 @@ gemm_bf16_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int OUT, bool GATHER, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int R, int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -265,7 +323,7 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, OUT, GATHER, GROUPED>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, R, OUT, GATHER, GROUPED>), dim3((unsigned)blocks),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -273,8 +331,8 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
 template <int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   switch (tile) {
-    case TILE_128x128: return launch_cfg<128, 128, 2, 2, OUT, GATHER, GROUPED>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 2, OUT, GATHER, GROUPED>(p, s);
+    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 4, OUT, GATHER, GROUPED>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 2, 4, OUT, GATHER, GROUPED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

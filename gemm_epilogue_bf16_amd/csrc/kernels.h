@@ -29,6 +29,7 @@ struct GemmParams {
   int act;                 // Act, GEMM_OUT_BF16 only
   // gather / grouped (mixture of experts)
   const int32_t* a_rows;     // gather: A row of each logical row, or nullptr
+  int64_t a_src_rows;        // gather: rows of A (a_src_rows * lda * 2 < 2^31)
   const int32_t* group_off;  // grouped: [groups+1] logical row offsets
   const int32_t* tile_off;   // grouped: [groups+1] prefix of m-tiles per group
   int groups;
@@ -40,7 +41,7 @@ struct GemmParams {
 // Tile configurations compiled in.
 enum GemmTile : int {
   TILE_128x128 = 0,   // 4 waves, 64x64 per wave
-  TILE_256x256 = 1,   // 8 waves, 128x64 per wave
+  TILE_256x256 = 1,   // 4 waves, 128x128 per wave
   TILE_COUNT
 };
 

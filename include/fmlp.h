@@ -25,8 +25,10 @@
  *              not alias inputs.
  *  Shapes:     every inner dimension (K, H, N, D) must be a positive multiple
  *              of 8 (16-byte rows), the analogue of the "align8" GEMM variants
- *              named on the page above; the token count M (or T) may be any
- *              value >= 0 (M == 0 is a no-op).
+ *              named on the page above, and below 2^22 (kernels address a
+ *              256-row tile of an operand with 32-bit byte offsets); the token
+ *              count M (or T) may be any value >= 0 below 2^31 (M == 0 is a
+ *              no-op).
  *  Streams:    fmlp_stream is a hipStream_t (NULL = the null stream).  Every
  *              call only enqueues work on that stream and returns; FMLP_OK means
  *              "enqueued".  Device faults surface at the caller's next sync.
@@ -128,6 +130,8 @@ size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H);
  * fp32 (deterministic; no atomics).  An expert id outside [0,E) contributes
  * nothing and is counted in the workspace error word (fmlp_moe_error_count
  * documents where).  Workspace: fmlp_moe_workspace_size(T,D,H,E,top_k) bytes.
+ * x must hold fewer than 2^30 elements (T*D < 2^30): routed rows are gathered
+ * from it with 32-bit byte offsets; a larger x is FMLP_E_SHAPE.
  */
 fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
                            const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd,

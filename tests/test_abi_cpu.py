@@ -61,6 +61,7 @@ def _err(L):
     ((X, W, None, 0, 4, 30, 8, Y, None), E_ALIGN, "K=30"),
     ((X, W, None, 0, 4, 32, 12, Y, None), E_ALIGN, "N=12"),
     ((X, W, None, 0, 4, 0, 8, Y, None), E_SHAPE, "K=0"),
+    ((X, W, None, 0, 4, 1 << 22, 8, Y, None), E_SHAPE, "K=4194304"),
     ((X, W, None, 0, -1, 32, 8, Y, None), E_SHAPE, "M=-1"),
     ((X, W, None, 7, 4, 32, 8, Y, None), E_ARG, "act=7"),
     ((None, W, None, 0, 4, 32, 8, Y, None), E_NULL, "x is NULL"),
@@ -130,6 +131,11 @@ def test_moe_validation(L):
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, D, H, E, k, Y, WS, need - 1, None) == E_WS
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, T, 4092, H, E, k, Y, WS, need, None) == E_ALIGN
     assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, 0, D, H, E, k, Y, WS, need, None) == OK
+    # routed rows are gathered from x with 32-bit byte offsets: x < 2^30 elements
+    big_t = (1 << 30) // D
+    big_need = L.fmlp_moe_workspace_size(big_t, D, H, E, k)
+    assert L.fmlp_moe_geglu(X, ids, gw, W, W, W, big_t, D, H, E, k, Y, WS, big_need, None) == E_SHAPE
+    assert "T*D" in _err(L)
     assert L.fmlp_moe_error_offset() < 8192
 
 
