@@ -41,13 +41,20 @@ namespace {
 
 constexpr int kBK = 32;  // k per LDS stage
 
-// LDS rows are 64 bytes (4 chunks of 16 B).  With 64 four-byte banks, four
-// rows share a bank line, so a 16-lane fragment read is conflict free when
-// (row & 3, slot of the chunk) differs across its 16 rows.  Activation
-// fragments read 16 consecutive rows; weight fragments read rows interleaved
-// in groups of 4 (8*(l/4) + (l%4)).  Each gets its own chunk permutation.
-__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
-__device__ __forceinline__ int swz_b(int r) { return (r >> 3) & 3; }
+// LDS rows are 64 bytes (4 chunks of 16 B).  A ds_read_b128 takes four LDS
+// cycles of 16 lanes (measured on gfx950): the cycle of lane l is set by its
+// half-wave (l >> 5) and the parity of its quad index bits ((l >> 2) & 7),
+// and within a cycle the lanes must hit distinct 16-byte bank groups (unit
+// index mod 16, i.e. 4 rows x 4 chunk slots here).  A fragment read puts k
+// group lg = l >> 4 and row offset li = l & 15 on each lane, so a cycle holds
+// two k groups, each with half of the row offsets.  Chunk c of row r sits at
+// slot c ^ kSwz[q], q = bits 2-3 of the row for activation fragments (16
+// consecutive rows) and bits 3-4 for weight fragments (rows interleaved in
+// groups of 4: 8*(l/4) + (l%4)); kSwz = {0, 2, 3, 1} makes every cycle of
+// both kinds of read conflict free, where the plain q would pair its lanes.
+__device__ __forceinline__ int swz_q(int q) { return (0x78 >> (2 * q)) & 3; }   // {0, 2, 3, 1}
+__device__ __forceinline__ int swz_a(int r) { return swz_q((r >> 2) & 3); }
+__device__ __forceinline__ int swz_b(int r) { return swz_q((r >> 3) & 3); }
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, int R, int OUT, bool GATHER, bool GROUPED>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
