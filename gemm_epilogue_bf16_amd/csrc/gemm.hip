@@ -56,6 +56,21 @@ __device__ __forceinline__ int swz_q(int q) { return (0x78 >> (2 * q)) & 3; }   
 __device__ __forceinline__ int swz_a(int r) { return swz_q((r >> 2) & 3); }
 __device__ __forceinline__ int swz_b(int r) { return swz_q((r >> 3) & 3); }
 
+// The main loop interleaves MFMAs with loads and LDS reads in a fixed order.
+// Instruction selection moves an MFMA builtin freely (it touches no memory),
+// so the loop issues them as volatile asm, which keeps its place among the
+// other volatile asm (loads into LDS, waits, barriers); the accumulator is
+// pinned in AGPRs and updated in place.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void mfma_ordered(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
+}
+// wait states between the last MFMA of the loop and the first read of its
+// accumulators by ordinary code (the hazard check cannot see into asm)
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
+#pragma clang diagnostic pop
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int R, int OUT, bool GATHER, bool GROUPED>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
@@ -146,37 +161,37 @@ gemm_bf16_kernel(GemmParams p) {
     b_k[i] = 8 * c;
     b_off[i] = n < n_here ? (uint32_t)(n * K * 2 + c * 16) : kOutOfRange;
   }
-  const uint32_t ring_lds = lds_addr(&ring[0]);
+  const uint32_t ring_lds = lds_addr(&ring[0]) + (uint32_t)wave * 1024u;
   // Stages run in pairs (the fragment register sets alternate within a
   // pair); an odd count gets one all-zero stage more, which adds nothing.
-  const int nk = (int)((K + kBK - 1) / kBK);
+  const int Kc = (int)K;                       // < 2^22
+  const int nk = (Kc + kBK - 1) / kBK;
   const int NS = (nk + 1) & ~1;
-  const int full = (int)(K / kBK);   // stages with no chunk past K
 
-  // stage s into ring slot `slot`
-  auto issue = [&](int s, int slot) {
-    const uint32_t kb = (uint32_t)s * (kBK * 2);
-    const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16) + (uint32_t)wave * 1024u;
-    if (s < full) {
+  // This wave's load offsets for stage s: chunks past K (the k tail, the
+  // padding stage and the stages issued past the end) are out of range.
+  auto stage_offs = [&](int s, uint32_t (&o)[LOADS]) {
+    const int k0 = s * kBK;
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i) asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, a_off[i], kb);
+    for (int i = 0; i < A_INS; ++i) o[i] = k0 + a_k[i] < Kc ? a_off[i] : kOutOfRange;
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i) {
-        const bool up = DUAL && 16 * (i * NW) >= BN / 2;   // compile-time per i
-        asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + i * NW * 1024), b_off[i], kb);
-      }
-    } else {   // the k tail, or the padding stage: chunks past K arrive as zeros
-      const int k0 = s * kBK;
-#pragma unroll
-      for (int i = 0; i < A_INS; ++i)
-        asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, k0 + a_k[i] < K ? a_off[i] : kOutOfRange, kb);
-#pragma unroll
-      for (int i = 0; i < B_INS; ++i) {
-        const bool up = DUAL && 16 * (i * NW) >= BN / 2;
-        asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + i * NW * 1024),
-                     k0 + b_k[i] < K ? b_off[i] : kOutOfRange, kb);
-      }
+    for (int i = 0; i < B_INS; ++i) o[A_INS + i] = k0 + b_k[i] < Kc ? b_off[i] : kOutOfRange;
+  };
+  // load i (of LOADS) of a stage into the slot at LDS byte address `base`
+  auto dma = [&](int i, uint32_t base, const uint32_t (&o)[LOADS], uint32_t kb) {
+    if (i < A_INS) {
+      asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, o[i], kb);
+    } else {
+      const int b = i - A_INS;
+      const bool up = DUAL && 16 * (b * NW) >= BN / 2;   // compile-time per i
+      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + b * NW * 1024), o[i], kb);
     }
+  };
+  auto issue_all = [&](int s, int slot) {
+    uint32_t o[LOADS];
+    stage_offs(s, o);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), o, (uint32_t)s * (kBK * 2));
   };
 
   // ---- LDS fragment positions (chunk index within a slot) --------------------
@@ -205,63 +220,76 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // Fragment registers: two sets, alternating by stage.  Read n of a stage
+  // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order the next stage's MFMAs
+  // consume them.
+  constexpr int NREADS = FM + FN;
   u32x4_t xf[2][FM], wf[2][FN];
-  auto read_frags = [&](int slot, auto set_c) {
+  auto frag_read = [&](int n, const u32x4_t* sl, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const u32x4_t* sl = ring + slot * SLOT;
-#pragma unroll
-    for (int f = 0; f < FM; ++f) xf[set][f] = sl[x_pos[f]];
-#pragma unroll
-    for (int f = 0; f < FN; ++f) wf[set][f] = sl[w_pos[f]];
+    if (n == 0) xf[set][0] = sl[x_pos[0]];
+    else if (n <= FN) wf[set][n - 1] = sl[w_pos[n - 1]];
+    else xf[set][n - FN] = sl[x_pos[n - FN]];
   };
-  auto mfmas = [&](auto set_c, int i0, int i1) {
+  auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a stage: row t / FN, column t % FN
     constexpr int set = decltype(set_c)::value;
-#pragma unroll
-    for (int i = i0; i < i1; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_16x16x32(wf[set][j], xf[set][i], acc[i][j]);
-  };
-  // Hand-off to stage s+1 (slot `next`), run after this wave's reads of stage
-  // s (slot `cur`) have been issued: wait for this wave's loads of stage s+1;
-  // barrier (stage s+1 is in LDS for every wave and every wave has finished
-  // reading slot `cur`); stage s+R goes to slot `cur`.  vmcnt cannot tell
-  // stages apart, so near the end, with fewer stages in flight, it drains.
-  auto hand_off = [&](int s, int cur) {
-    if (s + R - 1 < NS) wait_vm<LOADS * (R - 2)>(); else wait_vm<0>();
-    lds_barrier();
-    if (s + R < NS) issue(s + R, cur);
+    mfma_ordered(acc[t / FN][t % FN], wf[set][t % FN], xf[set][t / FN]);
   };
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
 
   // Prologue: stages 0 .. R-2 in flight, stage 0 published, R-1 issued.
+  // Every stage up to the last one read plus R - 1 is issued (past the end
+  // they load nothing), so every wait below is the same.
 #pragma unroll
-  for (int s = 0; s < R - 1; ++s)
-    if (s < NS) issue(s, s);
-  if (R - 1 <= NS) wait_vm<LOADS * (R - 2)>(); else wait_vm<0>();
+  for (int s = 0; s < R - 1; ++s) issue_all(s, s);
+  wait_vm<LOADS * (R - 2)>();
   lds_barrier();
-  if (R - 1 < NS) issue(R - 1, R - 1);
-  read_frags(0, Set0{});
+  issue_all(R - 1, R - 1);
+#pragma unroll
+  for (int n = 0; n < NREADS; ++n) frag_read(n, ring, Set0{});
 
-  // Stage s lives in slot s % R.  The second half of each stage's MFMAs runs
-  // after the next stage's fragment reads are issued, so LDS latency hides
-  // behind MFMA work; the first half runs before the barrier, from registers.
+  // One stage, from slot `slot` in register set CUR.  Phase A: the first
+  // half of its MFMAs, from registers only.  Hand-off: wait for this wave's
+  // loads of the next stage; barrier (the next stage is in LDS for every
+  // wave, and every wave has finished reading `slot`).  Phase B: the second
+  // half of the MFMAs, each followed by at most one other instruction of the
+  // hand-off stream: the loads of stage s + R into `slot`, then the fragment
+  // reads of the next stage into the other set, so the matrix core never
+  // waits for a run of memory instructions.
+  constexpr int NMA = (FM / 2) * FN;          // MFMAs per phase
+  constexpr int NOPS = LOADS + NREADS;
+  auto step = [&](int s, int slot, auto cur_c) {
+    constexpr int CUR = decltype(cur_c)::value;
+    using Nxt = std::integral_constant<int, CUR ^ 1>;
+    uint32_t o[LOADS];
+    stage_offs(s + R, o);
+#pragma unroll
+    for (int t = 0; t < NMA; ++t) mfma_t(t, cur_c);
+    wait_vm<LOADS * (R - 2)>();
+    lds_barrier();
+    const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16);
+    const uint32_t kb = (uint32_t)(s + R) * (kBK * 2);
+    const u32x4_t* sl = ring + (slot + 1 == R ? 0 : slot + 1) * SLOT;
+#pragma unroll
+    for (int t = 0; t < NMA; ++t) {
+      mfma_t(NMA + t, cur_c);
+#pragma unroll
+      for (int n = t * NOPS / NMA; n < (t + 1) * NOPS / NMA; ++n) {
+        if (n < LOADS) dma(n, base, o, kb);
+        else frag_read(n - LOADS, sl, Nxt{});
+      }
+    }
+  };
   int slot = 0;
   for (int g = 0; g < NS; g += 2) {
     const int s1 = slot + 1 == R ? 0 : slot + 1;
-    const int s2 = s1 + 1 == R ? 0 : s1 + 1;
-    mfmas(Set0{}, 0, FM / 2);
-    hand_off(g, slot);
-    read_frags(s1, Set1{});
-    mfmas(Set0{}, FM / 2, FM);
-    mfmas(Set1{}, 0, FM / 2);
-    if (g + 2 < NS) {
-      hand_off(g + 1, s1);
-      read_frags(s2, Set0{});
-    }
-    mfmas(Set1{}, FM / 2, FM);
-    slot = s2;
+    step(g, slot, Set0{});
+    step(g + 1, s1, Set1{});
+    slot = s1 + 1 == R ? 0 : s1 + 1;
   }
+  wait_vm<0>();   // the last stages' loads (of nothing) land before LDS is released
+  mfma_drain();
 
   // ---- epilogue -------------------------------------------------------------
 #pragma unroll
