@@ -38,14 +38,22 @@ COLD_BYTES = 1 << 30           # rotate weight copies until this many bytes (4x 
 # the page's fused 4096-wide GELU MLP at batch 1 on H100: 8.1 us (context only)
 PAGE_H100_FUSED_US = 8.1
 
-KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "decode.hip", "small_mlp.hip", "moe.hip"]
+# the files each kernel is built from (plus the build script, which sets flags)
+KERNEL_SOURCES = {
+    "decode_kernel": ["common.h", "kernels.h", "lds_dma.h", "decode.hip"],
+    "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
+    "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
+}
 
 
-def kernel_source_sha() -> str:
+def kernel_source_sha(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gemm_epilogue_bf16_amd", "csrc", f), "rb") as fh:
+    pkg = os.path.join(ROOT, "gemm_epilogue_bf16_amd")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(pkg, "csrc", f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(pkg, "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -208,8 +216,9 @@ def time_oracle(case: Case, seconds: float):
 
 
 def read_traffic(case: Case):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
-    were taken on the current kernel sources; else None."""
+    """HBM bytes per step (all of a step's launches of the kernel) from
+    committed rocprofv3 PMC summaries, if they were taken on the current
+    sources of that kernel; else None."""
     p = os.path.join(ROOT, "profiles", f"{case.kernel}__{case.w.name}__traffic.json")
     if not os.path.exists(p):
         return None
@@ -217,9 +226,9 @@ def read_traffic(case: Case):
         d = json.load(open(p))
     except Exception:
         return None
-    if d.get("kernel_source_sha") != kernel_source_sha():
+    if d.get("kernel_source_sha") != kernel_source_sha(case.kernel):
         return None
-    return d.get("bytes_per_launch")
+    return d.get("bytes_per_step", d.get("bytes_per_launch"))
 
 
 def main(argv=None):

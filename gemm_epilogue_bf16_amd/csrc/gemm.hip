@@ -14,17 +14,22 @@
 //                        the intermediate never makes an HBM round trip)
 //   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights)
 //
-// Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves.
-// K advances in stages of 32 (one MFMA k-step).  Stages stream from memory
-// straight into a ring of R LDS slots with buffer loads that write LDS, R - 1
-// stages ahead of the MFMAs and with no register staging; each wave waits
-// only for its own loads of the stage it is about to read, and one workgroup
-// barrier per stage publishes the stage and frees the slot the next load
-// goes to.  LDS rows are 64 bytes (4 chunks of 16 B); each 1 KB load
-// instruction fills 16 rows, a lane fetching the global chunk whose permuted
-// home (swz_a, swz_b below) is its own LDS position, so the 16-byte fragment
-// reads of 16 rows are bank-conflict free.  Rows past the tile's end and
-// chunks past K are requested out of range and arrive as zeros.
+// Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves
+// (256 x 256 with 4 waves of 128 x 128 for large inputs, so each wave keeps
+// 256 fp32 accumulators in AGPRs).  K advances in stages of BK (64 for the
+// large tile: 128-byte LDS rows, two ring slots; 32 for the small one:
+// 64-byte rows, four slots).  Stages stream from memory straight into the
+// LDS ring with buffer loads that write LDS, R - 1 stages ahead of the MFMAs
+// and with no register staging; each wave waits only for its own loads of
+// the stage it is about to read, and one workgroup barrier per stage
+// publishes the stage and frees the slot the next loads go to.  Each 1 KB
+// load instruction fills 1 KB of LDS in lane order, a lane fetching the
+// global chunk whose permuted home (swz_a, swz_b below) is its own LDS
+// position, so the 16-byte fragment reads are bank-conflict free.  Rows past
+// the tile's end and chunks past K are requested out of range and arrive as
+// zeros.  The loop is issued in a fixed order: MFMAs of a k-step run from
+// registers while the next k-step's fragments are read from LDS and the next
+// stage's loads are issued, one such instruction after each MFMA.
 // v_mfma_f32_16x16x32_bf16 is fed with the weight as the row operand and the
 // activation as the column operand; the weight rows of a fragment pair are
 // interleaved so each lane ends with 8 consecutive output columns of one row,
@@ -39,22 +44,30 @@ namespace fmlp {
 
 namespace {
 
-constexpr int kBK = 32;  // k per LDS stage
-
-// LDS rows are 64 bytes (4 chunks of 16 B).  A ds_read_b128 takes four LDS
-// cycles of 16 lanes (measured on gfx950): the cycle of lane l is set by its
-// half-wave (l >> 5) and the parity of its quad index bits ((l >> 2) & 7),
-// and within a cycle the lanes must hit distinct 16-byte bank groups (unit
-// index mod 16, i.e. 4 rows x 4 chunk slots here).  A fragment read puts k
-// group lg = l >> 4 and row offset li = l & 15 on each lane, so a cycle holds
-// two k groups, each with half of the row offsets.  Chunk c of row r sits at
-// slot c ^ kSwz[q], q = bits 2-3 of the row for activation fragments (16
-// consecutive rows) and bits 3-4 for weight fragments (rows interleaved in
-// groups of 4: 8*(l/4) + (l%4)); kSwz = {0, 2, 3, 1} makes every cycle of
-// both kinds of read conflict free, where the plain q would pair its lanes.
-__device__ __forceinline__ int swz_q(int q) { return (0x78 >> (2 * q)) & 3; }   // {0, 2, 3, 1}
-__device__ __forceinline__ int swz_a(int r) { return swz_q((r >> 2) & 3); }
-__device__ __forceinline__ int swz_b(int r) { return swz_q((r >> 3) & 3); }
+// LDS layout.  A stage holds BK k of every tile row: rows of BK * 2 bytes
+// (CH = BK / 8 chunks of 16 B).  A ds_read_b128 takes four LDS cycles of 16
+// lanes (measured on gfx950): the cycle of lane l is set by its half-wave
+// (l >> 5) and the parity of its quad index bits ((l >> 2) & 7), and within
+// a cycle the lanes must hit distinct 16-byte bank groups (unit index mod 16).
+// A fragment read puts k group lg = l >> 4 and row offset li = l & 15 on each
+// lane, so a cycle holds two k groups, each with half of the row offsets.
+// Chunk c of row r sits at slot c ^ swz(r), with one permutation for
+// activation fragments (16 consecutive rows) and one for weight fragments
+// (rows interleaved in groups of 4: 8*(l/4) + (l%4)), chosen so every cycle
+// of both kinds of read is conflict free:
+//   64-byte rows:  q = bits 2-3 (activation) or 3-4 (weight) of r, slot
+//                  permutation {0, 2, 3, 1}[q] (the plain q pairs lanes);
+//   128-byte rows: bits 1-3 of r (activation), bits 1, 3, 4 (weight).
+template <int CH>
+__device__ __forceinline__ int swz_a(int r) {
+  if constexpr (CH == 4) return (0x78 >> (2 * ((r >> 2) & 3))) & 3;
+  else return (r >> 1) & 7;
+}
+template <int CH>
+__device__ __forceinline__ int swz_b(int r) {
+  if constexpr (CH == 4) return (0x78 >> (2 * ((r >> 3) & 3))) & 3;
+  else return ((r >> 1) & 1) | ((r >> 2) & 6);
+}
 
 // The main loop interleaves MFMAs with loads and LDS reads in a fixed order.
 // Instruction selection moves an MFMA builtin freely (it touches no memory),
@@ -71,7 +84,7 @@ __device__ __forceinline__ void mfma_ordered(f32x4_t& acc, const u32x4_t& a, con
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 #pragma clang diagnostic pop
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int R, int OUT, bool GATHER, bool GROUPED>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -81,16 +94,20 @@ gemm_bf16_kernel(GemmParams p) {
   constexpr int FN = TN / 16;
   constexpr bool DUAL = (OUT == GEMM_OUT_GEGLU);
   constexpr int HALF = FN / 2;       // DUAL: gate fragments [0,HALF), up [HALF,FN)
-  constexpr int A_INS = BM / (16 * NW);   // 1 KB load instructions per wave and stage
-  constexpr int B_INS = BN / (16 * NW);
+  constexpr int CH = BK / 8;         // 16-byte chunks per LDS row
+  constexpr int KS = BK / 32;        // MFMA k-steps per stage
+  constexpr int RPI = 64 / CH;       // rows filled by one 1 KB load instruction
+  constexpr int A_INS = BM / (RPI * NW);   // load instructions per wave and stage
+  constexpr int B_INS = BN / (RPI * NW);
   constexpr int LOADS = A_INS + B_INS;
-  constexpr int SLOT = (BM + BN) * 4;     // 16-byte chunks per ring slot
+  constexpr int SLOT = (BM + BN) * CH;     // 16-byte chunks per ring slot
   constexpr int OUT_N = DUAL ? BN / 2 : BN;   // output columns per block
-  static_assert(A_INS >= 1 && B_INS >= 1 && BM % (16 * NW) == 0 && BN % (16 * NW) == 0, "load mapping");
-  static_assert(!DUAL || (BN / 2) % (16 * NW) == 0, "a load instruction stays in one weight set");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(A_INS >= 1 && B_INS >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "load mapping");
+  static_assert(!DUAL || (BN / 2) % (RPI * NW) == 0, "a load instruction stays in one weight set");
   static_assert(TM % 16 == 0 && TN % 16 == 0 && FM % 2 == 0, "wave tile");
   static_assert(DUAL ? (HALF % 2 == 0) : (FN % 2 == 0), "fragment pairs");
-  static_assert(R >= 3 && LOADS * (R - 2) < 64, "ring depth");
+  static_assert(R >= 2 && LOADS * (R - 2) < 64, "ring depth");
 
   __shared__ u32x4_t ring[R * SLOT];
 
@@ -127,11 +144,11 @@ gemm_bf16_kernel(GemmParams p) {
   const int64_t K = p.K, N = p.N;
 
   // ---- load descriptors and per-lane offsets -------------------------------
-  // Load instruction i of this wave fills tile rows 16 * (i * NW + wave) +
-  // lane / 4; the lane's LDS position in its row is lane % 4 and it fetches
+  // Load instruction i of this wave fills tile rows RPI * (i * NW + wave) +
+  // lane / CH; the lane's LDS position in its row is lane % CH and it fetches
   // the chunk that belongs there.  Byte spans fit 31 bits (checked by the
   // caller), so kOutOfRange is past every descriptor's end.
-  const int jr = lane >> 2, jp = lane & 3;
+  const int jr = lane / CH, jp = lane % CH;
   const int64_t a_rows_here = row_end - row_begin;
   const i32x4_t da = GATHER
       ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
@@ -143,8 +160,8 @@ gemm_bf16_kernel(GemmParams p) {
   int a_k[A_INS], b_k[B_INS];   // k offset of the lane's chunk within a stage
 #pragma unroll
   for (int i = 0; i < A_INS; ++i) {
-    const int r = 16 * (i * NW + wave) + jr;
-    const int c = jp ^ swz_a(r);
+    const int r = RPI * (i * NW + wave) + jr;
+    const int c = jp ^ swz_a<CH>(r);
     a_k[i] = 8 * c;
     if (r < a_rows_here) {
       const int64_t src = GATHER ? (int64_t)p.a_rows[row_begin + r] : (int64_t)r;
@@ -155,23 +172,24 @@ gemm_bf16_kernel(GemmParams p) {
   }
 #pragma unroll
   for (int i = 0; i < B_INS; ++i) {
-    const int r = 16 * (i * NW + wave) + jr;
-    const int c = jp ^ swz_b(r);
+    const int r = RPI * (i * NW + wave) + jr;
+    const int c = jp ^ swz_b<CH>(r);
     const int n = DUAL ? r % (BN / 2) : r;
     b_k[i] = 8 * c;
     b_off[i] = n < n_here ? (uint32_t)(n * K * 2 + c * 16) : kOutOfRange;
   }
   const uint32_t ring_lds = lds_addr(&ring[0]) + (uint32_t)wave * 1024u;
-  // Stages run in pairs (the fragment register sets alternate within a
-  // pair); an odd count gets one all-zero stage more, which adds nothing.
+  // The loop runs k-steps in pairs (the fragment register sets alternate);
+  // with one k-step per stage an odd stage count gets one all-zero stage
+  // more, which adds nothing.
   const int Kc = (int)K;                       // < 2^22
-  const int nk = (Kc + kBK - 1) / kBK;
-  const int NS = (nk + 1) & ~1;
+  const int nk = (Kc + BK - 1) / BK;
+  const int NS = KS == 2 ? nk : (nk + 1) & ~1;
 
   // This wave's load offsets for stage s: chunks past K (the k tail, the
   // padding stage and the stages issued past the end) are out of range.
   auto stage_offs = [&](int s, uint32_t (&o)[LOADS]) {
-    const int k0 = s * kBK;
+    const int k0 = s * BK;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) o[i] = k0 + a_k[i] < Kc ? a_off[i] : kOutOfRange;
 #pragma unroll
@@ -183,26 +201,23 @@ gemm_bf16_kernel(GemmParams p) {
       asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, o[i], kb);
     } else {
       const int b = i - A_INS;
-      const bool up = DUAL && 16 * (b * NW) >= BN / 2;   // compile-time per i
-      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * 64 + b * NW * 1024), o[i], kb);
+      const bool up = DUAL && RPI * (b * NW) >= BN / 2;   // compile-time per i
+      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024), o[i], kb);
     }
   };
   auto issue_all = [&](int s, int slot) {
     uint32_t o[LOADS];
     stage_offs(s, o);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), o, (uint32_t)s * (kBK * 2));
+    for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), o, (uint32_t)s * (BK * 2));
   };
 
-  // ---- LDS fragment positions (chunk index within a slot) --------------------
+  // ---- LDS fragment rows -----------------------------------------------------
   const int li = lane & 15;   // fragment row (weight) / column (activation)
   const int lg = lane >> 4;   // k group: 8 consecutive k
-  int x_pos[FM], w_pos[FN];
+  int x_row[FM], w_row[FN];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    const int r = wm * TM + f * 16 + li;
-    x_pos[f] = r * 4 + (lg ^ swz_a(r));
-  }
+  for (int f = 0; f < FM; ++f) x_row[f] = wm * TM + f * 16 + li;
 #pragma unroll
   for (int f = 0; f < FN; ++f) {
     // interleave the rows of a fragment pair: lane group g ends up holding
@@ -210,8 +225,7 @@ gemm_bf16_kernel(GemmParams p) {
     const int set = DUAL ? f / HALF : 0;
     const int fl = DUAL ? f % HALF : f;
     const int base = set * (BN / 2) + wn * (DUAL ? TN / 2 : TN) + (fl >> 1) * 32;
-    const int r = base + 8 * (li >> 2) + 4 * (fl & 1) + (li & 3);
-    w_pos[f] = BM * 4 + r * 4 + (lg ^ swz_b(r));
+    w_row[f] = base + 8 * (li >> 2) + 4 * (fl & 1) + (li & 3);
   }
 
   f32x4_t acc[FM][FN];
@@ -220,18 +234,24 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Fragment registers: two sets, alternating by stage.  Read n of a stage
-  // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order the next stage's MFMAs
-  // consume them.
+  // Fragment registers: two sets, alternating by k-step.  Read n of a k-step
+  // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order its MFMAs consume them.
   constexpr int NREADS = FM + FN;
   u32x4_t xf[2][FM], wf[2][FN];
-  auto frag_read = [&](int n, const u32x4_t* sl, auto set_c) {
+  auto frag_read = [&](int n, const u32x4_t* sl, int ks, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    if (n == 0) xf[set][0] = sl[x_pos[0]];
-    else if (n <= FN) wf[set][n - 1] = sl[w_pos[n - 1]];
-    else xf[set][n - FN] = sl[x_pos[n - FN]];
+    const int c = ks * 4 + lg;
+    if (n == 0) {
+      xf[set][0] = sl[x_row[0] * CH + (c ^ swz_a<CH>(x_row[0]))];
+    } else if (n <= FN) {
+      const int r = w_row[n - 1];
+      wf[set][n - 1] = sl[BM * CH + r * CH + (c ^ swz_b<CH>(r))];
+    } else {
+      const int r = x_row[n - FN];
+      xf[set][n - FN] = sl[r * CH + (c ^ swz_a<CH>(r))];
+    }
   };
-  auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a stage: row t / FN, column t % FN
+  auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a k-step: row t / FN, column t % FN
     constexpr int set = decltype(set_c)::value;
     mfma_ordered(acc[t / FN][t % FN], wf[set][t % FN], xf[set][t / FN]);
   };
@@ -247,21 +267,34 @@ gemm_bf16_kernel(GemmParams p) {
   lds_barrier();
   issue_all(R - 1, R - 1);
 #pragma unroll
-  for (int n = 0; n < NREADS; ++n) frag_read(n, ring, Set0{});
+  for (int n = 0; n < NREADS; ++n) frag_read(n, ring, 0, Set0{});
 
-  // One stage, from slot `slot` in register set CUR.  Phase A: the first
-  // half of its MFMAs, from registers only.  Hand-off: wait for this wave's
-  // loads of the next stage; barrier (the next stage is in LDS for every
-  // wave, and every wave has finished reading `slot`).  Phase B: the second
-  // half of the MFMAs, each followed by at most one other instruction of the
-  // hand-off stream: the loads of stage s + R into `slot`, then the fragment
-  // reads of the next stage into the other set, so the matrix core never
-  // waits for a run of memory instructions.
-  constexpr int NMA = (FM / 2) * FN;          // MFMAs per phase
+  // One k-step, register set CUR, of stage s in slot `slot`.
+  //  * Not the stage's last k-step: its MFMAs, each followed by at most one
+  //    fragment read of the next k-step (same slot) into the other set.
+  //  * The last one: the first half of its MFMAs; hand-off (wait for this
+  //    wave's loads of stage s + 1, then a barrier: stage s + 1 is in LDS for
+  //    every wave, and every wave has finished reading `slot`); the second
+  //    half, each MFMA followed by at most one instruction of the hand-off
+  //    stream: the loads of stage s + R into `slot`, then the fragment reads
+  //    of stage s + 1 into the other set.  The matrix core never waits for a
+  //    run of memory instructions.
+  constexpr int NMA = (FM / 2) * FN;          // MFMAs per half k-step
   constexpr int NOPS = LOADS + NREADS;
-  auto step = [&](int s, int slot, auto cur_c) {
+  auto kstep = [&](int s, int ks, int slot, auto cur_c) {
     constexpr int CUR = decltype(cur_c)::value;
     using Nxt = std::integral_constant<int, CUR ^ 1>;
+    if (ks + 1 < KS) {
+      const u32x4_t* sl = ring + slot * SLOT;
+#pragma unroll
+      for (int t = 0; t < 2 * NMA; ++t) {
+        mfma_t(t, cur_c);
+#pragma unroll
+        for (int n = t * NREADS / (2 * NMA); n < (t + 1) * NREADS / (2 * NMA); ++n)
+          frag_read(n, sl, ks + 1, Nxt{});
+      }
+      return;
+    }
     uint32_t o[LOADS];
     stage_offs(s + R, o);
 #pragma unroll
@@ -269,7 +302,7 @@ gemm_bf16_kernel(GemmParams p) {
     wait_vm<LOADS * (R - 2)>();
     lds_barrier();
     const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16);
-    const uint32_t kb = (uint32_t)(s + R) * (kBK * 2);
+    const uint32_t kb = (uint32_t)(s + R) * (BK * 2);
     const u32x4_t* sl = ring + (slot + 1 == R ? 0 : slot + 1) * SLOT;
 #pragma unroll
     for (int t = 0; t < NMA; ++t) {
@@ -277,16 +310,24 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
       for (int n = t * NOPS / NMA; n < (t + 1) * NOPS / NMA; ++n) {
         if (n < LOADS) dma(n, base, o, kb);
-        else frag_read(n - LOADS, sl, Nxt{});
+        else frag_read(n - LOADS, sl, 0, Nxt{});
       }
     }
   };
   int slot = 0;
-  for (int g = 0; g < NS; g += 2) {
-    const int s1 = slot + 1 == R ? 0 : slot + 1;
-    step(g, slot, Set0{});
-    step(g + 1, s1, Set1{});
-    slot = s1 + 1 == R ? 0 : s1 + 1;
+  if constexpr (KS == 2) {
+    for (int s = 0; s < NS; ++s) {
+      kstep(s, 0, slot, Set0{});
+      kstep(s, 1, slot, Set1{});
+      slot = slot + 1 == R ? 0 : slot + 1;
+    }
+  } else {
+    for (int s = 0; s < NS; s += 2) {
+      const int s1 = slot + 1 == R ? 0 : slot + 1;
+      kstep(s, 0, slot, Set0{});
+      kstep(s + 1, 0, s1, Set1{});
+      slot = s1 + 1 == R ? 0 : s1 + 1;
+    }
   }
   wait_vm<0>();   // the last stages' loads (of nothing) land before LDS is released
   mfma_drain();
@@ -349,16 +390,16 @@ gemm_bf16_kernel(GemmParams p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int R, int OUT, bool GATHER, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)((p.N + OUT_N - 1) / OUT_N);
-  p.group_m = 8;
+  p.group_m = 4;
   const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, R, OUT, GATHER, GROUPED>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED>), dim3((unsigned)blocks),
                      dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -366,8 +407,8 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
 template <int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   switch (tile) {
-    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 4, OUT, GATHER, GROUPED>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 2, 4, OUT, GATHER, GROUPED>(p, s);
+    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 2, 64, 2, OUT, GATHER, GROUPED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
