@@ -15,8 +15,9 @@
 //   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights)
 //
 // Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves
-// (256 x 256 with 4 waves of 128 x 128 for large inputs, so each wave keeps
-// 256 fp32 accumulators in AGPRs).  K advances in stages of BK (64 for the
+// (256 x 256 with 8 waves of 128 x 64 for large inputs: two waves per SIMD,
+// so one issues MFMAs while the other waits, each with 128 fp32 accumulators
+// in AGPRs).  K advances in stages of BK (64 for the
 // large tile: 128-byte LDS rows, two ring slots; 32 for the small one:
 // 64-byte rows, four slots).  Stages stream from memory straight into the
 // LDS ring with buffer loads that write LDS, R - 1 stages ahead of the MFMAs
@@ -408,7 +409,7 @@ template <int OUT, bool GATHER, bool GROUPED>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   switch (tile) {
     case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 2, 64, 2, OUT, GATHER, GROUPED>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

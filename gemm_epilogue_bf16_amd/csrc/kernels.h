@@ -41,7 +41,7 @@ struct GemmParams {
 // Tile configurations compiled in.
 enum GemmTile : int {
   TILE_128x128 = 0,   // 4 waves, 64x64 per wave
-  TILE_256x256 = 1,   // 4 waves, 128x128 per wave
+  TILE_256x256 = 1,   // 8 waves, 128x64 per wave
   TILE_COUNT
 };
 

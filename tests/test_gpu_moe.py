@@ -94,6 +94,31 @@ def test_moe_invalid_ids_counted_and_skipped():
     assert_parity(y, _oracle(x, ok_ids, gw0, Wg, Wu, Wd), "moe invalid ids")
 
 
+def test_moe_many_pairs_and_partial_expert_batch():
+    """More (token, slot) pairs than the routing kernel keeps in registers per
+    thread (the rest are re-read), an expert count that is not a multiple of
+    the routing batch, and invalid ids in both the register and re-read runs."""
+    rng = np.random.default_rng(6)
+    T, D, H, E, k = 5000, 64, 64, 6, 2
+    x = rand_bf16(rng, (T, D))
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    ids[0, 0] = -1          # first pair of the first run
+    ids[2503, 1] = E        # deep in a run (position 19 of 20)
+    ids[4999, 1] = 77       # the last pair
+    gw = rng.random((T, k)).astype(np.float32)
+    Wg, Wu, Wd = _experts(rng, E, D, H)
+    ws = F.workspace_for(DEV, F.fmlp_moe_workspace_size(T, D, H, E, k))
+    print("case moe many pairs", flush=True)
+    y = _run(x, ids, gw, Wg, Wu, Wd, ws)
+    assert F.moe_invalid_ids(ws) == 3
+    ok_ids = ids.copy()
+    gw0 = gw.copy()
+    bad = (ids < 0) | (ids >= E)
+    ok_ids[bad] = 0
+    gw0[bad] = 0.0
+    assert_parity(y, _oracle(x, ok_ids, gw0, Wg, Wu, Wd), "moe many pairs")
+
+
 def test_moe_determinism():
     rng = np.random.default_rng(4)
     T, D, H, E, k = 513, 256, 384, 8, 2
