@@ -209,11 +209,20 @@ fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16*
   return launched(gemm_linear(x, W, b, act, M, K, N, y, cus, s), "linear launch");
 }
 
+// The hidden activation between the two layers: M x H bf16, or at one token
+// H/2 words of {bf16 pair, epoch} (8 bytes each) for the decode kernel's
+// word-flag publish.
+size_t hidden_bytes(int64_t M, int64_t H) {
+  const size_t plain = (size_t)M * (size_t)H * 2;
+  const size_t words = M == 1 ? (size_t)H * 4 : 0;
+  return round_up(plain > words ? plain : words, 256);
+}
+
 size_t fmlp_mlp2_workspace_size(int64_t M, int64_t K, int64_t H, int64_t N) {
   (void)K;
   (void)N;
   if (M < 0 || H <= 0) return 0;
-  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+  return kHeader + hidden_bytes(M, H);
 }
 
 fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* b1,
@@ -267,7 +276,7 @@ fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* 
 size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H) {
   (void)D;
   if (M < 0 || H <= 0) return 0;
-  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+  return kHeader + hidden_bytes(M, H);
 }
 
 fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,

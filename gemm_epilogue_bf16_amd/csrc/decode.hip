@@ -9,15 +9,16 @@
 //
 // Streaming.  Weights and activation slices go from memory straight into an
 // LDS ring with buffer loads that write LDS (no register staging): one block
-// per CU keeps R - 1 stages in flight (112 KB of weights per CU at one token,
-// 48 KB at 16), which is what HBM latency times bandwidth asks for.  A stage is
+// per CU keeps R - 1 = 3 stages in flight (48 KB of weights per CU), which
+// holds HBM at its streaming rate without a long per-CU request queue.  A stage is
 // 16 weight rows x 512 k (one 1 KB piece per row), or 2 x 16 rows x 256 k when
 // the gate and up weights of GeGLU stream together, plus the same k range of
 // the <= 16 activation rows.  Each 1 KB load instruction writes 1 KB of LDS
 // contiguously, lane by lane; a lane picks the global 16-byte chunk whose
 // swizzled home is its own LDS slot (chunk c of row r lives at c ^ (r & 15)
 // within its group of 16), so loads stay fully coalesced and the MFMA fragment
-// reads of 16 rows are bank-conflict free.  The streaming loop is rolled (a
+// reads of 16 rows are bank-conflict free (for the four 16-lane cycles of a
+// ds_read_b128 on gfx950, as measured: see the GEMM's LDS layout note).  The streaming loop is rolled (a
 // ring slot is a runtime offset), so its few dozen instructions stay in the
 // instruction cache.
 //
@@ -64,15 +65,26 @@ constexpr int kSK1 = 512;                      // k per stage, one weight matrix
 constexpr int kSK2 = 256;                      // k per stage, gate + up together
 constexpr uint32_t kSpinLimit = 1u << 20;      // bounded waits
 constexpr int kLdsBudget = 160 * 1024;
+// Ring depth cap: R - 1 = 3 stages in flight per CU (51 KB at one token)
+// already keep HBM at its streaming rate; a deeper ring only lengthens the
+// per-CU request queue, which the latency-critical h exchange then waits
+// behind (measured: 4 slots 17.8 us against 8 slots 19.4 us per 4096^3
+// two-layer forward at one token, equal elsewhere).
+constexpr int kRingMax = 4;
+// One token and a hidden size up to kLLMaxH: h is published as 8-byte words
+// (two bf16 and the call's epoch), gathered by every block straight into LDS.
+constexpr int kLLMaxH = 4096;
 
 // Activation rows held per stage (a class of M) and the ring depth it leaves.
-template <int MC, bool DUAL1>
+template <int MC, bool DUAL1, bool LL>
 struct RingShape {
   static constexpr int kXChunks = MC * 64;                        // MC rows x 1 KB
   static constexpr int kSlotBytes = (kWChunks + kXChunks) * 16;
   static constexpr int kRedBytes = (DUAL1 ? 2 : 1) * kWorkers * 64 * 16;
-  static constexpr int kFixed = kRedBytes + 2 * 64 * 4 + 1024;    // partials, bias, sink
-  static constexpr int R = (kLdsBudget - kFixed) / kSlotBytes;
+  static constexpr int kFixed = kRedBytes + 2 * 64 * 4 + 1024     // partials, bias, sink
+                                + (LL ? kLLMaxH * 2 : 0);          // h gathered for layer 2
+  static constexpr int kFit = (kLdsBudget - kFixed) / kSlotBytes;
+  static constexpr int R = kFit < kRingMax ? kFit : kRingMax;
   static constexpr int XI = MC > 8 ? 2 : 1;                       // activation loads per wave and stage
   static constexpr int kLoads = 2 + XI;                           // loads per wave and stage
   static_assert(R >= 3 && R * kSlotBytes + kFixed <= kLdsBudget, "ring does not fit");
@@ -84,6 +96,18 @@ __device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
 }
 __device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Device-coherent (sc1) stores of h through a buffer descriptor.  A buffer
+// store counts in vmcnt only; a store through a generic pointer would be a
+// flat store, which also holds lgkmcnt until it completes and so stalls the
+// next LDS wait of the storing wave behind a write-through to memory.  The
+// 16-byte form writes two 8-byte words, each whole.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st_coherent_b64(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2_t v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ void st_coherent_b128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16 /* sc1 */);
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -178,10 +202,11 @@ __device__ __forceinline__ Seg seg_first(const Stream& st) {
   return q;
 }
 
-template <bool DUAL1, bool TWO, int MC>
+template <bool DUAL1, bool TWO, int MC, bool LL>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
-  using RS = RingShape<MC, DUAL1>;
+  static_assert(!LL || (TWO && MC == 1), "word-flag publish: two layers, one token");
+  using RS = RingShape<MC, DUAL1, LL>;
   constexpr int R = RS::R, XI = RS::XI;
   constexpr int kSets = DUAL1 ? 2 : 1;
   constexpr uint32_t kSlot = (uint32_t)RS::kSlotBytes;
@@ -189,6 +214,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   __shared__ float4 red[kSets][kWorkers * 64];
   __shared__ uint32_t bias_lds[2][64];         // bias of the control wave's current and next tile
   __shared__ u32x4_t sink[64];                 // destination of activation loads with no row
+  __shared__ u32x4_t h_lds[LL ? kLLMaxH / 8 : 1];   // layer-2 input, gathered (LL)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -315,7 +341,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       wbase = rows ? W + (uint64_t)((int64_t)n0 * K) * 2u : W;
       wrec = (uint32_t)(rows * K) * 2u;
       xbase = pick(i_l2, X1, X0);
-      xrec = real ? (uint32_t)(M * K) * 2u : 0u;
+      xrec = real && !(LL && i_l2) ? (uint32_t)(M * K) * 2u : 0u;   // LL: layer 2 reads h_lds
     };
     // all loads of one stage into ring slot `slot`: 2 weight pieces, then XI
     // activation pieces (h only once the barrier has passed)
@@ -386,7 +412,12 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
           for (int t = 0; t < 2; ++t) {
             u32x4_t a = *reinterpret_cast<const u32x4_t*>(sp + apos[t]);
             u32x4_t x = zero4();
-            if (bcol) x = *reinterpret_cast<const u32x4_t*>(sp + bpos[t]);
+            if (LL && c_l2) {
+              const int k = (st.S[1] - cs.left) * kSK1 + (8 * w + 4 * t + lg) * 8;
+              if (bcol && k < K1) x = h_lds[k >> 3];
+            } else if (bcol) {
+              x = *reinterpret_cast<const u32x4_t*>(sp + bpos[t]);
+            }
             if (tail && !pick(c_l2, aok[1][t], aok[0][t])) a = zero4();
             acc0 = mfma_16x16x32(a, x, acc0);
           }
@@ -412,7 +443,13 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       step(slot);
       slot = slot + 1 == (uint32_t)R ? 0 : slot + 1;
     }
-    if (TWO && st.total > st.first2) {
+    if (LL && st.total > st.first2) {
+      lds_barrier();   // the control wave has gathered h into h_lds
+      for (int g = st.first2; g < st.total; ++g) {
+        step(slot);
+        slot = slot + 1 == (uint32_t)R ? 0 : slot + 1;
+      }
+    } else if (TWO && st.total > st.first2) {
       lds_barrier();   // the control wave has seen every block's h
       h_ok = true;
       // h slices of the layer-2 stages already in flight, re-requested now
@@ -493,12 +530,15 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       for (int r = 0; r < 4; ++r)
         v[r] = dual ? gelu_tanh(g[r]) * u[r] : apply_act(g[r] + b[r], act);   // b = 0 without a bias
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(y + (int64_t)m * N + n);
-      if (TWO && !l2) {   // h: read by every block after the barrier
-        st_coherent(dst, lo);
-        st_coherent(dst + 1, hi);
-      } else {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+      if (LL && !l2) {    // h as two words {bf16 pair, epoch}: the data is its own flag
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(y, (uint32_t)N * 4u);
+        st_coherent_b128(rh, (uint32_t)n * 4u, u32x4_t{lo, target, hi, target});
+      } else if (TWO && !l2) {   // h: read by every block after the barrier
+        const __amdgpu_buffer_rsrc_t rh = make_rsrc(y, (uint32_t)(M * N) * 2u);
+        st_coherent_b64(rh, (uint32_t)(m * N + n) * 2u, u32x2_t{lo, hi});
+      } else {                   // the output: a plain buffer store (vmcnt only)
+        const __amdgpu_buffer_rsrc_t ry = make_rsrc(y, (uint32_t)(M * N) * 2u);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, ry, (uint32_t)(m * N + n) * 2u, 0, 0);
       }
     }
   };
@@ -532,6 +572,48 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
     }
     if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
   };
+  // LL: read every word of h with device-coherent loads until each carries
+  // this call's epoch (one pass when everything has landed: all of a lane's
+  // loads are in flight together), and keep the bf16 pairs in h_lds.  Every
+  // block owns a layer-1 tile (the launch guarantees it), so once block 0
+  // has seen every word, every block has read the generation: only then does
+  // it move forward.
+  auto ctrl_gather_words = [&]() {
+    if constexpr (LL) {
+      constexpr int kPer = kLLMaxH / 4 / 64;   // 16-byte pieces (two words) per lane
+      const int pieces = (int)(L2.K / 4);       // K of layer 2 = hidden size
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(L2.x, (uint32_t)pieces * 16u);
+      uint32_t pend = 0;
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (lane + 64 * i < pieces) pend |= 1u << i;
+      for (uint32_t spins = 0;; ++spins) {
+        u32x4_t v[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (pend & (1u << i))
+            v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rw, (uint32_t)(lane + 64 * i) * 16u, 0, 16 /* sc1 */));
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if ((pend & (1u << i)) && v[i][1] == target && v[i][3] == target) {
+            uint32_t* hw = reinterpret_cast<uint32_t*>(&h_lds[0]) + 2 * (lane + 64 * i);
+            hw[0] = v[i][0];
+            hw[1] = v[i][2];
+            pend &= ~(1u << i);
+          }
+        }
+        if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;
+        if (spins >= kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
+    }
+  };
   // the control wave meets the workers at each of their barriers
   Seg cs = seg_first<TWO>(st);
   Seg bq = cs;                // the tile whose bias is requested next
@@ -550,14 +632,18 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       ctrl_epilogue(q, bslot);
       ctrl_fetch_bias(bslot ^ 1, bq);
       bslot ^= 1;
-      if (TWO && q.kind == SEG_L1 && q.tile == st.nt[0] - 1) ctrl_arrive();
+      if (TWO && !LL && q.kind == SEG_L1 && q.tile == st.nt[0] - 1) ctrl_arrive();
     }
     --cs.left;
   };
 
-  if (TWO && st.first2 == 0) ctrl_arrive();   // no layer-1 tile: nothing to publish
+  if (TWO && !LL && st.first2 == 0) ctrl_arrive();   // no layer-1 tile: nothing to publish
   for (int g = 0; g < st.first2; ++g) ctrl_step();
-  if (TWO && st.total > st.first2) {
+  if (LL && st.total > st.first2) {
+    ctrl_gather_words();             // every block's h, word by word, into h_lds
+    lds_barrier();
+    for (int g = st.first2; g < st.total; ++g) ctrl_step();
+  } else if (TWO && st.total > st.first2) {
     ctrl_wait_all();                 // entering layer 2: every block's h is complete
     lds_barrier();
     lds_barrier();                   // the workers' h slices are in LDS
@@ -590,7 +676,7 @@ Occ occ() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return o;
     o.cus = prop.multiProcessorCount;
     const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &o.per_cu, reinterpret_cast<const void*>(&decode_kernel<true, true, 1>), kThreads,
+                        &o.per_cu, reinterpret_cast<const void*>(&decode_kernel<true, true, 1, false>), kThreads,
                         0) == hipSuccess;
     o.ok = ok && o.cus > 0 && o.per_cu > 0;
   }
@@ -601,12 +687,17 @@ Occ occ() {
 template <bool DUAL1, bool TWO>
 hipError_t launch_mc(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
                      hipStream_t s) {
-  if (M <= 1)
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+  // word-flag publish of h: one token, h fits h_lds, and every block owns a
+  // layer-1 tile (so every block writes words before block 0 can see them all)
+  const bool ll = TWO && M == 1 && L2.K <= kLLMaxH && (int64_t)grid <= (L1.N + 15) / 16;
+  if (M <= 1 && ll)
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1, TWO>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+  else if (M <= 1)
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
   else if (M <= 4)
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 4>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 4, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
   else
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 16>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
+    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 16, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
   return hipGetLastError();
 }
 
@@ -631,8 +722,10 @@ hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int
   const Occ o = occ();
   if (!o.ok) return hipErrorInvalidDevice;
   const int64_t tiles1 = (L1.N + 15) / 16, tiles2 = (L2.N + 15) / 16;
-  // every block must be resident at once: the barrier waits for all of them
-  const int64_t cap = std::min<int64_t>((int64_t)o.cus * o.per_cu, kDecodeMaxBlocks);
+  // every block must be resident at once: the barrier waits for all of them.
+  // One block per CU, whatever the occupancy query allows: residency of a
+  // second block per CU is not something the barrier may depend on.
+  const int64_t cap = std::min<int64_t>((int64_t)o.cus, kDecodeMaxBlocks);
   const unsigned grid = (unsigned)std::min<int64_t>(cap, std::max(tiles1, tiles2));
   if (grid == 0) return hipSuccess;
   if (L1.geglu) return launch_mc<true, true>(grid, L1, L2, M, sync, s);
