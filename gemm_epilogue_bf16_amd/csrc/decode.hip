@@ -359,7 +359,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const uint32_t off = pick(tail, pick(i_l2, wofft[1][i], wofft[0][i]), pick(i_l2, woff[1][i], woff[0][i]));
-        asm_load_lds(wd, lds_w + slot * kSlot + (uint32_t)i * 1024u, off);
+        asm_load_lds_stream(wd, lds_w + slot * kSlot + (uint32_t)i * 1024u, off);
       }
       const i32x4_t xd = make_desc(xbase, (i_l2 && !h_ok) ? 0u : xrec);
 #pragma unroll

@@ -69,6 +69,12 @@ __device__ __forceinline__ void asm_load_lds(const i32x4_t& d, uint32_t lds, uin
   asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :: "v"(off), "s"(d), "s"(lds) : "memory", "m0");
 }
+// the same for data read exactly once (a weight stream): the non-temporal
+// policy keeps it from displacing reused lines in L2 and the Infinity Cache
+__device__ __forceinline__ void asm_load_lds_stream(const i32x4_t& d, uint32_t lds, uint32_t off) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+               :: "v"(off), "s"(d), "s"(lds) : "memory", "m0");
+}
 // the same with a wave-uniform byte offset soff added to every lane's offset
 __device__ __forceinline__ void asm_load_lds(const i32x4_t& d, uint32_t lds, uint32_t off,
                                              uint32_t soff) {
