@@ -145,6 +145,33 @@ def test_decode_determinism_and_repeat():
     assert hdr[2] == 0, hdr                  # no wait gave up
 
 
+@pytest.mark.parametrize("K,H,N", [
+    (64, 64, 4096),     # second layer wider than the first: not every block owns a layer-1 tile
+    (256, 4104, 520),   # hidden size just past the word-flag limit
+    (256, 4096, 520),   # at the limit: word-flag publish
+    (512, 200, 40),     # word-flag publish, ragged tiles
+])
+def test_decode_one_token_publish_paths(K, H, N):
+    """At one token the hidden vector is published either as epoch-tagged
+    words or with per-block flags, depending on the shape; both must give the
+    oracle's result and advance the barrier generation once per call."""
+    rng = np.random.default_rng(K + H + N)
+    t = {"x": rand_bf16(rng, (1, K)),
+         "W1": rand_bf16(rng, (H, K), K ** -0.5, "uniform"), "b1": rand_bf16(rng, (H,), 0.2, "uniform"),
+         "W2": rand_bf16(rng, (N, H), H ** -0.5, "uniform"), "b2": rand_bf16(rng, (N,), 0.2, "uniform")}
+    d = _dev_inputs(t)
+    ws = F.workspace_for(DEV, F.fmlp_mlp2_workspace_size(1, K, H, N))
+    print(f"case decode one-token publish K={K} H={H} N={N}", flush=True)
+    gen0 = int(ws[:4].view(torch.int32).item())
+    for _ in range(3):
+        y = _run(d, "gelu_tanh", "decode", ws)
+    ref = oracle.mlp2(*(f64_of_bits(t[k]) for k in ("x", "W1", "b1", "W2", "b2")), "gelu_tanh")
+    assert_parity(y, ref, f"decode one token {K}/{H}/{N}")
+    hdr = ws[:12].view(torch.int32).cpu().numpy()
+    assert hdr[0] == gen0 + 3, hdr
+    assert hdr[2] == 0, hdr
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_decode_no_stale_hidden_vector(M):
     """Back-to-back persistent calls on alternating inputs into one output
