@@ -130,7 +130,7 @@ int choose_tile(int64_t M, int64_t out_cols_per_256_tile_n, int cus) {
 
 GemmParams dense_params(const uint16_t* A, int64_t lda, const uint16_t* B0, const uint16_t* B1,
                         const uint16_t* bias, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                        int act) {
+                        int act, int cus) {
   GemmParams p;
   std::memset(&p, 0, sizeof p);
   p.A = A;
@@ -144,19 +144,20 @@ GemmParams dense_params(const uint16_t* A, int64_t lda, const uint16_t* B0, cons
   p.N = N;
   p.K = K;
   p.act = act;
+  p.cus = cus;
   return p;
 }
 
 hipError_t gemm_linear(const uint16_t* x, const uint16_t* W, const uint16_t* b, int act, int64_t M,
                        int64_t K, int64_t N, uint16_t* y, int cus, hipStream_t s) {
   const int tile = choose_tile(M, (N + 255) / 256, cus);
-  return launch_gemm(GEMM_OUT_BF16, false, false, tile, dense_params(x, K, W, nullptr, b, y, N, M, N, K, act), s);
+  return launch_gemm(GEMM_OUT_BF16, false, false, tile, dense_params(x, K, W, nullptr, b, y, N, M, N, K, act, cus), s);
 }
 
 hipError_t gemm_geglu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int64_t M,
                              int64_t D, int64_t H, uint16_t* m, int cus, hipStream_t s) {
   const int tile = choose_tile(M, (H + 127) / 128, cus);
-  return launch_gemm(GEMM_OUT_GEGLU, false, false, tile, dense_params(x, D, Wg, Wu, nullptr, m, H, M, H, D, 0), s);
+  return launch_gemm(GEMM_OUT_GEGLU, false, false, tile, dense_params(x, D, Wg, Wu, nullptr, m, H, M, H, D, 0, cus), s);
 }
 
 }  // namespace
@@ -390,7 +391,7 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
   hipError_t e = launch_moe_route(expert_ids, gate_w, T, top_k, E, bm, r, s);
   if (e != hipSuccess) return launched(e, "moe route launch");
 
-  GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, 0);
+  GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, 0, cus);
   g.a_rows = r.tok_of;
   g.a_src_rows = T;
   g.group_off = r.group_off;
@@ -401,7 +402,7 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
   e = launch_gemm(GEMM_OUT_GEGLU, true, true, kMoeTile, g, s);
   if (e != hipSuccess) return launched(e, "moe gate+up launch");
 
-  GemmParams d = dense_params(m, H, Wd, nullptr, nullptr, ytilde, D, P, D, H, 0);
+  GemmParams d = dense_params(m, H, Wd, nullptr, nullptr, ytilde, D, P, D, H, 0, cus);
   d.group_off = r.group_off;
   d.tile_off = r.tile_off;
   d.groups = E;

@@ -35,6 +35,7 @@
 // activation as the column operand; the weight rows of a fragment pair are
 // interleaved so each lane ends with 8 consecutive output columns of one row,
 // stored as one 16-byte write.
+#include <algorithm>
 #include <utility>
 
 #include "common.h"
@@ -60,14 +61,45 @@ namespace {
 //                  permutation {0, 2, 3, 1}[q] (the plain q pairs lanes);
 //   128-byte rows: bits 1-3 of r (activation), bits 1, 3, 4 (weight).
 template <int CH>
-__device__ __forceinline__ int swz_a(int r) {
+__host__ __device__ constexpr int swz_a(int r) {
   if constexpr (CH == 4) return (0x78 >> (2 * ((r >> 2) & 3))) & 3;
   else return (r >> 1) & 7;
 }
 template <int CH>
-__device__ __forceinline__ int swz_b(int r) {
+__host__ __device__ constexpr int swz_b(int r) {
   if constexpr (CH == 4) return (0x78 >> (2 * ((r >> 3) & 3))) & 3;
   else return ((r >> 1) & 1) | ((r >> 2) & 6);
+}
+
+// Weight fragment f of a wave covers tile rows w_lane_row + w_delta(f): the
+// rows of a fragment pair interleave, so lane group g ends up holding output
+// columns 8g .. 8g+7 of the pair's 32 columns; with two weight sets, fragments
+// [0, FN/2) read the first and [FN/2, FN) the second.
+__host__ __device__ constexpr int w_delta(int f, int FN, int BN, bool dual) {
+  const int half = FN / 2;
+  const int set = dual ? f / half : 0;
+  const int fl = dual ? f % half : f;
+  return set * (BN / 2) + (fl >> 1) * 32 + 4 * (fl & 1);
+}
+__host__ __device__ constexpr int w_lane_row(int wn, int li, int TN, bool dual) {
+  return wn * (dual ? TN / 2 : TN) + 8 * (li >> 2) + (li & 3);
+}
+// The swizzles read only bits 1-4 of a row, so every fragment of a wave has
+// the same chunk permutation as its first one and its LDS address is the
+// first one's plus a constant.  Checked exhaustively at compile time.
+template <int CH, int TM, int TN, int FM, int FN, int BN, int WAVES_M, int WAVES_N, bool DUAL>
+constexpr bool fragment_swizzle_is_uniform() {
+  for (int li = 0; li < 16; ++li) {
+    for (int wm = 0; wm < WAVES_M; ++wm)
+      for (int f = 0; f < FM; ++f)
+        if (swz_a<CH>(wm * TM + f * 16 + li) != swz_a<CH>(wm * TM + li)) return false;
+    for (int wn = 0; wn < WAVES_N; ++wn) {
+      const int r0 = w_lane_row(wn, li, TN, DUAL);
+      for (int f = 0; f < FN; ++f)
+        if (swz_b<CH>(r0 + w_delta(f, FN, BN, DUAL)) != swz_b<CH>(r0)) return false;
+    }
+  }
+  return true;
 }
 
 // The main loop interleaves MFMAs with loads and LDS reads in a fixed order.
@@ -80,6 +112,19 @@ __device__ __forceinline__ int swz_b(int r) {
 __device__ __forceinline__ void mfma_ordered(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
 }
+// A copy of v the compiler cannot see through: what is computed from it
+// stays where it is written instead of being hoisted out of the tile loop and
+// kept live (in registers the main loop needs) across it.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+// materialise a value in AGPRs at this point of the instruction stream
+__device__ __forceinline__ void pin_agpr(f32x4_t& acc) { asm volatile("" : "+a"(acc)); }
+// the same, also ordered after every memory access before it: reads of the
+// accumulator cannot be hoisted above the preceding output stores (which
+// would have every accumulator copied to VGPRs at once)
+__device__ __forceinline__ void pin_agpr_ordered(f32x4_t& acc) { asm volatile("" : "+a"(acc) : : "memory"); }
 // wait states between the last MFMA of the loop and the first read of its
 // accumulators by ordinary code (the hazard check cannot see into asm)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
@@ -118,122 +163,178 @@ gemm_bf16_kernel(GemmParams p) {
   const int wm = wave / WAVES_N;
   const int wn = wave % WAVES_N;
 
-  // ---- which tile --------------------------------------------------------
-  int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-
-  int64_t row_begin, row_end;
-  const uint16_t* B0 = p.B0;
-  const uint16_t* B1 = p.B1;
-  if constexpr (GROUPED) {
-    const int total = p.tile_off[p.groups];
-    if (tm >= total) return;  // block-uniform
-    int lo = 0, hi = p.groups;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (p.tile_off[mid] <= tm) lo = mid; else hi = mid;
-    }
-    row_begin = (int64_t)p.group_off[lo] + (int64_t)(tm - p.tile_off[lo]) * BM;
-    row_end = min(row_begin + BM, (int64_t)p.group_off[lo + 1]);
-    B0 += (int64_t)lo * p.strideB;
-    if constexpr (DUAL) B1 += (int64_t)lo * p.strideB;
-  } else {
-    row_begin = (int64_t)tm * BM;
-    row_end = min(row_begin + BM, p.M);
-  }
-  const int64_t n0 = (int64_t)tn * OUT_N;
   const int64_t K = p.K, N = p.N;
+  const int Kc = (int)K;                       // < 2^22
+  const int li = lane & 15;   // fragment row (weight) / column (activation)
+  const int lg = lane >> 4;   // k group: 8 consecutive k
 
-  // ---- load descriptors and per-lane offsets -------------------------------
+  // ---- this block's tiles ----------------------------------------------------
+  // The grid is persistent (at most one block per CU).  Logical tiles (in
+  // grouped order) are split into one contiguous range per XCD, in
+  // proportion to its blocks, and the blocks of an XCD take its range
+  // round-robin, so at any time the blocks sharing an L2 work on
+  // neighbouring tiles.  Grouped mode counts only the tiles that exist.
+  const int tiles_m = GROUPED ? p.tile_off[p.groups] : p.tiles_m;
+  const int total = tiles_m * p.tiles_n;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid % kNumXcd, xj = bid / kNumXcd;
+  auto blocks_before = [&](int x) {   // blocks on XCDs 0 .. x-1
+    const int q = G / kNumXcd, r = G % kNumXcd;
+    return x * q + min(x, r);
+  };
+  const int nbx = blocks_before(xcd + 1) - blocks_before(xcd);
+  const int t_lo = (int)((int64_t)total * blocks_before(xcd) / G);
+  const int t_hi = (int)((int64_t)total * blocks_before(xcd + 1) / G);
+  const int nmine = xj < t_hi - t_lo ? (t_hi - t_lo - xj + nbx - 1) / nbx : 0;
+  if (nmine == 0) return;   // block-uniform: no barrier has been reached
+
+  struct Tile {
+    int64_t row_begin, row_end, n0;
+    const uint16_t* b0;
+    const uint16_t* b1;
+  };
+  auto tile_at = [&](int i) -> Tile {   // this block's i-th tile
+    int tm, tn;
+    grouped_tile(t_lo + xj + i * nbx, tiles_m, p.tiles_n, p.group_m, tm, tn);
+    Tile t;
+    t.b0 = p.B0;
+    t.b1 = p.B1;
+    if constexpr (GROUPED) {
+      int lo = 0, hi = p.groups;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.tile_off[mid] <= tm) lo = mid; else hi = mid;
+      }
+      t.row_begin = (int64_t)p.group_off[lo] + (int64_t)(tm - p.tile_off[lo]) * BM;
+      t.row_end = min(t.row_begin + BM, (int64_t)p.group_off[lo + 1]);
+      t.b0 += (int64_t)lo * p.strideB;
+      if constexpr (DUAL) t.b1 += (int64_t)lo * p.strideB;
+    } else {
+      t.row_begin = (int64_t)tm * BM;
+      t.row_end = min(t.row_begin + BM, p.M);
+    }
+    t.n0 = (int64_t)tn * OUT_N;
+    return t;
+  };
+
+  // ---- load descriptors and per-lane offsets (of the tile being issued) -----
   // Load instruction i of this wave fills tile rows RPI * (i * NW + wave) +
   // lane / CH; the lane's LDS position in its row is lane % CH and it fetches
-  // the chunk that belongs there.  Byte spans fit 31 bits (checked by the
-  // caller), so kOutOfRange is past every descriptor's end.
-  const int jr = lane / CH, jp = lane % CH;
-  const int64_t a_rows_here = row_end - row_begin;
-  const i32x4_t da = GATHER
-      ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
-      : make_desc(reinterpret_cast<uint64_t>(p.A + row_begin * p.lda), (uint32_t)(a_rows_here * p.lda * 2));
-  const int64_t n_here = min((int64_t)OUT_N, N - n0);   // weight rows of each set in this tile
-  const i32x4_t db0 = make_desc(reinterpret_cast<uint64_t>(B0 + n0 * K), (uint32_t)(n_here * K * 2));
-  const i32x4_t db1 = DUAL ? make_desc(reinterpret_cast<uint64_t>(B1 + n0 * K), (uint32_t)(n_here * K * 2)) : db0;
-  uint32_t a_off[A_INS], b_off[B_INS];
-  int a_k[A_INS], b_k[B_INS];   // k offset of the lane's chunk within a stage
+  // the chunk that belongs there.  RPI * NW is a multiple of 32 and the
+  // swizzles read bits 1-4 of a row, so that chunk is the same for every load
+  // instruction of the lane.  Byte spans fit 31 bits (checked by the caller),
+  // so 32-bit offsets suffice and kOutOfRange is past every descriptor's end.
+  // A tile's descriptors end at its last valid row, so rows past the end of
+  // the activation or weight arrive as zeros with no per-lane test; gathered
+  // rows past a group's end repeat its last row (their outputs are dropped).
+  // Only chunks past K need a mask: they would read the next row.
+  static_assert((RPI * NW) % 32 == 0, "one chunk permutation per lane");
+  const int ra = RPI * wave + lane / CH;      // tile row of the lane's load 0 (activation and weight)
+  const int a_k = 8 * ((lane % CH) ^ swz_a<CH>(ra));   // k of the lane's chunk in a stage
+  const int b_k = 8 * ((lane % CH) ^ swz_b<CH>(ra));
+  const uint32_t lda2 = (uint32_t)p.lda * 2u;
+  const uint32_t K2 = (uint32_t)Kc * 2u;
+  // offsets of the lane's load 0 within a tile (load i adds a constant number of rows)
+  const uint32_t a_lane = (uint32_t)ra * lda2 + (uint32_t)a_k * 2u;
+  const uint32_t b_lane = (uint32_t)ra * K2 + (uint32_t)b_k * 2u;
+  i32x4_t da, db0, db1;
+  uint32_t a_gat[GATHER ? A_INS : 1];   // gather: the lane's source-row offsets in this tile
+  auto issue_tile = [&](const Tile& t) {
+    const int a_rows_here = (int)(t.row_end - t.row_begin);
+    da = GATHER ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
+                : make_desc(reinterpret_cast<uint64_t>(p.A + t.row_begin * p.lda), (uint32_t)a_rows_here * lda2);
+    const int n_here = (int)min((int64_t)OUT_N, N - t.n0);   // weight rows of each set in this tile
+    db0 = make_desc(reinterpret_cast<uint64_t>(t.b0 + t.n0 * K), (uint32_t)n_here * K2);
+    db1 = DUAL ? make_desc(reinterpret_cast<uint64_t>(t.b1 + t.n0 * K), (uint32_t)n_here * K2) : db0;
+    if constexpr (GATHER) {
+      const int rt = RPI * wave + opaque(lane) / CH;
+      const int ak = 8 * ((opaque(lane) % CH) ^ swz_a<CH>(rt));
 #pragma unroll
-  for (int i = 0; i < A_INS; ++i) {
-    const int r = RPI * (i * NW + wave) + jr;
-    const int c = jp ^ swz_a<CH>(r);
-    a_k[i] = 8 * c;
-    if (r < a_rows_here) {
-      const int64_t src = GATHER ? (int64_t)p.a_rows[row_begin + r] : (int64_t)r;
-      a_off[i] = (uint32_t)(src * p.lda * 2 + c * 16);
-    } else {
-      a_off[i] = kOutOfRange;
+      for (int i = 0; i < A_INS; ++i) {
+        const int r = min(RPI * i * NW + rt, a_rows_here - 1);
+        a_gat[i] = (uint32_t)p.a_rows[t.row_begin + r] * lda2 + (uint32_t)ak * 2u;
+      }
     }
-  }
-#pragma unroll
-  for (int i = 0; i < B_INS; ++i) {
-    const int r = RPI * (i * NW + wave) + jr;
-    const int c = jp ^ swz_b<CH>(r);
-    const int n = DUAL ? r % (BN / 2) : r;
-    b_k[i] = 8 * c;
-    b_off[i] = n < n_here ? (uint32_t)(n * K * 2 + c * 16) : kOutOfRange;
-  }
+  };
+  static_assert(RPI * NW <= BN / 2, "weight row of a load");
   const uint32_t ring_lds = lds_addr(&ring[0]) + (uint32_t)wave * 1024u;
-  // The loop runs k-steps in pairs (the fragment register sets alternate);
-  // with one k-step per stage an odd stage count gets one all-zero stage
-  // more, which adds nothing.
-  const int Kc = (int)K;                       // < 2^22
+  // Stages of one tile; the loop runs k-steps in pairs (the fragment register
+  // sets alternate), so with one k-step per stage an odd count gets one
+  // all-zero stage more, which adds nothing.  The block's stream is its
+  // tiles' stages back to back: stream stage q is stage q % NS of tile q / NS.
   const int nk = (Kc + BK - 1) / BK;
   const int NS = KS == 2 ? nk : (nk + 1) & ~1;
+  issue_tile(tile_at(0));
 
-  // This wave's load offsets for stage s: chunks past K (the k tail, the
-  // padding stage and the stages issued past the end) are out of range.
-  auto stage_offs = [&](int s, uint32_t (&o)[LOADS]) {
-    const int k0 = s * BK;
-#pragma unroll
-    for (int i = 0; i < A_INS; ++i) o[i] = k0 + a_k[i] < Kc ? a_off[i] : kOutOfRange;
-#pragma unroll
-    for (int i = 0; i < B_INS; ++i) o[A_INS + i] = k0 + b_k[i] < Kc ? b_off[i] : kOutOfRange;
+  // How this wave loads the next stage of its stream (stages are issued once
+  // each, in order): the lane's chunks are out of range past K (the k tail,
+  // the padding stage) and for stages past the end of the stream; kb is the
+  // byte offset of the stage's k range (the loads' soffset).  The first stage
+  // of a tile switches the descriptors and offsets over to it.
+  int iss_t = 0, iss_s = 0;   // tile and stage within the tile of the next stage issued
+  struct StageIssue {
+    bool a_in, b_in;
+    uint32_t kb;
+  };
+  auto stage_begin = [&]() -> StageIssue {
+    const bool live = iss_t < nmine;   // block-uniform
+    if (live && iss_s == 0 && iss_t > 0) issue_tile(tile_at(iss_t));
+    const int k0 = live ? iss_s * BK : Kc;
+    const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, (uint32_t)(live ? iss_s : 0) * (BK * 2)};
+    if (++iss_s == NS) {
+      iss_s = 0;
+      ++iss_t;
+    }
+    return st;
   };
   // load i (of LOADS) of a stage into the slot at LDS byte address `base`
-  auto dma = [&](int i, uint32_t base, const uint32_t (&o)[LOADS], uint32_t kb) {
+  auto dma = [&](int i, uint32_t base, const StageIssue& st) {
     if (i < A_INS) {
-      asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, o[i], kb);
+      const uint32_t off = GATHER ? a_gat[GATHER ? i : 0] : a_lane + (uint32_t)(RPI * i * NW) * lda2;
+      asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, st.a_in ? off : kOutOfRange, st.kb);
     } else {
       const int b = i - A_INS;
       const bool up = DUAL && RPI * (b * NW) >= BN / 2;   // compile-time per i
-      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024), o[i], kb);
+      const uint32_t off = b_lane + (uint32_t)((RPI * b * NW) % (DUAL ? BN / 2 : BN)) * K2;
+      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024),
+                   st.b_in ? off : kOutOfRange, st.kb);
     }
   };
-  auto issue_all = [&](int s, int slot) {
-    uint32_t o[LOADS];
-    stage_offs(s, o);
+  auto issue_all = [&](int slot) {
+    const StageIssue st = stage_begin();
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), o, (uint32_t)s * (BK * 2));
+    for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), st);
   };
 
-  // ---- LDS fragment rows -----------------------------------------------------
-  const int li = lane & 15;   // fragment row (weight) / column (activation)
-  const int lg = lane >> 4;   // k group: 8 consecutive k
-  int x_row[FM], w_row[FN];
+  // ---- LDS fragment addresses (16-byte units within a slot) -----------------
+  // Activation fragment f: rows wm * TM + 16 f + li; weight fragment f: rows
+  // w_lane_row + w_delta(f).  One base per k-step, the rest compile-time.
+  static_assert(fragment_swizzle_is_uniform<CH, TM, TN, FM, FN, BN, WAVES_M, WAVES_N, DUAL>(),
+                "fragment addresses are affine");
+  const int wr0 = w_lane_row(wn, li, TN, DUAL);
+  int x_idx[KS], w_idx[KS];
 #pragma unroll
-  for (int f = 0; f < FM; ++f) x_row[f] = wm * TM + f * 16 + li;
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    // interleave the rows of a fragment pair: lane group g ends up holding
-    // output columns 8g..8g+7 of the pair's 32 columns
-    const int set = DUAL ? f / HALF : 0;
-    const int fl = DUAL ? f % HALF : f;
-    const int base = set * (BN / 2) + wn * (DUAL ? TN / 2 : TN) + (fl >> 1) * 32;
-    w_row[f] = base + 8 * (li >> 2) + 4 * (fl & 1) + (li & 3);
+  for (int ks = 0; ks < KS; ++ks) {
+    const int c = ks * 4 + lg;
+    x_idx[ks] = (wm * TM + li) * CH + (c ^ swz_a<CH>(wm * TM + li));
+    w_idx[ks] = BM * CH + wr0 * CH + (c ^ swz_b<CH>(wr0));
   }
 
   f32x4_t acc[FM][FN];
+  // The zeros are pinned into the accumulators here: the loop's MFMAs are
+  // asm, so the hazard check cannot see them read a register that a plain
+  // write set just before, and the compiler would otherwise sink each write
+  // to right before its MFMA.
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        pin_agpr(acc[i][j]);
+      }
+  };
+  zero_acc();
 
   // Fragment registers: two sets, alternating by k-step.  Read n of a k-step
   // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order its MFMAs consume them.
@@ -241,15 +342,12 @@ gemm_bf16_kernel(GemmParams p) {
   u32x4_t xf[2][FM], wf[2][FN];
   auto frag_read = [&](int n, const u32x4_t* sl, int ks, auto set_c) {
     constexpr int set = decltype(set_c)::value;
-    const int c = ks * 4 + lg;
     if (n == 0) {
-      xf[set][0] = sl[x_row[0] * CH + (c ^ swz_a<CH>(x_row[0]))];
+      xf[set][0] = sl[x_idx[ks]];
     } else if (n <= FN) {
-      const int r = w_row[n - 1];
-      wf[set][n - 1] = sl[BM * CH + r * CH + (c ^ swz_b<CH>(r))];
+      wf[set][n - 1] = sl[w_idx[ks] + w_delta(n - 1, FN, BN, DUAL) * CH];
     } else {
-      const int r = x_row[n - FN];
-      xf[set][n - FN] = sl[r * CH + (c ^ swz_a<CH>(r))];
+      xf[set][n - FN] = sl[x_idx[ks] + (n - FN) * 16 * CH];
     }
   };
   auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a k-step: row t / FN, column t % FN
@@ -259,31 +357,125 @@ gemm_bf16_kernel(GemmParams p) {
   using Set0 = std::integral_constant<int, 0>;
   using Set1 = std::integral_constant<int, 1>;
 
+  // ---- epilogue of a finished tile ------------------------------------------
+  // Global-address-space accesses: a store through a generic pointer is a flat
+  // store, which would also hold lgkmcnt and stall the next tile's fragment
+  // reads behind the write.
+  typedef __attribute__((address_space(1))) u32x4_t gu32x4_t;
+  auto gst16 = [](void* ptr, const u32x4_t& v) { *(gu32x4_t*)ptr = v; };
+  auto gld16 = [](const void* ptr) -> u32x4_t { return *(const gu32x4_t*)ptr; };
+  // The activation is a template argument so each copy of the epilogue is
+  // straight-line code (a per-element switch would branch around every value).
+  auto epilogue_act = [&](const Tile& t, auto act_c) {
+    constexpr int ACT = decltype(act_c)::value;
+    const int el = opaque(lane);
+    const int li = el & 15, lg = el >> 4;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t lrow = t.row_begin + wm * TM + i * 16 + li;
+      const bool row_ok = lrow < t.row_end;
+      if constexpr (OUT == GEMM_OUT_GEGLU) {
+#pragma unroll
+        for (int q = 0; q < HALF / 2; ++q) {
+          const int64_t n = t.n0 + wn * (TN / 2) + q * 32 + 8 * lg;
+          pin_agpr_ordered(acc[i][2 * q]);
+          pin_agpr_ordered(acc[i][2 * q + 1]);
+          pin_agpr_ordered(acc[i][HALF + 2 * q]);
+          pin_agpr_ordered(acc[i][HALF + 2 * q + 1]);
+          float v[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[r] = gelu_tanh(acc[i][2 * q][r]) * acc[i][HALF + 2 * q][r];
+            v[4 + r] = gelu_tanh(acc[i][2 * q + 1][r]) * acc[i][HALF + 2 * q + 1][r];
+          }
+          if (row_ok && n < N) gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < FN / 2; ++q) {
+          const int64_t n = t.n0 + wn * TN + q * 32 + 8 * lg;
+          pin_agpr_ordered(acc[i][2 * q]);
+          pin_agpr_ordered(acc[i][2 * q + 1]);
+          float v[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[r] = acc[i][2 * q][r];
+            v[4 + r] = acc[i][2 * q + 1][r];
+          }
+          if (!(row_ok && n < N)) continue;
+          if constexpr (OUT == GEMM_OUT_F32_SCALED) {
+            const float sc = p.row_scale[lrow];
+            float* dst = static_cast<float*>(p.C) + lrow * p.ldc + n;
+            u32x4_t lo, hi;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              lo[r] = __float_as_uint(v[r] * sc);
+              hi[r] = __float_as_uint(v[4 + r] * sc);
+            }
+            gst16(dst, lo);
+            gst16(dst + 4, hi);
+          } else {
+            if (p.bias) {
+              float b[8];
+              unpack_bf16x8(gld16(p.bias + n), b);
+#pragma unroll
+              for (int r = 0; r < 8; ++r) v[r] += b[r];
+            }
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              if constexpr (ACT == ACT_GELU_ERF) v[r] = gelu_erf(v[r]);
+              else if constexpr (ACT == ACT_GELU_TANH) v[r] = gelu_tanh(v[r]);
+            }
+            gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
+          }
+        }
+      }
+    }
+  };
+  auto epilogue = [&](const Tile& t) {
+    mfma_drain();
+    if constexpr (OUT == GEMM_OUT_BF16) {
+      if (p.act == ACT_GELU_ERF) epilogue_act(t, std::integral_constant<int, ACT_GELU_ERF>{});
+      else if (p.act == ACT_GELU_TANH) epilogue_act(t, std::integral_constant<int, ACT_GELU_TANH>{});
+      else epilogue_act(t, std::integral_constant<int, ACT_NONE>{});
+    } else {
+      epilogue_act(t, std::integral_constant<int, ACT_NONE>{});
+    }
+    zero_acc();
+  };
+
   // Prologue: stages 0 .. R-2 in flight, stage 0 published, R-1 issued.
   // Every stage up to the last one read plus R - 1 is issued (past the end
   // they load nothing), so every wait below is the same.
 #pragma unroll
-  for (int s = 0; s < R - 1; ++s) issue_all(s, s);
+  for (int q = 0; q < R - 1; ++q) issue_all(q);
   wait_vm<LOADS * (R - 2)>();
   lds_barrier();
-  issue_all(R - 1, R - 1);
+  issue_all(R - 1);
 #pragma unroll
   for (int n = 0; n < NREADS; ++n) frag_read(n, ring, 0, Set0{});
 
-  // One k-step, register set CUR, of stage s in slot `slot`.
+  // One k-step (ks of the stage q in slot `slot`), register set CUR.
   //  * Not the stage's last k-step: its MFMAs, each followed by at most one
   //    fragment read of the next k-step (same slot) into the other set.
   //  * The last one: the first half of its MFMAs; hand-off (wait for this
-  //    wave's loads of stage s + 1, then a barrier: stage s + 1 is in LDS for
+  //    wave's loads of stage q + 1, then a barrier: stage q + 1 is in LDS for
   //    every wave, and every wave has finished reading `slot`); the second
   //    half, each MFMA followed by at most one instruction of the hand-off
-  //    stream: the loads of stage s + R into `slot`, then the fragment reads
-  //    of stage s + 1 into the other set.  The matrix core never waits for a
-  //    run of memory instructions.
+  //    stream: the loads of stage q + R into `slot`, then the fragment reads
+  //    of stage q + 1 into the other set.  The matrix core never waits for a
+  //    run of memory instructions.  At the end of a tile (LAST) the fragment
+  //    reads wait until the epilogue has freed its registers.  After an
+  //    epilogue (whose stores count in vmcnt) the hand-off waits for every
+  //    access, so no wait count depends on how loads and stores retire
+  //    relative to each other.
   constexpr int NMA = (FM / 2) * FN;          // MFMAs per half k-step
   constexpr int NOPS = LOADS + NREADS;
-  auto kstep = [&](int s, int ks, int slot, auto cur_c) {
+  bool stored = false;   // an epilogue has stored since the last hand-off
+  auto next_slot = [&](int sl) { return sl + 1 == R ? 0 : sl + 1; };
+  auto kstep = [&](int ks, int slot, auto cur_c, auto last_c) {
     constexpr int CUR = decltype(cur_c)::value;
+    constexpr bool LAST = decltype(last_c)::value;
     using Nxt = std::integral_constant<int, CUR ^ 1>;
     if (ks + 1 < KS) {
       const u32x4_t* sl = ring + slot * SLOT;
@@ -296,99 +488,61 @@ gemm_bf16_kernel(GemmParams p) {
       }
       return;
     }
-    uint32_t o[LOADS];
-    stage_offs(s + R, o);
+    const StageIssue st = stage_begin();   // stage q + R
 #pragma unroll
     for (int t = 0; t < NMA; ++t) mfma_t(t, cur_c);
-    wait_vm<LOADS * (R - 2)>();
+    if (R > 2 && stored) wait_vm<0>(); else wait_vm<LOADS * (R - 2)>();
+    stored = false;
     lds_barrier();
     const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16);
-    const uint32_t kb = (uint32_t)(s + R) * (BK * 2);
-    const u32x4_t* sl = ring + (slot + 1 == R ? 0 : slot + 1) * SLOT;
+    const u32x4_t* sl = ring + next_slot(slot) * SLOT;
+    constexpr int OPS = LAST ? LOADS : NOPS;
 #pragma unroll
     for (int t = 0; t < NMA; ++t) {
       mfma_t(NMA + t, cur_c);
 #pragma unroll
-      for (int n = t * NOPS / NMA; n < (t + 1) * NOPS / NMA; ++n) {
-        if (n < LOADS) dma(n, base, o, kb);
+      for (int n = t * OPS / NMA; n < (t + 1) * OPS / NMA; ++n) {
+        if (n < LOADS) dma(n, base, st);
         else frag_read(n - LOADS, sl, 0, Nxt{});
       }
     }
   };
+  using Mid = std::false_type;
+  using Last = std::true_type;
+  // the end of this block's tile ti (its last k-step done): epilogue, then the
+  // first fragments of the next tile, from the next slot
+  auto tile_end = [&](int ti, int slot) {
+    epilogue(tile_at(ti));
+    stored = true;
+    const u32x4_t* sl = ring + next_slot(slot) * SLOT;
+#pragma unroll
+    for (int n = 0; n < NREADS; ++n) frag_read(n, sl, 0, Set0{});
+  };
   int slot = 0;
-  if constexpr (KS == 2) {
-    for (int s = 0; s < NS; ++s) {
-      kstep(s, 0, slot, Set0{});
-      kstep(s, 1, slot, Set1{});
-      slot = slot + 1 == R ? 0 : slot + 1;
-    }
-  } else {
-    for (int s = 0; s < NS; s += 2) {
-      const int s1 = slot + 1 == R ? 0 : slot + 1;
-      kstep(s, 0, slot, Set0{});
-      kstep(s + 1, 0, s1, Set1{});
-      slot = s1 + 1 == R ? 0 : s1 + 1;
-    }
-  }
-  wait_vm<0>();   // the last stages' loads (of nothing) land before LDS is released
-  mfma_drain();
-
-  // ---- epilogue -------------------------------------------------------------
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int64_t lrow = row_begin + wm * TM + i * 16 + li;
-    const bool row_ok = lrow < row_end;
-    if constexpr (OUT == GEMM_OUT_GEGLU) {
-#pragma unroll
-      for (int q = 0; q < HALF / 2; ++q) {
-        const int64_t n = n0 + wn * (TN / 2) + q * 32 + 8 * lg;
-        float v[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = gelu_tanh(acc[i][2 * q][r]) * acc[i][HALF + 2 * q][r];
-          v[4 + r] = gelu_tanh(acc[i][2 * q + 1][r]) * acc[i][HALF + 2 * q + 1][r];
-        }
-        if (row_ok && n < N)
-          st16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
+  for (int ti = 0; ti < nmine; ++ti) {
+    if constexpr (KS == 2) {
+      for (int q = 0; q < NS - 1; ++q) {
+        kstep(0, slot, Set0{}, Mid{});
+        kstep(1, slot, Set1{}, Mid{});
+        slot = next_slot(slot);
       }
+      kstep(0, slot, Set0{}, Mid{});
+      kstep(1, slot, Set1{}, Last{});
     } else {
-#pragma unroll
-      for (int q = 0; q < FN / 2; ++q) {
-        const int64_t n = n0 + wn * TN + q * 32 + 8 * lg;
-        float v[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][2 * q][r];
-          v[4 + r] = acc[i][2 * q + 1][r];
-        }
-        if (!(row_ok && n < N)) continue;
-        if constexpr (OUT == GEMM_OUT_F32_SCALED) {
-          const float s = p.row_scale[lrow];
-          float* dst = static_cast<float*>(p.C) + lrow * p.ldc + n;
-          u32x4_t lo, hi;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            lo[r] = __float_as_uint(v[r] * s);
-            hi[r] = __float_as_uint(v[4 + r] * s);
-          }
-          st16(dst, lo);
-          st16(dst + 4, hi);
-        } else {
-          if (p.bias) {
-            float b[8];
-            unpack_bf16x8(ld16(p.bias + n), b);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) v[r] += b[r];
-          }
-          if (p.act != ACT_NONE) {
-#pragma unroll
-            for (int r = 0; r < 8; ++r) v[r] = apply_act(v[r], p.act);
-          }
-          st16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
-        }
+      for (int q = 0; q < NS - 2; q += 2) {   // NS is even
+        kstep(0, slot, Set0{}, Mid{});
+        slot = next_slot(slot);
+        kstep(0, slot, Set1{}, Mid{});
+        slot = next_slot(slot);
       }
+      kstep(0, slot, Set0{}, Mid{});
+      slot = next_slot(slot);
+      kstep(0, slot, Set1{}, Last{});
     }
+    tile_end(ti, slot);
+    slot = next_slot(slot);
   }
+  wait_vm<0>();   // the stages issued past the end (loads of nothing) land before LDS is released
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED>
@@ -397,11 +551,19 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)((p.N + OUT_N - 1) / OUT_N);
   p.group_m = 4;
-  const int64_t blocks = (int64_t)p.tiles_m * p.tiles_n;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED>), dim3((unsigned)blocks),
-                     dim3(WM * WN * 64), 0, s, p);
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;   // grouped: an upper bound
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffff || p.cus <= 0) return hipErrorInvalidValue;
+  // persistent: as many blocks as fit on the chip at once, each looping over
+  // its tiles
+  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED>;
+  static const int per_cu = [&] {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, WM * WN * 64, 0) != hipSuccess) o = 1;
+    return std::max(o, 1);
+  }();
+  const int64_t blocks = std::min<int64_t>(tiles, (int64_t)p.cus * per_cu);
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -34,6 +34,7 @@ struct GemmParams {
   const int32_t* tile_off;   // grouped: [groups+1] prefix of m-tiles per group
   int groups;
   const float* row_scale;    // GEMM_OUT_F32_SCALED: per logical row
+  int cus;                   // compute units: the persistent grid's size cap
   // launch geometry, filled by launch_gemm
   int tiles_m, tiles_n, group_m;
 };
@@ -47,8 +48,9 @@ enum GemmTile : int {
 
 int gemm_tile_bm(int tile);
 int gemm_tile_bn(int tile);
-// Launch one GEMM.  For grouped mode p.tiles_m must be an upper bound on the
-// number of m tiles over all groups (extra blocks exit at once).
+// Launch one GEMM on a persistent grid of at most p.cus blocks.  For grouped
+// mode p.tiles_m must be an upper bound on the number of m tiles over all
+// groups (it sizes the grid; the kernel counts the tiles that exist).
 hipError_t launch_gemm(int out_kind, bool gather, bool grouped, int tile, GemmParams p,
                        hipStream_t s);
 
