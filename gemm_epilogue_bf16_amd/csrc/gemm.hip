@@ -462,7 +462,8 @@ gemm_bf16_kernel(GemmParams p) {
   //    wave's loads of stage q + 1, then a barrier: stage q + 1 is in LDS for
   //    every wave, and every wave has finished reading `slot`); the second
   //    half, each MFMA followed by at most one instruction of the hand-off
-  //    stream: the loads of stage q + R into `slot`, then the fragment reads
+  //    stream: the loads of stage q + R into `slot` (the first LNOW of them;
+  //    the rest lead the next stage's first k-step), then the fragment reads
   //    of stage q + 1 into the other set.  The matrix core never waits for a
   //    run of memory instructions.  At the end of a tile (LAST) the fragment
   //    reads wait until the epilogue has freed its registers.  After an
@@ -470,7 +471,19 @@ gemm_bf16_kernel(GemmParams p) {
   //    access, so no wait count depends on how loads and stores retire
   //    relative to each other.
   constexpr int NMA = (FM / 2) * FN;          // MFMAs per half k-step
-  constexpr int NOPS = LOADS + NREADS;
+  constexpr int NPRE = NMA;                   // MFMAs of the last k-step before the hand-off
+  constexpr int NPOST = 2 * NMA - NPRE;
+  static_assert(NPRE >= 1 && NPOST >= 1, "hand-off inside the last k-step");
+  // Loads of stage q + R issued in the hand-off window.  With two k-steps per
+  // stage half of them go out during the next stage's first k-step instead:
+  // every wave reaches the hand-off together, and eight loads each in a
+  // quarter of a stage queue behind one another in the address unit (measured
+  // 3-4 % faster on the large shapes; a quarter or none in the window is
+  // slower again).
+  constexpr int LNOW = KS == 2 ? LOADS / 2 : LOADS;
+  StageIssue pend_st{false, false, 0};
+  uint32_t pend_base = 0;
+  bool pend = false;   // block-uniform: the first stage has none
   bool stored = false;   // an epilogue has stored since the last hand-off
   auto next_slot = [&](int sl) { return sl + 1 == R ? 0 : sl + 1; };
   auto kstep = [&](int ks, int slot, auto cur_c, auto last_c) {
@@ -479,33 +492,41 @@ gemm_bf16_kernel(GemmParams p) {
     using Nxt = std::integral_constant<int, CUR ^ 1>;
     if (ks + 1 < KS) {
       const u32x4_t* sl = ring + slot * SLOT;
+      constexpr int OPS0 = NREADS + (LOADS - LNOW);   // the deferred loads, then the reads
 #pragma unroll
       for (int t = 0; t < 2 * NMA; ++t) {
         mfma_t(t, cur_c);
 #pragma unroll
-        for (int n = t * NREADS / (2 * NMA); n < (t + 1) * NREADS / (2 * NMA); ++n)
-          frag_read(n, sl, ks + 1, Nxt{});
+        for (int n = t * OPS0 / (2 * NMA); n < (t + 1) * OPS0 / (2 * NMA); ++n) {
+          if (n < LOADS - LNOW) {
+            if (pend) dma(LNOW + n, pend_base, pend_st);
+          }
+          else frag_read(n - (LOADS - LNOW), sl, ks + 1, Nxt{});
+        }
       }
       return;
     }
     const StageIssue st = stage_begin();   // stage q + R
 #pragma unroll
-    for (int t = 0; t < NMA; ++t) mfma_t(t, cur_c);
+    for (int t = 0; t < NPRE; ++t) mfma_t(t, cur_c);
     if (R > 2 && stored) wait_vm<0>(); else wait_vm<LOADS * (R - 2)>();
     stored = false;
     lds_barrier();
     const uint32_t base = ring_lds + (uint32_t)slot * (SLOT * 16);
     const u32x4_t* sl = ring + next_slot(slot) * SLOT;
-    constexpr int OPS = LAST ? LOADS : NOPS;
+    constexpr int OPS = LAST ? LNOW : LNOW + NREADS;
 #pragma unroll
-    for (int t = 0; t < NMA; ++t) {
-      mfma_t(NMA + t, cur_c);
+    for (int t = 0; t < NPOST; ++t) {
+      mfma_t(NPRE + t, cur_c);
 #pragma unroll
-      for (int n = t * OPS / NMA; n < (t + 1) * OPS / NMA; ++n) {
-        if (n < LOADS) dma(n, base, st);
-        else frag_read(n - LOADS, sl, 0, Nxt{});
+      for (int n = t * OPS / NPOST; n < (t + 1) * OPS / NPOST; ++n) {
+        if (n < LNOW) dma(n, base, st);
+        else frag_read(n - LNOW, sl, 0, Nxt{});
       }
     }
+    pend_st = st;
+    pend_base = base;
+    pend = true;
   };
   using Mid = std::false_type;
   using Last = std::true_type;
