@@ -41,6 +41,21 @@ def test_geglu_random(M, D, H):
         assert_parity(_run(*d, path=p), ref, f"geglu {M}x{D}x{H} {p}")
 
 
+def test_geglu_persistent_multi_tile_ragged():
+    """Gate+up on 256x256 tiles, 9 x 33 = 297 of them (more than 256 CUs),
+    with tails in tokens (2100 = 8*256 + 52), hidden (4104) and dim (264)."""
+    rng = np.random.default_rng(2100)
+    M, D, H = 2100, 264, 4104
+    x = rand_bf16(rng, (M, D))
+    Wg = rand_bf16(rng, (H, D), D ** -0.5, "uniform")
+    Wu = rand_bf16(rng, (H, D), D ** -0.5, "uniform")
+    Wd = rand_bf16(rng, (D, H), H ** -0.5, "uniform")
+    print(f"case geglu persistent M={M} D={D} H={H}", flush=True)
+    y = _run(*(to_dev(a) for a in (x, Wg, Wu, Wd)))
+    ref = oracle.geglu(f64_of_bits(x), f64_of_bits(Wg), f64_of_bits(Wu), f64_of_bits(Wd))
+    assert_parity(y, ref, f"geglu {M}x{D}x{H}")
+
+
 def test_geglu768_full():
     w = datagen.workload("geglu768")
     t = datagen.make_inputs(w, seed=0)

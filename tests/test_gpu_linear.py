@@ -36,6 +36,25 @@ def test_linear_random(M, K, N, act):
         assert_parity(y, ref, f"linear {M}x{K}x{N} {act}")
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (4100, 328, 4104),   # 256x256 tiles: 17 x 17 = 289 > 256 CUs, so some blocks run two
+    (8200, 136, 1000),   # 128x128 tiles: 65 x 8 = 520 > 512 block slots
+])
+@pytest.mark.parametrize("act", ["gelu_erf", "gelu_tanh"])
+def test_linear_persistent_multi_tile_ragged(M, K, N, act):
+    """More tiles than the persistent grid holds, with a tail in M, N and K:
+    blocks carry the load stream and the epilogue across tile boundaries."""
+    rng = np.random.default_rng(M + K + N)
+    x = rand_bf16(rng, (M, K))
+    W = rand_bf16(rng, (N, K), K ** -0.5, "uniform")
+    b = rand_bf16(rng, (N,), 0.5, "uniform")
+    print(f"case linear persistent M={M} K={K} N={N} act={act}", flush=True)
+    y = F.fmlp_linear(to_dev(x), to_dev(W), to_dev(b), act)
+    torch.cuda.synchronize()
+    ref = oracle.linear(f64_of_bits(x), f64_of_bits(W), f64_of_bits(b), act)
+    assert_parity(y, ref, f"linear {M}x{K}x{N} {act}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 40, 300])
 def test_gelu_variant_pin(M):
     """Identity W, no bias, x in [-4, -2.5]: here the two GELU forms differ by
