@@ -226,8 +226,8 @@ gemm_bf16_kernel(GemmParams p) {
   // so 32-bit offsets suffice and kOutOfRange is past every descriptor's end.
   // A tile's descriptors end at its last valid row, so rows past the end of
   // the activation or weight arrive as zeros with no per-lane test; gathered
-  // rows past a group's end repeat its last row (their outputs are dropped).
-  // Only chunks past K need a mask: they would read the next row.
+  // rows past a group's end get an out-of-range offset once per tile.  Only
+  // chunks past K need a mask per stage: they would read the next row.
   static_assert((RPI * NW) % 32 == 0, "one chunk permutation per lane");
   const int ra = RPI * wave + lane / CH;      // tile row of the lane's load 0 (activation and weight)
   const int a_k = 8 * ((lane % CH) ^ swz_a<CH>(ra));   // k of the lane's chunk in a stage
@@ -251,8 +251,9 @@ gemm_bf16_kernel(GemmParams p) {
       const int ak = 8 * ((opaque(lane) % CH) ^ swz_a<CH>(rt));
 #pragma unroll
       for (int i = 0; i < A_INS; ++i) {
-        const int r = min(RPI * i * NW + rt, a_rows_here - 1);
-        a_gat[i] = (uint32_t)p.a_rows[t.row_begin + r] * lda2 + (uint32_t)ak * 2u;
+        const int r = RPI * i * NW + rt;
+        const uint32_t src = (uint32_t)p.a_rows[t.row_begin + min(r, a_rows_here - 1)];
+        a_gat[i] = r < a_rows_here ? src * lda2 + (uint32_t)ak * 2u : kOutOfRange;
       }
     }
   };
