@@ -148,9 +148,22 @@ GemmParams dense_params(const uint16_t* A, int64_t lda, const uint16_t* B0, cons
   return p;
 }
 
+// Plain bf16-output GEMM.  Between "256 tiles fill the chip" and small
+// shapes, a width that is a multiple of 192 whose 128x192 tiles fit in one
+// round on the chip runs on those: every CU gets one tile, where 128x128
+// tiles would leave a second, partial round (the 768-wide down projection:
+// 256 tiles of 128x192 against 384 of 128x128 on 512 block slots).
+int choose_tile_linear(int64_t M, int64_t N, int cus) {
+  const int tile = choose_tile(M, (N + 255) / 256, cus);
+  if (tile == TILE_256x256) return tile;
+  const int64_t t192 = ((M + 127) / 128) * (N / 192);
+  if (N % 192 == 0 && t192 <= cus && 4 * t192 >= 3 * (int64_t)cus) return TILE_128x192;
+  return tile;
+}
+
 hipError_t gemm_linear(const uint16_t* x, const uint16_t* W, const uint16_t* b, int act, int64_t M,
                        int64_t K, int64_t N, uint16_t* y, int cus, hipStream_t s) {
-  const int tile = choose_tile(M, (N + 255) / 256, cus);
+  const int tile = choose_tile_linear(M, N, cus);
   return launch_gemm(GEMM_OUT_BF16, false, false, tile, dense_params(x, K, W, nullptr, b, y, N, M, N, K, act, cus), s);
 }
 

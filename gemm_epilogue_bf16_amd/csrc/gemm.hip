@@ -594,6 +594,11 @@ hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   switch (tile) {
     case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED>(p, s);
     case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED>(p, s);
+    case TILE_128x192:
+      if constexpr (OUT == GEMM_OUT_BF16 && !GATHER && !GROUPED)
+        return launch_cfg<128, 192, 4, 2, 64, 3, OUT, GATHER, GROUPED>(p, s);
+      else
+        return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -601,7 +606,7 @@ hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
 }  // namespace
 
 int gemm_tile_bm(int tile) { return tile == TILE_256x256 ? 256 : 128; }
-int gemm_tile_bn(int tile) { return tile == TILE_256x256 ? 256 : 128; }
+int gemm_tile_bn(int tile) { return tile == TILE_256x256 ? 256 : tile == TILE_128x192 ? 192 : 128; }
 
 hipError_t launch_gemm(int out_kind, bool gather, bool grouped, int tile, GemmParams p,
                        hipStream_t s) {

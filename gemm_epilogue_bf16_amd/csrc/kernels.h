@@ -43,6 +43,7 @@ struct GemmParams {
 enum GemmTile : int {
   TILE_128x128 = 0,   // 4 waves, 64x64 per wave
   TILE_256x256 = 1,   // 8 waves, 128x64 per wave
+  TILE_128x192 = 2,   // 8 waves, 32x96 per wave; plain bf16 output only
   TILE_COUNT
 };
 

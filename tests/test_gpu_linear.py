@@ -39,6 +39,7 @@ def test_linear_random(M, K, N, act):
 @pytest.mark.parametrize("M,K,N", [
     (4100, 328, 4104),   # 256x256 tiles: 17 x 17 = 289 > 256 CUs, so some blocks run two
     (8200, 136, 1000),   # 128x128 tiles: 65 x 8 = 520 > 512 block slots
+    (8000, 200, 768),    # 128x192 tiles: 63 x 4 = 252, one round; tails in M and K
 ])
 @pytest.mark.parametrize("act", ["gelu_erf", "gelu_tanh"])
 def test_linear_persistent_multi_tile_ragged(M, K, N, act):
