@@ -378,12 +378,14 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
     // ---- consume side: the stage in ring slot `slot` ------------------------
     // Once every stage has been requested (stream index >= quiet_from), the
     // first step waits for all loads and meets the other waves once; the
-    // rest read resident stages with no wait and no barrier.
+    // rest read resident stages with no wait and no barrier, except that a
+    // tile ending there meets the control wave before writing its partials.
     Seg cs = seg_first<TWO>(st);
     const int quiet_from = st.total - (R - 1) > 0 ? st.total - (R - 1) : 0;
     int gidx = 0;              // stream index of the stage being consumed
     auto step = [&](uint32_t slot) {
       if (cs.left == 0) seg_next<TWO>(st, cs);
+      const bool quiet = gidx > quiet_from;   // no barrier at the head of this step
       if (gidx < quiet_from) {
         wait_vm<RS::kLoads * (R - 2)>();   // this wave's loads of the stage
         lds_barrier();                     // the stage is in LDS for every wave; the slot before it is free
@@ -424,6 +426,9 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
         }
       }
       if (last) {                        // partial tile of this wave -> control wave
+        // with no barrier since the previous tile's end, the control wave may
+        // still be reading that tile's partials: meet it first
+        if (quiet) lds_barrier();
         red[0][w * 64 + lane] = make_float4(acc0[0], acc0[1], acc0[2], acc0[3]);
         if (DUAL1 && cs.kind == SEG_L1)
           red[kSets - 1][w * 64 + lane] = make_float4(acc1[0], acc1[1], acc1[2], acc1[3]);
@@ -623,9 +628,11 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   int gidx = 0;
   auto ctrl_step = [&]() {
     if (cs.left == 0) seg_next<TWO>(st, cs);
-    if (gidx <= quiet_from) lds_barrier();
+    const bool quiet = gidx > quiet_from;
+    if (!quiet) lds_barrier();
     ++gidx;
     if (cs.kind != SEG_END && cs.left == 1) {
+      if (quiet) lds_barrier();      // the previous epilogue is done with the partials
       lds_barrier();                 // the workers' partial tiles are in LDS
       const Seg q = cs;
       seg_next<TWO>(st, bq);         // request the next tile's bias

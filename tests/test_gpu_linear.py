@@ -56,6 +56,28 @@ def test_linear_persistent_multi_tile_ragged(M, K, N, act):
     assert_parity(y, ref, f"linear {M}x{K}x{N} {act}")
 
 
+@pytest.mark.parametrize("M,K,N", [
+    (1, 256, 12328),     # one-stage tiles, three or four per block (ragged last tile)
+    (16, 512, 12288),    # one-stage tiles, three per block, sixteen tokens
+    (3, 1024, 8192),     # two-stage tiles, two per block
+])
+def test_decode_short_tiles_at_stream_end(M, K, N):
+    """Tiles of one or two stages at the end of a block's stream, where steps
+    have no barrier of their own: each tile's partial sums must not be
+    overwritten by the next tile's before the control wave has reduced them."""
+    rng = np.random.default_rng(M + K + N)
+    x = rand_bf16(rng, (M, K))
+    W = rand_bf16(rng, (N, K), K ** -0.5, "uniform")
+    b = rand_bf16(rng, (N,), 0.5, "uniform")
+    print(f"case linear decode short tiles M={M} K={K} N={N}", flush=True)
+    with F.force_path("decode"):
+        for _ in range(3):
+            y = F.fmlp_linear(to_dev(x), to_dev(W), to_dev(b), "gelu_erf")
+    torch.cuda.synchronize()
+    ref = oracle.linear(f64_of_bits(x), f64_of_bits(W), f64_of_bits(b), "gelu_erf")
+    assert_parity(y, ref, f"linear decode {M}x{K}x{N}")
+
+
 @pytest.mark.parametrize("M", [1, 16, 40, 300])
 def test_gelu_variant_pin(M):
     """Identity W, no bias, x in [-4, -2.5]: here the two GELU forms differ by

@@ -55,6 +55,7 @@ SHAPES = [
     # (M, K, H, N)
     (1, 8, 8, 8), (1, 64, 200, 40), (3, 136, 520, 264), (16, 512, 256, 1024), (16, 1024, 4096, 64),
     (9, 4096, 1024, 4096), (17, 32, 64, 32), (40, 128, 128, 128), (100, 96, 40, 120),
+    (16, 1024, 512, 16384), (1, 2048, 256, 12288),   # one-stage layer-2 tiles, several per block
     (257, 256, 512, 136), (600, 768, 1024, 392),
 ]
 
@@ -150,6 +151,9 @@ def test_decode_determinism_and_repeat():
     (256, 4104, 520),   # hidden size just past the word-flag limit
     (256, 4096, 520),   # at the limit: word-flag publish
     (512, 200, 40),     # word-flag publish, ragged tiles
+    (2048, 1024, 512),  # word-flag publish on 64 blocks, half of them without a layer-2 tile
+    (1024, 4096, 8192), # word-flag publish, two layer-2 tiles per block
+    (1024, 4096, 520),  # word-flag publish, one-stage layer-1 tiles, most blocks own no layer-2 tile
 ])
 def test_decode_one_token_publish_paths(K, H, N):
     """At one token the hidden vector is published either as epoch-tagged
