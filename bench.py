@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the fused feed-forward path on one MI355X (gfx950).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--act ACT]
 
 A step is one forward of the workload's whole feed-forward block through the
 C ABI (one fmlp_* call) on synthetic seeded bf16 inputs already resident in
-HBM.  Default workload: the decode two-layer MLP 4096 -> 4096 -> 4096 with exact
+HBM.  --act replaces the workload's activation (two-layer MLPs) or its gate
+activation (gated blocks and MoE: "silu" runs SwiGLU).  Default workload: the decode two-layer MLP 4096 -> 4096 -> 4096 with exact
 GELU and biases at 1 token (the 4096-wide GELU MLP at batch 1 of ainews.cool
 "PyTorch fused MLP efficiency", section "benchmark data").  Its 64 MiB of
 weights fit the 256 MB Infinity Cache, so by default steps rotate through
@@ -85,13 +86,21 @@ def _copies_for(weight_bytes: int, cold: bool) -> int:
     return max(1, -(-COLD_BYTES // weight_bytes))
 
 
-def setup_case(name: str, cold: bool, dev, path: str):
+def setup_case(name: str, cold: bool, dev, path: str, act=None):
+    import dataclasses
+
     import torch
 
     import datagen
     import gemm_epilogue_bf16_amd as F
 
     w = datagen.workload(name)
+    gate_act = None
+    if act is not None:
+        if w.op == "mlp2":
+            w = dataclasses.replace(w, act=act)
+        else:
+            gate_act = act
     f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)  # noqa: E731
     R = _copies_for(w.weight_bytes, cold)
 
@@ -126,7 +135,10 @@ def setup_case(name: str, cold: bool, dev, path: str):
         else:
             ws = F.workspace_for(dev, F.fmlp_geglu_workspace_size(w.M, w.K, w.H))
             for s in sets:
-                calls.append(F.bind_geglu(x, s["Wg"], s["Wu"], s["Wd"], out=y, workspace=ws))
+                if gate_act is None:
+                    calls.append(F.bind_geglu(x, s["Wg"], s["Wu"], s["Wd"], out=y, workspace=ws))
+                else:
+                    calls.append(F.bind_glu(x, s["Wg"], s["Wu"], s["Wd"], gate_act, out=y, workspace=ws))
             if w.M <= 16:
                 kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             else:
@@ -140,6 +152,8 @@ def setup_case(name: str, cold: bool, dev, path: str):
                 if not cache:   # input decoding (bf16 bits -> float64), once, before timing
                     cache.update({k: f64(v) for k, v in t.items()})
                 c = cache
+                if gate_act is not None:
+                    return oracle.glu(c["x"][:rows], c["Wg"], c["Wu"], c["Wd"], gate_act)
                 return oracle.geglu(c["x"][:rows], c["Wg"], c["Wu"], c["Wd"])
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
         return Case(w, calls, kernel, launches, p, R, fn, sample)
@@ -156,7 +170,10 @@ def setup_case(name: str, cold: bool, dev, path: str):
     gw_d = torch.from_numpy(gw).to(dev)
     y = torch.empty_like(x)
     ws = F.workspace_for(dev, F.fmlp_moe_workspace_size(w.M, w.K, w.H, w.E, w.top_k))
-    calls = [F.bind_moe_geglu(x, ids_d, gw_d, Wg, Wu, Wd, out=y, workspace=ws)]
+    if gate_act is None:
+        calls = [F.bind_moe_geglu(x, ids_d, gw_d, Wg, Wu, Wd, out=y, workspace=ws)]
+    else:
+        calls = [F.bind_moe_glu(x, ids_d, gw_d, Wg, Wu, Wd, gate_act, out=y, workspace=ws)]
     import oracle
 
     toks = 32
@@ -168,7 +185,10 @@ def setup_case(name: str, cold: bool, dev, path: str):
             f64e[e] = tuple(datagen.bf16_to_f32(a).astype(np.float64) for a in experts[e])
         return f64e[e]
 
-    fn = lambda: oracle.moe_geglu(xs, ids[:toks], gw[:toks], get)  # noqa: E731
+    if gate_act is None:
+        fn = lambda: oracle.moe_geglu(xs, ids[:toks], gw[:toks], get)  # noqa: E731
+    else:
+        fn = lambda: oracle.moe_glu(xs, ids[:toks], gw[:toks], get, gate_act)  # noqa: E731
     return Case(w, calls, "gemm_bf16_kernel", 4, "route + grouped gate+up + grouped down + combine",
                 1, fn, (f"{toks} of {w.M} tokens (their experts' weights pre-converted)", toks / w.M))
 
@@ -238,6 +258,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode1",
                     choices=["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe"])
+    ap.add_argument("--act", default=None, choices=["none", "gelu_erf", "gelu_tanh", "relu", "silu"],
+                    help="activation of a two-layer MLP, or gate activation of a gated block")
     ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -262,7 +284,7 @@ def main(argv=None):
         copy_calibration(dev, args.copy_calibration << 20, 10)
         return 0
 
-    case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path)
+    case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path, act=args.act)
     w = case.w
     est_us = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
               "large16": 250, "large4096": 4000, "moe": 2500}[args.workload]
@@ -326,7 +348,7 @@ def main(argv=None):
     roof["us_per_launch_bracketed"] = round(per_launch_s * 1e6, 3)
 
     vs = None
-    if w.name.startswith("decode_mlp2_4096x4096x4096_M1"):
+    if w.name.startswith("decode_mlp2_4096x4096x4096_M1") and args.act in (None, "gelu_erf"):
         vs = round(value / (w.flops / (PAGE_H100_FUSED_US * 1e-6) / 1e12), 4)
 
     out = {
@@ -347,7 +369,7 @@ def main(argv=None):
             "op": w.op,
             "tokens": w.M,
             "dims": {"in": w.K, "hidden": w.H, "out": w.N, **({"experts": w.E, "top_k": w.top_k} if w.op == "moe" else {})},
-            "act": w.act if w.op == "mlp2" else "gelu_tanh (GeGLU)",
+            "act": w.act if w.op == "mlp2" else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)"),
             "bias": w.bias,
             "weights": (f"cold: {case.copies} rotated copies ({case.copies * w.weight_bytes / 2**20:.0f} MiB)"
                         if case.copies > 1 else "single copy"),

@@ -11,8 +11,12 @@ raises.
     fmlp_linear(x, W, b=None, act="none")          y = act(x W^T + b)
     fmlp_mlp2(x, W1, b1, W2, b2, act)               y = act(x W1^T + b1) W2^T + b2
     fmlp_geglu(x, Wg, Wu, Wd)                       y = (gelu_tanh(x Wg^T) * x Wu^T) Wd^T
+    fmlp_glu(x, Wg, Wu, Wd, gate_act)               y = (gate_act(x Wg^T) * x Wu^T) Wd^T
     fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd)
                                                     y[t] = sum_j w[t,j] geglu_{e[t,j]}(x[t])
+    fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act)
+
+Activations: "none", "gelu_erf", "gelu_tanh", "relu", "silu".
 """
 from __future__ import annotations
 
@@ -31,7 +35,9 @@ __all__ = [
     "fmlp_linear",
     "fmlp_mlp2",
     "fmlp_geglu",
+    "fmlp_glu",
     "fmlp_moe_geglu",
+    "fmlp_moe_glu",
     "fmlp_mlp2_workspace_size",
     "fmlp_geglu_workspace_size",
     "fmlp_moe_workspace_size",
@@ -42,7 +48,9 @@ __all__ = [
     "BoundCall",
     "bind_mlp2",
     "bind_geglu",
+    "bind_glu",
     "bind_moe_geglu",
+    "bind_moe_glu",
     "bind_linear",
     "linear",
     "mlp2",
@@ -50,7 +58,7 @@ __all__ = [
     "moe_geglu",
 ]
 
-ACT = {"none": 0, "gelu_erf": 1, "gelu_tanh": 2}
+ACT = {"none": 0, "gelu_erf": 1, "gelu_tanh": 2, "relu": 3, "silu": 4}
 PATHS = {"auto": 0, "decode": 1, "gemm": 2, "small": 3}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -89,15 +97,21 @@ def lib() -> ctypes.CDLL:
         L.fmlp_linear.argtypes = [_p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
         L.fmlp_mlp2.argtypes = [_p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p, _sz, _p]
         L.fmlp_geglu.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _p, _p, _sz, _p]
+        L.fmlp_glu.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _sz, _p]
         L.fmlp_moe_geglu.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i64, ctypes.c_int32,
                                      ctypes.c_int32, _p, _p, _sz, _p]
-        for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_moe_geglu", "fmlp_set_path"):
+        L.fmlp_moe_glu.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int32,
+                                   ctypes.c_int32, _p, _p, _sz, _p]
+        for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
+                  "fmlp_set_path"):
             getattr(L, f).restype = ctypes.c_int
         L.fmlp_set_path.argtypes = [ctypes.c_int]
         L.fmlp_mlp2_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
         L.fmlp_mlp2_workspace_size.restype = _sz
         L.fmlp_geglu_workspace_size.argtypes = [_i64, _i64, _i64]
         L.fmlp_geglu_workspace_size.restype = _sz
+        L.fmlp_glu_workspace_size.argtypes = [_i64, _i64, _i64]
+        L.fmlp_glu_workspace_size.restype = _sz
         L.fmlp_moe_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.c_int32, ctypes.c_int32]
         L.fmlp_moe_workspace_size.restype = _sz
         L.fmlp_moe_error_offset.argtypes = []
@@ -261,7 +275,7 @@ def fmlp_geglu_workspace_size(M, D, H) -> int:
     return int(lib().fmlp_geglu_workspace_size(M, D, H))
 
 
-def _geglu_call(x, Wg, Wu, Wd, out, workspace):
+def _geglu_call(x, Wg, Wu, Wd, out, workspace, gate_act=None):
     for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
         _dev_tensor(n, t)
     D = x.shape[-1]
@@ -273,8 +287,11 @@ def _geglu_call(x, Wg, Wu, Wd, out, workspace):
     L = lib()
     need = int(L.fmlp_geglu_workspace_size(M, D, H))
     ws = workspace if workspace is not None else workspace_for(x.device, need)
-    return BoundCall(L.fmlp_geglu, (_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), M, D, H, _ptr(y), _ptr(ws),
-                                    ws.numel(), _stream(x.device)), y, (x, Wg, Wu, Wd, ws))
+    if gate_act is None:
+        return BoundCall(L.fmlp_geglu, (_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), M, D, H, _ptr(y), _ptr(ws),
+                                        ws.numel(), _stream(x.device)), y, (x, Wg, Wu, Wd, ws))
+    return BoundCall(L.fmlp_glu, (_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), ACT[gate_act], M, D, H, _ptr(y),
+                                  _ptr(ws), ws.numel(), _stream(x.device)), y, (x, Wg, Wu, Wd, ws))
 
 
 def fmlp_geglu(x, Wg, Wu, Wd, out=None, workspace=None):
@@ -288,11 +305,22 @@ def bind_geglu(x, Wg, Wu, Wd, out=None, workspace=None) -> BoundCall:
         return _geglu_call(x, Wg, Wu, Wd, out, workspace)
 
 
+def fmlp_glu(x, Wg, Wu, Wd, gate_act: str = "silu", out=None, workspace=None):
+    """y = (gate_act(x Wg^T) * (x Wu^T)) Wd^T; "silu" is SwiGLU, "gelu_tanh" GeGLU."""
+    with torch.cuda.device(x.device):
+        return _geglu_call(x, Wg, Wu, Wd, out, workspace, gate_act)()
+
+
+def bind_glu(x, Wg, Wu, Wd, gate_act: str = "silu", out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _geglu_call(x, Wg, Wu, Wd, out, workspace, gate_act)
+
+
 def fmlp_moe_workspace_size(T, D, H, E, top_k) -> int:
     return int(lib().fmlp_moe_workspace_size(T, D, H, E, top_k))
 
 
-def _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace):
+def _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace, gate_act=None):
     for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
         _dev_tensor(n, t)
     _dev_tensor("expert_ids", expert_ids, torch.int32)
@@ -308,10 +336,14 @@ def _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace):
     L = lib()
     need = int(L.fmlp_moe_workspace_size(T, D, H, E, k))
     ws = workspace if workspace is not None else workspace_for(x.device, need)
-    return BoundCall(L.fmlp_moe_geglu, (_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu),
-                                        _ptr(Wd), T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(),
-                                        _stream(x.device)), y,
-                     (x, expert_ids, gate_w, Wg, Wu, Wd, ws))
+    keep = (x, expert_ids, gate_w, Wg, Wu, Wd, ws)
+    if gate_act is None:
+        return BoundCall(L.fmlp_moe_geglu, (_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu),
+                                            _ptr(Wd), T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(),
+                                            _stream(x.device)), y, keep)
+    return BoundCall(L.fmlp_moe_glu, (_ptr(x), _ptr(expert_ids), _ptr(gate_w), _ptr(Wg), _ptr(Wu), _ptr(Wd),
+                                      ACT[gate_act], T, D, H, E, k, _ptr(y), _ptr(ws), ws.numel(),
+                                      _stream(x.device)), y, keep)
 
 
 def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
@@ -324,6 +356,18 @@ def fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None):
 def bind_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd, out=None, workspace=None) -> BoundCall:
     with torch.cuda.device(x.device):
         return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace)
+
+
+def fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act: str = "silu", out=None, workspace=None):
+    """Top-k MoE of gated experts with the given gate activation ("silu": SwiGLU)."""
+    with torch.cuda.device(x.device):
+        return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace, gate_act)()
+
+
+def bind_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act: str = "silu", out=None,
+                 workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace, gate_act)
 
 
 # ---------------------------------------------------------------------------

@@ -71,9 +71,10 @@ fmlp_status check_inner(const char* name, int64_t v) {
   return FMLP_OK;
 }
 
-fmlp_status check_act(int act) {
-  if (act != FMLP_ACT_NONE && act != FMLP_ACT_GELU_ERF && act != FMLP_ACT_GELU_TANH)
-    return fail(FMLP_E_ARG, "act=%d is not an fmlp_act", act);
+fmlp_status check_act(int act, const char* name = "act") {
+  if (act != FMLP_ACT_NONE && act != FMLP_ACT_GELU_ERF && act != FMLP_ACT_GELU_TANH &&
+      act != FMLP_ACT_RELU && act != FMLP_ACT_SILU)
+    return fail(FMLP_E_ARG, "%s=%d is not an fmlp_act", name, act);
   return FMLP_OK;
 }
 
@@ -167,17 +168,18 @@ hipError_t gemm_linear(const uint16_t* x, const uint16_t* W, const uint16_t* b, 
   return launch_gemm(GEMM_OUT_BF16, false, false, tile, dense_params(x, K, W, nullptr, b, y, N, M, N, K, act, cus), s);
 }
 
-hipError_t gemm_geglu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int64_t M,
-                             int64_t D, int64_t H, uint16_t* m, int cus, hipStream_t s) {
+hipError_t gemm_glu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, int gate_act,
+                           int64_t M, int64_t D, int64_t H, uint16_t* m, int cus, hipStream_t s) {
   const int tile = choose_tile(M, (H + 127) / 128, cus);
-  return launch_gemm(GEMM_OUT_GEGLU, false, false, tile, dense_params(x, D, Wg, Wu, nullptr, m, H, M, H, D, 0, cus), s);
+  return launch_gemm(GEMM_OUT_GEGLU, false, false, tile,
+                     dense_params(x, D, Wg, Wu, nullptr, m, H, M, H, D, gate_act, cus), s);
 }
 
 }  // namespace
 
 extern "C" {
 
-int fmlp_version(void) { return 100; }
+int fmlp_version(void) { return 101; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {
@@ -293,12 +295,21 @@ size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H) {
   return kHeader + hidden_bytes(M, H);
 }
 
+size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H) { return fmlp_geglu_workspace_size(M, D, H); }
+
 fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
                        const fmlp_bf16* Wd, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
                        void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  return fmlp_glu(x, Wg, Wu, Wd, FMLP_ACT_GELU_TANH, M, D, H, y, workspace, workspace_bytes, stream);
+}
+
+fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
+                     const fmlp_bf16* Wd, int gate_act, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
+                     void* workspace, size_t workspace_bytes, fmlp_stream stream) {
   TRY(check_rows("M", M));
   TRY(check_inner("D", D));
   TRY(check_inner("H", H));
+  TRY(check_act(gate_act, "gate_act"));
   REQUIRE_PTR(x);
   REQUIRE_PTR(Wg);
   REQUIRE_PTR(Wu);
@@ -320,12 +331,12 @@ fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16*
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* m = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
   if (path == kPathDecode) {
-    GemvLayer L1{x, Wg, Wu, nullptr, m, D, H, FMLP_ACT_NONE, 1};
+    GemvLayer L1{x, Wg, Wu, nullptr, m, D, H, gate_act, 1};
     GemvLayer L2{m, Wd, nullptr, nullptr, y, H, D, FMLP_ACT_NONE, 0};
     return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
                     "geglu (decode, persistent) launch");
   }
-  hipError_t e = gemm_geglu_gateup(x, Wg, Wu, M, D, H, m, cus, s);
+  hipError_t e = gemm_glu_gateup(x, Wg, Wu, gate_act, M, D, H, m, cus, s);
   if (e != hipSuccess) return launched(e, "geglu gate+up launch");
   return launched(gemm_linear(m, Wd, nullptr, FMLP_ACT_NONE, M, H, D, y, cus, s), "geglu down launch");
 }
@@ -363,6 +374,15 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
                            const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int64_t T,
                            int64_t D, int64_t H, int32_t E, int32_t top_k, fmlp_bf16* y,
                            void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  return fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, FMLP_ACT_GELU_TANH, T, D, H, E, top_k, y, workspace,
+                      workspace_bytes, stream);
+}
+
+fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
+                         const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int gate_act,
+                         int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k, fmlp_bf16* y,
+                         void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_act(gate_act, "gate_act"));
   TRY(check_rows("T", T));
   TRY(check_inner("D", D));
   TRY(check_inner("H", H));
@@ -404,7 +424,7 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
   hipError_t e = launch_moe_route(expert_ids, gate_w, T, top_k, E, bm, r, s);
   if (e != hipSuccess) return launched(e, "moe route launch");
 
-  GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, 0, cus);
+  GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, gate_act, cus);
   g.a_rows = r.tok_of;
   g.a_src_rows = T;
   g.group_off = r.group_off;

@@ -1,4 +1,4 @@
-// Device helpers shared by the gfx950 kernels: bf16 <-> fp32, the GELU
+// Device helpers shared by the gfx950 kernels: bf16 <-> fp32, the activation
 // epilogues, the bf16 MFMA wrapper and the XCD-aware tile order.
 #pragma once
 
@@ -11,7 +11,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-enum Act : int { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2 };
+enum Act : int { ACT_NONE = 0, ACT_GELU_ERF = 1, ACT_GELU_TANH = 2, ACT_RELU = 3, ACT_SILU = 4 };
+constexpr int kActCount = 5;
 
 // ---------------------------------------------------------------------------
 // bf16
@@ -68,9 +69,32 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// ReLU: max(z, 0) (the two-layer MLP of ainews.cool "PyTorch fused MLP
+// efficiency", section "technical deep dive").
+__device__ __forceinline__ float relu(float z) { return z > 0.f ? z : 0.f; }
+
+// SiLU (swish): z * sigmoid(z) = z / (1 + exp(-z)), with the same hardware
+// exp2 and reciprocal as the tanh GELU above (a few relative 1e-7).  Limits:
+// z -> +inf gives z, z -> -inf gives -0.
+__device__ __forceinline__ float silu(float z) {
+  const float e = __builtin_amdgcn_exp2f(-1.44269504088896340736f * z);   // exp(-z)
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_of(float z) {
+  if constexpr (ACT == ACT_GELU_ERF) return gelu_erf(z);
+  else if constexpr (ACT == ACT_GELU_TANH) return gelu_tanh(z);
+  else if constexpr (ACT == ACT_RELU) return relu(z);
+  else if constexpr (ACT == ACT_SILU) return silu(z);
+  else return z;
+}
+
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == ACT_GELU_ERF) return gelu_erf(z);
   if (act == ACT_GELU_TANH) return gelu_tanh(z);
+  if (act == ACT_RELU) return relu(z);
+  if (act == ACT_SILU) return silu(z);
   return z;
 }
 

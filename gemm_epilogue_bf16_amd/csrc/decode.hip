@@ -533,7 +533,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       const float b[4] = {bf16_lo(bias.x), bf16_hi(bias.x), bf16_lo(bias.y), bf16_hi(bias.y)};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        v[r] = dual ? gelu_tanh(g[r]) * u[r] : apply_act(g[r] + b[r], act);   // b = 0 without a bias
+        v[r] = dual ? apply_act(g[r], act) * u[r] : apply_act(g[r] + b[r], act);   // b = 0 without a bias
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
       if (LL && !l2) {    // h as two words {bf16 pair, epoch}: the data is its own flag
         const __amdgpu_buffer_rsrc_t rh = make_rsrc(y, (uint32_t)N * 4u);

@@ -7,11 +7,13 @@
 // "Where did the transpose go? Kernel layouts and pre-ops".  The epilogue runs
 // on the fp32 accumulator in registers and writes only the final tile
 // (section "Why are there no separate mul and add kernels?"):
-//   GEMM_OUT_BF16        bias add + activation (none / exact GELU / tanh GELU)
+//   GEMM_OUT_BF16        bias add + activation (none / exact GELU / tanh GELU /
+//                        ReLU / SiLU)
 //   GEMM_OUT_GEGLU       gate and up projections share every A tile; the block
 //                        holds matching g and u accumulators and writes only
-//                        m = gelu_tanh(g) * u (section "The fused Triton kernel":
-//                        the intermediate never makes an HBM round trip)
+//                        m = act(g) * u, act = tanh GELU for GeGLU (section
+//                        "The fused Triton kernel": the intermediate never
+//                        makes an HBM round trip) or another gate activation
 //   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights)
 //
 // Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves
@@ -130,7 +132,12 @@ __device__ __forceinline__ void pin_agpr_ordered(f32x4_t& acc) { asm volatile(""
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 #pragma clang diagnostic pop
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED>
+// GACT: the gate activation of a gated (GEMM_OUT_GEGLU) kernel, fixed per
+// kernel so each carries one epilogue: with several epilogue copies behind a
+// runtime switch, the register allocator copied accumulator lanes out of AGPRs
+// inside the main loop, a few wait states after the (asm) MFMA that wrote them.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED,
+          int GACT = ACT_NONE>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -386,8 +393,8 @@ gemm_bf16_kernel(GemmParams p) {
           float v[8];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            v[r] = gelu_tanh(acc[i][2 * q][r]) * acc[i][HALF + 2 * q][r];
-            v[4 + r] = gelu_tanh(acc[i][2 * q + 1][r]) * acc[i][HALF + 2 * q + 1][r];
+            v[r] = act_of<ACT>(acc[i][2 * q][r]) * acc[i][HALF + 2 * q][r];
+            v[4 + r] = act_of<ACT>(acc[i][2 * q + 1][r]) * acc[i][HALF + 2 * q + 1][r];
           }
           if (row_ok && n < N) gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
         }
@@ -423,10 +430,7 @@ gemm_bf16_kernel(GemmParams p) {
               for (int r = 0; r < 8; ++r) v[r] += b[r];
             }
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-              if constexpr (ACT == ACT_GELU_ERF) v[r] = gelu_erf(v[r]);
-              else if constexpr (ACT == ACT_GELU_TANH) v[r] = gelu_tanh(v[r]);
-            }
+            for (int r = 0; r < 8; ++r) v[r] = act_of<ACT>(v[r]);
             gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
           }
         }
@@ -435,9 +439,13 @@ gemm_bf16_kernel(GemmParams p) {
   };
   auto epilogue = [&](const Tile& t) {
     mfma_drain();
-    if constexpr (OUT == GEMM_OUT_BF16) {
+    if constexpr (OUT == GEMM_OUT_GEGLU) {
+      epilogue_act(t, std::integral_constant<int, GACT>{});   // the gate's activation
+    } else if constexpr (OUT == GEMM_OUT_BF16) {
       if (p.act == ACT_GELU_ERF) epilogue_act(t, std::integral_constant<int, ACT_GELU_ERF>{});
       else if (p.act == ACT_GELU_TANH) epilogue_act(t, std::integral_constant<int, ACT_GELU_TANH>{});
+      else if (p.act == ACT_RELU) epilogue_act(t, std::integral_constant<int, ACT_RELU>{});
+      else if (p.act == ACT_SILU) epilogue_act(t, std::integral_constant<int, ACT_SILU>{});
       else epilogue_act(t, std::integral_constant<int, ACT_NONE>{});
     } else {
       epilogue_act(t, std::integral_constant<int, ACT_NONE>{});
@@ -567,7 +575,7 @@ gemm_bf16_kernel(GemmParams p) {
   wait_vm<0>();   // the stages issued past the end (loads of nothing) land before LDS is released
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED>
+template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED, int GACT>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -578,7 +586,7 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   if (tiles > 0x7fffffff || p.cus <= 0) return hipErrorInvalidValue;
   // persistent: as many blocks as fit on the chip at once, each looping over
   // its tiles
-  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED>;
+  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT>;
   static const int per_cu = [&] {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, WM * WN * 64, 0) != hipSuccess) o = 1;
@@ -589,14 +597,25 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int OUT, bool GATHER, bool GROUPED>
+template <int OUT, bool GATHER, bool GROUPED, int GACT = ACT_NONE>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
+  if constexpr (OUT == GEMM_OUT_GEGLU && GACT == ACT_NONE) {
+    // one kernel per gate activation
+    switch (p.act) {
+      case ACT_GELU_TANH: return launch_tile<OUT, GATHER, GROUPED, ACT_GELU_TANH>(tile, p, s);
+      case ACT_GELU_ERF: return launch_tile<OUT, GATHER, GROUPED, ACT_GELU_ERF>(tile, p, s);
+      case ACT_RELU: return launch_tile<OUT, GATHER, GROUPED, ACT_RELU>(tile, p, s);
+      case ACT_SILU: return launch_tile<OUT, GATHER, GROUPED, ACT_SILU>(tile, p, s);
+      case ACT_NONE: break;
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (tile) {
-    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED>(p, s);
+    case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED, GACT>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED, GACT>(p, s);
     case TILE_128x192:
       if constexpr (OUT == GEMM_OUT_BF16 && !GATHER && !GROUPED)
-        return launch_cfg<128, 192, 4, 2, 64, 3, OUT, GATHER, GROUPED>(p, s);
+        return launch_cfg<128, 192, 4, 2, 64, 3, OUT, GATHER, GROUPED, GACT>(p, s);
       else
         return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;

@@ -12,7 +12,7 @@ namespace fmlp {
 // ---------------------------------------------------------------------------
 enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 = act(acc + bias)
-  GEMM_OUT_GEGLU = 1,       // B0 = Wg, B1 = Wu; C bf16 [rows, N] = gelu_tanh(g) * u
+  GEMM_OUT_GEGLU = 1,       // B0 = Wg, B1 = Wu; C bf16 [rows, N] = act(g) * u
   GEMM_OUT_F32_SCALED = 2,  // C fp32 = acc * row_scale[row]
 };
 
@@ -26,7 +26,7 @@ struct GemmParams {
   void* C;                 // output, row stride ldc (elements)
   int64_t ldc;
   int64_t M, N, K;         // M: rows (dense mode)
-  int act;                 // Act, GEMM_OUT_BF16 only
+  int act;                 // Act: of the output (GEMM_OUT_BF16) or of the gate (GEMM_OUT_GEGLU)
   // gather / grouped (mixture of experts)
   const int32_t* a_rows;     // gather: A row of each logical row, or nullptr
   int64_t a_src_rows;        // gather: rows of A (a_src_rows * lda * 2 < 2^31)
@@ -66,8 +66,8 @@ struct GemvLayer {
   const uint16_t* bias;  // [N] or nullptr
   uint16_t* y;           // [M, N]
   int64_t K, N;
-  int act;               // Act; ignored for GeGLU layers
-  int geglu;             // 1: y = gelu_tanh(x W0^T) * (x W1^T)
+  int act;               // Act; for a gated layer, the gate's activation
+  int geglu;             // 1: y = act(x W0^T) * (x W1^T)
 };
 
 // One layer, one launch.

@@ -55,7 +55,10 @@ typedef void* fmlp_stream;   /* a hipStream_t */
 typedef enum {
   FMLP_ACT_NONE = 0,
   FMLP_ACT_GELU_ERF = 1,   /* exact GELU  z*Phi(z) */
-  FMLP_ACT_GELU_TANH = 2   /* z/2 * (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+  FMLP_ACT_GELU_TANH = 2,  /* z/2 * (1 + tanh(sqrt(2/pi) (z + 0.044715 z^3))) */
+  FMLP_ACT_RELU = 3,       /* max(z, 0): the two-layer MLP of ainews.cool "PyTorch fused
+                              MLP efficiency", section "technical deep dive" */
+  FMLP_ACT_SILU = 4        /* z * sigmoid(z) (swish); as a gate: SwiGLU */
 } fmlp_act;
 
 typedef enum {
@@ -118,6 +121,24 @@ fmlp_status fmlp_geglu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16*
 size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H);
 
 /*
+ * y[M,D] = (gate_act(x[M,D] . Wg[H,D]^T) * (x . Wu[H,D]^T)) . Wd[D,H]^T
+ *
+ * The gated feed-forward block with the gate's activation as an argument:
+ * gate_act = FMLP_ACT_GELU_TANH is fmlp_geglu; FMLP_ACT_SILU gives SwiGLU,
+ * FMLP_ACT_RELU ReGLU, FMLP_ACT_GELU_ERF GeGLU with the exact GELU and
+ * FMLP_ACT_NONE the bilinear form.  The three-Linear MLP blocks of the models
+ * ainews.cool "PyTorch fused MLP efficiency" names (section "technical deep
+ * dive": LLaMA-3; section "architectural impact": Mixtral experts) have this
+ * shape; the page does not name their gate activation.  Same kernels, paths,
+ * workspace (fmlp_glu_workspace_size == fmlp_geglu_workspace_size) and errors
+ * as fmlp_geglu; a gate_act that is not an fmlp_act is FMLP_E_ARG.
+ */
+fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
+                     const fmlp_bf16* Wd, int gate_act, int64_t M, int64_t D, int64_t H,
+                     fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
+
+/*
  * y[t,:] = sum_{j<top_k} gate_w[t,j] * geglu_{expert_ids[t,j]}(x[t,:])
  *
  * Mixture of GeGLU experts (ainews.cool "PyTorch fused MLP efficiency",
@@ -138,6 +159,16 @@ fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const 
                            int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k,
                            fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
 size_t fmlp_moe_workspace_size(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k);
+
+/*
+ * fmlp_moe_geglu with the experts' gate activation as an argument (as
+ * fmlp_glu; FMLP_ACT_SILU gives SwiGLU experts).  fmlp_moe_geglu is this call
+ * with FMLP_ACT_GELU_TANH.  Same workspace and errors.
+ */
+fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
+                         const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int gate_act,
+                         int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k,
+                         fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
 /* Byte offset, inside the MoE workspace, of the int32 count of invalid expert ids
  * seen by the last call (read it after a stream sync). */
 size_t fmlp_moe_error_offset(void);

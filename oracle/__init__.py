@@ -10,7 +10,11 @@ from .fmlp_oracle import (  # noqa: F401
     geglu,
     gelu_erf,
     gelu_tanh,
+    glu,
     linear,
     mlp2,
     moe_geglu,
+    moe_glu,
+    relu,
+    silu,
 )

@@ -22,6 +22,10 @@ Readings taken where the pages are silent (each is listed in the design doc):
     definition; the GPU's bf16 rounding of h/m is absorbed by the tolerance.
   * MoE: y[t] = sum_j gate_w[t, j] * geglu_{expert_ids[t, j]}(x[t]); duplicate
     expert ids within a token simply add.
+  * ReLU is max(z, 0) (ainews.cool "technical deep dive" names ReLU for the
+    two-layer MLP).  SiLU, z * sigmoid(z), is the gate activation of SwiGLU;
+    the pages name three-Linear MLP blocks (LLaMA-3, Mixtral experts) without
+    naming their gate activation, so the gated block takes it as an argument.
 
 Pins: tests/test_oracle_pins.py checks every function here against brute-force
 loops, library routines, closed forms, a printed worked example and invariants.
@@ -30,19 +34,24 @@ from __future__ import annotations
 
 import numpy as np
 from scipy.special import erfc as _erfc
+from scipy.special import expit as _expit
 
 __all__ = [
     "ACTS",
     "gelu_erf",
     "gelu_tanh",
+    "relu",
+    "silu",
     "activation",
     "linear",
     "mlp2",
     "geglu",
+    "glu",
     "moe_geglu",
+    "moe_glu",
 ]
 
-ACTS = ("none", "gelu_erf", "gelu_tanh")
+ACTS = ("none", "gelu_erf", "gelu_tanh", "relu", "silu")
 
 _SQRT_HALF = np.sqrt(0.5)
 _SQRT_2_OVER_PI = np.sqrt(2.0 / np.pi)
@@ -77,8 +86,24 @@ def gelu_tanh(z):
     return 0.5 * z * (1.0 + np.tanh(inner))
 
 
+def relu(z):
+    """ReLU, max(z, 0): the activation of the two-layer MLP in ainews.cool
+    "PyTorch fused MLP efficiency", section "technical deep dive"."""
+    z = _f64(z)
+    return np.where(z > 0.0, z, 0.0)
+
+
+def silu(z):
+    """SiLU (swish), z * sigmoid(z), with sigmoid from scipy's expit (stable in
+    both tails).  The gate activation of SwiGLU blocks; see the module notes
+    for why it is offered."""
+    z = _f64(z)
+    return z * _expit(z)
+
+
 def activation(z, act: str):
-    """The epilogue activation selected by name: none, gelu_erf or gelu_tanh.
+    """The epilogue activation selected by name: none, gelu_erf, gelu_tanh,
+    relu or silu.
 
     "Profiling in PyTorch (Part 2)", section "Why are there no separate mul and
     add kernels?": applying an activation is a classic GEMM epilogue.
@@ -89,6 +114,10 @@ def activation(z, act: str):
         return gelu_erf(z)
     if act == "gelu_tanh":
         return gelu_tanh(z)
+    if act == "relu":
+        return relu(z)
+    if act == "silu":
+        return silu(z)
     raise ValueError(f"unknown activation {act!r}; expected one of {ACTS}")
 
 
@@ -137,6 +166,36 @@ def geglu(x, Wg, Wu, Wd):
     u = linear(x, Wu)
     m = gelu_tanh(g) * u
     return linear(m, Wd)
+
+
+def glu(x, Wg, Wu, Wd, gate_act: str):
+    """Gated feed-forward block with a named gate activation:
+    y = (gate_act(x Wg^T) * (x Wu^T)) Wd^T, no biases.
+
+    The GeGLU block above with its gelu replaced by gate_act ("silu": SwiGLU,
+    "relu": ReGLU, "none": bilinear).  x [M,D], Wg/Wu [H,D], Wd [D,H].
+    """
+    g = linear(x, Wg)
+    u = linear(x, Wu)
+    m = activation(g, gate_act) * u
+    return linear(m, Wd)
+
+
+def moe_glu(x, expert_ids, gate_w, expert_weights, gate_act: str):
+    """moe_geglu with each expert the gated block glu(..., gate_act)."""
+    x = _f64(x)
+    ids = np.asarray(expert_ids)
+    w = _f64(gate_w)
+    if ids.shape != w.shape or ids.ndim != 2 or ids.shape[0] != x.shape[0]:
+        raise ValueError(f"routes shape mismatch: ids{ids.shape} w{w.shape} x{x.shape}")
+    get = expert_weights if callable(expert_weights) else (lambda e: expert_weights[e])
+    y = np.zeros_like(x)
+    for e in np.unique(ids):
+        tok, slot = np.nonzero(ids == e)
+        Wg, Wu, Wd = get(int(e))
+        ye = glu(x[tok], Wg, Wu, Wd, gate_act)
+        np.add.at(y, tok, w[tok, slot][:, None] * ye)
+    return y
 
 
 def moe_geglu(x, expert_ids, gate_w, expert_weights):

@@ -40,6 +40,10 @@ def _bf_act(z: float, act: str) -> float:
     if act == "gelu_tanh":
         c = math.sqrt(2.0 / math.pi)
         return 0.5 * z * (1.0 + math.tanh(c * (z + 0.044715 * z ** 3)))
+    if act == "relu":
+        return z if z > 0.0 else 0.0
+    if act == "silu":
+        return z / (1.0 + math.exp(-z)) if z > -700.0 else 0.0
     raise ValueError(act)
 
 
@@ -58,20 +62,20 @@ def bf_linear(x, W, b, act):
     return y
 
 
-def bf_geglu(x, Wg, Wu, Wd):
+def bf_geglu(x, Wg, Wu, Wd, gate_act="gelu_tanh"):
     g = bf_linear(x, Wg, None, "none")
     u = bf_linear(x, Wu, None, "none")
-    m = [[_bf_act(g[i][j], "gelu_tanh") * u[i][j] for j in range(len(g[0]))] for i in range(len(g))]
+    m = [[_bf_act(g[i][j], gate_act) * u[i][j] for j in range(len(g[0]))] for i in range(len(g))]
     return bf_linear(m, Wd, None, "none")
 
 
-def bf_moe(x, ids, gw, experts):
+def bf_moe(x, ids, gw, experts, gate_act="gelu_tanh"):
     T, D = len(x), len(x[0])
     y = [[0.0] * D for _ in range(T)]
     for t in range(T):
         for j in range(len(ids[t])):
             Wg, Wu, Wd = experts[int(ids[t][j])]
-            yt = bf_geglu([x[t]], Wg, Wu, Wd)[0]
+            yt = bf_geglu([x[t]], Wg, Wu, Wd, gate_act)[0]
             for d in range(D):
                 y[t][d] += float(gw[t][j]) * yt[d]
     return y
@@ -102,7 +106,7 @@ def check_linear_bruteforce(o):
         x = _bf16ish(rng, (M, K))
         W = _bf16ish(rng, (N, K), 0.5)
         b = _bf16ish(rng, (N,), 0.5)
-        for act in ("none", "gelu_erf", "gelu_tanh"):
+        for act in ("none", "gelu_erf", "gelu_tanh", "relu", "silu"):
             for bias in (None, b):
                 ref = bf_linear(x.tolist(), W.tolist(), None if bias is None else bias.tolist(), act)
                 _close(o.linear(x, W, bias, act), ref, what=f"linear {M}x{K}x{N} {act} bias={bias is not None}")
@@ -116,7 +120,7 @@ def check_mlp2_bruteforce(o):
         b1 = _bf16ish(rng, (H,), 0.5)
         W2 = _bf16ish(rng, (N, H), 0.5)
         b2 = _bf16ish(rng, (N,), 0.5)
-        for act in ("gelu_erf", "gelu_tanh", "none"):
+        for act in ("gelu_erf", "gelu_tanh", "none", "relu", "silu"):
             h = bf_linear(x.tolist(), W1.tolist(), b1.tolist(), act)
             ref = bf_linear(h, W2.tolist(), b2.tolist(), "none")
             _close(o.mlp2(x, W1, b1, W2, b2, act), ref, what=f"mlp2 {act}")
@@ -131,6 +135,9 @@ def check_geglu_bruteforce(o):
         Wd = _bf16ish(rng, (D, H), 0.7)
         ref = bf_geglu(x.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist())
         _close(o.geglu(x, Wg, Wu, Wd), ref, what=f"geglu {M}x{D}x{H}")
+        for act in ("gelu_tanh", "gelu_erf", "silu", "relu", "none"):
+            ref = bf_geglu(x.tolist(), Wg.tolist(), Wu.tolist(), Wd.tolist(), act)
+            _close(o.glu(x, Wg, Wu, Wd, act), ref, what=f"glu {act} {M}x{D}x{H}")
 
 
 def check_moe_bruteforce(o):
@@ -144,6 +151,9 @@ def check_moe_bruteforce(o):
     ref = bf_moe(x.tolist(), ids.tolist(), gw.tolist(),
                  [(a.tolist(), b.tolist(), c.tolist()) for a, b, c in experts])
     _close(o.moe_geglu(x, ids, gw, experts), ref, what="moe brute force")
+    ref = bf_moe(x.tolist(), ids.tolist(), gw.tolist(),
+                 [(a.tolist(), b.tolist(), c.tolist()) for a, b, c in experts], "silu")
+    _close(o.moe_glu(x, ids, gw, experts, "silu"), ref, what="moe silu brute force")
 
 
 def check_gelu_library(o):
@@ -188,6 +198,65 @@ def check_gelu_closed_forms(o):
     diff = np.abs(o.gelu_erf(x) - o.gelu_tanh(x))
     assert 4.70e-4 < diff.max() < 4.76e-4, diff.max()
     assert 2.6 < abs(x[diff.argmax()]) < 2.8
+
+
+def check_silu_relu_closed_forms(o):
+    """SiLU and ReLU against closed forms, identities and torch's F.silu/F.relu."""
+    import torch
+    import torch.nn.functional as F
+
+    # sigmoid(1) = 1 / (1 + 1/e)
+    assert abs(float(o.silu(1.0)) - 0.7310585786300049) < 1e-15
+    assert abs(float(o.silu(-1.0)) + 0.2689414213699951) < 1e-15
+    for a in (o.silu, o.relu):
+        assert float(a(0.0)) == 0.0
+        assert float(a(40.0)) == 40.0                 # -> x for x >> 0
+        assert -1e-15 <= float(a(-40.0)) <= 0.0       # -> 0- for x << 0
+        # odd-part identity a(x) - a(-x) = x (sigmoid(x) + sigmoid(-x) = 1; max(x,0) - max(-x,0) = x)
+        x = np.linspace(-6, 6, 1201)
+        _close(a(x) - a(-x), x, rtol=1e-14, atol=1e-14, what="odd-part identity")
+    # SiLU: derivative 1/2 at 0; its minimum x* solves x sigmoid(x) = 1 + x, so
+    # the minimum value is x* + 1 (x* = -1.278464542761074)
+    h = 1e-6
+    assert abs((float(o.silu(h)) - float(o.silu(-h))) / (2 * h) - 0.5) < 1e-9
+    xs = -1.278464542761074
+    assert abs(float(o.silu(xs)) - (xs + 1.0)) < 1e-14
+    x = np.linspace(-3, 0, 300001)
+    assert abs(x[np.argmin(o.silu(x))] - xs) < 2e-5
+    # ReLU is exactly max(x, 0)
+    x = np.linspace(-5, 5, 1001)
+    assert np.array_equal(o.relu(x), np.maximum(x, 0.0))
+    # library routines
+    z = np.concatenate([np.linspace(-30, 30, 6001), [-1e-3, 1e-3, 0.0]])
+    t = torch.from_numpy(z)
+    _close(o.silu(z), F.silu(t).numpy(), rtol=1e-14, atol=1e-15, what="silu vs F.silu")
+    _close(o.relu(z), F.relu(t).numpy(), rtol=0, atol=0, what="relu vs F.relu")
+    _close(o.activation(z, "silu"), F.silu(t).numpy(), rtol=1e-14, atol=1e-15, what="act silu")
+    _close(o.activation(z, "relu"), F.relu(t).numpy(), rtol=0, atol=0, what="act relu")
+
+
+def check_glu_special_cases(o):
+    """The gated block with each gate activation: identity weights give
+    act(x) * x; the up projection is linear; gate and up are not symmetric;
+    gelu_tanh reproduces the GeGLU block; the MoE form reduces to one expert."""
+    rng = np.random.default_rng(31)
+    x = _bf16ish(rng, (5, 6))
+    I = np.eye(6)
+    Wg, Wu, Wd = _bf16ish(rng, (9, 6)), _bf16ish(rng, (9, 6)), _bf16ish(rng, (6, 9))
+    for act in ("silu", "relu", "gelu_erf", "gelu_tanh", "none"):
+        ref = np.vectorize(lambda v: _bf_act(v, act) * v)(x)
+        _close(o.glu(x, I, I, I, act), ref, what=f"glu identity {act}")
+        a = o.glu(x, Wg, Wu, Wd, act)
+        _close(o.glu(x, Wg, 2 * Wu, Wd, act), 2 * a, what=f"glu linear in up {act}")
+        if act != "none":
+            assert np.max(np.abs(a - o.glu(x, Wu, Wg, Wd, act))) > 1e-3, act
+    _close(o.glu(x, Wg, Wu, Wd, "gelu_tanh"), o.geglu(x, Wg, Wu, Wd), what="glu tanh == geglu")
+    experts = [(_bf16ish(rng, (7, 6), 0.6), _bf16ish(rng, (7, 6), 0.6), _bf16ish(rng, (6, 7), 0.6))
+               for _ in range(3)]
+    for e in range(3):
+        ids = np.full((5, 1), e, dtype=np.int32)
+        _close(o.moe_glu(x, ids, np.ones((5, 1)), experts, "silu"), o.glu(x, *experts[e], "silu"),
+               what=f"moe_glu top1 expert {e}")
 
 
 def check_transpose_worked_example(o):
@@ -321,10 +390,12 @@ ALL_CHECKS = [
     check_moe_bruteforce,
     check_gelu_library,
     check_gelu_closed_forms,
+    check_silu_relu_closed_forms,
     check_transpose_worked_example,
     check_linear_special_cases,
     check_mlp2_bias_pins,
     check_geglu_special_cases,
+    check_glu_special_cases,
     check_fused_equals_unfused,
     check_moe_invariants,
 ]

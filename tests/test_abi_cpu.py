@@ -119,6 +119,27 @@ def test_geglu_validation(L):
     assert L.fmlp_geglu(X, W, W, W, 0, 64, 128, Y, WS, 1 << 20, None) == OK
 
 
+def test_glu_validation(L):
+    assert L.fmlp_glu_workspace_size(300, 512, 1024) == L.fmlp_geglu_workspace_size(300, 512, 1024)
+    for act in (0, 1, 2, 3, 4):   # every fmlp_act is a valid gate activation; M == 0 is a no-op
+        assert L.fmlp_glu(X, W, W, W, act, 0, 64, 128, Y, WS, 1 << 20, None) == OK
+    for act in (-1, 5):
+        assert L.fmlp_glu(X, W, W, W, act, 16, 64, 128, Y, WS, 1 << 20, None) == E_ARG
+        assert "gate_act" in _err(L)
+    assert L.fmlp_glu(X, W, W, W, 4, 16, 64, 128, Y, None, 0, None) == E_WS
+    ids, gw = 0x60000, 0x70000
+    need = L.fmlp_moe_workspace_size(64, 64, 128, 4, 2)
+    assert L.fmlp_moe_glu(X, ids, gw, W, W, W, 5, 64, 64, 128, 4, 2, Y, WS, need, None) == E_ARG
+    assert L.fmlp_moe_glu(X, ids, gw, W, W, W, 4, 0, 64, 128, 4, 2, Y, WS, need, None) == OK
+
+
+def test_new_acts_accepted(L):
+    for act in (3, 4):   # relu, silu
+        assert L.fmlp_linear(X, W, None, act, 0, 32, 8, Y, None) == OK
+        assert L.fmlp_mlp2(X, W, B, W, B, act, 0, 32, 64, 32, Y, WS, 1 << 20, None) == OK
+    assert L.fmlp_linear(X, W, None, 5, 4, 32, 8, Y, None) == E_ARG
+
+
 def test_moe_validation(L):
     T, D, H, E, k = 4096, 4096, 14336, 8, 2
     P = T * k

@@ -14,6 +14,7 @@ _orig_activation = fo.activation
 _orig_gelu_erf = fo.gelu_erf
 _orig_gelu_tanh = fo.gelu_tanh
 _orig_moe = fo.moe_geglu
+_orig_glu = fo.glu
 
 
 def _linear_no_bias(x, W, b=None, act="none"):
@@ -74,6 +75,29 @@ def _geglu_wrong_act(x, Wg, Wu, Wd):
     return _orig_linear(fo.gelu_erf(_orig_linear(x, Wg)) * _orig_linear(x, Wu), Wd)
 
 
+def _silu_is_sigmoid(z):
+    z = np.asarray(z, float)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _silu_double_slope(z):
+    z = np.asarray(z, float)
+    return z / (1.0 + np.exp(-2.0 * z))
+
+
+def _relu_leaky(z):
+    z = np.asarray(z, float)
+    return np.where(z > 0, z, 0.01 * z)
+
+
+def _glu_ignores_gate_act(x, Wg, Wu, Wd, gate_act):
+    return _orig_glu(x, Wg, Wu, Wd, "gelu_tanh")
+
+
+def _glu_gate_up_swapped(x, Wg, Wu, Wd, gate_act):
+    return _orig_glu(x, Wu, Wg, Wd, gate_act)
+
+
 def _mlp2_act_twice(x, W1, b1, W2, b2, act):
     return _orig_linear(_orig_linear(x, W1, b1, act), W2, b2, act)
 
@@ -123,6 +147,11 @@ MUTANTS = {
     "moe_ignores_gate_w": ("moe_geglu", _moe_unweighted),
     "moe_first_slot_only": ("moe_geglu", _moe_first_slot),
     "moe_overwrites_duplicates": ("moe_geglu", _moe_dedup),
+    "silu_is_sigmoid": ("silu", _silu_is_sigmoid),
+    "silu_double_slope": ("silu", _silu_double_slope),
+    "relu_leaky": ("relu", _relu_leaky),
+    "glu_ignores_gate_act": ("glu", _glu_ignores_gate_act),
+    "glu_gate_up_swapped": ("glu", _glu_gate_up_swapped),
 }
 
 
