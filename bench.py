@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["common.h", "kernels.h", "lds_dma.h", "decode.hip"],
     "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
     "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
+    "moe_router_lds_kernel": ["common.h", "kernels.h", "moe.hip"],
 }
 
 
@@ -158,6 +159,30 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None):
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
         return Case(w, calls, kernel, launches, p, R, fn, sample)
 
+    if w.op == "route":
+        # x streams once per step; x copies rotate (>= 1 GiB) so it is read from HBM
+        x_bits = datagen.make_inputs(datagen.workload("moe"), seed=0, with_weights=False)["x"]
+        Wr_bits = datagen.router_weights(w, seed=0)
+        xb = _dev(x_bits, torch, dev)
+        Wr = _dev(Wr_bits, torch, dev)
+        R = _copies_for(2 * w.M * w.K, cold)
+        xs_d = [xb] + [xb.clone() for _ in range(R - 1)]
+        ids_o = torch.empty(w.M, w.top_k, dtype=torch.int32, device=dev)
+        gw_o = torch.empty(w.M, w.top_k, dtype=torch.float32, device=dev)
+        calls = [F.bind_moe_route(xx, Wr, w.top_k, out=(ids_o, gw_o)) for xx in xs_d]
+        import oracle
+
+        toks = 1024
+        cache = {}
+
+        def fn():
+            if not cache:
+                cache["x"] = f64(x_bits[:toks])
+                cache["Wr"] = f64(Wr_bits)
+            return oracle.moe_router(cache["x"], cache["Wr"], w.top_k)
+        return Case(w, calls, "moe_router_lds_kernel", 1, "router: logits, top-k, softmax (1 launch)", R, fn,
+                    (f"{toks} of {w.M} tokens", toks / w.M))
+
     # mixture of experts
     x_bits = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
     ids, gw = datagen.make_routes(w.M, w.E, w.top_k, seed=0)
@@ -257,7 +282,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode1",
-                    choices=["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe"])
+                    choices=["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe",
+                             "router"])
     ap.add_argument("--act", default=None, choices=["none", "gelu_erf", "gelu_tanh", "relu", "silu"],
                     help="activation of a two-layer MLP, or gate activation of a gated block")
     ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
@@ -287,7 +313,7 @@ def main(argv=None):
     case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path, act=args.act)
     w = case.w
     est_us = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
-              "large16": 250, "large4096": 4000, "moe": 2500}[args.workload]
+              "large16": 250, "large4096": 4000, "moe": 2500, "router": 8}[args.workload]
     K = args.steps if args.steps is not None else max(20, int(1.5e6 / est_us))
     W = args.warmup if args.warmup is not None else max(5, K // 10)
     R = len(case.calls)
@@ -368,10 +394,14 @@ def main(argv=None):
             "workload": w.name,
             "op": w.op,
             "tokens": w.M,
-            "dims": {"in": w.K, "hidden": w.H, "out": w.N, **({"experts": w.E, "top_k": w.top_k} if w.op == "moe" else {})},
-            "act": w.act if w.op == "mlp2" else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)"),
+            "dims": {"in": w.K, "hidden": w.H, "out": w.N,
+                     **({"experts": w.E, "top_k": w.top_k} if w.op in ("moe", "route") else {})},
+            "act": (w.act if w.op == "mlp2" else "top-k + softmax" if w.op == "route"
+                    else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)")),
             "bias": w.bias,
-            "weights": (f"cold: {case.copies} rotated copies ({case.copies * w.weight_bytes / 2**20:.0f} MiB)"
+            "weights": (f"cold: {case.copies} rotated copies of x ({case.copies * 2 * w.M * w.K / 2**20:.0f} MiB)"
+                        if case.copies > 1 and w.op == "route" else
+                        f"cold: {case.copies} rotated copies ({case.copies * w.weight_bytes / 2**20:.0f} MiB)"
                         if case.copies > 1 else "single copy"),
             "path": case.path,
             "parallelism": "single GPU",

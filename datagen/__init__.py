@@ -42,6 +42,7 @@ __all__ = [
     "make_inputs",
     "make_routes",
     "expert_weights",
+    "router_weights",
 ]
 
 
@@ -94,8 +95,9 @@ class Workload:
     """One feed-forward workload.  All tensors row-major; weights [out, in].
 
     op: "mlp2" (x[M,K] -> W1[H,K],b1 -> act -> W2[N,H],b2),
-        "geglu" (x[M,D]; Wg,Wu[H,D]; Wd[D,H]), or
-        "moe" (x[T,D]; E experts of geglu; top_k routes per token).
+        "geglu" (x[M,D]; Wg,Wu[H,D]; Wd[D,H]),
+        "moe" (x[T,D]; E experts of geglu; top_k routes per token), or
+        "route" (x[T,D]; router Wr[E,D] -> top_k ids and gate weights).
     """
 
     name: str
@@ -125,6 +127,8 @@ class Workload:
             return 2 * self.M * 3 * self.K * self.H
         if self.op == "moe":
             return 2 * self.M * self.top_k * 3 * self.K * self.H
+        if self.op == "route":
+            return 2 * self.M * self.K * self.E
         raise ValueError(self.op)
 
     @property
@@ -138,13 +142,15 @@ class Workload:
             return 2 * 3 * self.K * self.H
         if self.op == "moe":
             return self.E * 2 * 3 * self.K * self.H
+        if self.op == "route":
+            return 2 * self.E * self.K
         raise ValueError(self.op)
 
     @property
     def bytes(self) -> int:
         """Algorithmic HBM bytes: weights (+biases) + x + y (+ routes), each once."""
         b = self.weight_bytes + 2 * self.M * self.K + 2 * self.M * self.N
-        if self.op == "moe":
+        if self.op in ("moe", "route"):
             b += self.M * self.top_k * (4 + 4)  # int32 ids + fp32 gate weights
         return b
 
@@ -184,6 +190,13 @@ def _moe(T: int = 4096) -> Workload:
         family="moe")
 
 
+def _router(T: int = 4096) -> Workload:
+    """The router of the 8-expert MoE layer: x [T, 4096], Wr [8, 4096], top-2."""
+    return Workload(
+        name=f"moe_router_8x4096_T{T}_top2", op="route", M=T, K=4096, H=0, N=0,
+        w1_bound=1 / math.sqrt(4096), E=8, top_k=2, family="moe")
+
+
 WORKLOADS = {
     "tiny": _tiny(),
     "decode1": _decode(1),
@@ -193,6 +206,7 @@ WORKLOADS = {
     "large16": _large(16),
     "large4096": _large(4096),
     "moe": _moe(),
+    "router": _router(),
 }
 
 
@@ -242,6 +256,11 @@ def make_routes(T: int, E: int, top_k: int, seed: int = 0, family: str = "moe"):
     z = np.exp(z - z.max(axis=1, keepdims=True))
     gate = (z / z.sum(axis=1, keepdims=True)).astype(np.float32)
     return np.ascontiguousarray(ids), np.ascontiguousarray(gate)
+
+
+def router_weights(w: Workload, seed: int = 0):
+    """bf16 bits of the router weight Wr [E, D] ~ U(+-1/sqrt(D)) of a MoE family."""
+    return uniform_bf16(rng_for(seed, w.family, "Wr"), (w.E, w.K), 1 / math.sqrt(w.K))
 
 
 def expert_weights(w: Workload, e: int, seed: int = 0):

@@ -15,6 +15,8 @@ raises.
     fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd)
                                                     y[t] = sum_j w[t,j] geglu_{e[t,j]}(x[t])
     fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act)
+    fmlp_moe_route(x, Wr, top_k)                    -> (expert_ids, gate_w[, logits]): top_k of x Wr^T,
+                                                       softmax over the chosen logits
 
 Activations: "none", "gelu_erf", "gelu_tanh", "relu", "silu".
 """
@@ -38,6 +40,8 @@ __all__ = [
     "fmlp_glu",
     "fmlp_moe_geglu",
     "fmlp_moe_glu",
+    "fmlp_moe_route",
+    "bind_moe_route",
     "fmlp_mlp2_workspace_size",
     "fmlp_geglu_workspace_size",
     "fmlp_moe_workspace_size",
@@ -102,8 +106,9 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_int32, _p, _p, _sz, _p]
         L.fmlp_moe_glu.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int32,
                                    ctypes.c_int32, _p, _p, _sz, _p]
+        L.fmlp_moe_route.argtypes = [_p, _p, _i64, _i64, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p]
         for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
-                  "fmlp_set_path"):
+                  "fmlp_moe_route", "fmlp_set_path"):
             getattr(L, f).restype = ctypes.c_int
         L.fmlp_set_path.argtypes = [ctypes.c_int]
         L.fmlp_mlp2_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
@@ -368,6 +373,41 @@ def bind_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act: str = "silu", out=
                  workspace=None) -> BoundCall:
     with torch.cuda.device(x.device):
         return _moe_call(x, expert_ids, gate_w, Wg, Wu, Wd, out, workspace, gate_act)
+
+
+def _route_call(x, Wr, top_k, with_logits, out):
+    _dev_tensor("x", x)
+    _dev_tensor("Wr", Wr)
+    T, D = x.shape
+    E = Wr.shape[0]
+    if Wr.shape != (E, D):
+        raise ValueError(f"Wr must be [E, {D}], got {tuple(Wr.shape)}")
+    if out is not None:
+        ids, gw = out[0], out[1]
+        lg = out[2] if with_logits else None
+    else:
+        ids = torch.empty(T, top_k, dtype=torch.int32, device=x.device)
+        gw = torch.empty(T, top_k, dtype=torch.float32, device=x.device)
+        lg = torch.empty(T, E, dtype=torch.float32, device=x.device) if with_logits else None
+    _dev_tensor("expert_ids", ids, torch.int32)
+    _dev_tensor("gate_w", gw, torch.float32)
+    if lg is not None:
+        _dev_tensor("logits", lg, torch.float32)
+    res = (ids, gw, lg) if with_logits else (ids, gw)
+    return BoundCall(lib().fmlp_moe_route, (_ptr(x), _ptr(Wr), T, D, E, top_k, _ptr(ids), _ptr(gw), _ptr(lg),
+                                           _stream(x.device)), res, (x, Wr, ids, gw, lg))
+
+
+def fmlp_moe_route(x, Wr, top_k: int, with_logits: bool = False, out=None):
+    """Routes on the device: x [T, D], Wr [E, D] -> expert_ids int32 [T, top_k],
+    gate_w fp32 [T, top_k] (and logits fp32 [T, E] with with_logits)."""
+    with torch.cuda.device(x.device):
+        return _route_call(x, Wr, top_k, with_logits, out)()
+
+
+def bind_moe_route(x, Wr, top_k: int, with_logits: bool = False, out=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _route_call(x, Wr, top_k, with_logits, out)
 
 
 # ---------------------------------------------------------------------------

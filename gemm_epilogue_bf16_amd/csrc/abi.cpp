@@ -448,4 +448,26 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
   return launched(launch_moe_combine(ytilde, r.pos_of, T, top_k, D, y, s), "moe combine launch");
 }
 
+fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, int64_t D, int32_t E,
+                           int32_t top_k, int32_t* expert_ids, float* gate_w, float* logits,
+                           fmlp_stream stream) {
+  TRY(check_rows("T", T));
+  TRY(check_inner("D", D));
+  if (E < 1 || E > kRouterMaxExperts) return fail(FMLP_E_ARG, "E=%d must be in [1, %d]", E, kRouterMaxExperts);
+  if (top_k < 1 || top_k > 8 || top_k > E)
+    return fail(FMLP_E_ARG, "top_k=%d must be in [1, min(8, E=%d)]", top_k, E);
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(Wr);
+  if (expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
+  if (gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
+  if ((reinterpret_cast<uintptr_t>(expert_ids) | reinterpret_cast<uintptr_t>(gate_w) |
+       reinterpret_cast<uintptr_t>(logits)) & 3u)
+    return fail(FMLP_E_ALIGN, "expert_ids, gate_w and logits must be 4-byte aligned");
+  if (T == 0) return ok();
+  TRY(check_device());
+  return launched(launch_moe_router(x, Wr, T, (int)D, E, top_k, expert_ids, gate_w, logits,
+                                    static_cast<hipStream_t>(stream)),
+                  "moe router launch");
+}
+
 }  // extern "C"

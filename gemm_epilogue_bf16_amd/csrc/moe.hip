@@ -15,6 +15,13 @@
 //   combine: y[t] = sum_j ytilde[pos(t, j)] in slot order j = 0, 1, ... in fp32
 //            (the gate weight was applied in the down-projection epilogue), then
 //            one bf16 rounding.  No atomics: bitwise deterministic.
+//   router:  the routes computed on the device: logits = x . Wr^T (fp32), the
+//            top_k experts by logit (a tie goes to the lower expert id), and
+//            gate weights = softmax over the chosen logits.  Bound by reading x
+//            once.  When the router weights fit (E * D * 2 <= 64 KB) a block
+//            first copies them into LDS, so HBM and L2 see them once per block;
+//            each wave takes two tokens and keeps four chunk steps of x in
+//            flight.  Otherwise they are read through the caches.
 #include "common.h"
 #include "kernels.h"
 
@@ -173,6 +180,224 @@ moe_combine_kernel(const float* __restrict__ ytilde, const int32_t* __restrict__
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// router
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kRouterThreads = 256;   // 4 waves, each its own tokens
+
+// acc + the dot product of two runs of 8 bf16 (exact fp32 products, fused
+// multiply-adds in a fixed order)
+__device__ __forceinline__ float dot8_bf16(const u32x4_t& a, const u32x4_t& b, float acc) {
+  float av[8], bv[8];
+  unpack_bf16x8(a, av);
+  unpack_bf16x8(b, bv);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc = fmaf(av[q], bv[q], acc);
+  return acc;
+}
+
+// top_k of one token's logits by selection (the largest remaining logit, the
+// lower id on a tie), then softmax over the chosen ones (sel[0] is their max).
+template <int EC>
+__device__ __forceinline__ void router_select(const float (&lg)[EC], int E, int top_k, int32_t* ids,
+                                              float* gate_w) {
+  uint64_t taken = 0;
+  float sel[8];
+  int id[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k >= top_k) break;
+    float best = 0.f;
+    int bi = -1;
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      if (e < E && !((taken >> e) & 1ull) && (bi < 0 || lg[e] > best)) {
+        best = lg[e];
+        bi = e;
+      }
+    }
+    taken |= 1ull << bi;
+    sel[k] = best;
+    id[k] = bi;
+  }
+  float sum = 0.f, ex[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k >= top_k) break;
+    ex[k] = expf(sel[k] - sel[0]);
+    sum += ex[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    if (k >= top_k) break;
+    ids[k] = id[k];
+    gate_w[k] = ex[k] / sum;
+  }
+}
+
+// EC: expert capacity (E <= EC); TW: tokens per wave.  Lane l owns the 16-byte
+// chunks l, l + 64, ... of a row; its partial dot products are summed in that
+// order and then over the wave by a butterfly, the same for every token.
+template <int EC, int TW>
+__global__ void __launch_bounds__(kRouterThreads)
+moe_router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, int64_t T, int D, int E,
+                  int top_k, int32_t* __restrict__ ids, float* __restrict__ gate_w, float* __restrict__ logits) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = ((int64_t)blockIdx.x * (kRouterThreads / 64) + wave) * TW;
+  if (t0 >= T) return;
+  const int nch = D / 8;   // 16-byte chunks per row
+  float acc[TW][EC];
+#pragma unroll
+  for (int j = 0; j < TW; ++j)
+#pragma unroll
+    for (int e = 0; e < EC; ++e) acc[j][e] = 0.f;
+  for (int c = lane; c < nch; c += 64) {
+    u32x4_t xv[TW];
+#pragma unroll
+    for (int j = 0; j < TW; ++j) {
+      xv[j] = zero4();
+      if (t0 + j < T) xv[j] = ld16(x + (t0 + j) * (int64_t)D + (int64_t)c * 8);
+    }
+#pragma unroll
+    for (int e = 0; e < EC; ++e) {
+      if (e < E) {
+        const u32x4_t w = ld16(Wr + (int64_t)e * D + (int64_t)c * 8);
+#pragma unroll
+        for (int j = 0; j < TW; ++j) acc[j][e] = dot8_bf16(xv[j], w, acc[j][e]);
+      }
+    }
+  }
+  // butterfly over the wave: every lane ends with every total
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int j = 0; j < TW; ++j)
+#pragma unroll
+      for (int e = 0; e < EC; ++e) acc[j][e] += __shfl_xor(acc[j][e], off, 64);
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int64_t t = t0 + j;
+    if (t >= T) break;
+    if (logits != nullptr) {
+#pragma unroll
+      for (int e = 0; e < EC; ++e)
+        if (e < E && lane == (e & 63)) logits[t * E + e] = acc[j][e];
+    }
+    if (lane == 0) router_select<EC>(acc[j], E, top_k, ids + t * top_k, gate_w + t * top_k);
+  }
+}
+
+// The same with Wr staged in LDS (E * D * 2 <= kRouterLdsBytes).
+constexpr int kRouterLdsThreads = 512;          // 8 waves
+constexpr int kRouterLdsBytes = 64 * 1024;
+
+template <int EC, int TW>
+__global__ void __launch_bounds__(kRouterLdsThreads)
+moe_router_lds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, int64_t T, int D, int E,
+                      int top_k, int32_t* __restrict__ ids, float* __restrict__ gate_w,
+                      float* __restrict__ logits) {
+  __shared__ u32x4_t wlds[kRouterLdsBytes / 16];
+  const int nch = D / 8;
+  for (int i = threadIdx.x; i < E * nch; i += kRouterLdsThreads)
+    wlds[i] = ld16(Wr + (int64_t)i * 8);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = ((int64_t)blockIdx.x * (kRouterLdsThreads / 64) + wave) * TW;
+  if (t0 >= T) return;
+  float acc[TW][EC];
+#pragma unroll
+  for (int j = 0; j < TW; ++j)
+#pragma unroll
+    for (int e = 0; e < EC; ++e) acc[j][e] = 0.f;
+  constexpr int U = 4;   // chunk steps whose x loads are in flight together
+  for (int c0 = lane; c0 < nch; c0 += 64 * U) {
+    u32x4_t xr[U][TW];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < TW; ++j) {
+        const int c = c0 + 64 * u;
+        xr[u][j] = (c < nch && t0 + j < T) ? ld16(x + (t0 + j) * (int64_t)D + (int64_t)c * 8) : zero4();
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 64 * u;
+      if (c >= nch) break;
+#pragma unroll
+      for (int e = 0; e < EC; ++e) {
+        if (e < E) {
+          const u32x4_t w = wlds[e * nch + c];
+#pragma unroll
+          for (int j = 0; j < TW; ++j) acc[j][e] = dot8_bf16(xr[u][j], w, acc[j][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+    for (int j = 0; j < TW; ++j)
+#pragma unroll
+      for (int e = 0; e < EC; ++e) acc[j][e] += __shfl_xor(acc[j][e], off, 64);
+#pragma unroll
+  for (int j = 0; j < TW; ++j) {
+    const int64_t t = t0 + j;
+    if (t >= T) break;
+    if (logits != nullptr) {
+#pragma unroll
+      for (int e = 0; e < EC; ++e)
+        if (e < E && lane == (e & 63)) logits[t * E + e] = acc[j][e];
+    }
+    if (lane == 0) router_select<EC>(acc[j], E, top_k, ids + t * top_k, gate_w + t * top_k);
+  }
+}
+
+template <int EC, int TW>
+hipError_t launch_router_lds_cfg(const uint16_t* x, const uint16_t* Wr, int64_t T, int D, int E, int top_k,
+                                 int32_t* ids, float* gate_w, float* logits, hipStream_t s) {
+  const int64_t per_block = (kRouterLdsThreads / 64) * TW;
+  const int64_t blocks = (T + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((moe_router_lds_kernel<EC, TW>), dim3((unsigned)blocks), dim3(kRouterLdsThreads), 0, s, x,
+                     Wr, T, D, E, top_k, ids, gate_w, logits);
+  return hipGetLastError();
+}
+
+template <int EC, int TW>
+hipError_t launch_router_cfg(const uint16_t* x, const uint16_t* Wr, int64_t T, int D, int E, int top_k,
+                             int32_t* ids, float* gate_w, float* logits, hipStream_t s) {
+  const int64_t per_block = (kRouterThreads / 64) * TW;
+  const int64_t blocks = (T + per_block - 1) / per_block;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((moe_router_kernel<EC, TW>), dim3((unsigned)blocks), dim3(kRouterThreads), 0, s, x, Wr, T, D,
+                     E, top_k, ids, gate_w, logits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_moe_router(const uint16_t* x, const uint16_t* Wr, int64_t T, int D, int E, int top_k,
+                             int32_t* ids, float* gate_w, float* logits, hipStream_t s) {
+  if (E < 1 || E > kRouterMaxExperts || top_k < 1 || top_k > 8 || top_k > E || D % 8 != 0)
+    return hipErrorInvalidValue;
+  if ((int64_t)E * D * 2 <= kRouterLdsBytes) {
+    if (E <= 8) return launch_router_lds_cfg<8, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+    if (E <= 16) return launch_router_lds_cfg<16, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+    if (E <= 32) return launch_router_lds_cfg<32, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+    return launch_router_lds_cfg<64, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+  }
+  if (E <= 8) return launch_router_cfg<8, 4>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+  if (E <= 16) return launch_router_cfg<16, 4>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+  if (E <= 32) return launch_router_cfg<32, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+  return launch_router_cfg<64, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
+}
 
 hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, int top_k, int E,
                             int bm, const MoeRouteOut& o, hipStream_t s) {

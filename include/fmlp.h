@@ -169,6 +169,24 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
                          const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int gate_act,
                          int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k,
                          fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+/*
+ * The routes on the device: logits[t,e] = x[t,:] . Wr[e,:] (fp32 accumulation),
+ * expert_ids[t,:] = the top_k experts by logit in descending order (a tie goes
+ * to the lower expert id), gate_w[t,:] = softmax over those top_k logits.
+ * The router of the MoE layer in ainews.cool "PyTorch fused MLP efficiency",
+ * section "architectural impact" (tokens routed to several experts); the page
+ * gives no router formula, and this is the plain linear router with top-k and a
+ * softmax over the chosen logits.  Its outputs are the routes fmlp_moe_glu /
+ * fmlp_moe_geglu take.
+ * x [T,D] bf16 and Wr [E,D] bf16 (16-byte aligned); expert_ids int32 [T,top_k],
+ * gate_w fp32 [T,top_k] and logits fp32 [T,E] (may be NULL: not written) are
+ * caller-owned device arrays, 4-byte aligned.  1 <= E <= 64,
+ * 1 <= top_k <= min(8, E).  One launch; no workspace; deterministic.
+ */
+fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, int64_t D, int32_t E,
+                           int32_t top_k, int32_t* expert_ids, float* gate_w, float* logits,
+                           fmlp_stream stream);
+
 /* Byte offset, inside the MoE workspace, of the int32 count of invalid expert ids
  * seen by the last call (read it after a stream sync). */
 size_t fmlp_moe_error_offset(void);

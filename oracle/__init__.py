@@ -15,6 +15,8 @@ from .fmlp_oracle import (  # noqa: F401
     mlp2,
     moe_geglu,
     moe_glu,
+    moe_router,
     relu,
+    route_topk,
     silu,
 )

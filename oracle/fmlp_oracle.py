@@ -49,6 +49,8 @@ __all__ = [
     "glu",
     "moe_geglu",
     "moe_glu",
+    "route_topk",
+    "moe_router",
 ]
 
 ACTS = ("none", "gelu_erf", "gelu_tanh", "relu", "silu")
@@ -196,6 +198,33 @@ def moe_glu(x, expert_ids, gate_w, expert_weights, gate_act: str):
         ye = glu(x[tok], Wg, Wu, Wd, gate_act)
         np.add.at(y, tok, w[tok, slot][:, None] * ye)
     return y
+
+
+def route_topk(logits, top_k: int):
+    """Top-k routes from given router logits [T, E]: the top_k experts of each
+    token by logit, largest first, a tie going to the lower expert id (a stable
+    sort of the negated logits), and gate weights = softmax over those top_k
+    logits.  Returns (ids int32 [T, top_k], gate_w float64 [T, top_k]).
+
+    The decision is taken in the precision of the logits handed in: the tests
+    hand in the kernel's own fp32 logits to check its integer ids exactly.
+    """
+    lg = _f64(logits)
+    ids = np.argsort(-lg, axis=1, kind="stable")[:, :top_k]
+    sel = np.take_along_axis(lg, ids, axis=1)
+    e = np.exp(sel - sel[:, :1])
+    return ids.astype(np.int32), e / e.sum(axis=1, keepdims=True)
+
+
+def moe_router(x, Wr, top_k: int):
+    """The MoE router: logits = x Wr^T, then route_topk.  ainews.cool "PyTorch
+    fused MLP efficiency", section "architectural impact", routes each token to
+    several experts; it gives no router formula, and this is the plain linear
+    router with a softmax over the chosen logits.  x [T,D], Wr [E,D].
+    Returns (ids, gate_w, logits)."""
+    logits = linear(x, Wr)
+    ids, gw = route_topk(logits, top_k)
+    return ids, gw, logits
 
 
 def moe_geglu(x, expert_ids, gate_w, expert_weights):

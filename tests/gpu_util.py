@@ -36,7 +36,10 @@ def tol_of(ref: np.ndarray) -> float:
 
 
 def assert_parity(gpu: torch.Tensor, ref: np.ndarray, what: str = "") -> float:
-    got = f64_of(gpu).reshape(ref.shape)
+    if gpu.dtype == torch.float32:
+        got = gpu.detach().cpu().numpy().astype(np.float64).reshape(ref.shape)
+    else:
+        got = f64_of(gpu).reshape(ref.shape)
     err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
     tol = tol_of(ref)
     print(f"  parity {what}: max|gpu-ref| = {err:.3e}  tol = {tol:.3e}", flush=True)

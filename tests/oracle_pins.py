@@ -81,6 +81,30 @@ def bf_moe(x, ids, gw, experts, gate_act="gelu_tanh"):
     return y
 
 
+def bf_router(x, Wr, top_k):
+    """Pure-Python router: dot products, then top_k by repeated scans for the
+    largest remaining logit (the first, i.e. lower id, on a tie), then a
+    softmax over the chosen ones with libm exp."""
+    ids, gws = [], []
+    for row in x:
+        lg = [sum(float(a) * float(b) for a, b in zip(row, w)) for w in Wr]
+        chosen = []
+        for _ in range(top_k):
+            best = None
+            for e, v in enumerate(lg):
+                if e in chosen:
+                    continue
+                if best is None or v > lg[best]:
+                    best = e
+            chosen.append(best)
+        m = lg[chosen[0]]
+        ex = [math.exp(lg[e] - m) for e in chosen]
+        s = sum(ex)
+        ids.append(chosen)
+        gws.append([v / s for v in ex])
+    return ids, gws
+
+
 def _close(a, b, rtol=1e-12, atol=1e-13, what=""):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -259,6 +283,42 @@ def check_glu_special_cases(o):
                what=f"moe_glu top1 expert {e}")
 
 
+def check_router(o):
+    """The router against a brute-force loop, closed forms and invariants."""
+    rng = np.random.default_rng(41)
+    for (T, D, E, k) in [(5, 4, 3, 2), (7, 8, 8, 2), (4, 6, 5, 5), (6, 3, 4, 1)]:
+        x = _bf16ish(rng, (T, D))
+        Wr = _bf16ish(rng, (E, D), 0.7)
+        ids, gw, lg = o.moe_router(x, Wr, k)
+        bids, bgw = bf_router(x.tolist(), Wr.tolist(), k)
+        assert ids.tolist() == bids, (ids.tolist(), bids)
+        _close(gw, bgw, what=f"router weights {T}x{D}x{E} k{k}")
+        _close(lg, bf_linear(x.tolist(), Wr.tolist(), None, "none"), what="router logits")
+        _close(gw.sum(axis=1), np.ones(T), what="router weights sum to 1")
+        # chosen in descending logit order, all distinct
+        sel = np.take_along_axis(lg, ids, axis=1)
+        assert np.all(np.diff(sel, axis=1) <= 0)
+        assert all(len(set(r)) == k for r in ids.tolist())
+    # two experts, both chosen: the weights are sigmoid(a - b) and sigmoid(b - a)
+    lg = np.array([[0.3, -1.2], [2.0, 2.5]])
+    ids, gw = o.route_topk(lg, 2)
+    assert ids.tolist() == [[0, 1], [1, 0]]
+    _close(gw[:, 0], 1.0 / (1.0 + np.exp(-np.array([1.5, 0.5]))), what="router sigmoid form")
+    # top-1: weight exactly 1; ties go to the lower id
+    ids, gw = o.route_topk(np.array([[1.0, 3.0, 3.0, 0.0]]), 1)
+    assert ids.tolist() == [[1]] and gw.tolist() == [[1.0]]
+    ids, _ = o.route_topk(np.array([[0.5, 0.5, 0.5, 0.5]]), 3)
+    assert ids.tolist() == [[0, 1, 2]]
+    # permuting the experts' router rows permutes the chosen ids
+    x = _bf16ish(rng, (9, 8))
+    Wr = _bf16ish(rng, (6, 8))
+    p = rng.permutation(6)
+    ids, gw, _ = o.moe_router(x, Wr, 2)
+    ids_p, gw_p, _ = o.moe_router(x, Wr[p], 2)
+    assert np.array_equal(p[ids_p], ids)
+    _close(gw_p, gw, what="router permutation")
+
+
 def check_transpose_worked_example(o):
     """The page's strides-and-views example: with W = M ([out=3, in=2]) and
     x = I_2, nn.Linear's y = x @ W.T is exactly the printed M.t()."""
@@ -398,4 +458,5 @@ ALL_CHECKS = [
     check_glu_special_cases,
     check_fused_equals_unfused,
     check_moe_invariants,
+    check_router,
 ]

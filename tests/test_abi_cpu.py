@@ -133,6 +133,20 @@ def test_glu_validation(L):
     assert L.fmlp_moe_glu(X, ids, gw, W, W, W, 4, 0, 64, 128, 4, 2, Y, WS, need, None) == OK
 
 
+def test_route_validation(L):
+    ids, gw, lg = 0x60000, 0x70000, 0x80000
+    assert L.fmlp_moe_route(X, W, 0, 4096, 8, 2, ids, gw, None, None) == OK        # T == 0: no-op
+    assert L.fmlp_moe_route(X, W, 16, 4096, 65, 2, ids, gw, None, None) == E_ARG
+    assert L.fmlp_moe_route(X, W, 16, 4096, 0, 1, ids, gw, None, None) == E_ARG
+    assert L.fmlp_moe_route(X, W, 16, 4096, 8, 9, ids, gw, None, None) == E_ARG
+    assert L.fmlp_moe_route(X, W, 16, 4096, 4, 5, ids, gw, None, None) == E_ARG
+    assert "top_k" in _err(L)
+    assert L.fmlp_moe_route(X, W, 16, 4092, 8, 2, ids, gw, None, None) == E_ALIGN
+    assert L.fmlp_moe_route(X, None, 16, 4096, 8, 2, ids, gw, None, None) == E_NULL
+    assert L.fmlp_moe_route(X, W, 16, 4096, 8, 2, None, gw, None, None) == E_NULL
+    assert L.fmlp_moe_route(X, W, 16, 4096, 8, 2, ids, gw + 2, lg, None) == E_ALIGN
+
+
 def test_new_acts_accepted(L):
     for act in (3, 4):   # relu, silu
         assert L.fmlp_linear(X, W, None, act, 0, 32, 8, Y, None) == OK

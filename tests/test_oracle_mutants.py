@@ -15,6 +15,7 @@ _orig_gelu_erf = fo.gelu_erf
 _orig_gelu_tanh = fo.gelu_tanh
 _orig_moe = fo.moe_geglu
 _orig_glu = fo.glu
+_orig_route_topk = fo.route_topk
 
 
 def _linear_no_bias(x, W, b=None, act="none"):
@@ -98,6 +99,24 @@ def _glu_gate_up_swapped(x, Wg, Wu, Wd, gate_act):
     return _orig_glu(x, Wu, Wg, Wd, gate_act)
 
 
+def _route_softmax_over_all(logits, top_k):
+    lg = np.asarray(logits, float)
+    ids = np.argsort(-lg, axis=1, kind="stable")[:, :top_k]
+    e = np.exp(lg - lg.max(axis=1, keepdims=True))
+    p = e / e.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), np.take_along_axis(p, ids, axis=1)
+
+
+def _route_ties_to_higher(logits, top_k):
+    lg = np.asarray(logits, float)[:, ::-1]
+    ids, gw = _orig_route_topk(lg, top_k)
+    return (lg.shape[1] - 1 - ids).astype(np.int32), gw
+
+
+def _route_smallest(logits, top_k):
+    return _orig_route_topk(-np.asarray(logits, float), top_k)
+
+
 def _mlp2_act_twice(x, W1, b1, W2, b2, act):
     return _orig_linear(_orig_linear(x, W1, b1, act), W2, b2, act)
 
@@ -152,6 +171,9 @@ MUTANTS = {
     "relu_leaky": ("relu", _relu_leaky),
     "glu_ignores_gate_act": ("glu", _glu_ignores_gate_act),
     "glu_gate_up_swapped": ("glu", _glu_gate_up_swapped),
+    "router_softmax_over_all_experts": ("route_topk", _route_softmax_over_all),
+    "router_ties_to_higher_id": ("route_topk", _route_ties_to_higher),
+    "router_picks_smallest": ("route_topk", _route_smallest),
 }
 
 
