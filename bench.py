@@ -44,7 +44,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["common.h", "kernels.h", "lds_dma.h", "decode.hip"],
     "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
     "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
-    "moe_router_lds_kernel": ["common.h", "kernels.h", "moe.hip"],
+    "moe_router_mfma_kernel": ["common.h", "kernels.h", "moe.hip"],
 }
 
 
@@ -180,7 +180,7 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None):
                 cache["x"] = f64(x_bits[:toks])
                 cache["Wr"] = f64(Wr_bits)
             return oracle.moe_router(cache["x"], cache["Wr"], w.top_k)
-        return Case(w, calls, "moe_router_lds_kernel", 1, "router: logits, top-k, softmax (1 launch)", R, fn,
+        return Case(w, calls, "moe_router_mfma_kernel", 1, "router: logits, top-k, softmax (1 launch)", R, fn,
                     (f"{toks} of {w.M} tokens", toks / w.M))
 
     # mixture of experts

@@ -18,10 +18,11 @@
 //   router:  the routes computed on the device: logits = x . Wr^T (fp32), the
 //            top_k experts by logit (a tie goes to the lower expert id), and
 //            gate weights = softmax over the chosen logits.  Bound by reading x
-//            once.  When the router weights fit (E * D * 2 <= 64 KB) a block
-//            first copies them into LDS, so HBM and L2 see them once per block;
-//            each wave takes two tokens and keeps four chunk steps of x in
-//            flight.  Otherwise they are read through the caches.
+//            once.  Up to 16 experts the logits are a 16 x 16 x 32 MFMA
+//            contraction: a block takes 16 tokens, its 8 waves split D and
+//            their partial tiles are summed in a fixed order.  Past 16 experts
+//            a VALU form: the router weights in LDS when they fit
+//            (E * D * 2 <= 64 KB), else read through the caches.
 #include "common.h"
 #include "kernels.h"
 
@@ -291,6 +292,66 @@ moe_router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W
   }
 }
 
+// Up to 16 experts: logits on the matrix cores.  D[e][t] = sum_k Wr[e][k] x[t][k]
+// with the router weights as the row operand (experts past E read as zero)
+// and 16 tokens as the column operand.  Wave w takes the 32-k steps w, w + 8,
+// ...; the 8 partial tiles go through LDS and wave 0 sums them in wave order.
+constexpr int kRouterMfmaWaves = 8;
+
+__global__ void __launch_bounds__(kRouterMfmaWaves * 64)
+moe_router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, int64_t T, int D, int E,
+                       int top_k, int32_t* __restrict__ ids, float* __restrict__ gate_w,
+                       float* __restrict__ logits) {
+  __shared__ float4 red[kRouterMfmaWaves][64];
+  __shared__ float lg[16][17];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t0 = (int64_t)blockIdx.x * 16;
+  const int li = lane & 15, kq = lane >> 4;
+  const bool row_ok = li < E;              // this lane's expert exists
+  const bool col_ok = t0 + li < T;         // this lane's token exists
+  const uint16_t* wrow = Wr + (int64_t)(row_ok ? li : 0) * D;
+  const uint16_t* xrow = x + (col_ok ? t0 + li : 0) * (int64_t)D;
+  const int steps = (D + 31) / 32;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 16;                    // k steps whose loads are in flight together
+  for (int s0 = wave; s0 < steps; s0 += kRouterMfmaWaves * U) {
+    u32x4_t a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + kRouterMfmaWaves * u;
+      const int k = s * 32 + kq * 8;
+      const bool in = s < steps && k < D;
+      a[u] = (in && row_ok) ? ld16(wrow + k) : zero4();
+      b[u] = (in && col_ok) ? ld16(xrow + k) : zero4();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc = mfma_16x16x32(a[u], b[u], acc);
+  }
+  red[wave][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  __syncthreads();
+  if (wave != 0) return;
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < kRouterMfmaWaves; ++w) {
+    const float4 v = red[w][lane];
+    sum[0] += v.x; sum[1] += v.y; sum[2] += v.z; sum[3] += v.w;
+  }
+  // lane holds D[4 * kq + r][li]: expert 4 * kq + r, token li
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lg[li][4 * kq + r] = sum[r];
+  __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  if (lane < 16 && t0 + lane < T) {
+    const int64_t t = t0 + lane;
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = lg[lane][e];
+    if (logits != nullptr)
+      for (int e = 0; e < E; ++e) logits[t * E + e] = v[e];
+    router_select<16>(v, E, top_k, ids + t * top_k, gate_w + t * top_k);
+  }
+}
+
 // The same with Wr staged in LDS (E * D * 2 <= kRouterLdsBytes).
 constexpr int kRouterLdsThreads = 512;          // 8 waves
 constexpr int kRouterLdsBytes = 64 * 1024;
@@ -387,14 +448,18 @@ hipError_t launch_moe_router(const uint16_t* x, const uint16_t* Wr, int64_t T, i
                              int32_t* ids, float* gate_w, float* logits, hipStream_t s) {
   if (E < 1 || E > kRouterMaxExperts || top_k < 1 || top_k > 8 || top_k > E || D % 8 != 0)
     return hipErrorInvalidValue;
+  if (E <= 16) {
+    const int64_t blocks = (T + 15) / 16;
+    if (blocks <= 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(moe_router_mfma_kernel, dim3((unsigned)blocks), dim3(kRouterMfmaWaves * 64), 0, s, x, Wr, T,
+                       D, E, top_k, ids, gate_w, logits);
+    return hipGetLastError();
+  }
   if ((int64_t)E * D * 2 <= kRouterLdsBytes) {
-    if (E <= 8) return launch_router_lds_cfg<8, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
-    if (E <= 16) return launch_router_lds_cfg<16, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
     if (E <= 32) return launch_router_lds_cfg<32, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
     return launch_router_lds_cfg<64, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
   }
-  if (E <= 8) return launch_router_cfg<8, 4>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
-  if (E <= 16) return launch_router_cfg<16, 4>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
   if (E <= 32) return launch_router_cfg<32, 2>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
   return launch_router_cfg<64, 1>(x, Wr, T, D, E, top_k, ids, gate_w, logits, s);
 }

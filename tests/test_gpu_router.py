@@ -42,8 +42,9 @@ def _check(x, Wr, k, what):
 @pytest.mark.parametrize("T,D,E,k", [
     (1, 64, 2, 1), (5, 128, 8, 2), (37, 520, 8, 2), (300, 4096, 8, 2), (1000, 256, 13, 3),
     (257, 1024, 16, 4), (130, 512, 32, 8), (99, 384, 64, 8), (64, 96, 1, 1), (77, 64, 64, 1),
-    # router weights past 64 KB: read through the caches instead of LDS
-    (33, 8192, 8, 2), (200, 4096, 16, 2), (70, 1536, 32, 3), (50, 2048, 64, 4),
+    # up to 16 experts on the matrix cores (k tails: D not a multiple of 32);
+    # past 16 with the router weights past 64 KB: read through the caches
+    (33, 8192, 8, 2), (200, 4104, 16, 2), (17, 40, 16, 8), (70, 1536, 32, 3), (50, 2048, 64, 4),
 ])
 def test_router_random(T, D, E, k):
     rng = np.random.default_rng(T + D + E + k)
