@@ -60,9 +60,6 @@ namespace {
 
 constexpr int kWorkers = 8;                    // streaming + MFMA waves
 constexpr int kThreads = (kWorkers + 1) * 64;  // + the control wave
-constexpr int kWChunks = 1024;                 // 16-byte weight chunks per stage (16 KB)
-constexpr int kSK1 = 512;                      // k per stage, one weight matrix
-constexpr int kSK2 = 256;                      // k per stage, gate + up together
 constexpr uint32_t kSpinLimit = 1u << 20;      // bounded waits
 constexpr int kLdsBudget = 160 * 1024;
 // Ring depth cap: R - 1 = 3 stages in flight per CU (51 KB at one token)
@@ -75,18 +72,38 @@ constexpr int kRingMax = 4;
 // (two bf16 and the call's epoch), gathered by every block straight into LDS.
 constexpr int kLLMaxH = 4096;
 
+// k per stage for a class of M.  A stage is 16 weight rows x SK k; longer
+// runs per row stream faster from HBM (a probe of this pattern: 2 KB per row
+// about 15-20 % above 1 KB), so up to 4 tokens a stage takes 1024 k.  At 16
+// tokens the activation slice of such a stage would crowd the ring out of LDS,
+// and with the word-flag publish (LL) bigger stages put more bytes in the
+// CU's queue ahead of the h exchange (measured slower at one token, 4096^3).
+template <int MC, bool LL>
+constexpr int stage_k() { return (MC <= 4 && !LL) ? 1024 : 512; }
+
 // Activation rows held per stage (a class of M) and the ring depth it leaves.
+// Gate+up stages: up to 4 tokens the gate and up rows alternate as stages of
+// 16 rows x SK (longer runs per row).  At 16 tokens that would load each
+// activation slice twice, so a stage is paired: 16 gate + 16 up rows x 256 k
+// sharing one activation slice (PAIR).
 template <int MC, bool DUAL1, bool LL>
 struct RingShape {
-  static constexpr int kXChunks = MC * 64;                        // MC rows x 1 KB
+  static constexpr bool PAIR = DUAL1 && MC > 4;
+  static constexpr int SK = stage_k<MC, LL>();
+  static constexpr int SK1 = PAIR ? 256 : SK;                      // k per layer-1 stage
+  static constexpr int CPR = SK / 8;                              // 16-byte chunks per stage row
+  static constexpr int kWChunks = 16 * CPR;                       // weight chunks per stage
+  static constexpr int NL = kWChunks / 64 / kWorkers;             // weight loads per wave and stage
+  static constexpr int NT = CPR / 32;                             // MFMA k-steps per wave and stage
+  static constexpr int kXChunks = MC * CPR;                       // MC activation rows
   static constexpr int kSlotBytes = (kWChunks + kXChunks) * 16;
   static constexpr int kRedBytes = (DUAL1 ? 2 : 1) * kWorkers * 64 * 16;
   static constexpr int kFixed = kRedBytes + 2 * 64 * 4 + 1024     // partials, bias, sink
                                 + (LL ? kLLMaxH * 2 : 0);          // h gathered for layer 2
   static constexpr int kFit = (kLdsBudget - kFixed) / kSlotBytes;
   static constexpr int R = kFit < kRingMax ? kFit : kRingMax;
-  static constexpr int XI = MC > 8 ? 2 : 1;                       // activation loads per wave and stage
-  static constexpr int kLoads = 2 + XI;                           // loads per wave and stage
+  static constexpr int XI = (MC * CPR / 64 + kWorkers - 1) / kWorkers;  // activation loads per wave and stage
+  static constexpr int kLoads = NL + XI;                          // loads per wave and stage
   static_assert(R >= 3 && R * kSlotBytes + kFixed <= kLdsBudget, "ring does not fit");
   static_assert(kLoads * (R - 2) < 64, "vmcnt range");
 };
@@ -141,19 +158,22 @@ struct Stream {
   int total;        // stages of this block
 };
 
-template <bool DUAL1, bool TWO>
+// A gate+up layer streams its gate and up rows as alternating stages of the
+// same k range (gate at even stage indices, up at odd), so every stage is 16
+// rows of one matrix.
+template <bool DUAL1, bool TWO, int SK, bool PAIR>
 __device__ __forceinline__ Stream make_stream(const GemvLayer& L1, const GemvLayer& L2) {
   Stream st;
   const int G = gridDim.x, b = blockIdx.x;
   const int tiles1 = (int)((L1.N + 15) / 16);
-  const int sk1 = DUAL1 ? kSK2 : kSK1;
+  constexpr int SK1 = PAIR ? 256 : SK;
   st.nt[0] = b < tiles1 ? (tiles1 - 1 - b) / G + 1 : 0;
-  st.S[0] = (int)((L1.K + sk1 - 1) / sk1);
+  st.S[0] = (int)((L1.K + SK1 - 1) / SK1) * ((DUAL1 && !PAIR) ? 2 : 1);
   st.first2 = st.nt[0] * st.S[0];
   if (TWO) {
     const int tiles2 = (int)((L2.N + 15) / 16);
     st.nt[1] = b < tiles2 ? (tiles2 - 1 - b) / G + 1 : 0;
-    st.S[1] = (int)((L2.K + kSK1 - 1) / kSK1);
+    st.S[1] = (int)((L2.K + SK - 1) / SK);
   } else {
     st.nt[1] = 0;
     st.S[1] = 1;
@@ -208,6 +228,10 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   static_assert(!LL || (TWO && MC == 1), "word-flag publish: two layers, one token");
   using RS = RingShape<MC, DUAL1, LL>;
   constexpr int R = RS::R, XI = RS::XI;
+  constexpr int SK = RS::SK, CPR = RS::CPR, NL = RS::NL, NT = RS::NT;
+  constexpr bool PAIR = RS::PAIR;
+  constexpr int SK1 = RS::SK1;
+  constexpr int kWChunks = RS::kWChunks;
   constexpr int kSets = DUAL1 ? 2 : 1;
   constexpr uint32_t kSlot = (uint32_t)RS::kSlotBytes;
   __shared__ u32x4_t ring[R][kWChunks + RS::kXChunks];
@@ -220,7 +244,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
   const int li = lane & 15, lg = lane >> 4;
-  const Stream st = make_stream<DUAL1, TWO>(L1, L2);
+  const Stream st = make_stream<DUAL1, TWO, SK, PAIR>(L1, L2);
   const int G = (int)gridDim.x, blk = (int)blockIdx.x;
 
   uint32_t target = 0;
@@ -237,84 +261,79 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
     const uint64_t X0 = in_sgpr(reinterpret_cast<uint64_t>(L1.x));
     const uint64_t X1 = in_sgpr(reinterpret_cast<uint64_t>(L2.x));
 
-    // Per-lane byte offsets, fixed for a whole layer: weight load i of this
-    // wave (stage row r, global chunk c of the row: chunk c of row r sits at
-    // LDS position c ^ (r & 15)), and activation load j (one 1 KB piece: one
-    // row, or two rows of 512 B for gate + up).  The *t variants are a tile's
-    // last stage, whose chunks past K go out of range.
-    uint32_t woff[2][2], wofft[2][2], xoff[2][XI], xofft[2][XI];
+    // Per-lane byte offsets, fixed for a whole layer.  A stage row holds
+    // CPR chunks of 16 bytes (a paired layer-1 stage: 32 rows of 32 chunks,
+    // gate rows 0-15 and up rows 16-31).  Load instruction g of a stage
+    // (1 KB) fills LDS chunks 64 g .. 64 g + 63; lane l's chunk P = 64 g + l
+    // is position P % CPR of stage row P / CPR, and the lane fetches the
+    // global chunk c whose swizzled home is that position (chunk c of row r
+    // lives at swz(c, r): an involution).  Weight load i of wave w is
+    // instruction NL * w + i; activation load j of wave w is instruction
+    // w + 8 * j of the activation area (MC rows).  The *t variants are for a
+    // tile's last k range, whose chunks past K go out of range.
+    uint32_t woff[2][NL], wofft[2][NL], xoff[2][XI], xofft[2][XI];
+    bool xhas[2][XI];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bool dual = DUAL1 && p == 0;
+      const bool pr = PAIR && p == 0;
+      const int cpr = pr ? 32 : CPR;
+      const int sk = pr ? SK1 : SK;
       const int K = pick(p != 0, K1, K0);
-      const int sk = dual ? kSK2 : kSK1;
-      const int klast = ((K + sk - 1) / sk - 1) * sk;   // k0 of a tile's last stage
+      const int klast = ((K + sk - 1) / sk - 1) * sk;   // k0 of a tile's last k range
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int inst = 2 * w + i;
-        int r, c;
-        if (dual) {
-          const int sr = 2 * inst + (lane >> 5);   // stage row 0..31: gate 0-15, up 16-31
-          r = sr & 15;
-          c = swz(lane & 31, sr);
-        } else {
-          r = inst;
-          c = swz(lane, inst);
-        }
-        woff[p][i] = (uint32_t)(r * K + c * 8) * 2u;
+      for (int i = 0; i < NL; ++i) {
+        const int P = 64 * (NL * w + i) + lane;
+        const int r = P / cpr;
+        const int c = swz(P % cpr, r);
+        woff[p][i] = (uint32_t)((r & 15) * K + c * 8) * 2u;   // paired: gate/up rows by wave
         wofft[p][i] = klast + c * 8 < K ? woff[p][i] : kOutOfRange;
       }
 #pragma unroll
       for (int j = 0; j < XI; ++j) {
-        int r, c;
-        if (dual) {
-          r = 2 * w + (lane >> 5);               // one load: rows 2w, 2w+1
-          c = swz(lane & 31, r);
-        } else {
-          r = w + 8 * j;
-          c = swz(lane, r);
-        }
-        const bool has = dual ? j == 0 : true;
-        xoff[p][j] = has ? (uint32_t)(r * K + c * 8) * 2u : kOutOfRange;
+        const int P = 64 * (w + 8 * j) + lane;
+        const int r = P / cpr;
+        const int c = swz(P % cpr, r);
+        xhas[p][j] = w + 8 * j < MC * cpr / 64;
+        xoff[p][j] = (uint32_t)(r * K + c * 8) * 2u;
         xofft[p][j] = klast + c * 8 < K ? xoff[p][j] : kOutOfRange;
       }
     }
-    // LDS: this wave's 1 KB weight pieces of a slot, its activation pieces
-    // (or the sink), and this lane's fragment positions
+    // LDS: this wave's weight pieces of a slot, its activation pieces (or
+    // the sink), and this lane's fragment positions
     const uint32_t ring0 = lds_addr(&ring[0][0]);
-    const uint32_t lds_w = ring0 + (uint32_t)(2 * w) * 1024u;
+    const uint32_t lds_w = ring0 + (uint32_t)(NL * w) * 1024u;
     const uint32_t sink_lds = lds_addr(&sink[0]);
     uint32_t lds_x[2][XI];   // [layer][load]: offset inside a slot, or the sink (bit 31)
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-      for (int j = 0; j < XI; ++j) {
-        const bool dual = DUAL1 && p == 0;
-        const int piece = dual ? w : w + 8 * j;        // which 1 KB piece of the slot's activation area
-        const bool fits = dual ? (j == 0 && 2 * w < MC) : (w + 8 * j < MC);
-        lds_x[p][j] = fits ? (uint32_t)(kWChunks * 16 + piece * 1024) : 0x80000000u;
-      }
-    }
-    uint32_t apos[2], bpos[2];
+      for (int j = 0; j < XI; ++j)
+        lds_x[p][j] = xhas[p][j] ? (uint32_t)(kWChunks * 16 + (w + 8 * j) * 1024) : 0x80000000u;
+    // wave w owns chunks [w * CPR / 8, (w + 1) * CPR / 8) of every stage row:
+    // NT k-steps of 4 chunks (32 k), lane group lg taking chunk 4 t + lg
+    uint32_t apos[NT], bpos[NT];
+    int kc[NT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int c = 8 * w + 4 * t + lg;
-      apos[t] = (uint32_t)(li * 64 + swz(c, li)) * 16u;
-      bpos[t] = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * 64 + swz(c, li)) * 16u;
+    for (int t = 0; t < NT; ++t) {
+      kc[t] = w * (CPR / 8) + 4 * t + lg;
+      apos[t] = (uint32_t)(li * CPR + swz(kc[t], li)) * 16u;
+      bpos[t] = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * CPR + swz(kc[t], li)) * 16u;
     }
-    const int cd = 4 * w + lg;   // gate + up: one k-step per stage
-    const uint32_t gpos = (uint32_t)(li * 32 + swz(cd, li)) * 16u;
-    const uint32_t bdpos = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * 32 + swz(cd, li)) * 16u;
+    // paired layer-1 stage: one k-step, chunk 4 w + lg of gate row li and up row 16 + li
+    const int kcp = 4 * w + lg;
+    const uint32_t gpos = (uint32_t)(li * 32 + swz(kcp, li)) * 16u;
+    const uint32_t upos = gpos + 16u * 32u * 16u;
+    const uint32_t bppos = (uint32_t)(kWChunks * 16) + (uint32_t)((li < MC ? li : 0) * 32 + swz(kcp, li)) * 16u;
     const bool bcol = li < M;    // this lane's activation row exists
-    bool aok[2][2];              // weight fragment inside K at a tile's last stage
+    bool aok[2][NT];             // weight fragment inside K in a tile's last k range
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bool dual = DUAL1 && p == 0;
+      const bool pr = PAIR && p == 0;
+      const int sk = pr ? SK1 : SK;
       const int K = pick(p != 0, K1, K0);
-      const int sk = dual ? kSK2 : kSK1;
       const int klast = ((K + sk - 1) / sk - 1) * sk;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) aok[p][t] = klast + (dual ? cd : 8 * w + 4 * t + lg) * 8 < K;
+      for (int t = 0; t < NT; ++t) aok[p][t] = klast + (pr ? kcp : kc[t]) * 8 < K;
     }
 
     f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -322,28 +341,34 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
     // ---- issue side: the next stage to load ---------------------------------
     Seg is = seg_first<TWO>(st);
     bool h_ok = false;         // h may be read (the barrier has passed)
-    uint64_t wbase = 0, xbase = 0;
-    uint32_t wrec = 0, xrec = 0, step_bytes = kSK1 * 2;
-    bool i_l2 = false, i_tailk = false;
+    uint64_t wtile[2] = {0, 0};   // this tile's first row: gate (or only) and up weights
+    uint32_t wrows = 0;        // this tile's weight bytes per matrix (rows * K * 2)
+    uint32_t xall = 0;         // activation bytes (M * K * 2), 0 when nothing is to be read
+    uint64_t xb = 0;
+    bool i_l2 = false, i_tailk = false, i_dual = false;
+    int i_nk = 1;              // k ranges per tile
+    int i_sk = SK;             // k per stage in this segment
     auto issue_enter = [&]() {   // issue state for the segment `is` begins
       i_l2 = TWO && is.kind == SEG_L2;
       const bool real = is.kind != SEG_END;
-      const bool dual = DUAL1 && is.kind == SEG_L1;
+      i_dual = DUAL1 && !PAIR && is.kind == SEG_L1;
       const int K = pick(i_l2, K1, K0);
       const int N = pick(i_l2, N1, N0);
-      const int sk = dual ? kSK2 : kSK1;
-      step_bytes = (uint32_t)sk * 2u;
+      const int sk = (PAIR && !i_l2) ? SK1 : SK;
       i_tailk = K % sk != 0;
+      i_nk = (K + sk - 1) / sk;
+      i_sk = sk;
       const int n0 = (blk + is.tile * G) * 16;
       const int left = N - n0;
       const int rows = real ? (left < 16 ? left : 16) : 0;
-      const uint64_t W = pick(i_l2, Wa1, (dual && w >= 4) ? Wb0 : Wa0);   // loads 8-15: up rows
-      wbase = rows ? W + (uint64_t)((int64_t)n0 * K) * 2u : W;
-      wrec = (uint32_t)(rows * K) * 2u;
-      xbase = pick(i_l2, X1, X0);
-      xrec = real && !(LL && i_l2) ? (uint32_t)(M * K) * 2u : 0u;   // LL: layer 2 reads h_lds
+      const uint64_t off = rows ? (uint64_t)((int64_t)n0 * K) * 2u : 0u;
+      wtile[0] = pick(i_l2, Wa1, Wa0) + off;
+      wtile[1] = Wb0 + off;
+      wrows = (uint32_t)(rows * K) * 2u;
+      xb = pick(i_l2, X1, X0);
+      xall = real && !(LL && i_l2) ? (uint32_t)(M * K) * 2u : 0u;   // LL: layer 2 reads h_lds
     };
-    // all loads of one stage into ring slot `slot`: 2 weight pieces, then XI
+    // all loads of one stage into ring slot `slot`: NL weight pieces, then XI
     // activation pieces (h only once the barrier has passed)
     int inext = 0;             // stream index of the next stage to load
     auto issue = [&](uint32_t slot) {
@@ -353,15 +378,21 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
         seg_next<TWO>(st, is);
         issue_enter();
       }
-      const bool tail = i_tailk && is.left == 1;
-      const i32x4_t wd = make_desc(wbase, wrec);
+      const int q = is.kind == SEG_END ? 0 : pick(i_l2, st.S[1], st.S[0]) - is.left;   // stage within the tile
+      // gate (0) or up (1): alternating stages, or (paired) waves 4-7 load up rows
+      const int sel = i_dual ? (q & 1) : ((PAIR && !i_l2 && w >= 4) ? 1 : 0);
+      const int kidx = i_dual ? (q >> 1) : q;                   // k range
+      const bool tail = i_tailk && kidx == i_nk - 1;
+      const uint32_t koff = (uint32_t)(kidx * i_sk) * 2u;
+      const i32x4_t wd = make_desc(pick(sel != 0, wtile[1], wtile[0]) + koff, wrows > koff ? wrows - koff : 0u);
       const uint32_t slot_lds = ring0 + slot * kSlot;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NL; ++i) {
         const uint32_t off = pick(tail, pick(i_l2, wofft[1][i], wofft[0][i]), pick(i_l2, woff[1][i], woff[0][i]));
         asm_load_lds_stream(wd, lds_w + slot * kSlot + (uint32_t)i * 1024u, off);
       }
-      const i32x4_t xd = make_desc(xbase, (i_l2 && !h_ok) ? 0u : xrec);
+      const uint32_t xrec = (i_l2 && !h_ok) ? 0u : (xall > koff ? xall - koff : 0u);
+      const i32x4_t xd = make_desc(xb + koff, xrec);
 #pragma unroll
       for (int j = 0; j < XI; ++j) {
         const uint32_t off = pick(tail, pick(i_l2, xofft[1][j], xofft[0][j]), pick(i_l2, xoff[1][j], xoff[0][j]));
@@ -369,10 +400,6 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
         asm_load_lds(xd, (where & 0x80000000u) ? sink_lds : slot_lds + where, off);
       }
       --is.left;
-      wbase += step_bytes;
-      wrec = wrec > step_bytes ? wrec - step_bytes : 0u;
-      xbase += step_bytes;
-      xrec = xrec > step_bytes ? xrec - step_bytes : 0u;
     };
 
     // ---- consume side: the stage in ring slot `slot` ------------------------
@@ -397,32 +424,41 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       ++gidx;
       const bool real = cs.kind != SEG_END;
       const bool last = real && cs.left == 1;
-      if (real) {
-        const bool c_l2 = TWO && cs.kind == SEG_L2;
-        const bool tail = last && (pick(c_l2, K1, K0) % ((DUAL1 && !c_l2) ? kSK2 : kSK1) != 0);
+      if (real && PAIR && cs.kind == SEG_L1) {
+        // paired stage: gate and up fragments share the activation fragment
+        const bool tail = last && (K0 % SK1 != 0);
         const char* sp = reinterpret_cast<const char*>(&ring[0][0]) + slot * kSlot;
-        if (DUAL1 && !c_l2) {
-          u32x4_t g = *reinterpret_cast<const u32x4_t*>(sp + gpos);
-          u32x4_t u = *reinterpret_cast<const u32x4_t*>(sp + gpos + 16 * 32 * 16);
-          u32x4_t x = zero4();               // lanes of absent rows read nothing
-          if (bcol) x = *reinterpret_cast<const u32x4_t*>(sp + bdpos);
-          if (tail && !aok[0][0]) g = u = zero4();
-          acc0 = mfma_16x16x32(g, x, acc0);
-          acc1 = mfma_16x16x32(u, x, acc1);
-        } else {
+        u32x4_t g = *reinterpret_cast<const u32x4_t*>(sp + gpos);
+        u32x4_t u = *reinterpret_cast<const u32x4_t*>(sp + upos);
+        u32x4_t x = zero4();
+        if (bcol) x = *reinterpret_cast<const u32x4_t*>(sp + bppos);
+        if (tail && !aok[0][0]) g = u = zero4();
+        acc0 = mfma_16x16x32(g, x, acc0);
+        acc1 = mfma_16x16x32(u, x, acc1);
+      } else if (real) {
+        const bool c_l2 = TWO && cs.kind == SEG_L2;
+        const bool dual = DUAL1 && !c_l2;
+        const int K = pick(c_l2, K1, K0);
+        const int q = pick(c_l2, st.S[1], st.S[0]) - cs.left;
+        const bool up = dual && (q & 1);
+        const int kidx = dual ? (q >> 1) : q;
+        const bool tail = (K % SK != 0) && kidx == (K + SK - 1) / SK - 1;
+        const char* sp = reinterpret_cast<const char*>(&ring[0][0]) + slot * kSlot;
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            u32x4_t a = *reinterpret_cast<const u32x4_t*>(sp + apos[t]);
-            u32x4_t x = zero4();
-            if (LL && c_l2) {
-              const int k = (st.S[1] - cs.left) * kSK1 + (8 * w + 4 * t + lg) * 8;
-              if (bcol && k < K1) x = h_lds[k >> 3];
-            } else if (bcol) {
-              x = *reinterpret_cast<const u32x4_t*>(sp + bpos[t]);
-            }
-            if (tail && !pick(c_l2, aok[1][t], aok[0][t])) a = zero4();
-            acc0 = mfma_16x16x32(a, x, acc0);
+        for (int t = 0; t < NT; ++t) {
+          u32x4_t a = *reinterpret_cast<const u32x4_t*>(sp + apos[t]);
+          u32x4_t x = zero4();               // lanes of absent rows read nothing
+          if (LL && c_l2) {
+            const int k = kidx * SK + kc[t] * 8;
+            if (bcol && k < K1) x = h_lds[k >> 3];
+          } else if (bcol) {
+            x = *reinterpret_cast<const u32x4_t*>(sp + bpos[t]);
           }
+          if (tail && !pick(c_l2, aok[1][t], aok[0][t])) a = zero4();
+          if (up)
+            acc1 = mfma_16x16x32(a, x, acc1);
+          else
+            acc0 = mfma_16x16x32(a, x, acc0);
         }
       }
       if (last) {                        // partial tile of this wave -> control wave
@@ -460,14 +496,14 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
       // h slices of the layer-2 stages already in flight, re-requested now
       // that h is complete (in order after the empty ones: they land later)
       const uint32_t hrec = (uint32_t)(M * K1) * 2u;
-      const bool htailk = K1 % kSK1 != 0;
+      const bool htailk = K1 % SK != 0;
       Seg hq = cs;
       uint32_t hs = slot;
       for (int e = 0; e < R - 1; ++e) {
         if (hq.left == 0) seg_next<TWO>(st, hq);
         if (hq.kind != SEG_L2) break;      // the rest was never requested
         const bool in = true;
-        const uint32_t k0b = (uint32_t)((st.S[1] - hq.left) * kSK1) * 2u;   // k0 of the stage, in bytes
+        const uint32_t k0b = (uint32_t)((st.S[1] - hq.left) * SK) * 2u;   // k0 of the stage, in bytes
         const i32x4_t hd = make_desc(X1 + (in ? k0b : 0u), in ? hrec - k0b : 0u);
         const bool tail = in && htailk && hq.left == 1;
 #pragma unroll
