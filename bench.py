@@ -72,6 +72,7 @@ class Case:
         self.copies = copies
         self.oracle_fn = oracle_fn    # () -> None, runs the oracle on the sample
         self.oracle_sample = oracle_sample  # (description, fraction of one step's flops)
+        self.unfused = None           # per weight copy: the same forward as separate launches
 
 
 def _dev(bits, torch, dev, dtype=None):
@@ -116,6 +117,11 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None):
             ws = F.workspace_for(dev, F.fmlp_mlp2_workspace_size(w.M, w.K, w.H, w.N))
             for s in sets:
                 calls.append(F.bind_mlp2(x, s["W1"], s.get("b1"), s["W2"], s.get("b2"), w.act, out=y, workspace=ws))
+            # unfused: the page's launch-per-layer form, here two of our own
+            # Linear launches (GEMM + bias + activation, then GEMM + bias)
+            h_un = torch.empty(w.M, w.H, dtype=torch.bfloat16, device=dev)
+            unfused = [(F.bind_linear(x, s["W1"], s.get("b1"), w.act, out=h_un),
+                        F.bind_linear(h_un, s["W2"], s.get("b2"), "none", out=y)) for s in sets]
             if w.M <= 16:
                 kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             elif max(w.K, w.H, w.N) <= 128:
@@ -133,6 +139,9 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None):
                 c = cache
                 return oracle.mlp2(c["x"][:rows], c["W1"], c.get("b1"), c["W2"], c.get("b2"), w.act)
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
+            case = Case(w, calls, kernel, launches, p, R, fn, sample)
+            case.unfused = unfused
+            return case
         else:
             ws = F.workspace_for(dev, F.fmlp_geglu_workspace_size(w.M, w.K, w.H))
             for s in sets:
@@ -349,7 +358,22 @@ def main(argv=None):
             calls[i % R]()
             ends[i].record(stream)
         torch.cuda.synchronize()
-        per_launch_s = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)])) * 1e-3
+        launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+        per_launch_s = float(np.mean(launch_ms)) * 1e-3
+
+        # the same forward unfused (separate launches), same weight rotation
+        unfused_s = None
+        if case.unfused is not None:
+            for i in range(W):
+                for c in case.unfused[i % R]:
+                    c()
+            torch.cuda.synchronize()
+            u0 = time.perf_counter()
+            for i in range(K):
+                for c in case.unfused[i % R]:
+                    c()
+            torch.cuda.synchronize()
+            unfused_s = (time.perf_counter() - u0) / K
 
     # one step = one forward; value = algorithmic TFLOP/s of the whole job
     value = w.flops / wall_s / 1e12
@@ -372,6 +396,7 @@ def main(argv=None):
     roof["algorithmic_bytes"] = w.bytes
     roof["us_per_step_events"] = round(kernel_s * 1e6, 3)
     roof["us_per_launch_bracketed"] = round(per_launch_s * 1e6, 3)
+    roof["us_per_launch_p10_p50_p90"] = [round(float(v) * 1e3, 3) for v in np.percentile(launch_ms, [10, 50, 90])]
 
     vs = None
     if w.name.startswith("decode_mlp2_4096x4096x4096_M1") and args.act in (None, "gelu_erf"):
@@ -409,6 +434,9 @@ def main(argv=None):
         "us_per_forward": round(wall_s * 1e6, 3),
         "us_per_forward_device": round(dev_s * 1e6, 3),
         "roofline": roof,
+        "unfused": ({"launches": 2, "us_per_forward": round(unfused_s * 1e6, 3),
+                     "form": "fmlp_linear (GEMM + bias + activation), then fmlp_linear (GEMM + bias)"}
+                    if unfused_s is not None else None),
         "baseline_note": ("vs_baseline = value / the page's H100 fused figure (8.1 us, same workload); "
                           "another machine, context only") if vs is not None else None,
     }
