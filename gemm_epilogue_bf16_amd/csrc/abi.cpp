@@ -346,6 +346,14 @@ namespace {
 struct MoeLayout {
   size_t tok_of, scale_of, pos_of, group_off, tile_off, m, ytilde, total;
 };
+// Split-K of the MoE down projection (K = H): two halves when the 64-k stage
+// count is even and long (the tail m-tile of every expert then costs half a
+// pass over K, and the partial round shrinks); the combine adds the halves.
+int moe_down_ksplit(int64_t H) {
+  const int64_t nk = (H + 63) / 64;
+  return (nk % 2 == 0 && nk >= 64) ? 2 : 1;
+}
+
 MoeLayout moe_layout(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k) {
   MoeLayout L;
   const size_t P = (size_t)T * (size_t)top_k;
@@ -356,7 +364,7 @@ MoeLayout moe_layout(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k) 
   L.group_off = o; o += round_up(((size_t)E + 1) * 4, 256);
   L.tile_off = o;  o += round_up(((size_t)E + 1) * 4, 256);
   L.m = o;         o += round_up(P * (size_t)H * 2, 256);
-  L.ytilde = o;    o += round_up(P * (size_t)D * 4, 256);
+  L.ytilde = o;    o += round_up(P * (size_t)D * 4, 256) * (size_t)moe_down_ksplit(H);
   L.total = o;
   return L;
 }
@@ -442,10 +450,14 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
   d.strideB = D * H;
   d.row_scale = r.scale_of;
   d.tiles_m = (int)((P + bm - 1) / bm + E);
+  const int ksplit = moe_down_ksplit(H);
+  const int64_t kstride = (int64_t)(round_up(P * (size_t)D * 4, 256) / 4);   // floats between the parts
+  d.ksplit = ksplit;
+  d.c_kstride = kstride;
   e = launch_gemm(GEMM_OUT_F32_SCALED, false, true, kMoeTile, d, s);
   if (e != hipSuccess) return launched(e, "moe down launch");
 
-  return launched(launch_moe_combine(ytilde, r.pos_of, T, top_k, D, y, s), "moe combine launch");
+  return launched(launch_moe_combine(ytilde, r.pos_of, T, top_k, D, ksplit, kstride, y, s), "moe combine launch");
 }
 
 fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, int64_t D, int32_t E,

@@ -182,7 +182,11 @@ gemm_bf16_kernel(GemmParams p) {
   // round-robin, so at any time the blocks sharing an L2 work on
   // neighbouring tiles.  Grouped mode counts only the tiles that exist.
   const int tiles_m = GROUPED ? p.tile_off[p.groups] : p.tiles_m;
-  const int total = tiles_m * p.tiles_n;
+  // split-K (fp32 output only): every tile appears KSP times, once per part
+  // of the K range, each writing its own output copy
+  constexpr bool SPLITK = OUT == GEMM_OUT_F32_SCALED;
+  const int KSP = SPLITK && p.ksplit > 1 ? p.ksplit : 1;
+  const int total = tiles_m * p.tiles_n * KSP;
   const int G = gridDim.x, bid = blockIdx.x;
   const int xcd = bid % kNumXcd, xj = bid / kNumXcd;
   auto blocks_before = [&](int x) {   // blocks on XCDs 0 .. x-1
@@ -197,12 +201,14 @@ gemm_bf16_kernel(GemmParams p) {
 
   struct Tile {
     int64_t row_begin, row_end, n0;
+    int kp;   // part of the K range (split-K)
     const uint16_t* b0;
     const uint16_t* b1;
   };
   auto tile_at = [&](int i) -> Tile {   // this block's i-th tile
     int tm, tn;
-    grouped_tile(t_lo + xj + i * nbx, tiles_m, p.tiles_n, p.group_m, tm, tn);
+    const int lt = t_lo + xj + i * nbx;
+    grouped_tile(lt / KSP, tiles_m, p.tiles_n, p.group_m, tm, tn);
     Tile t;
     t.b0 = p.B0;
     t.b1 = p.B1;
@@ -221,6 +227,7 @@ gemm_bf16_kernel(GemmParams p) {
       t.row_end = min(t.row_begin + BM, p.M);
     }
     t.n0 = (int64_t)tn * OUT_N;
+    t.kp = lt % KSP;
     return t;
   };
 
@@ -270,9 +277,16 @@ gemm_bf16_kernel(GemmParams p) {
   // sets alternate), so with one k-step per stage an odd count gets one
   // all-zero stage more, which adds nothing.  The block's stream is its
   // tiles' stages back to back: stream stage q is stage q % NS of tile q / NS.
+  // stages per tile: a split-K part's share (the caller splits only when the
+  // stage count divides evenly and stays even for one k-step per stage)
   const int nk = (Kc + BK - 1) / BK;
-  const int NS = KS == 2 ? nk : (nk + 1) & ~1;
-  issue_tile(tile_at(0));
+  const int NS = KSP > 1 ? nk / KSP : (KS == 2 ? nk : (nk + 1) & ~1);
+  int iss_kp = 0;   // K part of the tile whose stages are being issued
+  {
+    const Tile t0 = tile_at(0);
+    issue_tile(t0);
+    iss_kp = t0.kp;
+  }
 
   // How this wave loads the next stage of its stream (stages are issued once
   // each, in order): the lane's chunks are out of range past K (the k tail,
@@ -286,9 +300,14 @@ gemm_bf16_kernel(GemmParams p) {
   };
   auto stage_begin = [&]() -> StageIssue {
     const bool live = iss_t < nmine;   // block-uniform
-    if (live && iss_s == 0 && iss_t > 0) issue_tile(tile_at(iss_t));
-    const int k0 = live ? iss_s * BK : Kc;
-    const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, (uint32_t)(live ? iss_s : 0) * (BK * 2)};
+    if (live && iss_s == 0 && iss_t > 0) {
+      const Tile nt = tile_at(iss_t);
+      issue_tile(nt);
+      iss_kp = nt.kp;
+    }
+    const int ks0 = __builtin_amdgcn_readfirstlane(live ? iss_kp * NS + iss_s : 0);   // stage index within K
+    const int k0 = live ? ks0 * BK : Kc;
+    const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, (uint32_t)ks0 * (BK * 2)};
     if (++iss_s == NS) {
       iss_s = 0;
       ++iss_t;
@@ -413,7 +432,7 @@ gemm_bf16_kernel(GemmParams p) {
           if (!(row_ok && n < N)) continue;
           if constexpr (OUT == GEMM_OUT_F32_SCALED) {
             const float sc = p.row_scale[lrow];
-            float* dst = static_cast<float*>(p.C) + lrow * p.ldc + n;
+            float* dst = static_cast<float*>(p.C) + (int64_t)t.kp * p.c_kstride + lrow * p.ldc + n;
             u32x4_t lo, hi;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -581,7 +600,8 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)((p.N + OUT_N - 1) / OUT_N);
   p.group_m = 4;
-  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;   // grouped: an upper bound
+  const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n *   // grouped: an upper bound
+                        ((OUT == GEMM_OUT_F32_SCALED && p.ksplit > 1) ? p.ksplit : 1);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff || p.cus <= 0) return hipErrorInvalidValue;
   // persistent: as many blocks as fit on the chip at once, each looping over

@@ -34,6 +34,9 @@ struct GemmParams {
   const int32_t* tile_off;   // grouped: [groups+1] prefix of m-tiles per group
   int groups;
   const float* row_scale;    // GEMM_OUT_F32_SCALED: per logical row
+  int ksplit;                // GEMM_OUT_F32_SCALED: K split into this many equal parts (0 or 1: none);
+                             // part j of a tile writes C + j * c_kstride
+  int64_t c_kstride;
   int cus;                   // compute units: the persistent grid's size cap
   // launch geometry, filled by launch_gemm
   int tiles_m, tiles_n, group_m;
@@ -112,7 +115,7 @@ struct MoeRouteOut {
 hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, int top_k, int E,
                             int bm, const MoeRouteOut& o, hipStream_t s);
 hipError_t launch_moe_combine(const float* ytilde, const int32_t* pos_of, int64_t T, int top_k,
-                              int64_t D, uint16_t* y, hipStream_t s);
+                              int64_t D, int ksplit, int64_t kstride, uint16_t* y, hipStream_t s);
 // Router: logits = x[T,D] . Wr[E,D]^T (fp32), top_k ids per token (ties to the
 // lower id) and softmax gate weights over them; logits may be nullptr.
 constexpr int kRouterMaxExperts = 64;

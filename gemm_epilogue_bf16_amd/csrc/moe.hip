@@ -159,7 +159,7 @@ moe_route_kernel(const int32_t* __restrict__ ids, const float* __restrict__ gate
 
 __global__ void __launch_bounds__(256)
 moe_combine_kernel(const float* __restrict__ ytilde, const int32_t* __restrict__ pos_of, int64_t T,
-                   int top_k, int64_t D, uint16_t* __restrict__ y) {
+                   int top_k, int64_t D, int ksplit, int64_t kstride, uint16_t* __restrict__ y) {
   const int64_t chunks = D / 8;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * chunks) return;
@@ -169,12 +169,14 @@ moe_combine_kernel(const float* __restrict__ ytilde, const int32_t* __restrict__
   for (int j = 0; j < top_k; ++j) {
     const int pos = pos_of[t * top_k + j];
     if (pos < 0) continue;
-    const float* src = ytilde + (int64_t)pos * D + d;
-    const u32x4_t lo = ld16(src), hi = ld16(src + 4);
+    for (int kp = 0; kp < ksplit; ++kp) {   // the split-K parts of the down projection, in order
+      const float* src = ytilde + kp * kstride + (int64_t)pos * D + d;
+      const u32x4_t lo = ld16(src), hi = ld16(src + 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      acc[r] += __uint_as_float(lo[r]);
-      acc[4 + r] += __uint_as_float(hi[r]);
+      for (int r = 0; r < 4; ++r) {
+        acc[r] += __uint_as_float(lo[r]);
+        acc[4 + r] += __uint_as_float(hi[r]);
+      }
     }
   }
   st16(y + t * D + d, pack_bf16x8(acc));
@@ -472,13 +474,13 @@ hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, 
 }
 
 hipError_t launch_moe_combine(const float* ytilde, const int32_t* pos_of, int64_t T, int top_k,
-                              int64_t D, uint16_t* y, hipStream_t s) {
+                              int64_t D, int ksplit, int64_t kstride, uint16_t* y, hipStream_t s) {
   const int64_t work = T * (D / 8);
   if (work <= 0) return hipSuccess;
   const int64_t blocks = (work + 255) / 256;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ytilde, pos_of, T,
-                     top_k, D, y);
+                     top_k, D, ksplit, kstride, y);
   return hipGetLastError();
 }
 

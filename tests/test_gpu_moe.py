@@ -36,6 +36,7 @@ def _run(x, ids, gw, Wg, Wu, Wd, ws=None):
 @pytest.mark.parametrize("T,D,H,E,k", [
     (1, 64, 64, 2, 1), (5, 64, 128, 4, 2), (37, 128, 96, 4, 2), (300, 256, 512, 8, 2),
     (129, 64, 200, 3, 3), (1000, 128, 256, 16, 2), (64, 96, 64, 1, 1),
+    (300, 256, 4096, 4, 2), (700, 128, 4160, 8, 2),   # down projection split over K (K tail in the second)
 ])
 def test_moe_random(T, D, H, E, k):
     rng = np.random.default_rng(T * 17 + D + H + E + k)
