@@ -299,6 +299,8 @@ def main(argv=None):
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the unfused comparison (counter runs: one kernel variant only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of this many MiB (for PMC scaling) and exit")
     args = ap.parse_args(argv)
@@ -363,7 +365,7 @@ def main(argv=None):
 
         # the same forward unfused (separate launches), same weight rotation
         unfused_s = None
-        if case.unfused is not None:
+        if case.unfused is not None and not args.no_unfused:
             for i in range(W):
                 for c in case.unfused[i % R]:
                     c()
