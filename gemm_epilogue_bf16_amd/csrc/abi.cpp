@@ -53,6 +53,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if (!aligned16(p)) return fail(FMLP_E_ALIGN, "%s is not 16-byte aligned", #p); \
   } while (0)
 
+// Token-sized buffers (activations, outputs, routes) hold nothing when there
+// are no tokens: NULL is then accepted, a misaligned pointer is still not.
+#define TOKEN_PTR(p, rows)                                                  \
+  do {                                                                      \
+    if ((rows) > 0) REQUIRE_PTR(p);                                         \
+    else if ((p) != nullptr && !aligned16(p))                               \
+      return fail(FMLP_E_ALIGN, "%s is not 16-byte aligned", #p);           \
+  } while (0)
+
 #define OPTIONAL_PTR(p)                                                     \
   do {                                                                      \
     if ((p) != nullptr && !aligned16(p))                                    \
@@ -210,10 +219,10 @@ fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16*
   TRY(check_inner("K", K));
   TRY(check_inner("N", N));
   TRY(check_act(act));
-  REQUIRE_PTR(x);
+  TOKEN_PTR(x, M);
   REQUIRE_PTR(W);
   OPTIONAL_PTR(b);
-  REQUIRE_PTR(y);
+  TOKEN_PTR(y, M);
   if (M == 0) return ok();
   int cus = 0;
   TRY(check_device(&cus));
@@ -250,12 +259,12 @@ fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* 
   TRY(check_inner("H", H));
   TRY(check_inner("N", N));
   TRY(check_act(act));
-  REQUIRE_PTR(x);
+  TOKEN_PTR(x, M);
   REQUIRE_PTR(W1);
   OPTIONAL_PTR(b1);
   REQUIRE_PTR(W2);
   OPTIONAL_PTR(b2);
-  REQUIRE_PTR(y);
+  TOKEN_PTR(y, M);
   const bool small_ok = K <= kSmallMaxDim && H <= kSmallMaxDim && N <= kSmallMaxDim;
   int path = g_path;
   if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : (small_ok ? kPathSmall : kPathGemm);
@@ -310,11 +319,11 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
   TRY(check_inner("D", D));
   TRY(check_inner("H", H));
   TRY(check_act(gate_act, "gate_act"));
-  REQUIRE_PTR(x);
+  TOKEN_PTR(x, M);
   REQUIRE_PTR(Wg);
   REQUIRE_PTR(Wu);
   REQUIRE_PTR(Wd);
-  REQUIRE_PTR(y);
+  TOKEN_PTR(y, M);
   int path = g_path;
   if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : kPathGemm;
   if (path == kPathSmall) return fail(FMLP_E_ARG, "the small fused path is mlp2-only");
@@ -400,13 +409,13 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
     return fail(FMLP_E_SHAPE, "T*top_k=%lld is too large", (long long)T * top_k);
   if (T * D >= (int64_t(1) << 30))
     return fail(FMLP_E_SHAPE, "T*D=%lld must be below 2^30", (long long)(T * D));
-  REQUIRE_PTR(x);
-  if (expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
-  if (gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
+  TOKEN_PTR(x, T);
+  if (T > 0 && expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
+  if (T > 0 && gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
   REQUIRE_PTR(Wg);
   REQUIRE_PTR(Wu);
   REQUIRE_PTR(Wd);
-  REQUIRE_PTR(y);
+  TOKEN_PTR(y, T);
   const MoeLayout L = moe_layout(T, D, H, E, top_k);
   if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
@@ -468,10 +477,10 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
   if (E < 1 || E > kRouterMaxExperts) return fail(FMLP_E_ARG, "E=%d must be in [1, %d]", E, kRouterMaxExperts);
   if (top_k < 1 || top_k > 8 || top_k > E)
     return fail(FMLP_E_ARG, "top_k=%d must be in [1, min(8, E=%d)]", top_k, E);
-  REQUIRE_PTR(x);
+  TOKEN_PTR(x, T);
   REQUIRE_PTR(Wr);
-  if (expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
-  if (gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
+  if (T > 0 && expert_ids == nullptr) return fail(FMLP_E_NULL, "expert_ids is NULL");
+  if (T > 0 && gate_w == nullptr) return fail(FMLP_E_NULL, "gate_w is NULL");
   if ((reinterpret_cast<uintptr_t>(expert_ids) | reinterpret_cast<uintptr_t>(gate_w) |
        reinterpret_cast<uintptr_t>(logits)) & 3u)
     return fail(FMLP_E_ALIGN, "expert_ids, gate_w and logits must be 4-byte aligned");

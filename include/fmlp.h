@@ -22,7 +22,9 @@
  *              HIP device, 16-byte aligned.  The caller owns every buffer,
  *              including outputs and workspaces; the library never allocates
  *              on a call and keeps no pointer after it returns.  Outputs must
- *              not alias inputs.
+ *              not alias inputs.  With no tokens (M or T == 0) the token-sized
+ *              buffers (activations, outputs, routes) may be NULL: nothing is
+ *              read or written; weights are still checked.
  *  Shapes:     every inner dimension (K, H, N, D) must be a positive multiple
  *              of 8 (16-byte rows), the analogue of the "align8" GEMM variants
  *              named on the page above, and below 2^22 (kernels address a

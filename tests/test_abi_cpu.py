@@ -77,6 +77,14 @@ def test_linear_validation(L, args, status, msg):
 
 def test_linear_zero_rows_is_a_noop(L):
     assert L.fmlp_linear(X, W, None, 0, 0, 32, 8, Y, None) == OK
+    # no tokens: activations and outputs may be NULL (empty tensors), weights may not
+    assert L.fmlp_linear(None, W, None, 0, 0, 32, 8, None, None) == OK
+    assert L.fmlp_linear(None, None, None, 0, 0, 32, 8, None, None) == E_NULL
+    assert L.fmlp_linear(X + 2, W, None, 0, 0, 32, 8, Y, None) == E_ALIGN
+    assert L.fmlp_mlp2(None, W, B, W, B, 1, 0, 32, 64, 32, None, WS, 1 << 20, None) == OK
+    assert L.fmlp_glu(None, W, W, W, 4, 0, 64, 128, None, WS, 1 << 20, None) == OK
+    assert L.fmlp_moe_glu(None, None, None, W, W, W, 2, 0, 64, 128, 4, 2, None, WS, 1 << 20, None) == OK
+    assert L.fmlp_moe_route(None, W, 0, 64, 4, 2, None, None, None, None) == OK
 
 
 def test_mlp2_validation(L):
