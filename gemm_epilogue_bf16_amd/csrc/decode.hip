@@ -9,18 +9,21 @@
 //
 // Streaming.  Weights and activation slices go from memory straight into an
 // LDS ring with buffer loads that write LDS (no register staging): one block
-// per CU keeps R - 1 = 3 stages in flight (48 KB of weights per CU), which
-// holds HBM at its streaming rate without a long per-CU request queue.  A stage is
-// 16 weight rows x 512 k (one 1 KB piece per row), or 2 x 16 rows x 256 k when
-// the gate and up weights of GeGLU stream together, plus the same k range of
-// the <= 16 activation rows.  Each 1 KB load instruction writes 1 KB of LDS
-// contiguously, lane by lane; a lane picks the global 16-byte chunk whose
-// swizzled home is its own LDS slot (chunk c of row r lives at c ^ (r & 15)
-// within its group of 16), so loads stay fully coalesced and the MFMA fragment
-// reads of 16 rows are bank-conflict free (for the four 16-lane cycles of a
-// ds_read_b128 on gfx950, as measured: see the GEMM's LDS layout note).  The streaming loop is rolled (a
-// ring slot is a runtime offset), so its few dozen instructions stay in the
-// instruction cache.
+// per CU keeps up to R - 1 = 3 stages in flight, which holds HBM at its
+// streaming rate without a long per-CU request queue.  A stage is 16 weight
+// rows x SK k plus the same k range of the <= 16 activation rows: SK = 1024
+// (2 KB runs per row) up to 4 tokens, 512 at 16 tokens and on the one-token
+// word-flag path (stage_k below).  Gate+up layers stream gate and up rows as
+// alternating stages, or at 16 tokens as paired stages of 16 + 16 rows x 256
+// k that share one activation slice (RingShape::PAIR).  Each 1 KB load
+// instruction writes 1 KB of LDS contiguously, lane by lane; a lane picks the
+// global 16-byte chunk whose swizzled home is its own LDS slot (chunk c of
+// row r lives at c ^ (r & 15) within its group of 16), so loads stay fully
+// coalesced and the MFMA fragment reads of 16 rows are bank-conflict free
+// (for the four 16-lane cycles of a ds_read_b128 on gfx950, as measured: see
+// the GEMM's LDS layout note).  The streaming loop is rolled (a ring slot is
+// a runtime offset), so its few dozen instructions stay in the instruction
+// cache.
 //
 // Roles.  A block has 8 worker waves and 1 control wave.  Every worker issues
 // the same number of loads per stage, so a wave waits only for the stage it
@@ -30,8 +33,9 @@
 // activation rows as the column operand (zero for columns >= M).  The control
 // wave never loads a weight: it sums the 8 partial tiles in a fixed order
 // (bitwise deterministic), applies the epilogue (bias + activation, or
-// gelu_tanh(g) * u) in fp32 with one rounding to bf16, stores the result and,
-// in the two-layer form, publishes h and awaits every block's h.
+// act(g) * u for a gated layer) in fp32 with one rounding to bf16, stores the
+// result and, in the two-layer form, publishes h and awaits every block's h
+// (at one token as epoch-tagged words, below).
 //
 // One stream, two layers.  Layer-2 stages follow layer-1 stages in the same
 // ring, so layer-2 weights are in flight while the block waits for h.  The

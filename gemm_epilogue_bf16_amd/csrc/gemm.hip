@@ -14,7 +14,9 @@
 //                        m = act(g) * u, act = tanh GELU for GeGLU (section
 //                        "The fused Triton kernel": the intermediate never
 //                        makes an HBM round trip) or another gate activation
-//   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights)
+//   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights),
+//                        optionally split over K into parts that each write
+//                        their own copy (summed in order by the caller)
 //
 // Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves
 // (256 x 256 with 8 waves of 128 x 64 for large inputs: two waves per SIMD,

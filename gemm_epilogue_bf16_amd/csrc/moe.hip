@@ -2,8 +2,9 @@
 //
 // An MoE layer routes each token to several experts, each an MLP, and fusing
 // each expert's MLP cuts per-expert overhead (ainews.cool "PyTorch fused MLP
-// efficiency", section "architectural impact").  Here the experts are GeGLU
-// blocks; the routes (top_k expert ids and gate weights per token) are inputs.
+// efficiency", section "architectural impact").  Here the experts are gated
+// blocks (GeGLU, SwiGLU, ...); the routes (top_k expert ids and gate weights
+// per token) are inputs, or come from the router at the end of this file.
 //
 //   route:   (token, slot) pairs are bucketed per expert, stable in pair order,
 //            giving each expert one contiguous segment of rows; the grouped
@@ -13,8 +14,10 @@
 //            thread keeps its contiguous run of pairs in registers and the
 //            experts are counted four at a time per block scan.
 //   combine: y[t] = sum_j ytilde[pos(t, j)] in slot order j = 0, 1, ... in fp32
-//            (the gate weight was applied in the down-projection epilogue), then
-//            one bf16 rounding.  No atomics: bitwise deterministic.
+//            (the gate weight was applied in the down-projection epilogue; with
+//            the down projection split over K, the parts of each row are added
+//            in order), then one bf16 rounding.  No atomics: bitwise
+//            deterministic.
 //   router:  the routes computed on the device: logits = x . Wr^T (fp32), the
 //            top_k experts by logit (a tie goes to the lower expert id), and
 //            gate weights = softmax over the chosen logits.  Bound by reading x
