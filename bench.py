@@ -39,7 +39,7 @@ COLD_BYTES = 1 << 30           # rotate weight copies until this many bytes (4x 
 # the page's fused 4096-wide GELU MLP at batch 1 on H100: 8.1 us (context only)
 PAGE_H100_FUSED_US = 8.1
 
-# the files each kernel is built from (plus the build script, which sets flags)
+# the files each kernel is built from; the hash also covers their compile flags
 KERNEL_SOURCES = {
     "decode_kernel": ["common.h", "kernels.h", "lds_dma.h", "decode.hip"],
     "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
@@ -49,13 +49,15 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_sha(kernel: str) -> str:
+    from gemm_epilogue_bf16_amd import build as _build
+
     h = hashlib.sha256()
     pkg = os.path.join(ROOT, "gemm_epilogue_bf16_amd")
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(pkg, "csrc", f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(pkg, "build.py"), "rb") as fh:
-        h.update(fh.read())
+        h.update(" ".join(_build.EXTRA_FLAGS.get(f, [])).encode())
+    h.update(" ".join(_build.common_flags()).encode())
     return h.hexdigest()[:16]
 
 
