@@ -7,12 +7,17 @@ GPU library never imports it.
 from .fmlp_oracle import (  # noqa: F401
     ACTS,
     activation,
+    dequant_w8,
+    e4m3_decode,
     geglu,
     gelu_erf,
     gelu_tanh,
     glu,
+    glu_w8,
     linear,
+    linear_w8,
     mlp2,
+    mlp2_w8,
     moe_geglu,
     moe_glu,
     moe_router,

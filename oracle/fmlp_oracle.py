@@ -27,6 +27,11 @@ Readings taken where the pages are silent (each is listed in the design doc):
     the pages name three-Linear MLP blocks (LLaMA-3, Mixtral experts) without
     naming their gate activation, so the gated block takes it as an argument.
 
+  * FP8 weights (decode): the pages only note that decode is bound by the
+    weight bytes; the format is the OCP 8-bit floating point E4M3 encoding
+    ("e4m3fn") with one scale per output row, and the functions here
+    dequantise exactly and then call the bf16 definitions above.
+
 Pins: tests/test_oracle_pins.py checks every function here against brute-force
 loops, library routines, closed forms, a printed worked example and invariants.
 """
@@ -51,6 +56,11 @@ __all__ = [
     "moe_glu",
     "route_topk",
     "moe_router",
+    "e4m3_decode",
+    "dequant_w8",
+    "linear_w8",
+    "mlp2_w8",
+    "glu_w8",
 ]
 
 ACTS = ("none", "gelu_erf", "gelu_tanh", "relu", "silu")
@@ -255,3 +265,48 @@ def moe_geglu(x, expert_ids, gate_w, expert_weights):
         # np.add.at: a token routed twice to the same expert adds both terms.
         np.add.at(y, tok, w[tok, slot][:, None] * ye)
     return y
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) weights
+# ---------------------------------------------------------------------------
+def e4m3_decode(codes):
+    """Value of each OCP FP8 E4M3 ("e4m3fn") code, as float64.
+
+    The OCP 8-bit floating point specification (OFP8), format E4M3: bit 7 the
+    sign, bits 6..3 the exponent field e (bias 7), bits 2..0 the mantissa m.
+    e = 0: subnormal, m/8 * 2^(1-7); otherwise (1 + m/8) * 2^(e-7).  There are
+    no infinities; e = 15 with m = 7 is NaN (0x7F and 0xFF), so the largest
+    finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    v = sign * mag
+    return np.where((e == 15) & (c & 7 == 7), np.nan, v)
+
+
+def dequant_w8(Wq, scale):
+    """W[n, k] = scale[n] * e4m3(Wq[n, k]): per-output-row scaled FP8 weights."""
+    Wq = np.asarray(Wq, dtype=np.uint8)
+    scale = _f64(scale)
+    if Wq.ndim != 2 or scale.shape != (Wq.shape[0],):
+        raise ValueError(f"scale shape {scale.shape} does not match weights {Wq.shape}")
+    return scale[:, None] * e4m3_decode(Wq)
+
+
+def linear_w8(x, Wq, scale, b=None, act: str = "none"):
+    """linear() on the dequantised FP8 weights: act(x W^T + b), W = scale * e4m3(Wq)."""
+    return linear(x, dequant_w8(Wq, scale), b, act)
+
+
+def mlp2_w8(x, W1q, s1, b1, W2q, s2, b2, act: str):
+    """mlp2() on dequantised FP8 weights W1 = s1 * e4m3(W1q), W2 = s2 * e4m3(W2q)."""
+    return mlp2(x, dequant_w8(W1q, s1), b1, dequant_w8(W2q, s2), b2, act)
+
+
+def glu_w8(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act: str):
+    """glu() on dequantised FP8 weights (gate, up and down each with row scales)."""
+    return glu(x, dequant_w8(Wgq, sg), dequant_w8(Wuq, su), dequant_w8(Wdq, sd), gate_act)

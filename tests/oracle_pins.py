@@ -443,6 +443,65 @@ def check_moe_invariants(o):
     _close(o.moe_geglu(x, ids, gw, lambda e: experts[e]), y, what="moe callable")
 
 
+def _torch_e4m3(codes):
+    """torch's own float8_e4m3fn conversion of raw codes, to float64."""
+    import torch
+
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    return torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_e4m3_decode(o):
+    codes = np.arange(256, dtype=np.uint8)
+    v = o.e4m3_decode(codes)
+    ref = _torch_e4m3(codes)
+    assert np.array_equal(np.isnan(v), np.isnan(ref)), "e4m3 NaN codes differ from torch's"
+    fin = ~np.isnan(ref)
+    assert np.array_equal(v[fin], ref[fin]), "e4m3 values differ from torch's float8_e4m3fn"
+    assert np.array_equal(np.signbit(v[fin]), np.signbit(ref[fin])), "e4m3 signs of zero differ"
+    # closed forms of the encoding (sign, 4-bit exponent with bias 7, 3-bit mantissa)
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x30: 0.5,
+             0x38: 1.0, 0x39: 1.125, 0x3F: 1.875, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, val in known.items():
+        assert v[c] == val, f"e4m3 code {c:#04x}: {v[c]} != {val}"
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF]) and np.signbit(v[0x80])
+    # positive codes are ordered by value; the sign bit only negates
+    assert np.all(np.diff(v[:0x7F]) > 0), "e4m3 positive codes not increasing"
+    assert np.array_equal(v[0x80:0xFF], -v[0x00:0x7F])
+
+
+def _finite_codes(rng, shape):
+    c = rng.integers(0, 256, size=shape).astype(np.uint8)
+    return np.where((c & 0x7F) == 0x7F, c ^ 0x01, c).astype(np.uint8)   # no NaN codes
+
+
+def check_w8_layers(o):
+    rng = np.random.default_rng(23)
+    M, K, H, N = 3, 16, 7, 5
+    x = _bf16ish(rng, (M, K))
+    q1, q2 = _finite_codes(rng, (H, K)), _finite_codes(rng, (N, H))
+    s1, s2 = rng.random(H) * 0.02 + 0.005, rng.random(N) * 0.02 + 0.005
+    b1, b2 = _bf16ish(rng, (H,)), _bf16ish(rng, (N,))
+    W1 = s1[:, None] * _torch_e4m3(q1)
+    W2 = s2[:, None] * _torch_e4m3(q2)
+    for act in ("none", "gelu_tanh", "silu"):
+        _close(o.linear_w8(x, q1, s1, b1, act), bf_linear(x, W1, b1, act), what=f"linear_w8 {act}")
+    h = bf_linear(x, W1, b1, "gelu_erf")
+    _close(o.mlp2_w8(x, q1, s1, b1, q2, s2, b2, "gelu_erf"), bf_linear(h, W2, b2, "none"),
+           what="mlp2_w8")
+    # gated: D = K, H hidden
+    qg, qu, qd = _finite_codes(rng, (H, K)), _finite_codes(rng, (H, K)), _finite_codes(rng, (K, H))
+    sg, su, sd = (rng.random(H) * 0.02 + 0.005, rng.random(H) * 0.02 + 0.005,
+                  rng.random(K) * 0.02 + 0.005)
+    Wg, Wu, Wd = (sg[:, None] * _torch_e4m3(qg), su[:, None] * _torch_e4m3(qu),
+                  sd[:, None] * _torch_e4m3(qd))
+    for act in ("gelu_tanh", "silu"):
+        _close(o.glu_w8(x, qg, sg, qu, su, qd, sd, act), bf_geglu(x, Wg, Wu, Wd, act),
+               what=f"glu_w8 {act}")
+    # the row scale is linear: doubling it doubles a bias-free output
+    _close(o.linear_w8(x, q1, 2 * s1), 2 * o.linear_w8(x, q1, s1), what="linear_w8 scale")
+
+
 ALL_CHECKS = [
     check_linear_bruteforce,
     check_mlp2_bruteforce,
@@ -459,4 +518,6 @@ ALL_CHECKS = [
     check_fused_equals_unfused,
     check_moe_invariants,
     check_router,
+    check_e4m3_decode,
+    check_w8_layers,
 ]

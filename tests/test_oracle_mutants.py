@@ -147,6 +147,38 @@ def _moe_dedup(x, ids, gw, ew):
     return y
 
 
+_orig_e4m3 = fo.e4m3_decode
+_orig_dequant = fo.dequant_w8
+
+
+def _e4m3_bias8(codes):
+    return _orig_e4m3(codes) * 0.5
+
+
+def _e4m3_subnormal_as_normal(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    v = _orig_e4m3(c)
+    e = (c.astype(np.int64) >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    return np.where(e == 0, sign * (1.0 + m / 8.0) * 2.0 ** -7, v)
+
+
+def _e4m3_no_nan(codes):
+    c = np.asarray(codes, dtype=np.uint8)
+    v = _orig_e4m3(c)
+    return np.where((c & 0x7F) == 0x7F, np.where(c & 0x80, -480.0, 480.0), v)
+
+
+def _dequant_column_scale(Wq, scale):
+    Wq = np.asarray(Wq, dtype=np.uint8)
+    return fo.e4m3_decode(Wq) * np.asarray(scale, float)[None, :]
+
+
+def _dequant_ignores_scale(Wq, scale):
+    return fo.e4m3_decode(np.asarray(Wq, dtype=np.uint8))
+
+
 MUTANTS = {
     "linear_drops_bias": ("linear", _linear_no_bias),
     "linear_subtracts_bias": ("linear", _linear_bias_sub),
@@ -174,6 +206,11 @@ MUTANTS = {
     "router_softmax_over_all_experts": ("route_topk", _route_softmax_over_all),
     "router_ties_to_higher_id": ("route_topk", _route_ties_to_higher),
     "router_picks_smallest": ("route_topk", _route_smallest),
+    "e4m3_exponent_bias_8": ("e4m3_decode", _e4m3_bias8),
+    "e4m3_subnormals_as_normals": ("e4m3_decode", _e4m3_subnormal_as_normal),
+    "e4m3_nan_codes_finite": ("e4m3_decode", _e4m3_no_nan),
+    "w8_scale_per_column": ("dequant_w8", _dequant_column_scale),
+    "w8_scale_ignored": ("dequant_w8", _dequant_ignores_scale),
 }
 
 
