@@ -87,6 +87,20 @@ def uniform_bf16(rng: np.random.Generator, shape, bound: float) -> np.ndarray:
     return rne_bf16(a)
 
 
+def e4m3_weights(rng: np.random.Generator, rows: int, cols: int, bound: float):
+    """FP8 weights for the decode calls: E4M3 codes [rows, cols] (uint8) and one
+    fp32 scale per row.  The codes are torch's float8_e4m3fn rounding of
+    U(-224, 224) draws; scale[n] = bound / 224 * U(0.75, 1.25), so the
+    represented weights scale[n] * e4m3(q) spread over about U(-bound, bound).
+    NaN codes never occur (|draw| < 448)."""
+    import torch
+
+    u = rng.random(size=(rows, cols), dtype=np.float32) * np.float32(448.0) - np.float32(224.0)
+    q = torch.from_numpy(u).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    s = (np.float32(bound / 224.0) * (np.float32(0.75) + np.float32(0.5) * rng.random(rows, dtype=np.float32)))
+    return q, s.astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------

@@ -15,6 +15,9 @@ raises.
     fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd)
                                                     y[t] = sum_j w[t,j] geglu_{e[t,j]}(x[t])
     fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act)
+    fmlp_linear_w8(x, Wq, s, b, act)               the same forms with FP8 E4M3 weights and a
+    fmlp_mlp2_w8(x, W1q, s1, b1, W2q, s2, b2, act)  scale per output row, W = s[:, None] * e4m3(Wq);
+    fmlp_glu_w8(x, Wgq, sg, Wuq, su, Wdq, sd, act)  decode only (at most 16 tokens)
     fmlp_moe_route(x, Wr, top_k)                    -> (expert_ids, gate_w[, logits]): top_k of x Wr^T,
                                                        softmax over the chosen logits
 
@@ -41,6 +44,12 @@ __all__ = [
     "fmlp_moe_geglu",
     "fmlp_moe_glu",
     "fmlp_moe_route",
+    "fmlp_linear_w8",
+    "fmlp_mlp2_w8",
+    "fmlp_glu_w8",
+    "bind_linear_w8",
+    "bind_mlp2_w8",
+    "bind_glu_w8",
     "bind_moe_route",
     "fmlp_mlp2_workspace_size",
     "fmlp_geglu_workspace_size",
@@ -110,6 +119,12 @@ def lib() -> ctypes.CDLL:
         for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
                   "fmlp_moe_route", "fmlp_set_path"):
             getattr(L, f).restype = ctypes.c_int
+        L.fmlp_linear_w8.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
+        L.fmlp_mlp2_w8.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p,
+                                   _sz, _p]
+        L.fmlp_glu_w8.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p, _sz, _p]
+        L.fmlp_w8_workspace_size.argtypes = [_i64, _i64]
+        L.fmlp_w8_workspace_size.restype = _sz
         L.fmlp_set_path.argtypes = [ctypes.c_int]
         L.fmlp_mlp2_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
         L.fmlp_mlp2_workspace_size.restype = _sz
@@ -428,3 +443,112 @@ linear = fmlp_linear
 mlp2 = fmlp_mlp2
 geglu = fmlp_geglu
 moe_geglu = fmlp_moe_geglu
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) weights, decode
+# ---------------------------------------------------------------------------
+def _w8_codes(name: str, t: torch.Tensor) -> torch.Tensor:
+    """FP8 weights as raw E4M3 codes: a uint8 tensor, or a float8_e4m3fn one (same bytes)."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    return _dev_tensor(name, t, torch.uint8)
+
+
+def _w8_scale(name: str, t: torch.Tensor, rows: int) -> torch.Tensor:
+    _dev_tensor(name, t, torch.float32)
+    if t.shape != (rows,):
+        raise ValueError(f"{name} must be [{rows}] fp32, got {tuple(t.shape)}")
+    return t
+
+
+def _linear_w8_call(x, Wq, s, b, act, out):
+    _dev_tensor("x", x)
+    Wq = _w8_codes("Wq", Wq)
+    if b is not None:
+        _dev_tensor("b", b)
+    K = x.shape[-1]
+    N = Wq.shape[0]
+    if Wq.dim() != 2 or Wq.shape[1] != K:
+        raise ValueError(f"Wq must be [N, {K}], got {tuple(Wq.shape)}")
+    _w8_scale("w_scale", s, N)
+    M = x.numel() // K if K else 0
+    y = out if out is not None else torch.empty(*x.shape[:-1], N, dtype=torch.bfloat16, device=x.device)
+    _dev_tensor("out", y)
+    return BoundCall(lib().fmlp_linear_w8, (_ptr(x), _ptr(Wq), _ptr(s), _ptr(b), ACT[act], M, K, N, _ptr(y),
+                                            _stream(x.device)), y, (x, Wq, s, b))
+
+
+def fmlp_linear_w8(x, Wq, w_scale, b=None, act: str = "none", out=None):
+    """y = act(x W^T + b), W = w_scale[:, None] * e4m3(Wq); x [..., K] with at most 16 rows."""
+    with torch.cuda.device(x.device):
+        return _linear_w8_call(x, Wq, w_scale, b, act, out)()
+
+
+def bind_linear_w8(x, Wq, w_scale, b=None, act: str = "none", out=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _linear_w8_call(x, Wq, w_scale, b, act, out)
+
+
+def _mlp2_w8_call(x, W1q, s1, b1, W2q, s2, b2, act, out, workspace):
+    _dev_tensor("x", x)
+    W1q, W2q = _w8_codes("W1q", W1q), _w8_codes("W2q", W2q)
+    for n, t in (("b1", b1), ("b2", b2)):
+        if t is not None:
+            _dev_tensor(n, t)
+    K = x.shape[-1]
+    H, N = W1q.shape[0], W2q.shape[0]
+    if W1q.shape[1] != K or W2q.shape[1] != H:
+        raise ValueError(f"shape mismatch: x[...,{K}] W1q{tuple(W1q.shape)} W2q{tuple(W2q.shape)}")
+    _w8_scale("s1", s1, H)
+    _w8_scale("s2", s2, N)
+    M = x.numel() // K
+    y = out if out is not None else torch.empty(*x.shape[:-1], N, dtype=torch.bfloat16, device=x.device)
+    L = lib()
+    ws = workspace if workspace is not None else workspace_for(x.device, int(L.fmlp_w8_workspace_size(M, H)))
+    return BoundCall(L.fmlp_mlp2_w8, (_ptr(x), _ptr(W1q), _ptr(s1), _ptr(b1), _ptr(W2q), _ptr(s2), _ptr(b2),
+                                      ACT[act], M, K, H, N, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(x.device)), y, (x, W1q, s1, b1, W2q, s2, b2, ws))
+
+
+def fmlp_mlp2_w8(x, W1q, s1, b1, W2q, s2, b2, act: str = "gelu_erf", out=None, workspace=None):
+    """fmlp_mlp2 with FP8 weights W1 = s1 * e4m3(W1q) [H, K], W2 = s2 * e4m3(W2q) [N, H]."""
+    with torch.cuda.device(x.device):
+        return _mlp2_w8_call(x, W1q, s1, b1, W2q, s2, b2, act, out, workspace)()
+
+
+def bind_mlp2_w8(x, W1q, s1, b1, W2q, s2, b2, act: str = "gelu_erf", out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _mlp2_w8_call(x, W1q, s1, b1, W2q, s2, b2, act, out, workspace)
+
+
+def _glu_w8_call(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act, out, workspace):
+    _dev_tensor("x", x)
+    Wgq, Wuq, Wdq = _w8_codes("Wgq", Wgq), _w8_codes("Wuq", Wuq), _w8_codes("Wdq", Wdq)
+    D = x.shape[-1]
+    H = Wgq.shape[0]
+    if Wgq.shape != (H, D) or Wuq.shape != (H, D) or Wdq.shape != (D, H):
+        raise ValueError(f"shape mismatch: x[...,{D}] Wgq{tuple(Wgq.shape)} Wuq{tuple(Wuq.shape)} "
+                         f"Wdq{tuple(Wdq.shape)}")
+    _w8_scale("sg", sg, H)
+    _w8_scale("su", su, H)
+    _w8_scale("sd", sd, D)
+    M = x.numel() // D
+    y = out if out is not None else torch.empty_like(x)
+    L = lib()
+    ws = workspace if workspace is not None else workspace_for(x.device, int(L.fmlp_w8_workspace_size(M, H)))
+    return BoundCall(L.fmlp_glu_w8, (_ptr(x), _ptr(Wgq), _ptr(sg), _ptr(Wuq), _ptr(su), _ptr(Wdq), _ptr(sd),
+                                     ACT[gate_act], M, D, H, _ptr(y), _ptr(ws), 0 if ws is None else ws.numel(),
+                                     _stream(x.device)), y, (x, Wgq, sg, Wuq, su, Wdq, sd, ws))
+
+
+def fmlp_glu_w8(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act: str = "gelu_tanh", out=None, workspace=None):
+    """fmlp_glu with FP8 weights: Wg = sg * e4m3(Wgq), Wu = su * e4m3(Wuq) [H, D], Wd = sd * e4m3(Wdq) [D, H]."""
+    with torch.cuda.device(x.device):
+        return _glu_w8_call(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act, out, workspace)()
+
+
+def bind_glu_w8(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act: str = "gelu_tanh", out=None,
+                workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _glu_w8_call(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act, out, workspace)

@@ -18,15 +18,17 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfmlp.so")
-SOURCES = ["abi.cpp", "gemm.hip", "decode.hip", "small_mlp.hip", "moe.hip"]
+SOURCES = ["abi.cpp", "gemm.hip", "decode.hip", "decode_w8.hip", "small_mlp.hip", "moe.hip"]
 ARCH = "gfx950"
 # Per-source flags.  The GEMM main loop is written in issue order (fragment
 # reads of the next stage ahead of the MFMAs they hide behind); the pre-RA
 # machine scheduler reorders it so that the 256 fp32 accumulators of a wave no
 # longer fit in AGPRs next to the fragments, and the register allocator then
 # shuffles them between register files on every MFMA.  Keeping the source
-# order keeps them in place.
-EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-enable-misched=0"]}
+# order keeps them in place.  The FP8 decode loop is written the same way (one
+# register batch's loads issued before the previous batch is converted).
+EXTRA_FLAGS = {"gemm.hip": ["-mllvm", "-enable-misched=0"],
+               "decode_w8.hip": ["-mllvm", "-enable-misched=0"]}
 
 
 def hipcc() -> str:

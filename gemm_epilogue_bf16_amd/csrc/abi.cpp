@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 
+#include "decode_w8.h"
 #include "kernels.h"
 
 using namespace fmlp;
@@ -188,7 +189,7 @@ hipError_t gemm_glu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t
 
 extern "C" {
 
-int fmlp_version(void) { return 101; }
+int fmlp_version(void) { return 102; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {
@@ -489,6 +490,129 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
   return launched(launch_moe_router(x, Wr, T, (int)D, E, top_k, expert_ids, gate_w, logits,
                                     static_cast<hipStream_t>(stream)),
                   "moe router launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// FP8-weight decode calls
+// ---------------------------------------------------------------------------
+namespace {
+
+#define SCALE_PTR(p)                                                        \
+  do {                                                                      \
+    if ((p) == nullptr) return fail(FMLP_E_NULL, "%s is NULL", #p);         \
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0)                         \
+      return fail(FMLP_E_ALIGN, "%s is not 4-byte aligned", #p);            \
+  } while (0)
+
+fmlp_status check_w8_rows(int64_t M) {
+  TRY(check_rows("M", M));
+  if (M > kDecodeMaxM)
+    return fail(FMLP_E_ARG, "FP8-weight calls take M <= %lld tokens (M=%lld)", (long long)kDecodeMaxM,
+                (long long)M);
+  return FMLP_OK;
+}
+
+fmlp_status check_w8_inner(const char* name, int64_t v) {
+  TRY(check_inner(name, v));
+  if (v % 16 != 0) return fail(FMLP_E_ALIGN, "%s=%lld is not a multiple of 16", name, (long long)v);
+  return FMLP_OK;
+}
+
+fmlp_status check_w8_workspace(int64_t M, int64_t H, void* workspace, size_t workspace_bytes) {
+  const size_t need = (size_t)M * (size_t)H * 2;
+  if (need == 0) return FMLP_OK;
+  if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FMLP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return FMLP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fmlp_w8_workspace_size(int64_t M, int64_t H) {
+  if (M < 0 || H <= 0) return 0;
+  return round_up((size_t)M * (size_t)H * 2, 256);
+}
+
+fmlp_status fmlp_linear_w8(const fmlp_bf16* x, const fmlp_fp8* Wq, const float* w_scale,
+                           const fmlp_bf16* b, int act, int64_t M, int64_t K, int64_t N,
+                           fmlp_bf16* y, fmlp_stream stream) {
+  TRY(check_w8_rows(M));
+  TRY(check_w8_inner("K", K));
+  TRY(check_inner("N", N));
+  TRY(check_act(act));
+  TOKEN_PTR(x, M);
+  REQUIRE_PTR(Wq);
+  SCALE_PTR(w_scale);
+  OPTIONAL_PTR(b);
+  TOKEN_PTR(y, M);
+  if (M == 0) return ok();
+  TRY(check_device());
+  W8Layer L{x, Wq, w_scale, nullptr, nullptr, b, y, K, N, act};
+  return launched(launch_decode_w8(L, (int)M, static_cast<hipStream_t>(stream)),
+                  "linear (fp8 weights) launch");
+}
+
+fmlp_status fmlp_mlp2_w8(const fmlp_bf16* x, const fmlp_fp8* W1q, const float* s1,
+                         const fmlp_bf16* b1, const fmlp_fp8* W2q, const float* s2,
+                         const fmlp_bf16* b2, int act, int64_t M, int64_t K, int64_t H, int64_t N,
+                         fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_w8_rows(M));
+  TRY(check_w8_inner("K", K));
+  TRY(check_w8_inner("H", H));
+  TRY(check_inner("N", N));
+  TRY(check_act(act));
+  TOKEN_PTR(x, M);
+  REQUIRE_PTR(W1q);
+  SCALE_PTR(s1);
+  OPTIONAL_PTR(b1);
+  REQUIRE_PTR(W2q);
+  SCALE_PTR(s2);
+  OPTIONAL_PTR(b2);
+  TOKEN_PTR(y, M);
+  TRY(check_w8_workspace(M, H, workspace, workspace_bytes));
+  if (M == 0) return ok();
+  TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* h = static_cast<uint16_t*>(workspace);
+  W8Layer L1{x, W1q, s1, nullptr, nullptr, b1, h, K, H, act};
+  W8Layer L2{h, W2q, s2, nullptr, nullptr, b2, y, H, N, FMLP_ACT_NONE};
+  hipError_t e = launch_decode_w8(L1, (int)M, s);
+  if (e != hipSuccess) return launched(e, "mlp2 (fp8 weights) layer-1 launch");
+  return launched(launch_decode_w8(L2, (int)M, s), "mlp2 (fp8 weights) layer-2 launch");
+}
+
+fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg,
+                        const fmlp_fp8* Wuq, const float* su, const fmlp_fp8* Wdq, const float* sd,
+                        int gate_act, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
+                        void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_w8_rows(M));
+  TRY(check_w8_inner("D", D));
+  TRY(check_w8_inner("H", H));
+  TRY(check_act(gate_act, "gate_act"));
+  TOKEN_PTR(x, M);
+  REQUIRE_PTR(Wgq);
+  SCALE_PTR(sg);
+  REQUIRE_PTR(Wuq);
+  SCALE_PTR(su);
+  REQUIRE_PTR(Wdq);
+  SCALE_PTR(sd);
+  TOKEN_PTR(y, M);
+  TRY(check_w8_workspace(M, H, workspace, workspace_bytes));
+  if (M == 0) return ok();
+  TRY(check_device());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* m = static_cast<uint16_t*>(workspace);
+  W8Layer L1{x, Wgq, sg, Wuq, su, nullptr, m, D, H, gate_act};
+  W8Layer L2{m, Wdq, sd, nullptr, nullptr, nullptr, y, H, D, FMLP_ACT_NONE};
+  hipError_t e = launch_decode_w8(L1, (int)M, s);
+  if (e != hipSuccess) return launched(e, "glu (fp8 weights) gate+up launch");
+  return launched(launch_decode_w8(L2, (int)M, s), "glu (fp8 weights) down launch");
 }
 
 }  // extern "C"

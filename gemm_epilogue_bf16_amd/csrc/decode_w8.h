@@ -1,0 +1,28 @@
+// Launch interface of the FP8-weight decode kernel (decode_w8.hip).  Internal
+// to the library, like kernels.h; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fmlp {
+
+// One decode layer (M <= 16 tokens) with weights stored as OCP E4M3 codes
+// [N, K] and one fp32 scale per row: W[n, k] = s[n] * e4m3(q[n, k]); K % 16 == 0.
+// With W1 set it is the gate+up layer y = act(s0 * (x q0^T)) * (s1 * (x q1^T)),
+// else y = act(s0 * (x q0^T) + bias).  One launch.
+struct W8Layer {
+  const uint16_t* x;     // [M, K] bf16
+  const uint8_t* W0;     // [N, K] E4M3
+  const float* s0;       // [N]
+  const uint8_t* W1;     // [N, K] E4M3 (gate+up: the up rows) or nullptr
+  const float* s1;       // [N] or nullptr
+  const uint16_t* bias;  // [N] or nullptr (ungated only)
+  uint16_t* y;           // [M, N] bf16
+  int64_t K, N;
+  int act;               // Act; for a gated layer, the gate's activation
+};
+
+hipError_t launch_decode_w8(const W8Layer& L, int M, hipStream_t s);
+
+}  // namespace fmlp

@@ -141,6 +141,52 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
 size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
 
 /*
+ * FP8 weights for decode (1 <= M <= 16 tokens)
+ *
+ * At a few tokens a feed-forward layer is bound by reading its weights once
+ * (ainews.cool "PyTorch fused MLP efficiency", section "architectural impact":
+ * decode is memory-bandwidth bound); one byte per weight halves those bytes.
+ * Each weight matrix is passed as OCP FP8 E4M3 codes (fmlp_fp8: sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F and 0xFF
+ * are NaN; largest finite value 448) with one fp32 scale per output row:
+ *     W[n, k] = scale[n] * e4m3(q[n, k]).
+ * The calls compute exactly what fmlp_linear / fmlp_mlp2 / fmlp_glu compute on
+ * that W: x . e4m3(q)^T is accumulated in fp32 (the codes convert to bf16
+ * exactly), multiplied by the row's scale, then bias and activation; h (or m)
+ * is rounded to bf16 once.  Activations, biases and outputs are bf16 as above.
+ * Besides the shared rules: M <= 16 (larger M is FMLP_E_ARG; M == 0 is a
+ * no-op), every dimension a layer contracts over (K, H, D) a multiple of 16
+ * (FMLP_E_ALIGN; an output-only N keeps the multiple of 8), code arrays
+ * 16-byte aligned, scale arrays [N] fp32, 4-byte aligned and finite.  One
+ * launch per layer: the two-layer forms write h or m [M, H] bf16 to the
+ * workspace (fmlp_w8_workspace_size bytes; no initialisation needed) and
+ * launch twice on the stream.
+ */
+typedef uint8_t fmlp_fp8;  /* OCP FP8 E4M3 ("e4m3fn") code */
+
+/* y[M,N] = act(x[M,K] . (w_scale[N] * e4m3(Wq[N,K]))^T + b[N]); b may be NULL. */
+fmlp_status fmlp_linear_w8(const fmlp_bf16* x, const fmlp_fp8* Wq, const float* w_scale,
+                           const fmlp_bf16* b, int act, int64_t M, int64_t K, int64_t N,
+                           fmlp_bf16* y, fmlp_stream stream);
+
+/* fmlp_mlp2 with W1 = s1 * e4m3(W1q) [H,K] and W2 = s2 * e4m3(W2q) [N,H]. */
+fmlp_status fmlp_mlp2_w8(const fmlp_bf16* x, const fmlp_fp8* W1q, const float* s1,
+                         const fmlp_bf16* b1, const fmlp_fp8* W2q, const float* s2,
+                         const fmlp_bf16* b2, int act, int64_t M, int64_t K, int64_t H, int64_t N,
+                         fmlp_bf16* y, void* workspace, size_t workspace_bytes, fmlp_stream stream);
+
+/* fmlp_glu with Wg = sg * e4m3(Wgq), Wu = su * e4m3(Wuq) [H,D], Wd = sd * e4m3(Wdq) [D,H].
+ * The gate and up rows of each tile are read together and act(g) * u is
+ * applied in registers, as in fmlp_glu. */
+fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg,
+                        const fmlp_fp8* Wuq, const float* su, const fmlp_fp8* Wdq, const float* sd,
+                        int gate_act, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
+                        void* workspace, size_t workspace_bytes, fmlp_stream stream);
+
+/* bytes of workspace the two-layer FP8 calls need: h or m, M x H bf16 */
+size_t fmlp_w8_workspace_size(int64_t M, int64_t H);
+
+/*
  * y[t,:] = sum_{j<top_k} gate_w[t,j] * geglu_{expert_ids[t,j]}(x[t,:])
  *
  * Mixture of GeGLU experts (ainews.cool "PyTorch fused MLP efficiency",

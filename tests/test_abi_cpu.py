@@ -190,3 +190,23 @@ def test_no_fallback_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(F, "library_path", lambda: str(tmp_path / "absent.so"))
     with pytest.raises(F.FmlpError, match="not built"):
         F.lib()
+
+
+def test_w8_validation(L):
+    S = 0x90000   # a 4-byte aligned stand-in for a scale array (never dereferenced)
+    assert L.fmlp_w8_workspace_size(16, 4096) == 16 * 4096 * 2
+    assert L.fmlp_linear_w8(X, W, S, None, 0, 0, 64, 32, Y, None) == OK          # M == 0: no-op
+    assert L.fmlp_linear_w8(X, W, S, None, 0, 17, 64, 32, Y, None) == E_ARG
+    assert "M <= 16" in _err(L)
+    assert L.fmlp_linear_w8(X, W, S, None, 0, 4, 24, 32, Y, None) == E_ALIGN     # K % 16
+    assert "multiple of 16" in _err(L)
+    assert L.fmlp_linear_w8(X, W, S, None, 0, 4, 64, 36, Y, None) == E_ALIGN     # N % 8
+    assert L.fmlp_linear_w8(X, W, None, None, 0, 4, 64, 32, Y, None) == E_NULL
+    assert L.fmlp_linear_w8(X, W, S + 2, None, 0, 4, 64, 32, Y, None) == E_ALIGN
+    assert L.fmlp_linear_w8(X, W, S, None, 9, 4, 64, 32, Y, None) == E_ARG
+    assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 4, 64, 128, 64, Y, None, 0, None) == E_WS
+    assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 4, 64, 128, 64, Y, WS, 4 * 128 * 2 - 2, None) == E_WS
+    assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 0, 64, 128, 64, Y, None, 0, None) == OK
+    assert L.fmlp_glu_w8(X, W, S, W, S, W, None, 2, 4, 64, 128, Y, WS, 1 << 20, None) == E_NULL
+    assert L.fmlp_glu_w8(X, W, S, W, S, W, S, 2, 17, 64, 128, Y, WS, 1 << 20, None) == E_ARG
+    assert L.fmlp_glu_w8(X, W, S, W, S, W, S, 2, 0, 64, 128, Y, WS, 1 << 20, None) == OK
