@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
     "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
     "moe_router_mfma_kernel": ["common.h", "kernels.h", "moe.hip"],
+    "decode_w8_kernel": ["common.h", "decode_w8.h", "decode_w8.hip"],
 }
 
 
@@ -75,6 +76,8 @@ class Case:
         self.oracle_fn = oracle_fn    # () -> None, runs the oracle on the sample
         self.oracle_sample = oracle_sample  # (description, fraction of one step's flops)
         self.unfused = None           # per weight copy: the same forward as separate launches
+        self.bytes = w.bytes          # algorithmic HBM bytes of one forward
+        self.weights = "bf16"
 
 
 def _dev(bits, torch, dev, dtype=None):
@@ -90,7 +93,70 @@ def _copies_for(weight_bytes: int, cold: bool) -> int:
     return max(1, -(-COLD_BYTES // weight_bytes))
 
 
-def setup_case(name: str, cold: bool, dev, path: str, act=None):
+def _setup_w8(w, cold: bool, dev, gate_act):
+    """The decode workloads with FP8 E4M3 weights (one fp32 scale per row):
+    same shapes, activations and biases as the bf16 workload; the weights are
+    drawn as codes by datagen.e4m3_weights with the same bounds."""
+    import torch
+
+    import datagen
+    import gemm_epilogue_bf16_amd as F
+    import oracle
+
+    if w.M > 16 or w.op not in ("mlp2", "geglu"):
+        raise SystemExit("--weights fp8 is for the decode workloads (decode1, decode16, large1, large16)")
+    f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)  # noqa: E731
+    t = datagen.make_inputs(w, seed=0, with_weights=False)
+    if w.op == "mlp2" and w.bias:   # the bf16 workload's biases (same streams)
+        t["b1"] = datagen.uniform_bf16(datagen.rng_for(0, w.family, "b1"), (w.H,), w.b1_bound)
+        t["b2"] = datagen.uniform_bf16(datagen.rng_for(0, w.family, "b2"), (w.N,), w.b2_bound)
+    x = _dev(t["x"], torch, dev)
+    y = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
+    if w.op == "mlp2":
+        shapes = {"W1": (w.H, w.K, w.w1_bound), "W2": (w.N, w.H, w.w2_bound)}
+    else:
+        shapes = {"Wg": (w.H, w.K, w.w1_bound), "Wu": (w.H, w.K, w.w1_bound), "Wd": (w.N, w.H, w.w2_bound)}
+    host = {k: datagen.e4m3_weights(datagen.rng_for(0, w.family, k + "_e4m3"), r, c, bd)
+            for k, (r, c, bd) in shapes.items()}
+    wbytes = sum(r * c + 4 * r for (r, c, _) in shapes.values())
+    if w.op == "mlp2" and w.bias:
+        wbytes += 2 * (w.H + w.N)
+    R = _copies_for(wbytes, cold)
+    sets = []
+    for i in range(R):
+        sets.append({k: (torch.from_numpy(q).to(dev), torch.from_numpy(sc).to(dev)) for k, (q, sc) in host.items()})
+    ws = F.workspace_for(dev, int(F.lib().fmlp_w8_workspace_size(w.M, w.H)))
+    calls = []
+    rows = w.M
+    cache = {}
+    if w.op == "mlp2":
+        b1 = _dev(t["b1"], torch, dev) if "b1" in t else None
+        b2 = _dev(t["b2"], torch, dev) if "b2" in t else None
+        for st in sets:
+            calls.append(F.bind_mlp2_w8(x, *st["W1"], b1, *st["W2"], b2, w.act, out=y, workspace=ws))
+
+        def fn():
+            if not cache:
+                cache.update({k: f64(v) for k, v in t.items()})
+            c = cache
+            return oracle.mlp2_w8(c["x"], *host["W1"], c.get("b1"), *host["W2"], c.get("b2"), w.act)
+    else:
+        act = gate_act or "gelu_tanh"
+        for st in sets:
+            calls.append(F.bind_glu_w8(x, *st["Wg"], *st["Wu"], *st["Wd"], act, out=y, workspace=ws))
+
+        def fn():
+            if not cache:
+                cache.update({k: f64(v) for k, v in t.items()})
+            return oracle.glu_w8(cache["x"], *host["Wg"], *host["Wu"], *host["Wd"], act)
+    case = Case(w, calls, "decode_w8_kernel", 2, "FP8-weight decode (one launch per layer)", R, fn,
+                (f"{rows} of {w.M} token rows, full weights", 1.0))
+    case.bytes = wbytes + 2 * w.M * w.K + 2 * w.M * w.N
+    case.weights = "fp8_e4m3, one fp32 scale per output row"
+    return case
+
+
+def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False):
     import dataclasses
 
     import torch
@@ -107,6 +173,9 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None):
             gate_act = act
     f64 = lambda b: datagen.bf16_to_f32(b).astype(np.float64)  # noqa: E731
     R = _copies_for(w.weight_bytes, cold)
+
+    if w8:
+        return _setup_w8(w, cold, dev, gate_act)
 
     if w.op in ("mlp2", "geglu"):
         t = datagen.make_inputs(w, seed=0)
@@ -299,6 +368,8 @@ def main(argv=None):
                     help="activation of a two-layer MLP, or gate activation of a gated block")
     ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small"])
+    ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
+                    help="fp8: the decode workloads with E4M3 weights and per-row scales")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true",
@@ -323,7 +394,8 @@ def main(argv=None):
         copy_calibration(dev, args.copy_calibration << 20, 10)
         return 0
 
-    case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path, act=args.act)
+    case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path, act=args.act,
+                      w8=args.weights == "fp8")
     w = case.w
     est_us = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
               "large16": 250, "large4096": 4000, "moe": 2500, "router": 8}[args.workload]
@@ -381,12 +453,12 @@ def main(argv=None):
 
     # one step = one forward; value = algorithmic TFLOP/s of the whole job
     value = w.flops / wall_s / 1e12
-    memory_bound = w.flops / w.bytes < 300.0
+    memory_bound = w.flops / case.bytes < 300.0
     # HIP-event time per step over the timed region: for a one-launch step this
     # is the average launch duration (incl. the dispatch gap to the next launch)
     kernel_s = dev_s
     if memory_bound:
-        achieved = w.bytes / kernel_s / 1e9
+        achieved = case.bytes / kernel_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBPS, 4)}
     else:
@@ -397,13 +469,14 @@ def main(argv=None):
     roof["kernel"] = case.kernel
     roof["launches_per_step"] = case.launches
     roof["algorithmic_flops"] = w.flops
-    roof["algorithmic_bytes"] = w.bytes
+    roof["algorithmic_bytes"] = case.bytes
     roof["us_per_step_events"] = round(kernel_s * 1e6, 3)
     roof["us_per_launch_bracketed"] = round(per_launch_s * 1e6, 3)
     roof["us_per_launch_p10_p50_p90"] = [round(float(v) * 1e3, 3) for v in np.percentile(launch_ms, [10, 50, 90])]
 
     vs = None
-    if w.name.startswith("decode_mlp2_4096x4096x4096_M1") and args.act in (None, "gelu_erf"):
+    if (w.name.startswith("decode_mlp2_4096x4096x4096_M1") and args.act in (None, "gelu_erf")
+            and case.weights == "bf16"):
         vs = round(value / (w.flops / (PAGE_H100_FUSED_US * 1e-6) / 1e12), 4)
 
     out = {
@@ -428,9 +501,11 @@ def main(argv=None):
             "act": (w.act if w.op == "mlp2" else "top-k + softmax" if w.op == "route"
                     else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)")),
             "bias": w.bias,
+            "weight_format": case.weights,
             "weights": (f"cold: {case.copies} rotated copies of x ({case.copies * 2 * w.M * w.K / 2**20:.0f} MiB)"
                         if case.copies > 1 and w.op == "route" else
-                        f"cold: {case.copies} rotated copies ({case.copies * w.weight_bytes / 2**20:.0f} MiB)"
+                        f"cold: {case.copies} rotated copies "
+                        f"({case.copies * (case.bytes - 2 * w.M * (w.K + w.N)) / 2**20:.0f} MiB)"
                         if case.copies > 1 else "single copy"),
             "path": case.path,
             "parallelism": "single GPU",
