@@ -58,7 +58,8 @@ def kernel_source_sha(kernel: str) -> str:
         with open(os.path.join(pkg, "csrc", f), "rb") as fh:
             h.update(fh.read())
         h.update(" ".join(_build.EXTRA_FLAGS.get(f, [])).encode())
-    h.update(" ".join(_build.common_flags()).encode())
+    # the include path names the checkout's location, which is not part of the build
+    h.update(" ".join(f.replace(_build.ROOT, "<repo>") for f in _build.common_flags()).encode())
     return h.hexdigest()[:16]
 
 
