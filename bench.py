@@ -6,15 +6,22 @@
 A step is one forward of the workload's whole feed-forward block through the
 C ABI (one fmlp_* call) on synthetic seeded bf16 inputs already resident in
 HBM.  --act replaces the workload's activation (two-layer MLPs) or its gate
-activation (gated blocks and MoE: "silu" runs SwiGLU).  Default workload: the decode two-layer MLP 4096 -> 4096 -> 4096 with exact
-GELU and biases at 1 token (the 4096-wide GELU MLP at batch 1 of ainews.cool
-"PyTorch fused MLP efficiency", section "benchmark data").  Its 64 MiB of
-weights fit the 256 MB Infinity Cache, so by default steps rotate through
-enough weight copies (>= 1 GiB) that every step reads its weights from HBM.
+activation (gated blocks and MoE: "silu" runs SwiGLU).
+
+Default workload (the headline): the GeGLU feed-forward block of dim 8192 and
+hidden 28672 at 4096 tokens, the largest configuration and the one bound by
+the matrix cores (the flattened-token GEMM shapes of "Profiling in PyTorch
+(Part 2)", section "Why are there two kinds of GEMM kernels?").  After it, the
+same JSON line carries a "configs" table with every other workload timed on
+its own: the tiny MLP, the 4096^3 decode MLP at 1 and 16 tokens (the 4096-wide
+GELU MLP at batch 1 of ainews.cool "PyTorch fused MLP efficiency", section
+"benchmark data"), the 768/3072 GeGLU, the large GeGLU at 1 and 16 tokens, the
+MoE and the router.  Weights that would fit the 256 MB Infinity Cache rotate
+through enough copies (>= 1 GiB) that every step reads them from HBM.
 
 Prints ONE JSON line: metric/value (TFLOP/s), ms_per_step, the roofline of the
-dominant kernel (HIP-event time over the timed region) and the fp64 CPU
-oracle timed on a bounded sample on this host's cores.
+dominant kernel (HIP-event time over the timed region), the fp64 CPU oracle
+timed on a bounded sample on this host's cores, and the configs table.
 """
 from __future__ import annotations
 
@@ -86,6 +93,30 @@ def _dev(bits, torch, dev, dtype=None):
     if dtype is None:
         return _t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(_t.bfloat16).to(dev)
     return _t.from_numpy(np.ascontiguousarray(bits)).to(dev)
+
+
+_HOST_CACHE: dict = {}
+_DEV_CACHE: dict = {}
+
+
+def _inputs(w):
+    """datagen.make_inputs, with the weights of a workload family generated
+    once per process (the weights do not depend on the token count)."""
+    import datagen
+
+    key = (w.family, w.op)
+    if key not in _HOST_CACHE:
+        _HOST_CACHE[key] = {k: v for k, v in datagen.make_inputs(w, seed=0).items() if k != "x"}
+    t = dict(_HOST_CACHE[key])
+    t["x"] = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
+    return t
+
+
+def _dev_weights(w, t, torch, dev):
+    key = (w.family, w.op)
+    if key not in _DEV_CACHE:
+        _DEV_CACHE[key] = {k: _dev(v, torch, dev) for k, v in t.items() if k != "x"}
+    return _DEV_CACHE[key]
 
 
 def _copies_for(weight_bytes: int, cold: bool) -> int:
@@ -179,9 +210,9 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
         return _setup_w8(w, cold, dev, gate_act)
 
     if w.op in ("mlp2", "geglu"):
-        t = datagen.make_inputs(w, seed=0)
+        t = _inputs(w)
         x = _dev(t["x"], torch, dev)
-        base = {k: _dev(v, torch, dev) for k, v in t.items() if k != "x"}
+        base = _dev_weights(w, t, torch, dev)
         sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
         y = torch.empty(w.M, w.N, dtype=torch.bfloat16, device=dev)
         calls = []
@@ -213,6 +244,7 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
             case = Case(w, calls, kernel, launches, p, R, fn, sample)
             case.unfused = unfused
+            case.workspace = ws
             return case
         else:
             ws = F.workspace_for(dev, F.fmlp_geglu_workspace_size(w.M, w.K, w.H))
@@ -238,7 +270,9 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
                     return oracle.glu(c["x"][:rows], c["Wg"], c["Wu"], c["Wd"], gate_act)
                 return oracle.geglu(c["x"][:rows], c["Wg"], c["Wu"], c["Wd"])
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
-        return Case(w, calls, kernel, launches, p, R, fn, sample)
+        case = Case(w, calls, kernel, launches, p, R, fn, sample)
+        case.workspace = ws
+        return case
 
     if w.op == "route":
         # x streams once per step; x copies rotate (>= 1 GiB) so it is read from HBM
@@ -357,14 +391,114 @@ def read_traffic(case: Case):
     return d.get("bytes_per_step", d.get("bytes_per_launch"))
 
 
+EST_US = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
+          "large16": 250, "large4096": 4000, "moe": 2500, "router": 8}
+# every workload of the configuration table, in the order the rows are printed
+CONFIG_ROWS = ["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe", "router"]
+
+
+def run_timed(case: Case, K: int, W: int, path: str, stream, torch, F, unfused: bool = True) -> dict:
+    """W untimed steps, then exactly K timed steps bracketed by synchronize on
+    both sides (wall clock and HIP events on the stream the launches go to),
+    then up to 200 single steps each between two events (per-step spread)."""
+    R = len(case.calls)
+    calls = case.calls
+    with F.force_path(path):
+        for i in range(W):
+            calls[i % R]()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(K):
+            calls[i % R]()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        res = {"wall_s": (t1 - t0) / K, "dev_s": ev0.elapsed_time(ev1) * 1e-3 / K}
+
+        n_ev = min(K, 200)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+        torch.cuda.synchronize()
+        for i in range(n_ev):
+            starts[i].record(stream)
+            calls[i % R]()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        res["launch_ms"] = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+
+        res["unfused_s"] = None
+        if unfused and case.unfused is not None:
+            for i in range(W):
+                for c in case.unfused[i % R]:
+                    c()
+            torch.cuda.synchronize()
+            u0 = time.perf_counter()
+            for i in range(K):
+                for c in case.unfused[i % R]:
+                    c()
+            torch.cuda.synchronize()
+            res["unfused_s"] = (time.perf_counter() - u0) / K
+    return res
+
+
+def roofline_of(case: Case, kernel_s: float) -> dict:
+    """Roofline of the step's dominant kernel family: algorithmic work of one
+    step over the step's HIP-event time (for a one-launch step: the average
+    launch duration, including the dispatch gap to the next launch)."""
+    w = case.w
+    if w.flops / case.bytes < 300.0:
+        achieved = case.bytes / kernel_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        achieved = w.flops / kernel_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = read_traffic(case)
+    return roof
+
+
+def decode_timeouts(case: Case, F):
+    """Barrier waits that gave up in the one-launch decode kernel (0 expected)."""
+    ws = getattr(case, "workspace", None)
+    if case.kernel != "decode_kernel" or ws is None:
+        return None
+    return F.barrier_timeouts(ws)
+
+
+def config_row(name: str, dev, stream, torch, F, act=None) -> dict:
+    """One row of the configuration table: the workload's forward timed on its
+    own (cold weights), with its roofline fraction from HIP events."""
+    case = setup_case(name, cold=True, dev=dev, path="auto", act=act)
+    est = EST_US[name]
+    K = max(20, min(2000, int(0.4e6 / est)))
+    r = run_timed(case, K, max(5, K // 10), "auto", stream, torch, F, unfused=False)
+    roof = roofline_of(case, r["dev_s"])
+    w = case.w
+    row = {"workload": w.name, "tokens": w.M, "path": case.path, "launches": case.launches,
+           "kernel": case.kernel, "steps": K,
+           "us_per_forward": round(r["wall_s"] * 1e6, 3),
+           "us_per_forward_device": round(r["dev_s"] * 1e6, 3),
+           "tflops": round(w.flops / r["dev_s"] / 1e12, 2),
+           "roofline": roof}
+    t = decode_timeouts(case, F)
+    if t is not None:
+        row["barrier_timeouts"] = t
+    del case
+    torch.cuda.empty_cache()
+    return row
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode1",
-                    choices=["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe",
-                             "router"])
+    ap.add_argument("--workload", default="large4096", choices=CONFIG_ROWS)
     ap.add_argument("--act", default=None, choices=["none", "gelu_erf", "gelu_tanh", "relu", "silu"],
                     help="activation of a two-layer MLP, or gate activation of a gated block")
     ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
@@ -375,6 +509,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true",
                     help="skip the unfused comparison (counter runs: one kernel variant only)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="only the headline workload (no table of the other workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB",
                     help="only run a plain copy of this many MiB (for PMC scaling) and exit")
     args = ap.parse_args(argv)
@@ -398,75 +534,18 @@ def main(argv=None):
     case = setup_case(args.workload, cold=not args.warm, dev=dev, path=args.path, act=args.act,
                       w8=args.weights == "fp8")
     w = case.w
-    est_us = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
-              "large16": 250, "large4096": 4000, "moe": 2500, "router": 8}[args.workload]
-    K = args.steps if args.steps is not None else max(20, int(1.5e6 / est_us))
+    K = args.steps if args.steps is not None else max(20, int(1.5e6 / EST_US[args.workload]))
     W = args.warmup if args.warmup is not None else max(5, K // 10)
-    R = len(case.calls)
-    calls = case.calls
     stream = torch.cuda.current_stream(dev)
-
-    with F.force_path(args.path):
-        for i in range(W):
-            calls[i % R]()
-        torch.cuda.synchronize()
-
-        # ---- timed region: K steps, synchronize on both sides -------------
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(K):
-            calls[i % R]()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        wall_s = (t1 - t0) / K
-        dev_s = ev0.elapsed_time(ev1) * 1e-3 / K
-
-        # ---- per-launch events (same stream) for the kernel duration ------
-        n_ev = min(K, 200)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-        torch.cuda.synchronize()
-        for i in range(n_ev):
-            starts[i].record(stream)
-            calls[i % R]()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        launch_ms = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-        per_launch_s = float(np.mean(launch_ms)) * 1e-3
-
-        # the same forward unfused (separate launches), same weight rotation
-        unfused_s = None
-        if case.unfused is not None and not args.no_unfused:
-            for i in range(W):
-                for c in case.unfused[i % R]:
-                    c()
-            torch.cuda.synchronize()
-            u0 = time.perf_counter()
-            for i in range(K):
-                for c in case.unfused[i % R]:
-                    c()
-            torch.cuda.synchronize()
-            unfused_s = (time.perf_counter() - u0) / K
+    print(f"bench: {w.name}, {K} timed steps after {W} warm-up steps", file=sys.stderr, flush=True)
+    r = run_timed(case, K, W, args.path, stream, torch, F, unfused=not args.no_unfused)
+    wall_s, dev_s, launch_ms, unfused_s = r["wall_s"], r["dev_s"], r["launch_ms"], r["unfused_s"]
+    per_launch_s = float(np.mean(launch_ms)) * 1e-3
 
     # one step = one forward; value = algorithmic TFLOP/s of the whole job
     value = w.flops / wall_s / 1e12
-    memory_bound = w.flops / case.bytes < 300.0
-    # HIP-event time per step over the timed region: for a one-launch step this
-    # is the average launch duration (incl. the dispatch gap to the next launch)
     kernel_s = dev_s
-    if memory_bound:
-        achieved = case.bytes / kernel_s / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBPS, 4)}
-    else:
-        achieved = w.flops / kernel_s / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    roof["traffic"] = read_traffic(case)
+    roof = roofline_of(case, kernel_s)
     roof["kernel"] = case.kernel
     roof["launches_per_step"] = case.launches
     roof["algorithmic_flops"] = w.flops
@@ -474,6 +553,7 @@ def main(argv=None):
     roof["us_per_step_events"] = round(kernel_s * 1e6, 3)
     roof["us_per_launch_bracketed"] = round(per_launch_s * 1e6, 3)
     roof["us_per_launch_p10_p50_p90"] = [round(float(v) * 1e3, 3) for v in np.percentile(launch_ms, [10, 50, 90])]
+    timeouts = decode_timeouts(case, F)
 
     vs = None
     if (w.name.startswith("decode_mlp2_4096x4096x4096_M1") and args.act in (None, "gelu_erf")
@@ -520,8 +600,20 @@ def main(argv=None):
         "baseline_note": ("vs_baseline = value / the page's H100 fused figure (8.1 us, same workload); "
                           "another machine, context only") if vs is not None else None,
     }
+    if timeouts is not None:
+        out["barrier_timeouts"] = timeouts
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = time_oracle(case, args.cpu_seconds)
+    if not args.no_configs and args.weights == "bf16" and args.act is None and args.path == "auto":
+        # the other workloads, each timed on its own after the headline
+        del case
+        rows = []
+        for name in CONFIG_ROWS:
+            if name == args.workload:
+                continue
+            print(f"bench: config row {name}", file=sys.stderr, flush=True)
+            rows.append(config_row(name, dev, stream, torch, F))
+        out["configs"] = rows
     print(json.dumps(out), flush=True)
     return 0
 

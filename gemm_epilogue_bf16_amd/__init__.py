@@ -57,6 +57,7 @@ __all__ = [
     "force_path",
     "workspace_for",
     "barrier_timeouts",
+    "decode_generation",
     "moe_invalid_ids",
     "BoundCall",
     "bind_mlp2",
@@ -136,6 +137,9 @@ def lib() -> ctypes.CDLL:
         L.fmlp_moe_workspace_size.restype = _sz
         L.fmlp_moe_error_offset.argtypes = []
         L.fmlp_moe_error_offset.restype = _sz
+        for f in ("fmlp_decode_timeout_offset", "fmlp_decode_generation_offset"):
+            getattr(L, f).argtypes = []
+            getattr(L, f).restype = _sz
         L.fmlp_status_string.argtypes = [ctypes.c_int]
         L.fmlp_status_string.restype = ctypes.c_char_p
         L.fmlp_last_error.argtypes = []
@@ -428,9 +432,19 @@ def bind_moe_route(x, Wr, top_k: int, with_logits: bool = False, out=None) -> Bo
 # ---------------------------------------------------------------------------
 # diagnostics (read after a sync)
 # ---------------------------------------------------------------------------
+def _ws_word(workspace: torch.Tensor, off: int) -> int:
+    return int(workspace[off:off + 4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
 def barrier_timeouts(workspace: torch.Tensor) -> int:
-    """Times the persistent decode kernel's device-wide barrier gave up waiting."""
-    return int(workspace[8:12].view(torch.int32).item())
+    """Times the persistent decode kernel's device-wide barrier gave up waiting
+    (cumulative over the calls on this workspace)."""
+    return _ws_word(workspace, int(lib().fmlp_decode_timeout_offset()))
+
+
+def decode_generation(workspace: torch.Tensor) -> int:
+    """The workspace's decode generation: advanced by one per one-launch decode call."""
+    return _ws_word(workspace, int(lib().fmlp_decode_generation_offset()))
 
 
 def moe_invalid_ids(workspace: torch.Tensor) -> int:

@@ -388,6 +388,9 @@ size_t fmlp_moe_workspace_size(int64_t T, int64_t D, int64_t H, int32_t E, int32
 
 size_t fmlp_moe_error_offset(void) { return 16; }
 
+size_t fmlp_decode_timeout_offset(void) { return (size_t)kSyncTimeoutWord * 4; }
+size_t fmlp_decode_generation_offset(void) { return (size_t)kSyncGenWord * 4; }
+
 fmlp_status fmlp_moe_geglu(const fmlp_bf16* x, const int32_t* expert_ids, const float* gate_w,
                            const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd, int64_t T,
                            int64_t D, int64_t H, int32_t E, int32_t top_k, fmlp_bf16* y,
@@ -497,6 +500,11 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
 // ---------------------------------------------------------------------------
 // FP8-weight decode calls
 // ---------------------------------------------------------------------------
+extern "C" size_t fmlp_w8_workspace_size(int64_t M, int64_t H) {
+  if (M <= 0 || H <= 0) return 0;
+  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+}
+
 namespace {
 
 #define SCALE_PTR(p)                                                        \
@@ -520,8 +528,11 @@ fmlp_status check_w8_inner(const char* name, int64_t v) {
   return FMLP_OK;
 }
 
+// The two-layer FP8 calls keep h (or m) after the same 8 KB header as the
+// bf16 calls, which they never touch: one workspace can serve both kinds of
+// call in any order without disturbing the decode barrier words.
 fmlp_status check_w8_workspace(int64_t M, int64_t H, void* workspace, size_t workspace_bytes) {
-  const size_t need = (size_t)M * (size_t)H * 2;
+  const size_t need = fmlp_w8_workspace_size(M, H);
   if (need == 0) return FMLP_OK;
   if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
   if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
@@ -534,10 +545,6 @@ fmlp_status check_w8_workspace(int64_t M, int64_t H, void* workspace, size_t wor
 
 extern "C" {
 
-size_t fmlp_w8_workspace_size(int64_t M, int64_t H) {
-  if (M < 0 || H <= 0) return 0;
-  return round_up((size_t)M * (size_t)H * 2, 256);
-}
 
 fmlp_status fmlp_linear_w8(const fmlp_bf16* x, const fmlp_fp8* Wq, const float* w_scale,
                            const fmlp_bf16* b, int act, int64_t M, int64_t K, int64_t N,
@@ -579,7 +586,7 @@ fmlp_status fmlp_mlp2_w8(const fmlp_bf16* x, const fmlp_fp8* W1q, const float* s
   if (M == 0) return ok();
   TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* h = static_cast<uint16_t*>(workspace);
+  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
   W8Layer L1{x, W1q, s1, nullptr, nullptr, b1, h, K, H, act};
   W8Layer L2{h, W2q, s2, nullptr, nullptr, b2, y, H, N, FMLP_ACT_NONE};
   hipError_t e = launch_decode_w8(L1, (int)M, s);
@@ -607,7 +614,7 @@ fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg
   if (M == 0) return ok();
   TRY(check_device());
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* m = static_cast<uint16_t*>(workspace);
+  uint16_t* m = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
   W8Layer L1{x, Wgq, sg, Wuq, su, nullptr, m, D, H, gate_act};
   W8Layer L2{m, Wdq, sd, nullptr, nullptr, nullptr, y, H, D, FMLP_ACT_NONE};
   hipError_t e = launch_decode_w8(L1, (int)M, s);

@@ -51,7 +51,11 @@
 // masked by buffer offsets (loads past the end return 0 without a memory
 // access), never by a branch around a load; fragments past K are also zeroed
 // at the read, so stale LDS never meets the MFMA.
+#include <unistd.h>
+
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "common.h"
@@ -155,6 +159,13 @@ __device__ __forceinline__ T in_sgpr(T v) {
 // position of 16-byte chunk c of stage row r inside the row (an involution)
 __device__ __forceinline__ int swz(int c, int r) { return (c & ~15) | ((c ^ r) & 15); }
 
+// The epoch of a call: generation g (odd multiplier: distinct g give distinct
+// values) plus the launch's salt; never 0, the value of a zeroed flag.
+__device__ __forceinline__ uint32_t epoch_of(uint32_t g, uint32_t salt) {
+  const uint32_t e = g * 0x9E3779B1u + salt;
+  return e ? e : 1u;
+}
+
 struct Stream {
   int nt[2];        // tiles this block owns in each layer
   int S[2];         // stages per tile in each layer
@@ -228,7 +239,7 @@ __device__ __forceinline__ Seg seg_first(const Stream& st) {
 
 template <bool DUAL1, bool TWO, int MC, bool LL>
 __global__ void __launch_bounds__(kThreads)
-decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
+decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync, uint32_t salt) {
   static_assert(!LL || (TWO && MC == 1), "word-flag publish: two layers, one token");
   using RS = RingShape<MC, DUAL1, LL>;
   constexpr int R = RS::R, XI = RS::XI;
@@ -251,8 +262,15 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
   const Stream st = make_stream<DUAL1, TWO, SK, PAIR>(L1, L2);
   const int G = (int)gridDim.x, blk = (int)blockIdx.x;
 
-  uint32_t target = 0;
-  if (TWO) target = ld_coherent(sync + kSyncGenWord) + 1u;
+  // This call's epoch (what its h words and flags carry): the generation it
+  // advances the workspace to, mixed with the launch's salt, so that neither a
+  // header zeroed again nor a replay of the same launch repeats an epoch that
+  // words or flags of an earlier call still hold.
+  uint32_t gen_next = 0, target = 0;
+  if (TWO) {
+    gen_next = ld_coherent(sync + kSyncGenWord) + 1u;
+    target = epoch_of(gen_next, salt);
+  }
 
   if (wave < kWorkers) {
     // ======================= worker waves =====================================
@@ -615,7 +633,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
+    if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, gen_next);
   };
   // LL: read every word of h with device-coherent loads until each carries
   // this call's epoch (one pass when everything has landed: all of a lane's
@@ -656,7 +674,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync) {
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, target);
+      if (blk == 0 && lane == 0) st_coherent(sync + kSyncGenWord, gen_next);
     }
   };
   // the control wave meets the workers at each of their barriers
@@ -730,6 +748,40 @@ Occ occ() {
   return o;
 }
 
+// A salt per launch: a process-wide counter through a bijective mix, seeded
+// from the clock and the process id, so every launch of this process gets a
+// different value (for 2^32 launches) and other processes most likely others.
+uint32_t mix32(uint32_t v) {
+  v ^= v >> 16;
+  v *= 0x85EBCA6Bu;
+  v ^= v >> 13;
+  v *= 0xC2B2AE35u;
+  v ^= v >> 16;
+  return v;
+}
+uint32_t next_salt() {
+  static const uint32_t seed = mix32((uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
+                                     (uint32_t)getpid() * 0x9E3779B1u);
+  static std::atomic<uint32_t> counter{0};
+  return mix32(seed ^ counter.fetch_add(1u, std::memory_order_relaxed) * 0x27D4EB2Du);
+}
+
+// One kernel variant on `grid` blocks.  The two-layer form waits for every
+// block at its barrier; the grid is capped at one block per CU (the LDS ring
+// admits one), so on an otherwise idle device every block is resident.  A
+// cooperative launch would also refuse a grid that cannot be co-resident, but
+// it was measured to add about 18 us to every call (the 4096^3 two-layer
+// forward at one token: 36 us against 18 us), twice the whole forward's
+// roofline time; the plain launch is kept, and a barrier wait that gives up is
+// counted in the workspace header for the caller to check.
+template <bool DUAL1, bool TWO, int MC, bool LL>
+hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
+                          hipStream_t s) {
+  const uint32_t salt = TWO ? next_salt() : 0u;
+  hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync, salt);
+  return hipGetLastError();
+}
+
 // activation-row class of M: the rows an LDS stage holds
 template <bool DUAL1, bool TWO>
 hipError_t launch_mc(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
@@ -737,15 +789,10 @@ hipError_t launch_mc(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, in
   // word-flag publish of h: one token, h fits h_lds, and every block owns a
   // layer-1 tile (so every block writes words before block 0 can see them all)
   const bool ll = TWO && M == 1 && L2.K <= kLLMaxH && (int64_t)grid <= (L1.N + 15) / 16;
-  if (M <= 1 && ll)
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1, TWO>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  else if (M <= 1)
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 1, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  else if (M <= 4)
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 4, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  else
-    hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, 16, false>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync);
-  return hipGetLastError();
+  if (M <= 1 && ll) return launch_variant<DUAL1, TWO, 1, TWO>(grid, L1, L2, M, sync, s);
+  if (M <= 1) return launch_variant<DUAL1, TWO, 1, false>(grid, L1, L2, M, sync, s);
+  if (M <= 4) return launch_variant<DUAL1, TWO, 4, false>(grid, L1, L2, M, sync, s);
+  return launch_variant<DUAL1, TWO, 16, false>(grid, L1, L2, M, sync, s);
 }
 
 }  // namespace

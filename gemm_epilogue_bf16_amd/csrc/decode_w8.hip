@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   const uint32_t wrow = (uint32_t)(r * K + g * 16);
   const uint32_t xrow = (uint32_t)(r * K * 2 + g * 32);
   const int xstride = 2 * K + 16;
-  const uint8_t* xl = xs + r * xstride + g * 32;
+  // lanes of a token past M read token 0's row (inside xs) and drop the value
+  const uint8_t* xl = xs + (r < M ? r : 0) * xstride + g * 32;
 
   const int chunks = (K + 63) / 64;
   const int nb = (chunks + kW8Waves * U - 1) / (kW8Waves * U);

@@ -97,9 +97,22 @@ fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16*
  * Paths (chosen from the shape): M <= 16: one persistent decode launch;
  * K, H, N <= 128: one fused small-MLP launch; otherwise two GEMM launches with
  * h in the workspace.  workspace must hold fmlp_mlp2_workspace_size(M,K,H,N)
- * bytes (it may be NULL when that size is 0) and its first 8192 bytes (the
- * decode kernel's barrier words) must be zero before the first call that uses
- * it; later calls keep them consistent, whatever their shapes.
+ * bytes (it may be NULL when that size is 0).  Its first 8192 bytes are the
+ * decode kernel's header: 32-bit word 0 (fmlp_decode_generation_offset) is a
+ * generation that each one-launch decode call advances by exactly one, word 2
+ * (fmlp_decode_timeout_offset) counts device-wide barrier waits that gave up,
+ * and the rest holds per-block arrival flags.  Zero the header once before the
+ * first call (the timeout count starts there).  After that nothing else is
+ * required: every launch tags what it publishes (h words, flags) with an epoch
+ * mixed from the next generation and a per-launch salt, so neither a header
+ * zeroed again between calls, nor recycled memory, nor words left by an
+ * earlier call are ever taken for this call's h.  The same workspace may be
+ * shared, in stream order, by every call of this header (the FP8 calls and
+ * fmlp_geglu/fmlp_glu keep their data after the 8192-byte header too).
+ * The one-launch decode form needs every block resident at once: its grid is
+ * at most one block per CU, so on a device not shared with long-running work
+ * it always is.  A barrier wait that gives up (after 2^20 polls of the flags)
+ * leaves y wrong; it is counted in word 2, which a caller checks after a sync.
  */
 fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* b1,
                       const fmlp_bf16* W2, const fmlp_bf16* b2, int act,
@@ -159,8 +172,10 @@ size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
  * (FMLP_E_ALIGN; an output-only N keeps the multiple of 8), code arrays
  * 16-byte aligned, scale arrays [N] fp32, 4-byte aligned and finite.  One
  * launch per layer: the two-layer forms write h or m [M, H] bf16 to the
- * workspace (fmlp_w8_workspace_size bytes; no initialisation needed) and
- * launch twice on the stream.
+ * workspace after its first 8192 bytes, which they never touch (so one
+ * workspace can also serve fmlp_mlp2 / fmlp_glu calls in between);
+ * fmlp_w8_workspace_size bytes, no initialisation needed; two launches on the
+ * stream.
  */
 typedef uint8_t fmlp_fp8;  /* OCP FP8 E4M3 ("e4m3fn") code */
 
@@ -183,7 +198,8 @@ fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg
                         int gate_act, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
                         void* workspace, size_t workspace_bytes, fmlp_stream stream);
 
-/* bytes of workspace the two-layer FP8 calls need: h or m, M x H bf16 */
+/* bytes of workspace the two-layer FP8 calls need: an untouched 8192-byte
+ * header, then h or m, M x H bf16 (0 for M == 0) */
 size_t fmlp_w8_workspace_size(int64_t M, int64_t H);
 
 /*
@@ -238,6 +254,14 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
 /* Byte offset, inside the MoE workspace, of the int32 count of invalid expert ids
  * seen by the last call (read it after a stream sync). */
 size_t fmlp_moe_error_offset(void);
+
+/* Byte offsets, inside an fmlp_mlp2 / fmlp_geglu / fmlp_glu workspace, of the
+ * one-launch decode kernel's uint32 words: the count of device-wide barrier
+ * waits that gave up (cumulative; nonzero means a decode result written since
+ * it was last seen is wrong), and the generation (advanced by one per
+ * one-launch decode call).  Read them after a stream sync. */
+size_t fmlp_decode_timeout_offset(void);
+size_t fmlp_decode_generation_offset(void);
 
 /*
  * Path override for tests and benchmarks (thread-local; applies to the calling

@@ -194,7 +194,9 @@ def test_no_fallback_without_library(tmp_path, monkeypatch):
 
 def test_w8_validation(L):
     S = 0x90000   # a 4-byte aligned stand-in for a scale array (never dereferenced)
-    assert L.fmlp_w8_workspace_size(16, 4096) == 16 * 4096 * 2
+    # h after the untouched 8 KB decode header (a workspace shared with the bf16 calls)
+    assert L.fmlp_w8_workspace_size(16, 4096) == 8192 + 16 * 4096 * 2
+    assert L.fmlp_w8_workspace_size(0, 4096) == 0
     assert L.fmlp_linear_w8(X, W, S, None, 0, 0, 64, 32, Y, None) == OK          # M == 0: no-op
     assert L.fmlp_linear_w8(X, W, S, None, 0, 17, 64, 32, Y, None) == E_ARG
     assert "M <= 16" in _err(L)
@@ -205,8 +207,46 @@ def test_w8_validation(L):
     assert L.fmlp_linear_w8(X, W, S + 2, None, 0, 4, 64, 32, Y, None) == E_ALIGN
     assert L.fmlp_linear_w8(X, W, S, None, 9, 4, 64, 32, Y, None) == E_ARG
     assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 4, 64, 128, 64, Y, None, 0, None) == E_WS
-    assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 4, 64, 128, 64, Y, WS, 4 * 128 * 2 - 2, None) == E_WS
+    assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 4, 64, 128, 64, Y, WS, 4 * 128 * 2 + 8190, None) == E_WS
     assert L.fmlp_mlp2_w8(X, W, S, None, W, S, None, 1, 0, 64, 128, 64, Y, None, 0, None) == OK
     assert L.fmlp_glu_w8(X, W, S, W, S, W, None, 2, 4, 64, 128, Y, WS, 1 << 20, None) == E_NULL
     assert L.fmlp_glu_w8(X, W, S, W, S, W, S, 2, 17, 64, 128, Y, WS, 1 << 20, None) == E_ARG
     assert L.fmlp_glu_w8(X, W, S, W, S, W, S, 2, 0, 64, 128, Y, WS, 1 << 20, None) == OK
+
+
+def test_decode_header_words(L):
+    """The decode kernel's generation and timeout words sit inside the 8 KB
+    header, apart from each other and from the MoE error word."""
+    gen, tmo, moe = L.fmlp_decode_generation_offset(), L.fmlp_decode_timeout_offset(), L.fmlp_moe_error_offset()
+    assert len({gen, tmo, moe}) == 3
+    assert all(o % 4 == 0 and o + 4 <= 8192 for o in (gen, tmo, moe))
+    # the FP8 and bf16 two-layer calls share a workspace: both keep data after the header
+    assert L.fmlp_mlp2_workspace_size(16, 4096, 4096, 4096) >= 8192 + 16 * 4096 * 2
+    assert L.fmlp_w8_workspace_size(16, 4096) >= 8192 + 16 * 4096 * 2
+
+
+def test_abi_under_host_sanitizers(tmp_path):
+    """abi.cpp built for the host alone with AddressSanitizer and
+    UndefinedBehaviorSanitizer (kernel launchers stubbed out), driven through
+    every entry point with rejected and no-op arguments: every status is the
+    documented one and neither sanitizer reports anything."""
+    import shutil
+    import subprocess
+
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists("/opt/rocm/lib/libamdhip64.so"):
+        pytest.skip("needs g++ and the ROCm runtime library")
+    here = os.path.join(ROOT, "tests", "abi_host")
+    exe = str(tmp_path / "abi_san")
+    cmd = [gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+           os.path.join(ROOT, "gemm_epilogue_bf16_amd", "csrc", "abi.cpp"),
+           os.path.join(here, "stub_launch.cpp"), os.path.join(here, "driver.cpp"),
+           "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert "ALL OK" in r.stdout
+    assert "runtime error" not in r.stderr and "AddressSanitizer" not in r.stderr

@@ -29,3 +29,20 @@ def test_router_counts():
     w = datagen.workload("router")
     assert w.flops == 2 * 4096 * 4096 * 8
     assert w.bytes == 2 * 4096 * 4096 + 2 * 8 * 4096 + 4096 * 2 * 8
+
+
+def test_default_headline_is_the_largest_config():
+    """With no flags the headline is the 8192/28672 GeGLU at 4096 tokens (the
+    largest single-GPU workload, bound by the matrix cores), and the configs
+    table names every other workload."""
+    import importlib.util
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="large4096"' in src
+    big = max(datagen.WORKLOADS.values(), key=lambda w: w.flops if w.op == "geglu" else 0)
+    assert big.name == datagen.workload("large4096").name
+    assert set(bench.CONFIG_ROWS) == set(datagen.WORKLOADS)
+    assert set(bench.EST_US) == set(datagen.WORKLOADS)

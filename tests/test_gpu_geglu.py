@@ -65,39 +65,64 @@ def test_geglu768_full():
     assert_parity(y, ref, w.name)
 
 
+class _LargeWeights(dict):
+    """The 8192/28672 weights as bits, on the device, and (once) in fp64."""
+
+    def f64(self):
+        if "_f64" not in self:
+            self["_f64"] = tuple(f64_of_bits(self["bits"][k]) for k in ("Wg", "Wu", "Wd"))
+        return self["_f64"]
+
+
 @pytest.fixture(scope="module")
 def large_weights():
     w = datagen.workload("large1")
     t = datagen.make_inputs(w, seed=0)
-    return t, {k: to_dev(t[k]) for k in ("Wg", "Wu", "Wd")}
+    lw = _LargeWeights(bits=t)
+    return t, {k: to_dev(t[k]) for k in ("Wg", "Wu", "Wd")}, lw
 
 
 @pytest.mark.slow
 @pytest.mark.parametrize("T", [1, 16])
 def test_large_decode_full(large_weights, T):
-    t, dw = large_weights
+    t, dw, lw = large_weights
     w = datagen.workload(f"large{T}")
     x = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
     ws = F.workspace_for(DEV, F.fmlp_geglu_workspace_size(T, w.K, w.H))
     print(f"case {w.name} full", flush=True)
     y = _run(to_dev(x), dw["Wg"], dw["Wu"], dw["Wd"], ws=ws)
-    ref = oracle.geglu(f64_of_bits(x), *(f64_of_bits(t[k]) for k in ("Wg", "Wu", "Wd")))
+    ref = oracle.geglu(f64_of_bits(x), *lw.f64())
     assert_parity(y, ref, w.name)
     assert F.barrier_timeouts(ws) == 0
 
 
+def prefill_sample_rows(T: int, tile: int = 256, frag: int = 16) -> np.ndarray:
+    """One row from every 16-row fragment group of every 256-row tile of T
+    rows, its offset inside the group cycling through all 16 positions (so
+    every fragment row of the MFMA layout and every m-tile is compared), plus
+    the first and last rows."""
+    groups = np.arange((T + frag - 1) // frag)
+    rows = groups * frag + (groups * 5 + (groups // (tile // frag))) % frag
+    rows = np.concatenate([[0, T - 1], rows[rows < T]])
+    return np.unique(rows)
+
+
 @pytest.mark.slow
 def test_large_prefill_sampled_rows(large_weights):
-    """T = 4096 through the tiled path; rows are independent, so the oracle on
-    a row sample is the oracle of those rows."""
-    t, dw = large_weights
+    """T = 4096 through the tiled path, compared on 256 rows (one in every
+    16-row fragment group of every 256-row m-tile) over all 8192 columns;
+    rows are independent, so the oracle on a row sample is the oracle of those
+    rows.  The rest of y must be finite."""
+    t, dw, lw = large_weights
     w = datagen.workload("large4096")
     x = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
     print(f"case {w.name} (sampled rows)", flush=True)
     y = _run(to_dev(x), dw["Wg"], dw["Wu"], dw["Wd"])
-    rows = np.array([0, 1, 255, 256, 1000, 2047, 2048, 3333, 4094, 4095])
-    ref = oracle.geglu(f64_of_bits(x[rows]), *(f64_of_bits(t[k]) for k in ("Wg", "Wu", "Wd")))
-    assert_parity(y[torch.from_numpy(rows).to(DEV)], ref, f"{w.name} rows")
+    rows = prefill_sample_rows(w.M)
+    assert len(rows) >= 256
+    assert len(np.unique(rows // 256)) == w.M // 256 and len(np.unique(rows % 16)) == 16
+    ref = oracle.geglu(f64_of_bits(x[rows]), *lw.f64())
+    assert_parity(y[torch.from_numpy(rows).to(DEV)], ref, f"{w.name} {len(rows)} rows")
     assert np.isfinite(f64_of(y)).all()
 
 

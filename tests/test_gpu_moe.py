@@ -131,10 +131,34 @@ def test_moe_determinism():
     assert np.array_equal(bits_of(_run(x, ids, gw, Wg, Wu, Wd)), bits_of(_run(x, ids, gw, Wg, Wu, Wd)))
 
 
+def moe_sample_tokens(ids: np.ndarray, E: int, n_min: int = 512, tile: int = 256, seed: int = 0) -> np.ndarray:
+    """Tokens whose routed rows sit at the edges of every expert's segment and
+    of every 256-row tile in it (positions 0, 255, 256, ..., last of the
+    segment: tail tiles included), topped up with random tokens to at least
+    n_min.  Pairs are bucketed per expert stably in pair order (t * top_k + j)."""
+    T, k = ids.shape
+    pick = set()
+    flat = ids.reshape(-1)
+    for e in range(E):
+        seg = np.nonzero(flat == e)[0] // k       # tokens of expert e's rows, in segment order
+        if len(seg) == 0:
+            continue
+        edges = {0, len(seg) - 1}
+        for b in range(0, len(seg), tile):
+            edges.update({b, min(b + tile - 1, len(seg) - 1)})
+        pick.update(int(seg[i]) for i in edges)
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(pick, dtype=np.int64))
+    extra = rng.choice(rest, size=max(0, n_min - len(pick)), replace=False)
+    return np.unique(np.concatenate([np.fromiter(pick, dtype=np.int64), extra]))
+
+
 @pytest.mark.slow
 def test_moe_workload_sampled_tokens():
-    """The 8 x (4096/14336) top-2 workload at 4096 tokens, checked on a token
-    sample (tokens are independent)."""
+    """The 8 x (4096/14336) top-2 workload at 4096 tokens, compared on at least
+    512 tokens (tokens are independent) that include the first and last routed
+    row of every expert segment and of every 256-row tile in it, so tail tiles
+    and both K halves of the down projection are compared."""
     w = datagen.workload("moe")
     x = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
     ids, gw = datagen.make_routes(w.M, w.E, w.top_k, seed=0)
@@ -143,10 +167,14 @@ def test_moe_workload_sampled_tokens():
     Wu = torch.stack([to_dev(e[1]) for e in experts])
     Wd = torch.stack([to_dev(e[2]) for e in experts])
     print(f"case {w.name} (sampled tokens)", flush=True)
-    y = F.fmlp_moe_geglu(to_dev(x), to_dev(ids, torch.int32), to_dev(gw, torch.float32), Wg, Wu, Wd)
+    ws = F.workspace_for(DEV, F.fmlp_moe_workspace_size(w.M, w.K, w.H, w.E, w.top_k))
+    y = F.fmlp_moe_geglu(to_dev(x), to_dev(ids, torch.int32), to_dev(gw, torch.float32), Wg, Wu, Wd,
+                         workspace=ws)
     torch.cuda.synchronize()
-    toks = np.array([0, 1, 2, 511, 1024, 2047, 3000, 4095])
+    assert F.moe_invalid_ids(ws) == 0
+    toks = moe_sample_tokens(ids, w.E)
+    assert len(toks) >= 512
     ref = oracle.moe_geglu(f64_of_bits(x[toks]), ids[toks], gw[toks].astype(np.float64),
                            lambda e: tuple(f64_of_bits(a) for a in experts[e]))
-    assert_parity(y[torch.from_numpy(toks).to(DEV)], ref, f"{w.name} tokens")
+    assert_parity(y[torch.from_numpy(toks).to(DEV)], ref, f"{w.name} {len(toks)} tokens")
     assert np.isfinite(f64_of(y)).all()
