@@ -12,6 +12,7 @@ raises.
     fmlp_mlp2(x, W1, b1, W2, b2, act)               y = act(x W1^T + b1) W2^T + b2
     fmlp_geglu(x, Wg, Wu, Wd)                       y = (gelu_tanh(x Wg^T) * x Wu^T) Wd^T
     fmlp_glu(x, Wg, Wu, Wd, gate_act)               y = (gate_act(x Wg^T) * x Wu^T) Wd^T
+    fmlp_glu_noalloc(x, Wg, Wu, Wd, gate_act)       the same with the library's own scratch array
     fmlp_moe_geglu(x, expert_ids, gate_w, Wg, Wu, Wd)
                                                     y[t] = sum_j w[t,j] geglu_{e[t,j]}(x[t])
     fmlp_moe_glu(x, expert_ids, gate_w, Wg, Wu, Wd, gate_act)
@@ -41,6 +42,7 @@ __all__ = [
     "fmlp_mlp2",
     "fmlp_geglu",
     "fmlp_glu",
+    "fmlp_glu_noalloc",
     "fmlp_moe_geglu",
     "fmlp_moe_glu",
     "fmlp_moe_route",
@@ -117,6 +119,8 @@ def lib() -> ctypes.CDLL:
         L.fmlp_moe_glu.argtypes = [_p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int32,
                                    ctypes.c_int32, _p, _p, _sz, _p]
         L.fmlp_moe_route.argtypes = [_p, _p, _i64, _i64, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p]
+        L.fmlp_glu_noalloc.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
+        L.fmlp_glu_noalloc.restype = ctypes.c_int
         for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
                   "fmlp_moe_route", "fmlp_set_path"):
             getattr(L, f).restype = ctypes.c_int
@@ -338,6 +342,26 @@ def fmlp_glu(x, Wg, Wu, Wd, gate_act: str = "silu", out=None, workspace=None):
 def bind_glu(x, Wg, Wu, Wd, gate_act: str = "silu", out=None, workspace=None) -> BoundCall:
     with torch.cuda.device(x.device):
         return _geglu_call(x, Wg, Wu, Wd, out, workspace, gate_act)
+
+
+def fmlp_glu_noalloc(x, Wg, Wu, Wd, gate_act: str = "silu", out=None):
+    """fmlp_glu without a workspace: the library's own fixed device array serves
+    as one (for callers that cannot allocate).  Calls on one device must be
+    ordered on one stream."""
+    with torch.cuda.device(x.device):
+        for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd)):
+            _dev_tensor(n, t)
+        D = x.shape[-1]
+        H = Wg.shape[0]
+        if Wg.shape != (H, D) or Wu.shape != (H, D) or Wd.shape != (D, H):
+            raise ValueError(f"shape mismatch: x[...,{D}] Wg{tuple(Wg.shape)} Wu{tuple(Wu.shape)} "
+                             f"Wd{tuple(Wd.shape)}")
+        M = x.numel() // D
+        y = out if out is not None else torch.empty_like(x)
+        _dev_tensor("out", y)
+        _check(lib().fmlp_glu_noalloc(_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), ACT[gate_act], M, D, H, _ptr(y),
+                                      _stream(x.device)))
+        return y
 
 
 def fmlp_moe_workspace_size(T, D, H, E, top_k) -> int:

@@ -187,9 +187,15 @@ hipError_t gemm_glu_gateup(const uint16_t* x, const uint16_t* Wg, const uint16_t
 
 }  // namespace
 
+namespace fmlp {
+// The status and detail text of a failure found outside this file (the
+// no-allocation entry point), for fmlp_last_error().
+fmlp_status record_error(fmlp_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace fmlp
+
 extern "C" {
 
-int fmlp_version(void) { return 102; }
+int fmlp_version(void) { return 103; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {

@@ -154,6 +154,27 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
 size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
 
 /*
+ * fmlp_glu without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, kernels, paths, results and errors
+ * as fmlp_glu; the workspace is instead a device array inside this library of
+ * FMLP_GLU_NOALLOC_SCRATCH_BYTES (64 MiB), one per device the library runs on,
+ * held until the process ends.  A shape whose fmlp_glu_workspace_size exceeds
+ * it is FMLP_E_WORKSPACE (the 8192-token 768/3072 block and every shape of up
+ * to 16 tokens fit).  No call allocates anything: the first call on a device
+ * looks up the array's device address once (with that device current) and
+ * clears its 8 KB decode header with a small kernel on `stream`; make that
+ * first call outside graph capture.  Every call on a device shares that
+ * device's array, which keeps the last call's contents: calls that overlap on
+ * one device (on different streams, or from different threads without
+ * ordering) race and give wrong results; order them on one stream.
+ */
+#define FMLP_GLU_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+fmlp_status fmlp_glu_noalloc(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu,
+                             const fmlp_bf16* Wd, int gate_act, int64_t M, int64_t D, int64_t H,
+                             fmlp_bf16* y, fmlp_stream stream);
+
+/*
  * FP8 weights for decode (1 <= M <= 16 tokens)
  *
  * At a few tokens a feed-forward layer is bound by reading its weights once
