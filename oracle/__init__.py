@@ -6,6 +6,7 @@ GPU library never imports it.
 """
 from .fmlp_oracle import (  # noqa: F401
     ACTS,
+    act_grad,
     activation,
     dequant_w8,
     e4m3_decode,
@@ -13,10 +14,13 @@ from .fmlp_oracle import (  # noqa: F401
     gelu_erf,
     gelu_tanh,
     glu,
+    glu_bwd,
     glu_w8,
     linear,
+    linear_bwd,
     linear_w8,
     mlp2,
+    mlp2_bwd,
     mlp2_w8,
     moe_geglu,
     moe_glu,

@@ -27,6 +27,13 @@ Readings taken where the pages are silent (each is listed in the design doc):
     the pages name three-Linear MLP blocks (LLaMA-3, Mixtral experts) without
     naming their gate activation, so the gated block takes it as an argument.
 
+  * Backward pass: the pages profile the forward only; Liger's fused gelu*mul
+    ("Profiling in PyTorch (Part 2)", section "Let's use hand tuned kernels":
+    LigerGELUMulFunction) is an autograd Function, so its backward exists but
+    is not described.  The gradients here are the chain rule applied to the
+    forward definitions above, with the derivative of each activation written
+    out from its formula (act_grad), and nothing rounded.
+
   * FP8 weights (decode): the pages only note that decode is bound by the
     weight bytes; the format is the OCP 8-bit floating point E4M3 encoding
     ("e4m3fn") with one scale per output row, and the functions here
@@ -61,6 +68,10 @@ __all__ = [
     "linear_w8",
     "mlp2_w8",
     "glu_w8",
+    "act_grad",
+    "linear_bwd",
+    "mlp2_bwd",
+    "glu_bwd",
 ]
 
 ACTS = ("none", "gelu_erf", "gelu_tanh", "relu", "silu")
@@ -310,3 +321,83 @@ def mlp2_w8(x, W1q, s1, b1, W2q, s2, b2, act: str):
 def glu_w8(x, Wgq, sg, Wuq, su, Wdq, sd, gate_act: str):
     """glu() on dequantised FP8 weights (gate, up and down each with row scales)."""
     return glu(x, dequant_w8(Wgq, sg), dequant_w8(Wuq, su), dequant_w8(Wdq, sd), gate_act)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of the forward definitions above)
+# ---------------------------------------------------------------------------
+def act_grad(z, act: str):
+    """d act(z) / dz, from each activation's formula:
+      none       1
+      gelu_erf   Phi(z) + z phi(z), phi the standard normal density
+      gelu_tanh  (1 + tanh a)/2 + z/2 (1 - tanh^2 a) sqrt(2/pi) (1 + 3*0.044715 z^2),
+                 a = sqrt(2/pi) (z + 0.044715 z^3)
+      relu       1 where z > 0, else 0 (0 at z = 0, PyTorch's convention)
+      silu       sigmoid(z) (1 + z (1 - sigmoid(z)))
+    """
+    z = _f64(z)
+    if act == "none":
+        return np.ones_like(z)
+    if act == "gelu_erf":
+        phi = np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+        return 0.5 * _erfc(-z * _SQRT_HALF) + z * phi
+    if act == "gelu_tanh":
+        a = _SQRT_2_OVER_PI * (z + _GELU_TANH_CUBIC * z * z * z)
+        t = np.tanh(a)
+        da = _SQRT_2_OVER_PI * (1.0 + 3.0 * _GELU_TANH_CUBIC * z * z)
+        return 0.5 * (1.0 + t) + 0.5 * z * (1.0 - t * t) * da
+    if act == "relu":
+        return np.where(z > 0.0, 1.0, 0.0)
+    if act == "silu":
+        sg = _expit(z)
+        return sg * (1.0 + z * (1.0 - sg))
+    raise ValueError(f"unknown activation {act!r}; expected one of {ACTS}")
+
+
+def linear_bwd(x, W, b, act: str, dy):
+    """Gradients of y = act(x W^T + b) (linear above) for an upstream gradient
+    dy [M, N]:  z = x W^T + b,  dz = dy * act'(z),
+        dx = dz W  [M, K],   dW = dz^T x  [N, K],   db = sum_m dz  [N] (None
+    without a bias).  Returns (dx, dW, db)."""
+    x = _f64(x)
+    W = _f64(W)
+    dy = _f64(dy)
+    z = x @ W.T
+    if b is not None:
+        z = z + _f64(b)[None, :]
+    if dy.shape != z.shape:
+        raise ValueError(f"dy shape {dy.shape} != {z.shape}")
+    dz = dy * act_grad(z, act)
+    return dz @ W, dz.T @ x, (dz.sum(axis=0) if b is not None else None)
+
+
+def mlp2_bwd(x, W1, b1, W2, b2, act: str, dy):
+    """Gradients of y = act(x W1^T + b1) W2^T + b2 (mlp2 above): the second
+    layer's backward on h = act(x W1^T + b1), then the first layer's with the
+    gradient reaching h.  Returns (dx, dW1, db1, dW2, db2)."""
+    h = linear(x, W1, b1, act)
+    dh, dW2, db2 = linear_bwd(h, W2, b2, "none", dy)
+    dx, dW1, db1 = linear_bwd(x, W1, b1, act, dh)
+    return dx, dW1, db1, dW2, db2
+
+
+def glu_bwd(x, Wg, Wu, Wd, gate_act: str, dy):
+    """Gradients of the gated block y = (gate_act(x Wg^T) * (x Wu^T)) Wd^T
+    (glu above; gelu_tanh gives GeGLU) for an upstream gradient dy [M, D]:
+        g = x Wg^T, u = x Wu^T, m = act(g) * u,
+        dWd = dy^T m,   dm = dy Wd,
+        dg = dm * u * act'(g),   du = dm * act(g),
+        dx = dg Wg + du Wu,   dWg = dg^T x,   dWu = du^T x.
+    Returns (dx, dWg, dWu, dWd)."""
+    x = _f64(x)
+    Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+    dy = _f64(dy)
+    g = x @ Wg.T
+    u = x @ Wu.T
+    a = activation(g, gate_act)
+    m = a * u
+    dWd = dy.T @ m
+    dm = dy @ Wd
+    dg = dm * u * act_grad(g, gate_act)
+    du = dm * a
+    return dg @ Wg + du @ Wu, dg.T @ x, du.T @ x, dWd

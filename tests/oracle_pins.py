@@ -502,7 +502,212 @@ def check_w8_layers(o):
     _close(o.linear_w8(x, q1, 2 * s1), 2 * o.linear_w8(x, q1, s1), what="linear_w8 scale")
 
 
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+def _bf_act_grad(z: float, act: str, h: float = 1e-6) -> float:
+    """Central difference of the pure-Python activation (libm), a derivative
+    that shares nothing with the oracle's closed-form act_grad."""
+    if act == "relu":        # the kink: PyTorch's convention, 0 at z <= 0
+        return 1.0 if z > 0.0 else 0.0
+    return (_bf_act(z + h, act) - _bf_act(z - h, act)) / (2.0 * h)
+
+
+def bf_linear_bwd(x, W, b, act, dy):
+    """Pure-Python loops: z, dz = dy * act'(z) by central differences, then
+    dx[m][k] = sum_n dz W[n][k], dW[n][k] = sum_m dz x[m][k], db[n] = sum_m dz."""
+    M, K, N = len(x), len(x[0]), len(W)
+    dz = [[0.0] * N for _ in range(M)]
+    for m in range(M):
+        for n in range(N):
+            s = sum(float(x[m][k]) * float(W[n][k]) for k in range(K)) + (float(b[n]) if b is not None else 0.0)
+            dz[m][n] = float(dy[m][n]) * _bf_act_grad(s, act)
+    dx = [[sum(dz[m][n] * float(W[n][k]) for n in range(N)) for k in range(K)] for m in range(M)]
+    dW = [[sum(dz[m][n] * float(x[m][k]) for m in range(M)) for k in range(K)] for n in range(N)]
+    db = [sum(dz[m][n] for m in range(M)) for n in range(N)] if b is not None else None
+    return dx, dW, db
+
+
+def check_act_grad_closed_forms(o):
+    """Derivatives at points with known values, and the identities that follow
+    from the odd-part identity a(x) - a(-x) = x: a'(x) + a'(-x) = 1."""
+    phi1 = math.exp(-0.5) / math.sqrt(2.0 * math.pi)          # standard normal density at 1
+    assert abs(float(o.act_grad(1.0, "gelu_erf")) - (0.8413447460685429 + phi1)) < 1e-15
+    assert abs(float(o.act_grad(-1.0, "gelu_erf")) - (0.15865525393145707 - phi1)) < 1e-15
+    for act in ("gelu_erf", "gelu_tanh", "silu"):
+        assert float(o.act_grad(0.0, act)) == 0.5
+        assert abs(float(o.act_grad(40.0, act)) - 1.0) < 1e-12     # a(x) -> x
+        assert abs(float(o.act_grad(-40.0, act))) < 1e-9           # a(x) -> 0
+        x = np.linspace(-7, 7, 1401)
+        _close(o.act_grad(x, act) + o.act_grad(-x, act), np.ones_like(x), rtol=1e-13, atol=1e-13,
+               what=f"{act}: a'(x) + a'(-x) = 1")
+    # gelu_tanh'(1) from its formula by hand: s = sigmoid(2a), a = sqrt(2/pi)(1.044715)
+    a = math.sqrt(2.0 / math.pi) * 1.044715
+    sg = 1.0 / (1.0 + math.exp(-2.0 * a))
+    want = sg + 2.0 * sg * (1.0 - sg) * math.sqrt(2.0 / math.pi) * (1.0 + 3 * 0.044715)
+    assert abs(float(o.act_grad(1.0, "gelu_tanh")) - want) < 1e-14
+    # SiLU's minimum x* = -1.278464542761074 (SiLU(x*) = x* + 1): derivative 0 there
+    assert abs(float(o.act_grad(-1.278464542761074, "silu"))) < 1e-14
+    assert list(o.act_grad(np.array([-1.0, 0.0, 1e-30, 3.0]), "relu")) == [0.0, 0.0, 1.0, 1.0]
+    assert list(o.act_grad(np.array([-2.0, 0.0, 5.0]), "none")) == [1.0, 1.0, 1.0]
+
+
+def check_act_grad_finite_differences(o):
+    """Central differences of the (separately pinned) forward activations."""
+    z = np.concatenate([np.linspace(-8, 8, 641), [-3.3, -0.01, 0.013, 2.7]])
+    h = 1e-6
+    for act in ("none", "gelu_erf", "gelu_tanh", "silu"):
+        fd = (o.activation(z + h, act) - o.activation(z - h, act)) / (2 * h)
+        _close(o.act_grad(z, act), fd, rtol=1e-8, atol=1e-8, what=f"{act}' vs central differences")
+    zr = z[np.abs(z) > 1e-3]
+    fd = (o.activation(zr + h, "relu") - o.activation(zr - h, "relu")) / (2 * h)
+    _close(o.act_grad(zr, "relu"), fd, rtol=1e-8, atol=1e-8, what="relu' vs central differences")
+
+
+def check_act_grad_library(o):
+    """torch autograd (float64) through F.gelu, F.gelu(tanh), F.silu, F.relu."""
+    import torch
+    import torch.nn.functional as F
+
+    z = np.concatenate([np.linspace(-10, 10, 2001), [0.0, -1e-4, 1e-4]])
+    fns = {"gelu_erf": F.gelu, "gelu_tanh": lambda t: F.gelu(t, approximate="tanh"), "silu": F.silu,
+           "relu": F.relu, "none": lambda t: t * 1.0}
+    for act, fn in fns.items():
+        t = torch.from_numpy(z.copy()).requires_grad_(True)
+        fn(t).sum().backward()
+        _close(o.act_grad(z, act), t.grad.numpy(), rtol=1e-13, atol=1e-14, what=f"{act}' vs torch autograd")
+
+
+def check_linear_bwd_bruteforce(o):
+    rng = np.random.default_rng(77)
+    for (M, K, N, act, bias) in [(1, 1, 1, "none", True), (2, 3, 5, "gelu_erf", True), (3, 4, 2, "gelu_tanh", False),
+                                 (4, 5, 3, "silu", True), (3, 3, 3, "relu", True), (5, 2, 4, "gelu_tanh", True)]:
+        x = _bf16ish(rng, (M, K))
+        W = _bf16ish(rng, (N, K), 0.5)
+        b = _bf16ish(rng, (N,), 0.3) if bias else None
+        dy = _bf16ish(rng, (M, N))
+        dx, dW, db = o.linear_bwd(x, W, b, act, dy)
+        bx, bW, bb = bf_linear_bwd(x.tolist(), W.tolist(), None if b is None else b.tolist(), act, dy.tolist())
+        _close(dx, bx, rtol=1e-8, atol=1e-9, what=f"linear_bwd dx {M}x{K}x{N} {act}")
+        _close(dW, bW, rtol=1e-8, atol=1e-9, what=f"linear_bwd dW {M}x{K}x{N} {act}")
+        if bias:
+            _close(db, bb, rtol=1e-8, atol=1e-9, what=f"linear_bwd db {act}")
+        else:
+            assert db is None
+
+
+def _torch_grads(fn, arrays, dy):
+    import torch
+
+    ts = [None if a is None else torch.from_numpy(np.array(a, dtype=np.float64)).requires_grad_(True) for a in arrays]
+    out = fn(*ts)
+    out.backward(torch.from_numpy(np.asarray(dy, dtype=np.float64)))
+    return [None if t is None else t.grad.numpy() for t in ts]
+
+
+_TORCH_ACT = {
+    "none": lambda t: t,
+    "gelu_erf": lambda t: __import__("torch").nn.functional.gelu(t),
+    "gelu_tanh": lambda t: __import__("torch").nn.functional.gelu(t, approximate="tanh"),
+    "relu": lambda t: __import__("torch").nn.functional.relu(t),
+    "silu": lambda t: __import__("torch").nn.functional.silu(t),
+}
+
+
+def check_backward_library(o):
+    """linear_bwd, mlp2_bwd and glu_bwd against torch autograd in float64 (the
+    forward written with torch's F.linear and activations)."""
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(5)
+    M, K, H, N = 7, 12, 10, 6
+    x = _bf16ish(rng, (M, K))
+    for act in ("none", "gelu_erf", "gelu_tanh", "relu", "silu"):
+        W = _bf16ish(rng, (N, K), 0.4)
+        b = _bf16ish(rng, (N,), 0.2)
+        dy = _bf16ish(rng, (M, N))
+        gx, gW, gb = _torch_grads(lambda x_, W_, b_: _TORCH_ACT[act](F.linear(x_, W_, b_)), [x, W, b], dy)
+        dx, dW, db = o.linear_bwd(x, W, b, act, dy)
+        for a, r, n in ((dx, gx, "dx"), (dW, gW, "dW"), (db, gb, "db")):
+            _close(a, r, rtol=1e-12, atol=1e-13, what=f"linear_bwd {n} {act} vs autograd")
+        W1 = _bf16ish(rng, (H, K), 0.4)
+        b1 = _bf16ish(rng, (H,), 0.2)
+        W2 = _bf16ish(rng, (N, H), 0.4)
+        b2 = _bf16ish(rng, (N,), 0.2)
+        ref = _torch_grads(lambda x_, a_, c_, d_, e_: F.linear(_TORCH_ACT[act](F.linear(x_, a_, c_)), d_, e_),
+                           [x, W1, b1, W2, b2], dy)
+        got = o.mlp2_bwd(x, W1, b1, W2, b2, act, dy)
+        for a, r, n in zip(got, [ref[0], ref[1], ref[2], ref[3], ref[4]], ("dx", "dW1", "db1", "dW2", "db2")):
+            _close(a, r, rtol=1e-12, atol=1e-13, what=f"mlp2_bwd {n} {act} vs autograd")
+        D = K
+        Wg = _bf16ish(rng, (H, D), 0.4)
+        Wu = _bf16ish(rng, (H, D), 0.4)
+        Wd = _bf16ish(rng, (D, H), 0.4)
+        dyd = _bf16ish(rng, (M, D))
+        ref = _torch_grads(lambda x_, g_, u_, d_: F.linear(_TORCH_ACT[act](F.linear(x_, g_)) * F.linear(x_, u_), d_),
+                           [x, Wg, Wu, Wd], dyd)
+        got = o.glu_bwd(x, Wg, Wu, Wd, act, dyd)
+        for a, r, n in zip(got, ref, ("dx", "dWg", "dWu", "dWd")):
+            _close(a, r, rtol=1e-12, atol=1e-13, what=f"glu_bwd {n} {act} vs autograd")
+
+
+def check_glu_bwd_directional(o):
+    """<dy, glu(theta + e v) - glu(theta - e v)> / 2e = <grad, v> for a random
+    direction v of each input (the forward glu is pinned separately)."""
+    rng = np.random.default_rng(11)
+    M, D, H = 5, 6, 8
+    x = _bf16ish(rng, (M, D))
+    Wg, Wu = _bf16ish(rng, (H, D), 0.5), _bf16ish(rng, (H, D), 0.5)
+    Wd = _bf16ish(rng, (D, H), 0.5)
+    dy = _bf16ish(rng, (M, D))
+    e = 1e-6
+    for act in ("gelu_tanh", "gelu_erf", "silu"):
+        grads = o.glu_bwd(x, Wg, Wu, Wd, act, dy)
+        args = [x, Wg, Wu, Wd]
+        for i in range(4):
+            v = rng.standard_normal(args[i].shape)
+            plus = [a + e * v if j == i else a for j, a in enumerate(args)]
+            minus = [a - e * v if j == i else a for j, a in enumerate(args)]
+            fd = np.sum(dy * (o.glu(*plus, act) - o.glu(*minus, act))) / (2 * e)
+            got = np.sum(grads[i] * v)
+            assert abs(fd - got) <= 1e-7 * max(1.0, abs(got)), (act, i, fd, got)
+
+
+def check_backward_special_cases(o):
+    """Identity weights: dx = dy * act'(x) with W = I; W = 0 gives dx = 0 and
+    dW = dz^T x with dz = dy * act'(b); the gated block's gradient through
+    Wu = 0 vanishes for dx and dWg (m = 0 makes dWd = 0 too)."""
+    rng = np.random.default_rng(3)
+    M, K = 6, 5
+    x = _bf16ish(rng, (M, K))
+    dy = _bf16ish(rng, (M, K))
+    I = np.eye(K)
+    for act in ("gelu_erf", "silu"):
+        dx, dW, db = o.linear_bwd(x, I, None, act, dy)
+        _close(dx, dy * o.act_grad(x, act), rtol=1e-14, atol=1e-15, what=f"identity W dx {act}")
+        b = _bf16ish(rng, (K,), 0.5)
+        dx, dW, db = o.linear_bwd(x, np.zeros((K, K)), b, act, dy)
+        dz = dy * o.act_grad(np.broadcast_to(b, (M, K)), act)
+        _close(dx, np.zeros_like(dx), what="W=0 dx")
+        _close(dW, dz.T @ x, rtol=1e-14, atol=1e-15, what="W=0 dW")
+        _close(db, dz.sum(axis=0), rtol=1e-14, atol=1e-15, what="W=0 db")
+    H = 4
+    Wg = _bf16ish(rng, (H, K), 0.5)
+    Wd = _bf16ish(rng, (K, H), 0.5)
+    dx, dWg, dWu, dWd = o.glu_bwd(x, Wg, np.zeros((H, K)), Wd, "gelu_tanh", dy)
+    for a, n in ((dx, "dx"), (dWg, "dWg"), (dWd, "dWd")):
+        _close(a, np.zeros_like(a), what=f"Wu=0 {n}")
+    assert np.max(np.abs(dWu)) > 1e-3
+
+
 ALL_CHECKS = [
+    check_act_grad_closed_forms,
+    check_act_grad_finite_differences,
+    check_act_grad_library,
+    check_linear_bwd_bruteforce,
+    check_backward_library,
+    check_glu_bwd_directional,
+    check_backward_special_cases,
     check_linear_bruteforce,
     check_mlp2_bruteforce,
     check_geglu_bruteforce,

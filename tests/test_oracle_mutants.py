@@ -179,7 +179,106 @@ def _dequant_ignores_scale(Wq, scale):
     return fo.e4m3_decode(np.asarray(Wq, dtype=np.uint8))
 
 
+_orig_act_grad = fo.act_grad
+_orig_linear_bwd = fo.linear_bwd
+_orig_glu_bwd = fo.glu_bwd
+
+
+def _grad_erf_no_density_term(z, act):
+    if act == "gelu_erf":
+        return 0.5 * erfc(-np.asarray(z, float) * np.sqrt(0.5))
+    return _orig_act_grad(z, act)
+
+
+def _grad_tanh_no_cubic_term(z, act):
+    if act == "gelu_tanh":
+        z = np.asarray(z, float)
+        t = np.tanh(np.sqrt(2 / np.pi) * (z + 0.044715 * z ** 3))
+        return 0.5 * (1 + t) + 0.5 * z * (1 - t * t) * np.sqrt(2 / np.pi)
+    return _orig_act_grad(z, act)
+
+
+def _grad_silu_is_sigmoid(z, act):
+    if act == "silu":
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, float)))
+    return _orig_act_grad(z, act)
+
+
+def _grad_relu_one_at_zero(z, act):
+    if act == "relu":
+        return np.where(np.asarray(z, float) >= 0, 1.0, 0.0)
+    return _orig_act_grad(z, act)
+
+
+def _grad_names_swapped(z, act):
+    return _orig_act_grad(z, {"gelu_erf": "gelu_tanh", "gelu_tanh": "gelu_erf"}.get(act, act))
+
+
+def _linear_bwd_no_act_grad(x, W, b, act, dy):
+    return _orig_linear_bwd(x, W, b, "none", dy)
+
+
+def _linear_bwd_dW_of_dy(x, W, b, act, dy):
+    dx, dW, db = _orig_linear_bwd(x, W, b, act, dy)
+    return dx, np.asarray(dy, float).T @ np.asarray(x, float), db
+
+
+def _linear_bwd_dx_transposed_W(x, W, b, act, dy):
+    dx, dW, db = _orig_linear_bwd(x, W, b, act, dy)
+    W = np.asarray(W, float)
+    if W.shape[0] == W.shape[1]:
+        z = np.asarray(x, float) @ W.T + (0 if b is None else np.asarray(b, float))
+        dx = (np.asarray(dy, float) * fo.act_grad(z, act)) @ W.T
+    return dx, dW, db
+
+
+def _linear_bwd_db_of_dy(x, W, b, act, dy):
+    dx, dW, db = _orig_linear_bwd(x, W, b, act, dy)
+    return dx, dW, (None if b is None else np.asarray(dy, float).sum(axis=0))
+
+
+def _glu_bwd_dg_du_swapped(x, Wg, Wu, Wd, gate_act, dy):
+    dx, dWg, dWu, dWd = _orig_glu_bwd(x, Wg, Wu, Wd, gate_act, dy)
+    return dx, dWu, dWg, dWd
+
+
+def _glu_bwd_gate_grad_on_up(x, Wg, Wu, Wd, gate_act, dy):
+    x, Wg, Wu, Wd, dy = (np.asarray(a, float) for a in (x, Wg, Wu, Wd, dy))
+    g, u = x @ Wg.T, x @ Wu.T
+    a = fo.activation(g, gate_act)
+    dm = dy @ Wd
+    dg = dm * u
+    du = dm * a * fo.act_grad(g, gate_act)
+    return dg @ Wg + du @ Wu, dg.T @ x, du.T @ x, dy.T @ (a * u)
+
+
+def _glu_bwd_dWd_of_u(x, Wg, Wu, Wd, gate_act, dy):
+    dx, dWg, dWu, dWd = _orig_glu_bwd(x, Wg, Wu, Wd, gate_act, dy)
+    return dx, dWg, dWu, np.asarray(dy, float).T @ (np.asarray(x, float) @ np.asarray(Wu, float).T)
+
+
+def _glu_bwd_dx_gate_only(x, Wg, Wu, Wd, gate_act, dy):
+    x, Wg, Wu, Wd, dy = (np.asarray(a, float) for a in (x, Wg, Wu, Wd, dy))
+    _, dWg, dWu, dWd = _orig_glu_bwd(x, Wg, Wu, Wd, gate_act, dy)
+    g, u = x @ Wg.T, x @ Wu.T
+    dg = (dy @ Wd) * u * fo.act_grad(g, gate_act)
+    return dg @ Wg, dWg, dWu, dWd
+
+
 MUTANTS = {
+    "act_grad_erf_without_z_phi": ("act_grad", _grad_erf_no_density_term),
+    "act_grad_tanh_without_cubic_term": ("act_grad", _grad_tanh_no_cubic_term),
+    "act_grad_silu_is_sigmoid": ("act_grad", _grad_silu_is_sigmoid),
+    "act_grad_relu_one_at_zero": ("act_grad", _grad_relu_one_at_zero),
+    "act_grad_names_swapped": ("act_grad", _grad_names_swapped),
+    "linear_bwd_ignores_act_grad": ("linear_bwd", _linear_bwd_no_act_grad),
+    "linear_bwd_dW_from_dy": ("linear_bwd", _linear_bwd_dW_of_dy),
+    "linear_bwd_dx_through_W_transposed": ("linear_bwd", _linear_bwd_dx_transposed_W),
+    "linear_bwd_db_from_dy": ("linear_bwd", _linear_bwd_db_of_dy),
+    "glu_bwd_dWg_dWu_swapped": ("glu_bwd", _glu_bwd_dg_du_swapped),
+    "glu_bwd_gate_grad_on_up": ("glu_bwd", _glu_bwd_gate_grad_on_up),
+    "glu_bwd_dWd_from_u": ("glu_bwd", _glu_bwd_dWd_of_u),
+    "glu_bwd_dx_gate_path_only": ("glu_bwd", _glu_bwd_dx_gate_only),
     "linear_drops_bias": ("linear", _linear_no_bias),
     "linear_subtracts_bias": ("linear", _linear_bias_sub),
     "linear_square_W_not_transposed": ("linear", _linear_square_transposed),
