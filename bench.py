@@ -104,18 +104,18 @@ def _inputs(w):
     once per process (the weights do not depend on the token count)."""
     import datagen
 
-    key = (w.family, w.op)
+    key = (w.family, "geglu" if w.op == "glu_bwd" else w.op)   # a backward shares its forward's weights
     if key not in _HOST_CACHE:
         _HOST_CACHE[key] = {k: v for k, v in datagen.make_inputs(w, seed=0).items() if k != "x"}
     t = dict(_HOST_CACHE[key])
-    t["x"] = datagen.make_inputs(w, seed=0, with_weights=False)["x"]
+    t.update(datagen.make_inputs(w, seed=0, with_weights=False))   # x (and dy)
     return t
 
 
 def _dev_weights(w, t, torch, dev):
-    key = (w.family, w.op)
+    key = (w.family, "geglu" if w.op == "glu_bwd" else w.op)
     if key not in _DEV_CACHE:
-        _DEV_CACHE[key] = {k: _dev(v, torch, dev) for k, v in t.items() if k != "x"}
+        _DEV_CACHE[key] = {k: _dev(v, torch, dev) for k, v in t.items() if k not in ("x", "dy")}
     return _DEV_CACHE[key]
 
 
@@ -274,6 +274,35 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
         case.workspace = ws
         return case
 
+    if w.op == "glu_bwd":
+        # the gated block's backward: every gradient of a GeGLU forward for an
+        # upstream gradient dy; the oracle times glu_bwd on the first rows tokens
+        t = _inputs(w)
+        x, dy = _dev(t["x"], torch, dev), _dev(t["dy"], torch, dev)
+        base = _dev_weights(w, t, torch, dev)
+        sets = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+        outs = (torch.empty_like(x), torch.empty_like(base["Wg"]), torch.empty_like(base["Wu"]),
+                torch.empty_like(base["Wd"]))
+        ws = torch.empty(int(F.lib().fmlp_glu_bwd_workspace_size(w.M, w.K, w.H)), dtype=torch.uint8, device=dev)
+        calls = [F.bind_glu_bwd(x, s_["Wg"], s_["Wu"], s_["Wd"], "gelu_tanh", dy, out=outs, workspace=ws)
+                 for s_ in sets]
+        import oracle
+
+        rows = 64 if w.K * w.H > 1e8 else 512
+        cache = {}
+
+        def fn():
+            if not cache:
+                cache.update({k: f64(v[:rows] if k in ("x", "dy") else v) for k, v in t.items()})
+            c = cache
+            return oracle.glu_bwd(c["x"], c["Wg"], c["Wu"], c["Wd"], "gelu_tanh", c["dy"])
+        case = Case(w, calls, "gemm_bf16_kernel", 13,
+                    "backward: dm GEMM, gate+up GEMM with the dGeGLU epilogue, dx GEMM over [dg|du], "
+                    "3 weight-gradient GEMMs, 7 transposes (13 launches)", R, fn,
+                    (f"{rows} of {w.M} token rows, full weights", rows / w.M))
+        case.workspace = ws
+        return case
+
     if w.op == "route":
         # x streams once per step; x copies rotate (>= 1 GiB) so it is read from HBM
         x_bits = datagen.make_inputs(datagen.workload("moe"), seed=0, with_weights=False)["x"]
@@ -392,9 +421,11 @@ def read_traffic(case: Case):
 
 
 EST_US = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 250,
-          "large16": 250, "large4096": 4000, "moe": 2500, "router": 8}
+          "large16": 250, "large4096": 4000, "moe": 2500, "router": 8, "geglu768_bwd": 300,
+          "large4096_bwd": 9000}
 # every workload of the configuration table, in the order the rows are printed
-CONFIG_ROWS = ["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe", "router"]
+CONFIG_ROWS = ["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe", "router",
+               "geglu768_bwd", "large4096_bwd"]
 
 
 def run_timed(case: Case, K: int, W: int, path: str, stream, torch, F, unfused: bool = True) -> dict:
@@ -580,7 +611,8 @@ def main(argv=None):
             "dims": {"in": w.K, "hidden": w.H, "out": w.N,
                      **({"experts": w.E, "top_k": w.top_k} if w.op in ("moe", "route") else {})},
             "act": (w.act if w.op == "mlp2" else "top-k + softmax" if w.op == "route"
-                    else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)")),
+                    else (f"{args.act} gate" if args.act else "gelu_tanh (GeGLU)")
+                    + (", backward" if w.op == "glu_bwd" else "")),
             "bias": w.bias,
             "weight_format": case.weights,
             "weights": (f"cold: {case.copies} rotated copies of x ({case.copies * 2 * w.M * w.K / 2**20:.0f} MiB)"

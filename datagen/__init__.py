@@ -143,6 +143,9 @@ class Workload:
             return 2 * self.M * self.top_k * 3 * self.K * self.H
         if self.op == "route":
             return 2 * self.M * self.K * self.E
+        if self.op == "glu_bwd":
+            # dm = dy Wd, dx = dg Wg + du Wu, dWd = dy^T m, dWg = dg^T x, dWu = du^T x
+            return 2 * self.M * 6 * self.K * self.H
         raise ValueError(self.op)
 
     @property
@@ -152,7 +155,7 @@ class Workload:
             if self.bias:
                 wb += 2 * (self.H + self.N)
             return wb
-        if self.op == "geglu":
+        if self.op in ("geglu", "glu_bwd"):
             return 2 * 3 * self.K * self.H
         if self.op == "moe":
             return self.E * 2 * 3 * self.K * self.H
@@ -164,6 +167,8 @@ class Workload:
     def bytes(self) -> int:
         """Algorithmic HBM bytes: weights (+biases) + x + y (+ routes), each once."""
         b = self.weight_bytes + 2 * self.M * self.K + 2 * self.M * self.N
+        if self.op == "glu_bwd":   # + the weight gradients written and dy read
+            b += self.weight_bytes + 2 * self.M * self.N
         if self.op in ("moe", "route"):
             b += self.M * self.top_k * (4 + 4)  # int32 ids + fp32 gate weights
         return b
@@ -211,6 +216,14 @@ def _router(T: int = 4096) -> Workload:
         w1_bound=1 / math.sqrt(4096), E=8, top_k=2, family="moe")
 
 
+def _glu_bwd(base: Workload) -> Workload:
+    """The backward pass of a GeGLU workload (same family, so the same weights
+    and x), with an upstream gradient dy ~ N(0, 1) of y's shape."""
+    import dataclasses
+
+    return dataclasses.replace(base, name=base.name + "_bwd", op="glu_bwd")
+
+
 WORKLOADS = {
     "tiny": _tiny(),
     "decode1": _decode(1),
@@ -221,6 +234,8 @@ WORKLOADS = {
     "large4096": _large(4096),
     "moe": _moe(),
     "router": _router(),
+    "geglu768_bwd": _glu_bwd(_geglu768()),
+    "large4096_bwd": _glu_bwd(_large(4096)),
 }
 
 
@@ -234,10 +249,13 @@ def workload(name: str) -> Workload:
 def make_inputs(w: Workload, seed: int = 0, with_weights: bool = True) -> dict:
     """bf16-bit arrays (uint16) for a dense workload (mlp2 / geglu).
 
-    mlp2: x, W1, b1, W2, b2 (biases only when w.bias);  geglu: x, Wg, Wu, Wd.
+    mlp2: x, W1, b1, W2, b2 (biases only when w.bias);  geglu: x, Wg, Wu, Wd;
+    glu_bwd: x, dy, Wg, Wu, Wd.
     """
     f = w.family
     out = {"x": normal_bf16(rng_for(seed, f, f"x{w.M}"), (w.M, w.K))}
+    if w.op == "glu_bwd":   # the upstream gradient of a backward workload
+        out["dy"] = normal_bf16(rng_for(seed, f, f"dy{w.M}"), (w.M, w.N))
     if not with_weights:
         return out
     if w.op == "mlp2":
@@ -246,7 +264,7 @@ def make_inputs(w: Workload, seed: int = 0, with_weights: bool = True) -> dict:
         if w.bias:
             out["b1"] = uniform_bf16(rng_for(seed, f, "b1"), (w.H,), w.b1_bound)
             out["b2"] = uniform_bf16(rng_for(seed, f, "b2"), (w.N,), w.b2_bound)
-    elif w.op == "geglu":
+    elif w.op in ("geglu", "glu_bwd"):
         out["Wg"] = uniform_bf16(rng_for(seed, f, "Wg"), (w.H, w.K), w.w1_bound)
         out["Wu"] = uniform_bf16(rng_for(seed, f, "Wu"), (w.H, w.K), w.w1_bound)
         out["Wd"] = uniform_bf16(rng_for(seed, f, "Wd"), (w.N, w.H), w.w2_bound)

@@ -22,6 +22,9 @@ raises.
     fmlp_moe_route(x, Wr, top_k)                    -> (expert_ids, gate_w[, logits]): top_k of x Wr^T,
                                                        softmax over the chosen logits
 
+    fmlp_linear_bwd(x, W, b, act, dy)               -> (dx, dW, db): gradients of fmlp_linear
+    fmlp_glu_bwd(x, Wg, Wu, Wd, gate_act, dy)       -> (dx, dWg, dWu, dWd): gradients of fmlp_glu
+
 Activations: "none", "gelu_erf", "gelu_tanh", "relu", "silu".
 """
 from __future__ import annotations
@@ -43,6 +46,10 @@ __all__ = [
     "fmlp_geglu",
     "fmlp_glu",
     "fmlp_glu_noalloc",
+    "fmlp_linear_bwd",
+    "fmlp_glu_bwd",
+    "bind_linear_bwd",
+    "bind_glu_bwd",
     "fmlp_moe_geglu",
     "fmlp_moe_glu",
     "fmlp_moe_route",
@@ -121,6 +128,13 @@ def lib() -> ctypes.CDLL:
         L.fmlp_moe_route.argtypes = [_p, _p, _i64, _i64, ctypes.c_int32, ctypes.c_int32, _p, _p, _p, _p]
         L.fmlp_glu_noalloc.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
         L.fmlp_glu_noalloc.restype = ctypes.c_int
+        L.fmlp_linear_bwd.argtypes = [_p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i64, _p, _p, _p, _p, _sz, _p]
+        L.fmlp_linear_bwd.restype = ctypes.c_int
+        L.fmlp_glu_bwd.argtypes = [_p, _p, _p, _p, ctypes.c_int, _p, _i64, _i64, _i64, _p, _p, _p, _p, _p, _sz, _p]
+        L.fmlp_glu_bwd.restype = ctypes.c_int
+        for f, n in (("fmlp_linear_bwd_workspace_size", 3), ("fmlp_glu_bwd_workspace_size", 3)):
+            getattr(L, f).argtypes = [_i64] * n
+            getattr(L, f).restype = _sz
         for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
                   "fmlp_moe_route", "fmlp_set_path"):
             getattr(L, f).restype = ctypes.c_int
@@ -362,6 +376,81 @@ def fmlp_glu_noalloc(x, Wg, Wu, Wd, gate_act: str = "silu", out=None):
         _check(lib().fmlp_glu_noalloc(_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), ACT[gate_act], M, D, H, _ptr(y),
                                       _stream(x.device)))
         return y
+
+
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+def _linear_bwd_call(x, W, b, act, dy, out, workspace):
+    _dev_tensor("x", x)
+    _dev_tensor("W", W)
+    _dev_tensor("dy", dy)
+    if b is not None:
+        _dev_tensor("b", b)
+    K = x.shape[-1]
+    N = W.shape[0]
+    if W.dim() != 2 or W.shape[1] != K:
+        raise ValueError(f"W must be [N, {K}], got {tuple(W.shape)}")
+    M = x.numel() // K
+    if dy.numel() != M * N:
+        raise ValueError(f"dy must hold {M} x {N} values")
+    if out is not None:
+        dx, dW, db = out
+    else:
+        dx = torch.empty_like(x)
+        dW = torch.empty_like(W)
+        db = torch.empty(N, dtype=torch.bfloat16, device=x.device) if b is not None else None
+    for n, t in (("dx", dx), ("dW", dW)):
+        _dev_tensor(n, t)
+    L = lib()
+    need = int(L.fmlp_linear_bwd_workspace_size(M, K, N))
+    ws = workspace if workspace is not None else workspace_for(x.device, need)
+    return BoundCall(L.fmlp_linear_bwd, (_ptr(x), _ptr(W), _ptr(b), ACT[act], _ptr(dy), M, K, N, _ptr(dx), _ptr(dW),
+                                         _ptr(db), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device)),
+                     (dx, dW, db), (x, W, b, dy, dx, dW, db, ws))
+
+
+def fmlp_linear_bwd(x, W, b, act: str, dy, out=None, workspace=None):
+    """Gradients of y = act(x W^T + b): returns (dx, dW, db) (db None without b)."""
+    with torch.cuda.device(x.device):
+        return _linear_bwd_call(x, W, b, act, dy, out, workspace)()
+
+
+def bind_linear_bwd(x, W, b, act: str, dy, out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _linear_bwd_call(x, W, b, act, dy, out, workspace)
+
+
+def _glu_bwd_call(x, Wg, Wu, Wd, gate_act, dy, out, workspace):
+    for n, t in (("x", x), ("Wg", Wg), ("Wu", Wu), ("Wd", Wd), ("dy", dy)):
+        _dev_tensor(n, t)
+    D = x.shape[-1]
+    H = Wg.shape[0]
+    if Wg.shape != (H, D) or Wu.shape != (H, D) or Wd.shape != (D, H) or dy.shape != x.shape:
+        raise ValueError("shape mismatch: x, dy [..., D]; Wg, Wu [H, D]; Wd [D, H]")
+    M = x.numel() // D
+    if out is not None:
+        dx, dWg, dWu, dWd = out
+    else:
+        dx, dWg, dWu, dWd = torch.empty_like(x), torch.empty_like(Wg), torch.empty_like(Wu), torch.empty_like(Wd)
+    L = lib()
+    need = int(L.fmlp_glu_bwd_workspace_size(M, D, H))
+    ws = workspace if workspace is not None else workspace_for(x.device, need)
+    return BoundCall(L.fmlp_glu_bwd, (_ptr(x), _ptr(Wg), _ptr(Wu), _ptr(Wd), ACT[gate_act], _ptr(dy), M, D, H,
+                                      _ptr(dx), _ptr(dWg), _ptr(dWu), _ptr(dWd), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream(x.device)),
+                     (dx, dWg, dWu, dWd), (x, Wg, Wu, Wd, dy, dx, dWg, dWu, dWd, ws))
+
+
+def fmlp_glu_bwd(x, Wg, Wu, Wd, gate_act: str, dy, out=None, workspace=None):
+    """Gradients of the gated block ("gelu_tanh": GeGLU): returns (dx, dWg, dWu, dWd)."""
+    with torch.cuda.device(x.device):
+        return _glu_bwd_call(x, Wg, Wu, Wd, gate_act, dy, out, workspace)()
+
+
+def bind_glu_bwd(x, Wg, Wu, Wd, gate_act: str, dy, out=None, workspace=None) -> BoundCall:
+    with torch.cuda.device(x.device):
+        return _glu_bwd_call(x, Wg, Wu, Wd, gate_act, dy, out, workspace)
 
 
 def fmlp_moe_workspace_size(T, D, H, E, top_k) -> int:

@@ -504,6 +504,192 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// Backward pass
+// ---------------------------------------------------------------------------
+namespace {
+// Token counts of a backward call bound the contraction over tokens, which the
+// GEMM reads with 32-bit offsets like any inner dimension.
+constexpr int64_t kBwdMaxTokens = kMaxInner;
+
+size_t ws_bf16(int64_t rows, int64_t cols) { return round_up((size_t)rows * (size_t)cols * 2, 256); }
+int64_t pad8(int64_t v) { return (v + 7) / 8 * 8; }
+
+struct LinearBwdLayout {
+  size_t dz, wt, dzt, xt, total;
+};
+LinearBwdLayout linear_bwd_layout(int64_t M, int64_t K, int64_t N) {
+  const int64_t Mp = pad8(M);
+  LinearBwdLayout L;
+  size_t o = 0;
+  L.dz = o;  o += ws_bf16(M, N);
+  L.wt = o;  o += ws_bf16(K, N);
+  L.dzt = o; o += ws_bf16(N, Mp);
+  L.xt = o;  o += ws_bf16(K, Mp);
+  L.total = o;
+  return L;
+}
+
+struct GluBwdLayout {
+  size_t wdt, dm, m, dgdu, wgut, dyt, mt, dgdut, xt, total;
+};
+GluBwdLayout glu_bwd_layout(int64_t M, int64_t D, int64_t H) {
+  const int64_t Mp = pad8(M);
+  GluBwdLayout L;
+  size_t o = 0;
+  L.wdt = o;   o += ws_bf16(H, D);
+  L.dm = o;    o += ws_bf16(M, H);
+  L.m = o;     o += ws_bf16(M, H);
+  L.dgdu = o;  o += ws_bf16(M, 2 * H);
+  L.wgut = o;  o += ws_bf16(D, 2 * H);
+  L.dyt = o;   o += ws_bf16(D, Mp);
+  L.mt = o;    o += ws_bf16(H, Mp);
+  L.dgdut = o; o += ws_bf16(2 * H, Mp);
+  L.xt = o;    o += ws_bf16(D, Mp);
+  L.total = o;
+  return L;
+}
+
+fmlp_status check_workspace(void* workspace, size_t workspace_bytes, size_t need) {
+  if (need == 0) return FMLP_OK;
+  if (workspace == nullptr) return fail(FMLP_E_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(workspace)) return fail(FMLP_E_ALIGN, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need) return fail(FMLP_E_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  return FMLP_OK;
+}
+
+#define HIP_TRY(expr, what)                               \
+  do {                                                    \
+    hipError_t e_ = (expr);                               \
+    if (e_ != hipSuccess) return launched(e_, what);      \
+  } while (0)
+}  // namespace
+
+extern "C" {
+
+size_t fmlp_linear_bwd_workspace_size(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K <= 0 || N <= 0) return 0;
+  return linear_bwd_layout(M, K, N).total;
+}
+
+fmlp_status fmlp_linear_bwd(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16* b, int act,
+                            const fmlp_bf16* dy, int64_t M, int64_t K, int64_t N, fmlp_bf16* dx, fmlp_bf16* dW,
+                            fmlp_bf16* db, void* workspace, size_t workspace_bytes, fmlp_stream stream) {
+  TRY(check_rows("M", M));
+  if (M >= kBwdMaxTokens) return fail(FMLP_E_SHAPE, "M=%lld must be below 2^22 for the backward pass", (long long)M);
+  TRY(check_inner("K", K));
+  TRY(check_inner("N", N));
+  TRY(check_act(act));
+  TOKEN_PTR(x, M);
+  REQUIRE_PTR(W);
+  OPTIONAL_PTR(b);
+  TOKEN_PTR(dy, M);
+  TOKEN_PTR(dx, M);
+  REQUIRE_PTR(dW);
+  OPTIONAL_PTR(db);
+  const LinearBwdLayout L = linear_bwd_layout(M, K, N);
+  TRY(check_workspace(workspace, workspace_bytes, L.total));
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {   // no tokens: the weight and bias gradients are sums over nothing
+    HIP_TRY(launch_fill_zero(dW, N * K, s), "linear_bwd zero dW");
+    if (db) HIP_TRY(launch_fill_zero(db, N, s), "linear_bwd zero db");
+    return ok();
+  }
+  char* ws = static_cast<char*>(workspace);
+  const int64_t Mp = pad8(M);
+  uint16_t* wt = reinterpret_cast<uint16_t*>(ws + L.wt);
+  uint16_t* dzt = reinterpret_cast<uint16_t*>(ws + L.dzt);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(ws + L.xt);
+  const uint16_t* dz = dy;
+  if (act != FMLP_ACT_NONE) {   // dz = dy * act'(x W^T + b): the forward GEMM with the derivative epilogue
+    uint16_t* dzw = reinterpret_cast<uint16_t*>(ws + L.dz);
+    GemmParams p = dense_params(x, K, W, nullptr, b, dzw, N, M, N, K, act, cus);
+    p.E = dy;
+    p.lde = N;
+    HIP_TRY(launch_gemm(GEMM_OUT_DACT, false, false, choose_tile(M, (N + 255) / 256, cus), p, s),
+            "linear_bwd dz launch");
+    dz = dzw;
+  }
+  // dx = dz W: the contraction runs over W's rows, so W is read transposed
+  HIP_TRY(launch_transpose(W, N, K, K, wt, N, N, s), "linear_bwd transpose W");
+  HIP_TRY(gemm_linear(dz, wt, nullptr, FMLP_ACT_NONE, M, N, K, dx, cus, s), "linear_bwd dx launch");
+  // dW = dz^T x and db = sum over tokens: both contract over the token rows
+  HIP_TRY(launch_transpose(dz, M, N, N, dzt, Mp, Mp, s), "linear_bwd transpose dz");
+  HIP_TRY(launch_transpose(x, M, K, K, xt, Mp, Mp, s), "linear_bwd transpose x");
+  HIP_TRY(gemm_linear(dzt, xt, nullptr, FMLP_ACT_NONE, N, Mp, K, dW, cus, s), "linear_bwd dW launch");
+  if (db) HIP_TRY(launch_rowsum(dzt, N, Mp, Mp, db, s), "linear_bwd db launch");
+  return ok();
+}
+
+size_t fmlp_glu_bwd_workspace_size(int64_t M, int64_t D, int64_t H) {
+  if (M < 0 || D <= 0 || H <= 0) return 0;
+  return glu_bwd_layout(M, D, H).total;
+}
+
+fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd,
+                         int gate_act, const fmlp_bf16* dy, int64_t M, int64_t D, int64_t H, fmlp_bf16* dx,
+                         fmlp_bf16* dWg, fmlp_bf16* dWu, fmlp_bf16* dWd, void* workspace, size_t workspace_bytes,
+                         fmlp_stream stream) {
+  TRY(check_rows("M", M));
+  if (M >= kBwdMaxTokens) return fail(FMLP_E_SHAPE, "M=%lld must be below 2^22 for the backward pass", (long long)M);
+  TRY(check_inner("D", D));
+  TRY(check_inner("H", H));
+  if (2 * H >= kMaxInner) return fail(FMLP_E_SHAPE, "H=%lld: 2H must be below 2^22", (long long)H);
+  TRY(check_act(gate_act, "gate_act"));
+  TOKEN_PTR(x, M);
+  REQUIRE_PTR(Wg);
+  REQUIRE_PTR(Wu);
+  REQUIRE_PTR(Wd);
+  TOKEN_PTR(dy, M);
+  TOKEN_PTR(dx, M);
+  REQUIRE_PTR(dWg);
+  REQUIRE_PTR(dWu);
+  REQUIRE_PTR(dWd);
+  const GluBwdLayout L = glu_bwd_layout(M, D, H);
+  TRY(check_workspace(workspace, workspace_bytes, L.total));
+  int cus = 0;
+  TRY(check_device(&cus));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    HIP_TRY(launch_fill_zero(dWg, H * D, s), "glu_bwd zero dWg");
+    HIP_TRY(launch_fill_zero(dWu, H * D, s), "glu_bwd zero dWu");
+    HIP_TRY(launch_fill_zero(dWd, D * H, s), "glu_bwd zero dWd");
+    return ok();
+  }
+  char* ws = static_cast<char*>(workspace);
+  auto at = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  const int64_t Mp = pad8(M);
+  // dm = dy Wd (contraction over Wd's rows: Wd read transposed)
+  HIP_TRY(launch_transpose(Wd, D, H, H, at(L.wdt), D, D, s), "glu_bwd transpose Wd");
+  HIP_TRY(gemm_linear(dy, at(L.wdt), nullptr, FMLP_ACT_NONE, M, D, H, at(L.dm), cus, s), "glu_bwd dm launch");
+  // the gate+up GEMM again, with the derivative epilogue: m, and [dg | du]
+  GemmParams p = dense_params(x, D, Wg, Wu, nullptr, at(L.m), H, M, H, D, gate_act, cus);
+  p.E = at(L.dm);
+  p.lde = H;
+  p.C2 = at(L.dgdu);
+  p.ldc2 = 2 * H;
+  HIP_TRY(launch_gemm(GEMM_OUT_DGLU, false, false, choose_tile(M, (H + 127) / 128, cus), p, s),
+          "glu_bwd gate+up launch");
+  // dx = dg Wg + du Wu = [dg | du] [Wg ; Wu]: one GEMM over 2H
+  HIP_TRY(launch_transpose(Wg, H, D, D, at(L.wgut), 2 * H, H, s), "glu_bwd transpose Wg");
+  HIP_TRY(launch_transpose(Wu, H, D, D, at(L.wgut) + H, 2 * H, H, s), "glu_bwd transpose Wu");
+  HIP_TRY(gemm_linear(at(L.dgdu), at(L.wgut), nullptr, FMLP_ACT_NONE, M, 2 * H, D, dx, cus, s), "glu_bwd dx launch");
+  // weight gradients: contractions over the token rows
+  HIP_TRY(launch_transpose(dy, M, D, D, at(L.dyt), Mp, Mp, s), "glu_bwd transpose dy");
+  HIP_TRY(launch_transpose(at(L.m), M, H, H, at(L.mt), Mp, Mp, s), "glu_bwd transpose m");
+  HIP_TRY(launch_transpose(at(L.dgdu), M, 2 * H, 2 * H, at(L.dgdut), Mp, Mp, s), "glu_bwd transpose dg|du");
+  HIP_TRY(launch_transpose(x, M, D, D, at(L.xt), Mp, Mp, s), "glu_bwd transpose x");
+  HIP_TRY(gemm_linear(at(L.dyt), at(L.mt), nullptr, FMLP_ACT_NONE, D, Mp, H, dWd, cus, s), "glu_bwd dWd launch");
+  HIP_TRY(gemm_linear(at(L.dgdut), at(L.xt), nullptr, FMLP_ACT_NONE, H, Mp, D, dWg, cus, s), "glu_bwd dWg launch");
+  HIP_TRY(gemm_linear(at(L.dgdut) + H * Mp, at(L.xt), nullptr, FMLP_ACT_NONE, H, Mp, D, dWu, cus, s),
+          "glu_bwd dWu launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // FP8-weight decode calls
 // ---------------------------------------------------------------------------
 extern "C" size_t fmlp_w8_workspace_size(int64_t M, int64_t H) {

@@ -90,6 +90,44 @@ __device__ __forceinline__ float act_of(float z) {
   else return z;
 }
 
+// ---------------------------------------------------------------------------
+// Backward epilogues: each activation and its derivative at z, from the same
+// formulas (and the same hardware exp2 / reciprocal) as the forward ones.
+//   gelu_erf   a = z Phi(z),        a' = Phi(z) + z phi(z)
+//   gelu_tanh  a = z s, s = sigmoid(2u), u = sqrt(2/pi)(z + 0.044715 z^3),
+//              a' = s + 2 z s (1 - s) sqrt(2/pi)(1 + 3*0.044715 z^2)
+//              ((1 + tanh u)/2 = s and (1 - tanh^2 u)/2 = 2 s (1 - s))
+//   relu       a = max(z, 0),       a' = 1 for z > 0, else 0
+//   silu       a = z s, s = sigmoid(z), a' = s (1 + z (1 - s))
+// In the far tails exp2 saturates to inf or 0 and s to 0 or 1, which gives
+// the limits a' -> 0 and a' -> 1 with no NaN.
+// ---------------------------------------------------------------------------
+template <int ACT>
+__device__ __forceinline__ void act_and_grad(float z, float& a, float& da) {
+  if constexpr (ACT == ACT_GELU_ERF) {
+    const float Phi = 0.5f * erfcf(-0.70710678118654752440f * z);
+    const float phi = 0.39894228040143267794f * __builtin_amdgcn_exp2f(-0.72134752044448170368f * z * z);
+    a = z * Phi;
+    da = fmaf(z, phi, Phi);
+  } else if constexpr (ACT == ACT_GELU_TANH) {
+    const float k = 0.79788456080286535588f;
+    const float u = k * fmaf(0.044715f * z, z * z, z);
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-2.88539008177792681472f * u));
+    a = z * s;
+    da = fmaf(2.0f * z * s * (1.0f - s), k * fmaf(0.134145f * z, z, 1.0f), s);
+  } else if constexpr (ACT == ACT_RELU) {
+    a = z > 0.f ? z : 0.f;
+    da = z > 0.f ? 1.f : 0.f;
+  } else if constexpr (ACT == ACT_SILU) {
+    const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896340736f * z));
+    a = z * s;
+    da = s * fmaf(z, 1.0f - s, 1.0f);
+  } else {
+    a = z;
+    da = 1.f;
+  }
+}
+
 __device__ __forceinline__ float apply_act(float z, int act) {
   if (act == ACT_GELU_ERF) return gelu_erf(z);
   if (act == ACT_GELU_TANH) return gelu_tanh(z);

@@ -17,6 +17,12 @@
 //   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights),
 //                        optionally split over K into parts that each write
 //                        their own copy (summed in order by the caller)
+//   GEMM_OUT_DACT        backward of a Linear + activation: the forward GEMM
+//                        recomputes z = x W^T + b in registers and writes only
+//                        dz = dy * act'(z)
+//   GEMM_OUT_DGLU        backward of the gated block: the gate+up GEMM
+//                        recomputes g and u and, with the incoming dm, writes
+//                        m = act(g) * u, dg = dm * u * act'(g) and du = dm * act(g)
 //
 // Structure: a block computes a BM x BN tile with WAVES_M x WAVES_N waves
 // (256 x 256 with 8 waves of 128 x 64 for large inputs: two waves per SIMD,
@@ -134,8 +140,9 @@ __device__ __forceinline__ void pin_agpr_ordered(f32x4_t& acc) { asm volatile(""
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 #pragma clang diagnostic pop
 
-// GACT: the gate activation of a gated (GEMM_OUT_GEGLU) kernel, fixed per
-// kernel so each carries one epilogue: with several epilogue copies behind a
+// GACT: the gate activation of a gated (GEMM_OUT_GEGLU, GEMM_OUT_DGLU) kernel,
+// or the activation of a GEMM_OUT_DACT kernel, fixed per kernel so each
+// carries one epilogue: with several epilogue copies behind a
 // runtime switch, the register allocator copied accumulator lanes out of AGPRs
 // inside the main loop, a few wait states after the (asm) MFMA that wrote them.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED,
@@ -147,7 +154,7 @@ gemm_bf16_kernel(GemmParams p) {
   constexpr int TN = BN / WAVES_N;   // wave tile width in B-tile rows
   constexpr int FM = TM / 16;
   constexpr int FN = TN / 16;
-  constexpr bool DUAL = (OUT == GEMM_OUT_GEGLU);
+  constexpr bool DUAL = (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU);
   constexpr int HALF = FN / 2;       // DUAL: gate fragments [0,HALF), up [HALF,FN)
   constexpr int CH = BK / 8;         // 16-byte chunks per LDS row
   constexpr int KS = BK / 32;        // MFMA k-steps per stage
@@ -419,6 +426,41 @@ gemm_bf16_kernel(GemmParams p) {
           }
           if (row_ok && n < N) gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
         }
+      } else if constexpr (OUT == GEMM_OUT_DGLU) {
+        // recomputed g and u with the incoming dm: m for the down projection's
+        // weight gradient, dg and du for the input and gate/up weight gradients
+#pragma unroll
+        for (int q = 0; q < HALF / 2; ++q) {
+          const int64_t n = t.n0 + wn * (TN / 2) + q * 32 + 8 * lg;
+          pin_agpr_ordered(acc[i][2 * q]);
+          pin_agpr_ordered(acc[i][2 * q + 1]);
+          pin_agpr_ordered(acc[i][HALF + 2 * q]);
+          pin_agpr_ordered(acc[i][HALF + 2 * q + 1]);
+          float g[8], u[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            g[r] = acc[i][2 * q][r];
+            g[4 + r] = acc[i][2 * q + 1][r];
+            u[r] = acc[i][HALF + 2 * q][r];
+            u[4 + r] = acc[i][HALF + 2 * q + 1][r];
+          }
+          if (!(row_ok && n < N)) continue;
+          float dm[8];
+          unpack_bf16x8(gld16(p.E + lrow * p.lde + n), dm);
+          float m[8], dg[8], du[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r) {
+            float a, da;
+            act_and_grad<ACT>(g[r], a, da);
+            m[r] = a * u[r];
+            dg[r] = dm[r] * u[r] * da;
+            du[r] = dm[r] * a;
+          }
+          gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(m));
+          uint16_t* d2 = static_cast<uint16_t*>(p.C2) + lrow * p.ldc2 + n;
+          gst16(d2, pack_bf16x8(dg));
+          gst16(d2 + N, pack_bf16x8(du));
+        }
       } else {
 #pragma unroll
         for (int q = 0; q < FN / 2; ++q) {
@@ -450,8 +492,20 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
               for (int r = 0; r < 8; ++r) v[r] += b[r];
             }
+            if constexpr (OUT == GEMM_OUT_DACT) {
+              // the recomputed pre-activation z: dz = dy * act'(z)
+              float dy[8];
+              unpack_bf16x8(gld16(p.E + lrow * p.lde + n), dy);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) v[r] = act_of<ACT>(v[r]);
+              for (int r = 0; r < 8; ++r) {
+                float a, da;
+                act_and_grad<ACT>(v[r], a, da);
+                v[r] = dy[r] * da;
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 8; ++r) v[r] = act_of<ACT>(v[r]);
+            }
             gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
           }
         }
@@ -460,8 +514,8 @@ gemm_bf16_kernel(GemmParams p) {
   };
   auto epilogue = [&](const Tile& t) {
     mfma_drain();
-    if constexpr (OUT == GEMM_OUT_GEGLU) {
-      epilogue_act(t, std::integral_constant<int, GACT>{});   // the gate's activation
+    if constexpr (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU || OUT == GEMM_OUT_DACT) {
+      epilogue_act(t, std::integral_constant<int, GACT>{});   // the (gate's) activation
     } else if constexpr (OUT == GEMM_OUT_BF16) {
       if (p.act == ACT_GELU_ERF) epilogue_act(t, std::integral_constant<int, ACT_GELU_ERF>{});
       else if (p.act == ACT_GELU_TANH) epilogue_act(t, std::integral_constant<int, ACT_GELU_TANH>{});
@@ -598,7 +652,7 @@ gemm_bf16_kernel(GemmParams p) {
 
 template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED, int GACT>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
-  constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU) ? BN / 2 : BN;
+  constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
   p.tiles_n = (int)((p.N + OUT_N - 1) / OUT_N);
   p.group_m = 4;
@@ -621,8 +675,8 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
 
 template <int OUT, bool GATHER, bool GROUPED, int GACT = ACT_NONE>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
-  if constexpr (OUT == GEMM_OUT_GEGLU && GACT == ACT_NONE) {
-    // one kernel per gate activation
+  if constexpr ((OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU || OUT == GEMM_OUT_DACT) && GACT == ACT_NONE) {
+    // one kernel per (gate) activation
     switch (p.act) {
       case ACT_GELU_TANH: return launch_tile<OUT, GATHER, GROUPED, ACT_GELU_TANH>(tile, p, s);
       case ACT_GELU_ERF: return launch_tile<OUT, GATHER, GROUPED, ACT_GELU_ERF>(tile, p, s);
@@ -655,6 +709,9 @@ hipError_t launch_gemm(int out_kind, bool gather, bool grouped, int tile, GemmPa
   if (out_kind == GEMM_OUT_GEGLU && !gather && !grouped) return launch_tile<GEMM_OUT_GEGLU, false, false>(tile, p, s);
   if (out_kind == GEMM_OUT_GEGLU && gather && grouped) return launch_tile<GEMM_OUT_GEGLU, true, true>(tile, p, s);
   if (out_kind == GEMM_OUT_F32_SCALED && !gather && grouped) return launch_tile<GEMM_OUT_F32_SCALED, false, true>(tile, p, s);
+  if (out_kind == GEMM_OUT_DACT && !gather && !grouped && tile != TILE_128x192)
+    return launch_tile<GEMM_OUT_DACT, false, false>(tile, p, s);
+  if (out_kind == GEMM_OUT_DGLU && !gather && !grouped) return launch_tile<GEMM_OUT_DGLU, false, false>(tile, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -14,6 +14,9 @@ enum GemmOut : int {
   GEMM_OUT_BF16 = 0,        // C bf16 = act(acc + bias)
   GEMM_OUT_GEGLU = 1,       // B0 = Wg, B1 = Wu; C bf16 [rows, N] = act(g) * u
   GEMM_OUT_F32_SCALED = 2,  // C fp32 = acc * row_scale[row]
+  GEMM_OUT_DACT = 3,        // backward: C bf16 = E * act'(acc + bias)  (E = dy, z recomputed)
+  GEMM_OUT_DGLU = 4,        // backward, B0 = Wg, B1 = Wu, E = dm [rows, N]: C = m = act(g) * u,
+                            // C2 [rows, 2N]: columns [0, N) dg = dm * u * act'(g), [N, 2N) du = dm * act(g)
 };
 
 struct GemmParams {
@@ -37,10 +40,29 @@ struct GemmParams {
   int ksplit;                // GEMM_OUT_F32_SCALED: K split into this many equal parts (0 or 1: none);
                              // part j of a tile writes C + j * c_kstride
   int64_t c_kstride;
+  const uint16_t* E;         // GEMM_OUT_DACT / GEMM_OUT_DGLU: the incoming gradient tile source
+  int64_t lde;               //   (bf16, row stride lde)
+  void* C2;                  // GEMM_OUT_DGLU: dg | du output, bf16, row stride ldc2
+  int64_t ldc2;
   int cus;                   // compute units: the persistent grid's size cap
   // launch geometry, filled by launch_gemm
   int tiles_m, tiles_n, group_m;
 };
+
+// ---------------------------------------------------------------------------
+// Layout helpers of the backward pass (transpose.hip).
+// ---------------------------------------------------------------------------
+// out[c, r] = in[r, c] for bf16 in [R, C] (row stride ldi) into out with row
+// stride ldo starting at column 0; columns R .. ldo_pad-1 of every output row
+// are written as zeros (the contraction over R may then run to ldo_pad).
+hipError_t launch_transpose(const uint16_t* in, int64_t R, int64_t C, int64_t ldi, uint16_t* out, int64_t ldo,
+                            int64_t ldo_pad, hipStream_t s);
+// out[r] = bf16(sum_c in[r, c]) for bf16 in [R, C] (row stride ld), summed in
+// fp32 in a fixed order (deterministic).
+hipError_t launch_rowsum(const uint16_t* in, int64_t R, int64_t C, int64_t ld, uint16_t* out, hipStream_t s);
+
+// out[0, n) = 0 (bf16): the weight gradients of a call with no tokens.
+hipError_t launch_fill_zero(uint16_t* out, int64_t n, hipStream_t s);
 
 // Tile configurations compiled in.
 enum GemmTile : int {

@@ -154,6 +154,51 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
 size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
 
 /*
+ * Backward pass (training)
+ *
+ * The gradients of fmlp_linear and fmlp_glu for an upstream gradient dy: the
+ * chain rule on the forward definitions.  The pages profile the forward only;
+ * the fused gelu*mul of "Profiling in PyTorch (Part 2)", section "Let's use
+ * hand tuned kernels" (LigerGELUMulFunction) is an autograd Function whose
+ * backward the page does not describe.  Activations' derivatives:
+ *   gelu_erf   Phi(z) + z phi(z)
+ *   gelu_tanh  (1 + tanh u)/2 + z/2 (1 - tanh^2 u) sqrt(2/pi)(1 + 3*0.044715 z^2),
+ *              u = sqrt(2/pi)(z + 0.044715 z^3)
+ *   relu       1 for z > 0, else 0;   silu  sigmoid(z)(1 + z(1 - sigmoid(z)))
+ * Pre-activations are recomputed by the forward GEMM with a derivative
+ * epilogue (nothing of the forward is saved).  Every gradient is accumulated
+ * in fp32 and written as bf16 once; the intermediate dz (or dm, m, dg, du) is
+ * rounded to bf16 once before the GEMM that consumes it, as eager PyTorch
+ * stores it.  Results are bitwise deterministic.  Operands that a backward
+ * GEMM contracts over their rows are first written transposed into the
+ * workspace.  Outputs are caller-owned bf16, must not alias inputs, and
+ * M < 2^22; with M == 0 the weight and bias gradients are written as zeros.
+ * Workspace: the *_bwd_workspace_size bytes, no initialisation needed.
+ */
+
+/* Linear + activation, y = act(x[M,K] . W[N,K]^T + b[N]):
+ *   dz = dy[M,N] * act'(x W^T + b),  dx[M,K] = dz W,  dW[N,K] = dz^T x,
+ *   db[N] = sum over tokens of dz.
+ * b may be NULL (no bias in the forward); db may be NULL (not computed). */
+fmlp_status fmlp_linear_bwd(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16* b, int act,
+                            const fmlp_bf16* dy, int64_t M, int64_t K, int64_t N,
+                            fmlp_bf16* dx, fmlp_bf16* dW, fmlp_bf16* db,
+                            void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_linear_bwd_workspace_size(int64_t M, int64_t K, int64_t N);
+
+/* The gated block, y = (gate_act(x Wg^T) * (x Wu^T)) Wd^T (FMLP_ACT_GELU_TANH:
+ * GeGLU), x [M,D], Wg, Wu [H,D], Wd [D,H], dy [M,D]:
+ *   g = x Wg^T, u = x Wu^T, m = act(g) * u, dWd[D,H] = dy^T m, dm = dy Wd,
+ *   dg = dm * u * act'(g), du = dm * act(g),
+ *   dx[M,D] = dg Wg + du Wu,  dWg[H,D] = dg^T x,  dWu[H,D] = du^T x.
+ * 2H must be below 2^22. */
+fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* Wu, const fmlp_bf16* Wd,
+                         int gate_act, const fmlp_bf16* dy, int64_t M, int64_t D, int64_t H,
+                         fmlp_bf16* dx, fmlp_bf16* dWg, fmlp_bf16* dWu, fmlp_bf16* dWd,
+                         void* workspace, size_t workspace_bytes, fmlp_stream stream);
+size_t fmlp_glu_bwd_workspace_size(int64_t M, int64_t D, int64_t H);
+
+/*
  * fmlp_glu without a workspace argument, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc).  Same arguments, kernels, paths, results and errors

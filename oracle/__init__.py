@@ -15,6 +15,7 @@ from .fmlp_oracle import (  # noqa: F401
     gelu_tanh,
     glu,
     glu_bwd,
+    glu_bwd_sampled,
     glu_w8,
     linear,
     linear_bwd,

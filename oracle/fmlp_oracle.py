@@ -72,6 +72,7 @@ __all__ = [
     "linear_bwd",
     "mlp2_bwd",
     "glu_bwd",
+    "glu_bwd_sampled",
 ]
 
 ACTS = ("none", "gelu_erf", "gelu_tanh", "relu", "silu")
@@ -401,3 +402,31 @@ def glu_bwd(x, Wg, Wu, Wd, gate_act: str, dy):
     dg = dm * u * act_grad(g, gate_act)
     du = dm * a
     return dg @ Wg + du @ Wu, dg.T @ x, du.T @ x, dWd
+
+
+def glu_bwd_sampled(x, Wg, Wu, Wd, gate_act: str, dy, rows, hidden):
+    """Exactly the entries glu_bwd returns for a subset, without the full
+    products (for full-size shapes):
+      dx[rows]          needs dg, du of those token rows only (all hidden units);
+      dWg[hidden], dWu[hidden], dWd[:, hidden]
+                        need g, u, dm of those hidden units only (all tokens).
+    Same definitions as glu_bwd; returns (dx_rows, dWg_h, dWu_h, dWd_h)."""
+    x = _f64(x)
+    Wg, Wu, Wd = _f64(Wg), _f64(Wu), _f64(Wd)
+    dy = _f64(dy)
+    rows = np.asarray(rows)
+    hidden = np.asarray(hidden)
+    # token rows: every hidden unit
+    xr, dyr = x[rows], dy[rows]
+    g, u = xr @ Wg.T, xr @ Wu.T
+    a = activation(g, gate_act)
+    dm = dyr @ Wd
+    dx = (dm * u * act_grad(g, gate_act)) @ Wg + (dm * a) @ Wu
+    # hidden units: every token
+    g = x @ Wg[hidden].T
+    u = x @ Wu[hidden].T
+    a = activation(g, gate_act)
+    dm = dy @ Wd[:, hidden]
+    dg = dm * u * act_grad(g, gate_act)
+    du = dm * a
+    return dx, dg.T @ x, du.T @ x, dy.T @ (a * u)

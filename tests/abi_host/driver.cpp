@@ -94,6 +94,29 @@ int main() {
          FMLP_E_WORKSPACE);
   expect("glu_w8 null scale", fmlp_glu_w8(X, Q, S, Q, S, Q, nullptr, 2, 4, 64, 128, Y, WS, 1 << 20, nullptr),
          FMLP_E_NULL);
+  // backward
+  const size_t wsl = fmlp_linear_bwd_workspace_size(64, 256, 512);
+  expect("linear_bwd null dW", fmlp_linear_bwd(X, W, B, 1, X, 64, 256, 512, Y, nullptr, nullptr, WS, wsl, nullptr),
+         FMLP_E_NULL);
+  expect("linear_bwd small ws", fmlp_linear_bwd(X, W, B, 1, X, 64, 256, 512, Y, Y, nullptr, WS, wsl - 1, nullptr),
+         FMLP_E_WORKSPACE);
+  expect("linear_bwd bad act", fmlp_linear_bwd(X, W, B, 7, X, 64, 256, 512, Y, Y, nullptr, WS, wsl, nullptr),
+         FMLP_E_ARG);
+  expect("linear_bwd K%8", fmlp_linear_bwd(X, W, B, 1, X, 64, 250, 512, Y, Y, nullptr, WS, wsl, nullptr),
+         FMLP_E_ALIGN);
+  expect("linear_bwd huge M", fmlp_linear_bwd(X, W, B, 1, X, int64_t(1) << 22, 256, 512, Y, Y, nullptr, WS,
+                                              size_t(1) << 40, nullptr),
+         FMLP_E_SHAPE);
+  const size_t wsb = fmlp_glu_bwd_workspace_size(64, 256, 512);
+  expect("glu_bwd small ws", fmlp_glu_bwd(X, W, W, W, 2, X, 64, 256, 512, Y, Y, Y, Y, WS, wsb - 1, nullptr),
+         FMLP_E_WORKSPACE);
+  expect("glu_bwd null dWd", fmlp_glu_bwd(X, W, W, W, 2, X, 64, 256, 512, Y, Y, Y, nullptr, WS, wsb, nullptr),
+         FMLP_E_NULL);
+  expect("glu_bwd bad gate", fmlp_glu_bwd(X, W, W, W, 9, X, 64, 256, 512, Y, Y, Y, Y, WS, wsb, nullptr),
+         FMLP_E_ARG);
+  expect("glu_bwd huge H", fmlp_glu_bwd(X, W, W, W, 2, X, 64, 256, int64_t(1) << 21, Y, Y, Y, Y, WS,
+                                        size_t(1) << 50, nullptr),
+         FMLP_E_SHAPE);
   // support calls
   for (int st = 0; st < 8; ++st)
     if (std::strncmp(fmlp_status_string((fmlp_status)st), "FMLP_", 5) != 0) {

@@ -40,4 +40,11 @@ hipError_t launch_moe_router(const uint16_t*, const uint16_t*, int64_t, int, int
   reached("launch_moe_router");
 }
 hipError_t launch_decode_w8(const W8Layer&, int, hipStream_t) { reached("launch_decode_w8"); }
+hipError_t launch_transpose(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, int64_t, int64_t, hipStream_t) {
+  reached("launch_transpose");
+}
+hipError_t launch_rowsum(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, hipStream_t) {
+  reached("launch_rowsum");
+}
+hipError_t launch_fill_zero(uint16_t*, int64_t, hipStream_t) { reached("launch_fill_zero"); }
 }  // namespace fmlp

@@ -673,6 +673,23 @@ def check_glu_bwd_directional(o):
             assert abs(fd - got) <= 1e-7 * max(1.0, abs(got)), (act, i, fd, got)
 
 
+def check_glu_bwd_sampled(o):
+    """The sampled backward equals the full backward restricted to its rows
+    and hidden units (it is a restriction of the same definitions)."""
+    rng = np.random.default_rng(21)
+    M, D, H = 9, 8, 12
+    x, dy = _bf16ish(rng, (M, D)), _bf16ish(rng, (M, D))
+    Wg, Wu, Wd = _bf16ish(rng, (H, D), 0.5), _bf16ish(rng, (H, D), 0.5), _bf16ish(rng, (D, H), 0.5)
+    rows, hidden = np.array([0, 3, 8]), np.array([1, 2, 7, 11])
+    for act in ("gelu_tanh", "silu"):
+        full = o.glu_bwd(x, Wg, Wu, Wd, act, dy)
+        got = o.glu_bwd_sampled(x, Wg, Wu, Wd, act, dy, rows, hidden)
+        _close(got[0], full[0][rows], rtol=1e-13, atol=1e-14, what="sampled dx")
+        _close(got[1], full[1][hidden], rtol=1e-13, atol=1e-14, what="sampled dWg")
+        _close(got[2], full[2][hidden], rtol=1e-13, atol=1e-14, what="sampled dWu")
+        _close(got[3], full[3][:, hidden], rtol=1e-13, atol=1e-14, what="sampled dWd")
+
+
 def check_backward_special_cases(o):
     """Identity weights: dx = dy * act'(x) with W = I; W = 0 gives dx = 0 and
     dW = dz^T x with dz = dy * act'(b); the gated block's gradient through
@@ -708,6 +725,7 @@ ALL_CHECKS = [
     check_backward_library,
     check_glu_bwd_directional,
     check_backward_special_cases,
+    check_glu_bwd_sampled,
     check_linear_bruteforce,
     check_mlp2_bruteforce,
     check_geglu_bruteforce,

@@ -56,3 +56,11 @@ def test_algorithmic_counts():
     m = dg.workload("moe")
     assert m.flops == 2_886_218_022_912
     assert m.weight_bytes == 8 * 3 * 4096 * 14336 * 2
+
+
+def test_backward_counts_are_twice_the_forward_products():
+    for name in ("geglu768", "large4096"):
+        f, b = dg.workload(name), dg.workload(name + "_bwd")
+        assert (b.M, b.K, b.H, b.N, b.family) == (f.M, f.K, f.H, f.N, f.family)
+        assert b.flops == 2 * f.flops
+        assert b.bytes == 2 * 3 * 2 * f.K * f.H + 3 * 2 * f.M * f.K
