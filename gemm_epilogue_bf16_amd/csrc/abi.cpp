@@ -520,7 +520,7 @@ struct LinearBwdLayout {
 LinearBwdLayout linear_bwd_layout(int64_t M, int64_t K, int64_t N) {
   const int64_t Mp = pad8(M);
   LinearBwdLayout L;
-  size_t o = 0;
+  size_t o = kHeader;   // the decode header stays untouched: one workspace serves every call
   L.dz = o;  o += ws_bf16(M, N);
   L.wt = o;  o += ws_bf16(K, N);
   L.dzt = o; o += ws_bf16(N, Mp);
@@ -535,7 +535,7 @@ struct GluBwdLayout {
 GluBwdLayout glu_bwd_layout(int64_t M, int64_t D, int64_t H) {
   const int64_t Mp = pad8(M);
   GluBwdLayout L;
-  size_t o = 0;
+  size_t o = kHeader;
   L.wdt = o;   o += ws_bf16(H, D);
   L.dm = o;    o += ws_bf16(M, H);
   L.m = o;     o += ws_bf16(M, H);

@@ -46,6 +46,7 @@
 // interleaved so each lane ends with 8 consecutive output columns of one row,
 // stored as one 16-byte write.
 #include <algorithm>
+#include <type_traits>
 #include <utility>
 
 #include "common.h"
@@ -81,36 +82,75 @@ __host__ __device__ constexpr int swz_b(int r) {
   else return ((r >> 1) & 1) | ((r >> 2) & 6);
 }
 
-// Weight fragment f of a wave covers tile rows w_lane_row + w_delta(f): the
-// rows of a fragment pair interleave, so lane group g ends up holding output
-// columns 8g .. 8g+7 of the pair's 32 columns; with two weight sets, fragments
-// [0, FN/2) read the first and [FN/2, FN) the second.
-__host__ __device__ constexpr int w_delta(int f, int FN, int BN, bool dual) {
+// Weight fragment f of a wave covers tile rows w_lane_row + w_delta(f), with
+// the rows permuted so that every lane ends up holding runs of 8 consecutive
+// output columns (one 16-byte store each):
+//   16x16x32 (M32 = false): the rows of a fragment pair interleave, so lane
+//     group g holds columns 8g .. 8g+7 of the pair's 32 columns;
+//   32x32x16 (M32 = true): fragment row i (= lane % 32) reads weight row
+//     rho(i) = 16 (i >> 4) + 8 ((i >> 2) & 1) + 4 ((i >> 3) & 1) + (i & 3), so
+//     the 16 results of lane half h (accumulator registers 0-7 and 8-15) are
+//     columns 8h .. 8h+7 and 16+8h .. 16+8h+7 of the fragment's 32.
+// With two weight sets, fragments [0, FN/2) read the first and [FN/2, FN) the
+// second.
+__host__ __device__ constexpr int rho32(int i) {
+  return 16 * (i >> 4) + 8 * ((i >> 2) & 1) + 4 * ((i >> 3) & 1) + (i & 3);
+}
+__host__ __device__ constexpr int w_delta(int f, int FN, int BN, bool dual, bool m32) {
   const int half = FN / 2;
   const int set = dual ? f / half : 0;
   const int fl = dual ? f % half : f;
-  return set * (BN / 2) + (fl >> 1) * 32 + 4 * (fl & 1);
+  return set * (BN / 2) + (m32 ? fl * 32 : (fl >> 1) * 32 + 4 * (fl & 1));
 }
-__host__ __device__ constexpr int w_lane_row(int wn, int li, int TN, bool dual) {
-  return wn * (dual ? TN / 2 : TN) + 8 * (li >> 2) + (li & 3);
+__host__ __device__ constexpr int w_lane_row(int wn, int li, int TN, bool dual, bool m32) {
+  return wn * (dual ? TN / 2 : TN) + (m32 ? rho32(li) : 8 * (li >> 2) + (li & 3));
 }
 // The swizzles read only bits 1-4 of a row, so every fragment of a wave has
 // the same chunk permutation as its first one and its LDS address is the
 // first one's plus a constant.  Checked exhaustively at compile time.
-template <int CH, int TM, int TN, int FM, int FN, int BN, int WAVES_M, int WAVES_N, bool DUAL>
+template <int CH, int TM, int TN, int FM, int FN, int BN, int WAVES_M, int WAVES_N, bool DUAL, bool M32>
 constexpr bool fragment_swizzle_is_uniform() {
-  for (int li = 0; li < 16; ++li) {
+  constexpr int MR = M32 ? 32 : 16;
+  for (int li = 0; li < MR; ++li) {
     for (int wm = 0; wm < WAVES_M; ++wm)
       for (int f = 0; f < FM; ++f)
-        if (swz_a<CH>(wm * TM + f * 16 + li) != swz_a<CH>(wm * TM + li)) return false;
+        if (swz_a<CH>(wm * TM + f * MR + li) != swz_a<CH>(wm * TM + li)) return false;
     for (int wn = 0; wn < WAVES_N; ++wn) {
-      const int r0 = w_lane_row(wn, li, TN, DUAL);
+      const int r0 = w_lane_row(wn, li, TN, DUAL, M32);
       for (int f = 0; f < FN; ++f)
-        if (swz_b<CH>(r0 + w_delta(f, FN, BN, DUAL)) != swz_b<CH>(r0)) return false;
+        if (swz_b<CH>(r0 + w_delta(f, FN, BN, DUAL, M32)) != swz_b<CH>(r0)) return false;
     }
   }
   return true;
 }
+// The 32-row fragment reads are bank-conflict free under the measured model
+// of a ds_read_b128 (four 16-lane cycles; cycle of lane l: l >> 5 and the
+// parity of the bits of (l >> 2) & 7; units within a cycle distinct mod 16):
+// checked exhaustively at compile time for both operands' row maps.
+template <int CH>
+constexpr bool m32_reads_conflict_free(bool weights) {
+  if (CH != 8) return false;
+  for (int c0 = 0; c0 < CH; c0 += 2)
+    for (int base = 0; base < 256; base += 32)
+      for (int cyc = 0; cyc < 4; ++cyc) {
+        bool seen[16] = {};
+        for (int l = 0; l < 64; ++l) {
+          const int q = (l >> 2) & 7;
+          const int par = (q ^ (q >> 1) ^ (q >> 2)) & 1;
+          if (((l >> 5) << 1 | par) != cyc) continue;
+          const int i = l & 31;
+          const int r = base + (weights ? rho32(i) : i);
+          const int c = c0 + (l >> 5);
+          const int slot = c ^ (weights ? swz_b<CH>(r) : swz_a<CH>(r));
+          const int unit = (r * CH + slot) & 15;
+          if (seen[unit]) return false;
+          seen[unit] = true;
+        }
+      }
+  return true;
+}
+static_assert(m32_reads_conflict_free<8>(false) && m32_reads_conflict_free<8>(true),
+              "32-row fragment reads of 128-byte rows");
 
 // The main loop interleaves MFMAs with loads and LDS reads in a fixed order.
 // Instruction selection moves an MFMA builtin freely (it touches no memory),
@@ -122,6 +162,12 @@ constexpr bool fragment_swizzle_is_uniform() {
 __device__ __forceinline__ void mfma_ordered(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
 }
+// D[32x32] += A[32x16] B[16x32]: lane l supplies row (l % 32) of A and column
+// (l % 32) of B, each as 8 consecutive k of k-group l / 32, and receives
+// column l % 32 of D, rows 8 (r / 4) + 4 (l / 32) + r % 4 in register r.
+__device__ __forceinline__ void mfma_ordered(f32x16_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b) : "memory");
+}
 // A copy of v the compiler cannot see through: what is computed from it
 // stays where it is written instead of being hoisted out of the tile loop and
 // kept live (in registers the main loop needs) across it.
@@ -131,10 +177,12 @@ __device__ __forceinline__ int opaque(int v) {
 }
 // materialise a value in AGPRs at this point of the instruction stream
 __device__ __forceinline__ void pin_agpr(f32x4_t& acc) { asm volatile("" : "+a"(acc)); }
+__device__ __forceinline__ void pin_agpr(f32x16_t& acc) { asm volatile("" : "+a"(acc)); }
 // the same, also ordered after every memory access before it: reads of the
 // accumulator cannot be hoisted above the preceding output stores (which
 // would have every accumulator copied to VGPRs at once)
 __device__ __forceinline__ void pin_agpr_ordered(f32x4_t& acc) { asm volatile("" : "+a"(acc) : : "memory"); }
+__device__ __forceinline__ void pin_agpr_ordered(f32x16_t& acc) { asm volatile("" : "+a"(acc) : : "memory"); }
 // wait states between the last MFMA of the loop and the first read of its
 // accumulators by ordinary code (the hazard check cannot see into asm)
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
@@ -145,19 +193,26 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\
 // carries one epilogue: with several epilogue copies behind a
 // runtime switch, the register allocator copied accumulator lanes out of AGPRs
 // inside the main loop, a few wait states after the (asm) MFMA that wrote them.
+// M32: the wave tile runs on v_mfma_f32_32x32x16_bf16 (32x32 fragments, 16 k
+// per MFMA) instead of v_mfma_f32_16x16x32_bf16: half the MFMA instructions
+// and half the operand register reads per flop, the same LDS bytes.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED,
-          int GACT = ACT_NONE>
+          int GACT = ACT_NONE, bool M32 = false>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N;
   constexpr int TM = BM / WAVES_M;   // wave tile rows (activation rows)
   constexpr int TN = BN / WAVES_N;   // wave tile width in B-tile rows
-  constexpr int FM = TM / 16;
-  constexpr int FN = TN / 16;
+  constexpr int MR = M32 ? 32 : 16;  // rows (and columns) of one MFMA's output
+  constexpr int KSTEP = M32 ? 16 : 32;   // k per MFMA
+  typedef typename std::conditional<M32, f32x16_t, f32x4_t>::type acc_t;
+  constexpr int NACC = M32 ? 16 : 4;     // accumulator registers per MFMA tile
+  constexpr int FM = TM / MR;
+  constexpr int FN = TN / MR;
   constexpr bool DUAL = (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU);
   constexpr int HALF = FN / 2;       // DUAL: gate fragments [0,HALF), up [HALF,FN)
   constexpr int CH = BK / 8;         // 16-byte chunks per LDS row
-  constexpr int KS = BK / 32;        // MFMA k-steps per stage
+  constexpr int KS = BK / KSTEP;     // MFMA k-steps per stage
   constexpr int RPI = 64 / CH;       // rows filled by one 1 KB load instruction
   constexpr int A_INS = BM / (RPI * NW);   // load instructions per wave and stage
   constexpr int B_INS = BN / (RPI * NW);
@@ -167,8 +222,10 @@ gemm_bf16_kernel(GemmParams p) {
   static_assert(BK == 32 || BK == 64, "stage depth");
   static_assert(A_INS >= 1 && B_INS >= 1 && BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "load mapping");
   static_assert(!DUAL || (BN / 2) % (RPI * NW) == 0, "a load instruction stays in one weight set");
-  static_assert(TM % 16 == 0 && TN % 16 == 0 && FM % 2 == 0, "wave tile");
-  static_assert(DUAL ? (HALF % 2 == 0) : (FN % 2 == 0), "fragment pairs");
+  static_assert(TM % MR == 0 && TN % MR == 0 && FM % 2 == 0, "wave tile");
+  static_assert(M32 || (DUAL ? (HALF % 2 == 0) : (FN % 2 == 0)), "fragment pairs");
+  static_assert(!DUAL || HALF >= 1, "gate and up fragments");
+  static_assert(KS == 1 || KS % 2 == 0, "k-steps per stage");
   static_assert(R >= 2 && LOADS * (R - 2) < 64, "ring depth");
 
   __shared__ u32x4_t ring[R * SLOT];
@@ -181,8 +238,8 @@ gemm_bf16_kernel(GemmParams p) {
 
   const int64_t K = p.K, N = p.N;
   const int Kc = (int)K;                       // < 2^22
-  const int li = lane & 15;   // fragment row (weight) / column (activation)
-  const int lg = lane >> 4;   // k group: 8 consecutive k
+  const int li = lane & (MR - 1);   // fragment row (weight) / column (activation)
+  const int lg = lane / MR;         // k group: 8 consecutive k
 
   // ---- this block's tiles ----------------------------------------------------
   // The grid is persistent (at most one block per CU).  Logical tiles (in
@@ -289,7 +346,7 @@ gemm_bf16_kernel(GemmParams p) {
   // stages per tile: a split-K part's share (the caller splits only when the
   // stage count divides evenly and stays even for one k-step per stage)
   const int nk = (Kc + BK - 1) / BK;
-  const int NS = KSP > 1 ? nk / KSP : (KS == 2 ? nk : (nk + 1) & ~1);
+  const int NS = KSP > 1 ? nk / KSP : (KS % 2 == 0 ? nk : (nk + 1) & ~1);
   int iss_kp = 0;   // K part of the tile whose stages are being issued
   {
     const Tile t0 = tile_at(0);
@@ -341,22 +398,21 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) dma(i, ring_lds + (uint32_t)slot * (SLOT * 16), st);
   };
-
   // ---- LDS fragment addresses (16-byte units within a slot) -----------------
   // Activation fragment f: rows wm * TM + 16 f + li; weight fragment f: rows
   // w_lane_row + w_delta(f).  One base per k-step, the rest compile-time.
-  static_assert(fragment_swizzle_is_uniform<CH, TM, TN, FM, FN, BN, WAVES_M, WAVES_N, DUAL>(),
+  static_assert(fragment_swizzle_is_uniform<CH, TM, TN, FM, FN, BN, WAVES_M, WAVES_N, DUAL, M32>(),
                 "fragment addresses are affine");
-  const int wr0 = w_lane_row(wn, li, TN, DUAL);
+  const int wr0 = w_lane_row(wn, li, TN, DUAL, M32);
   int x_idx[KS], w_idx[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    const int c = ks * 4 + lg;
+    const int c = ks * (KSTEP / 8) + lg;
     x_idx[ks] = (wm * TM + li) * CH + (c ^ swz_a<CH>(wm * TM + li));
     w_idx[ks] = BM * CH + wr0 * CH + (c ^ swz_b<CH>(wr0));
   }
 
-  f32x4_t acc[FM][FN];
+  acc_t acc[FM][FN];
   // The zeros are pinned into the accumulators here: the loop's MFMAs are
   // asm, so the hazard check cannot see them read a register that a plain
   // write set just before, and the compiler would otherwise sink each write
@@ -366,7 +422,8 @@ gemm_bf16_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < NACC; ++r) acc[i][j][r] = 0.f;
         pin_agpr(acc[i][j]);
       }
   };
@@ -381,9 +438,9 @@ gemm_bf16_kernel(GemmParams p) {
     if (n == 0) {
       xf[set][0] = sl[x_idx[ks]];
     } else if (n <= FN) {
-      wf[set][n - 1] = sl[w_idx[ks] + w_delta(n - 1, FN, BN, DUAL) * CH];
+      wf[set][n - 1] = sl[w_idx[ks] + w_delta(n - 1, FN, BN, DUAL, M32) * CH];
     } else {
-      xf[set][n - FN] = sl[x_idx[ks] + (n - FN) * 16 * CH];
+      xf[set][n - FN] = sl[x_idx[ks] + (n - FN) * MR * CH];
     }
   };
   auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a k-step: row t / FN, column t % FN
@@ -400,50 +457,63 @@ gemm_bf16_kernel(GemmParams p) {
   typedef __attribute__((address_space(1))) u32x4_t gu32x4_t;
   auto gst16 = [](void* ptr, const u32x4_t& v) { *(gu32x4_t*)ptr = v; };
   auto gld16 = [](const void* ptr) -> u32x4_t { return *(const gu32x4_t*)ptr; };
+  // Runs of 8 consecutive output columns a lane holds for activation fragment
+  // i, RUNS per weight set (the weight-row permutation above makes them
+  // consecutive):
+  //   16x16x32: run q is accumulator pair (2q, 2q+1), 4 values each, columns
+  //             32 q + 8 lg of the wave's columns;
+  //   32x32x16: run q is registers 8 (q % 2) .. +7 of accumulator q / 2,
+  //             columns 32 (q / 2) + 16 (q % 2) + 8 lg.
+  constexpr int SETF = DUAL ? HALF : FN;   // fragments per weight set
+  constexpr int RUNS = M32 ? 2 * SETF : SETF / 2;
+  auto run_col = [](int q, int lgv) { return M32 ? (q >> 1) * 32 + 16 * (q & 1) + 8 * lgv : q * 32 + 8 * lgv; };
+  auto run_vals = [&](int i, int q, int set, float v[8]) {   // set 0: gate (or the only set), 1: up
+    if constexpr (M32) {
+      const int f = set * HALF + (q >> 1);
+      pin_agpr_ordered(acc[i][f]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) v[r] = acc[i][f][8 * (q & 1) + r];
+    } else {
+      const int f0 = set * HALF + 2 * q;
+      pin_agpr_ordered(acc[i][f0]);
+      pin_agpr_ordered(acc[i][f0 + 1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[i][f0][r];
+        v[4 + r] = acc[i][f0 + 1][r];
+      }
+    }
+  };
   // The activation is a template argument so each copy of the epilogue is
   // straight-line code (a per-element switch would branch around every value).
   auto epilogue_act = [&](const Tile& t, auto act_c) {
     constexpr int ACT = decltype(act_c)::value;
     const int el = opaque(lane);
-    const int li = el & 15, lg = el >> 4;
+    const int li = el & (MR - 1), lg = el / MR;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int64_t lrow = t.row_begin + wm * TM + i * 16 + li;
+      const int64_t lrow = t.row_begin + wm * TM + i * MR + li;
       const bool row_ok = lrow < t.row_end;
       if constexpr (OUT == GEMM_OUT_GEGLU) {
 #pragma unroll
-        for (int q = 0; q < HALF / 2; ++q) {
-          const int64_t n = t.n0 + wn * (TN / 2) + q * 32 + 8 * lg;
-          pin_agpr_ordered(acc[i][2 * q]);
-          pin_agpr_ordered(acc[i][2 * q + 1]);
-          pin_agpr_ordered(acc[i][HALF + 2 * q]);
-          pin_agpr_ordered(acc[i][HALF + 2 * q + 1]);
-          float v[8];
+        for (int q = 0; q < RUNS; ++q) {
+          const int64_t n = t.n0 + wn * (TN / 2) + run_col(q, lg);
+          float g[8], u[8], v[8];
+          run_vals(i, q, 0, g);
+          run_vals(i, q, 1, u);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = act_of<ACT>(acc[i][2 * q][r]) * acc[i][HALF + 2 * q][r];
-            v[4 + r] = act_of<ACT>(acc[i][2 * q + 1][r]) * acc[i][HALF + 2 * q + 1][r];
-          }
+          for (int r = 0; r < 8; ++r) v[r] = act_of<ACT>(g[r]) * u[r];
           if (row_ok && n < N) gst16(static_cast<uint16_t*>(p.C) + lrow * p.ldc + n, pack_bf16x8(v));
         }
       } else if constexpr (OUT == GEMM_OUT_DGLU) {
         // recomputed g and u with the incoming dm: m for the down projection's
         // weight gradient, dg and du for the input and gate/up weight gradients
 #pragma unroll
-        for (int q = 0; q < HALF / 2; ++q) {
-          const int64_t n = t.n0 + wn * (TN / 2) + q * 32 + 8 * lg;
-          pin_agpr_ordered(acc[i][2 * q]);
-          pin_agpr_ordered(acc[i][2 * q + 1]);
-          pin_agpr_ordered(acc[i][HALF + 2 * q]);
-          pin_agpr_ordered(acc[i][HALF + 2 * q + 1]);
+        for (int q = 0; q < RUNS; ++q) {
+          const int64_t n = t.n0 + wn * (TN / 2) + run_col(q, lg);
           float g[8], u[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            g[r] = acc[i][2 * q][r];
-            g[4 + r] = acc[i][2 * q + 1][r];
-            u[r] = acc[i][HALF + 2 * q][r];
-            u[4 + r] = acc[i][HALF + 2 * q + 1][r];
-          }
+          run_vals(i, q, 0, g);
+          run_vals(i, q, 1, u);
           if (!(row_ok && n < N)) continue;
           float dm[8];
           unpack_bf16x8(gld16(p.E + lrow * p.lde + n), dm);
@@ -463,16 +533,10 @@ gemm_bf16_kernel(GemmParams p) {
         }
       } else {
 #pragma unroll
-        for (int q = 0; q < FN / 2; ++q) {
-          const int64_t n = t.n0 + wn * TN + q * 32 + 8 * lg;
-          pin_agpr_ordered(acc[i][2 * q]);
-          pin_agpr_ordered(acc[i][2 * q + 1]);
+        for (int q = 0; q < RUNS; ++q) {
+          const int64_t n = t.n0 + wn * TN + run_col(q, lg);
           float v[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = acc[i][2 * q][r];
-            v[4 + r] = acc[i][2 * q + 1][r];
-          }
+          run_vals(i, q, 0, v);
           if (!(row_ok && n < N)) continue;
           if constexpr (OUT == GEMM_OUT_F32_SCALED) {
             const float sc = p.row_scale[lrow];
@@ -564,28 +628,32 @@ gemm_bf16_kernel(GemmParams p) {
   // quarter of a stage queue behind one another in the address unit (measured
   // 3-4 % faster on the large shapes; a quarter or none in the window is
   // slower again).
-  constexpr int LNOW = KS == 2 ? LOADS / 2 : LOADS;
+  constexpr int LNOW = KS >= 2 ? LOADS / 2 : LOADS;
   StageIssue pend_st{false, false, 0};
   uint32_t pend_base = 0;
   bool pend = false;   // block-uniform: the first stage has none
   bool stored = false;   // an epilogue has stored since the last hand-off
   auto next_slot = [&](int sl) { return sl + 1 == R ? 0 : sl + 1; };
-  auto kstep = [&](int ks, int slot, auto cur_c, auto last_c) {
+  auto kstep = [&](auto ks_c, int slot, auto cur_c, auto last_c) {
+    constexpr int ks = decltype(ks_c)::value;
     constexpr int CUR = decltype(cur_c)::value;
     constexpr bool LAST = decltype(last_c)::value;
     using Nxt = std::integral_constant<int, CUR ^ 1>;
-    if (ks + 1 < KS) {
+    if constexpr (ks + 1 < KS) {
       const u32x4_t* sl = ring + slot * SLOT;
-      constexpr int OPS0 = NREADS + (LOADS - LNOW);   // the deferred loads, then the reads
+      // the stage's first k-step leads with the loads deferred from the
+      // hand-off window, then every k-step reads the next one's fragments
+      constexpr int DEF = ks == 0 ? LOADS - LNOW : 0;
+      constexpr int OPS0 = NREADS + DEF;
 #pragma unroll
       for (int t = 0; t < 2 * NMA; ++t) {
         mfma_t(t, cur_c);
 #pragma unroll
         for (int n = t * OPS0 / (2 * NMA); n < (t + 1) * OPS0 / (2 * NMA); ++n) {
-          if (n < LOADS - LNOW) {
+          if (n < DEF) {
             if (pend) dma(LNOW + n, pend_base, pend_st);
           }
-          else frag_read(n - (LOADS - LNOW), sl, ks + 1, Nxt{});
+          else frag_read(n - DEF, sl, ks + 1, Nxt{});
         }
       }
       return;
@@ -623,26 +691,37 @@ gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
     for (int n = 0; n < NREADS; ++n) frag_read(n, sl, 0, Set0{});
   };
+  // every k-step of one stage (KS even: the register sets alternate within it)
+  auto stage = [&](int slot, auto last_c) {
+    auto step = [&](auto self, auto k_c) {
+      constexpr int K = decltype(k_c)::value;
+      if constexpr (K < KS) {
+        kstep(k_c, slot, std::integral_constant<int, K & 1>{},
+              std::integral_constant<bool, decltype(last_c)::value && K + 1 == KS>{});
+        self(self, std::integral_constant<int, K + 1>{});
+      }
+    };
+    step(step, std::integral_constant<int, 0>{});
+  };
+  using K0 = std::integral_constant<int, 0>;
   int slot = 0;
   for (int ti = 0; ti < nmine; ++ti) {
-    if constexpr (KS == 2) {
+    if constexpr (KS >= 2) {
       for (int q = 0; q < NS - 1; ++q) {
-        kstep(0, slot, Set0{}, Mid{});
-        kstep(1, slot, Set1{}, Mid{});
+        stage(slot, Mid{});
         slot = next_slot(slot);
       }
-      kstep(0, slot, Set0{}, Mid{});
-      kstep(1, slot, Set1{}, Last{});
+      stage(slot, Last{});
     } else {
       for (int q = 0; q < NS - 2; q += 2) {   // NS is even
-        kstep(0, slot, Set0{}, Mid{});
+        kstep(K0{}, slot, Set0{}, Mid{});
         slot = next_slot(slot);
-        kstep(0, slot, Set1{}, Mid{});
+        kstep(K0{}, slot, Set1{}, Mid{});
         slot = next_slot(slot);
       }
-      kstep(0, slot, Set0{}, Mid{});
+      kstep(K0{}, slot, Set0{}, Mid{});
       slot = next_slot(slot);
-      kstep(0, slot, Set1{}, Last{});
+      kstep(K0{}, slot, Set1{}, Last{});
     }
     tile_end(ti, slot);
     slot = next_slot(slot);
@@ -650,7 +729,8 @@ gemm_bf16_kernel(GemmParams p) {
   wait_vm<0>();   // the stages issued past the end (loads of nothing) land before LDS is released
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED, int GACT>
+template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED, int GACT,
+          bool M32 = false>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -662,7 +742,7 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   if (tiles > 0x7fffffff || p.cus <= 0) return hipErrorInvalidValue;
   // persistent: as many blocks as fit on the chip at once, each looping over
   // its tiles
-  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT>;
+  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT, M32>;
   static const int per_cu = [&] {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, WM * WN * 64, 0) != hipSuccess) o = 1;
@@ -672,6 +752,17 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(WM * WN * 64), 0, s, p);
   return hipGetLastError();
 }
+
+// The 256x256 tile's MFMA shape (see gemm_bf16_kernel's M32).  The 32x32x16
+// form halves MFMA instructions and operand register reads, but was measured
+// 6 % slower on the large GeGLU (4295-4300 us against 4055-4061 us for the
+// 16x16x32 form, same sources and box); 16x16x32 stays the default and the
+// 32x32x16 form is built only with -DFMLP_TILE256_M32=1.
+#ifndef FMLP_TILE256_M32
+#define FMLP_TILE256_M32 0
+#endif
+constexpr bool kTile256M32 = FMLP_TILE256_M32 != 0;
+
 
 template <int OUT, bool GATHER, bool GROUPED, int GACT = ACT_NONE>
 hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
@@ -688,7 +779,7 @@ hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
   }
   switch (tile) {
     case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED, GACT>(p, s);
-    case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED, GACT>(p, s);
+    case TILE_256x256: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, GATHER, GROUPED, GACT, kTile256M32>(p, s);
     case TILE_128x192:
       if constexpr (OUT == GEMM_OUT_BF16 && !GATHER && !GROUPED)
         return launch_cfg<128, 192, 4, 2, 64, 3, OUT, GATHER, GROUPED, GACT>(p, s);

@@ -173,7 +173,9 @@ size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
  * GEMM contracts over their rows are first written transposed into the
  * workspace.  Outputs are caller-owned bf16, must not alias inputs, and
  * M < 2^22; with M == 0 the weight and bias gradients are written as zeros.
- * Workspace: the *_bwd_workspace_size bytes, no initialisation needed.
+ * Workspace: the *_bwd_workspace_size bytes, no initialisation needed; the
+ * first 8192 bytes (the decode header of fmlp_mlp2 / fmlp_glu) are never
+ * written, so one workspace can serve forward and backward calls in turn.
  */
 
 /* Linear + activation, y = act(x[M,K] . W[N,K]^T + b[N]):

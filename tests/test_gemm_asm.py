@@ -12,7 +12,9 @@ from each MFMA (and forwards from it) to check the distances, in wait states:
 
   * VALU writes a register that the MFMA reads:  at least 2 apart
   * the MFMA's result used or overwritten by any non-MFMA instruction: at
-    least 18 apart (more than the 16x16x32 bf16 MFMA's pipeline depth)
+    least 18 apart after a 16x16x32 bf16 MFMA and 19 after a 32x32x16 one
+    (more than each one's pipeline depth; 19 is the distance the CDNA3 table
+    gives for the longest, 16-pass, MFMAs)
 """
 import os
 import re
@@ -26,6 +28,7 @@ SRC = os.path.join(ROOT, "gemm_epilogue_bf16_amd", "csrc", "gemm.hip")
 
 VALU_TO_MFMA = 2
 MFMA_TO_USE = 18
+MFMA32_TO_USE = 19
 
 
 def _regs(tok):
@@ -151,12 +154,11 @@ def _hazards(k):
                 found.append(f"{d} wait states: '{t}' then '{u}'")
 
         k.walk(pos, k.preds, VALU_TO_MFMA, before)
-        k.walk(pos, k.succs, MFMA_TO_USE, after)
+        k.walk(pos, k.succs, MFMA32_TO_USE if "32x32" in t else MFMA_TO_USE, after)
     return found
 
 
-@pytest.fixture(scope="module")
-def gemm_asm(tmp_path_factory):
+def _compile_asm(tmp_path_factory, defines=()):
     from gemm_epilogue_bf16_amd import build as B
 
     try:
@@ -164,11 +166,22 @@ def gemm_asm(tmp_path_factory):
     except RuntimeError:
         pytest.skip("hipcc not available")
     out = str(tmp_path_factory.mktemp("asm") / "gemm.s")
-    cmd = [cc, *B.common_flags(), *B.EXTRA_FLAGS.get("gemm.hip", []), "-x", "hip",
+    cmd = [cc, *B.common_flags(), *B.EXTRA_FLAGS.get("gemm.hip", []), *defines, "-x", "hip",
            "--cuda-device-only", "-S", SRC, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     return open(out).read()
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    return _compile_asm(tmp_path_factory)
+
+
+@pytest.fixture(scope="module")
+def gemm_asm_m32(tmp_path_factory):
+    """The build option that runs the 256x256 tile on the 32x32x16 MFMA."""
+    return _compile_asm(tmp_path_factory, ("-DFMLP_TILE256_M32=1",))
 
 
 def test_every_gemm_kernel_compiled(gemm_asm):
@@ -181,6 +194,24 @@ def test_every_gemm_kernel_compiled(gemm_asm):
 def test_no_mfma_hazard_in_asm_loop(gemm_asm):
     problems = []
     for k in _kernels(gemm_asm):
+        for h in _hazards(k):
+            problems.append(f"{k.name[:80]}: {h}")
+    assert not problems, "\n".join(problems[:20])
+
+
+@pytest.mark.parametrize("m32", [False, True])
+def test_tile256_mfma_shape(gemm_asm, gemm_asm_m32, m32):
+    ks = [k for k in _kernels(gemm_asm_m32 if m32 else gemm_asm) if "ILi256ELi256E" in k.name]
+    assert ks
+    want = "v_mfma_f32_32x32x16_bf16" if m32 else "v_mfma_f32_16x16x32_bf16"
+    for k in ks:
+        m = [t for kind, t in k.ins if kind == "I" and t.startswith("v_mfma")]
+        assert m and all(t.startswith(want) for t in m), k.name
+
+
+def test_no_mfma_hazard_with_32x32_tiles(gemm_asm_m32):
+    problems = []
+    for k in _kernels(gemm_asm_m32):
         for h in _hazards(k):
             problems.append(f"{k.name[:80]}: {h}")
     assert not problems, "\n".join(problems[:20])

@@ -110,3 +110,26 @@ def test_generation_moves_once_per_call_and_replays_differ():
         assert np.array_equal(bits_of(outs[i]), want[i % 2]), f"call {i}"
     assert F.decode_generation(ws) == 32
     assert F.barrier_timeouts(ws) == 0
+
+
+def test_backward_calls_leave_the_decode_header_alone():
+    """A backward call between two one-token decode calls on the same cached
+    workspace: the generation still moves by one per decode call and the
+    timeout count stays put."""
+    rng = np.random.default_rng(8)
+    K, H, N = 256, 4096, 512
+    t = _mlp2_inputs(rng, K, H, N)
+    d = {k: to_dev(v) for k, v in t.items()}
+    x = rand_bf16(rng, (1, K))
+    ws = F.workspace_for(DEV, max(F.fmlp_mlp2_workspace_size(1, K, H, N),
+                                  int(F.lib().fmlp_linear_bwd_workspace_size(64, K, H))))
+    print("case decode / linear_bwd / decode on one workspace", flush=True)
+    gen0, tmo0 = F.decode_generation(ws), F.barrier_timeouts(ws)
+    F.fmlp_mlp2(to_dev(x), d["W1"], d["b1"], d["W2"], d["b2"], "gelu_erf", workspace=ws)
+    xb = to_dev(rand_bf16(rng, (64, K)))
+    F.fmlp_linear_bwd(xb, d["W1"], d["b1"], "gelu_erf", to_dev(rand_bf16(rng, (64, H))), workspace=ws)
+    y = F.fmlp_mlp2(to_dev(x), d["W1"], d["b1"], d["W2"], d["b2"], "gelu_erf", workspace=ws)
+    torch.cuda.synchronize()
+    assert_parity(y, _ref(x, t, "gelu_erf"), "decode after a backward call")
+    assert F.decode_generation(ws) == (gen0 + 2) & 0xFFFFFFFF
+    assert F.barrier_timeouts(ws) == tmo0
