@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
     "moe_router_mfma_kernel": ["common.h", "kernels.h", "moe.hip"],
     "decode_w8_kernel": ["common.h", "decode_w8.h", "decode_w8.hip"],
+    "glu_fused_kernel": ["common.h", "kernels.h", "lds_dma.h", "glu_fused.hip"],
 }
 
 
@@ -253,7 +254,9 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
                     calls.append(F.bind_geglu(x, s["Wg"], s["Wu"], s["Wd"], out=y, workspace=ws))
                 else:
                     calls.append(F.bind_glu(x, s["Wg"], s["Wu"], s["Wd"], gate_act, out=y, workspace=ws))
-            if w.M <= 16:
+            if path == "fused":
+                kernel, launches, p = "glu_fused_kernel", 1, "whole block in one launch, m kept on chip"
+            elif w.M <= 16:
                 kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             else:
                 kernel, launches, p = "gemm_bf16_kernel", 2, "fused gate+up GEMM + down GEMM (2 launches)"
@@ -426,6 +429,9 @@ EST_US = {"tiny": 5, "decode1": 12, "decode16": 12, "geglu768": 100, "large1": 2
 # every workload of the configuration table, in the order the rows are printed
 CONFIG_ROWS = ["tiny", "decode1", "decode16", "geglu768", "large1", "large16", "large4096", "moe", "router",
                "geglu768_bwd", "large4096_bwd"]
+# a workload timed again on another path (same inputs): the gated block in one
+# launch with m on chip, against the default two launches of its own row
+CONFIG_PATH_ROWS = [("geglu768", "fused")]
 
 
 def run_timed(case: Case, K: int, W: int, path: str, stream, torch, F, unfused: bool = True) -> dict:
@@ -501,13 +507,13 @@ def decode_timeouts(case: Case, F):
     return F.barrier_timeouts(ws)
 
 
-def config_row(name: str, dev, stream, torch, F, act=None) -> dict:
+def config_row(name: str, dev, stream, torch, F, act=None, path: str = "auto") -> dict:
     """One row of the configuration table: the workload's forward timed on its
     own (cold weights), with its roofline fraction from HIP events."""
-    case = setup_case(name, cold=True, dev=dev, path="auto", act=act)
+    case = setup_case(name, cold=True, dev=dev, path=path, act=act)
     est = EST_US[name]
     K = max(20, min(2000, int(0.4e6 / est)))
-    r = run_timed(case, K, max(5, K // 10), "auto", stream, torch, F, unfused=False)
+    r = run_timed(case, K, max(5, K // 10), path, stream, torch, F, unfused=False)
     roof = roofline_of(case, r["dev_s"])
     w = case.w
     row = {"workload": w.name, "tokens": w.M, "path": case.path, "launches": case.launches,
@@ -533,7 +539,8 @@ def main(argv=None):
     ap.add_argument("--act", default=None, choices=["none", "gelu_erf", "gelu_tanh", "relu", "silu"],
                     help="activation of a two-layer MLP, or gate activation of a gated block")
     ap.add_argument("--warm", action="store_true", help="no weight rotation (weights may sit in the 256 MB cache)")
-    ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small"])
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "gemm", "small", "fused"],
+                    help="fused: the gated block in one launch with m on chip (D <= 1024)")
     ap.add_argument("--weights", default="bf16", choices=["bf16", "fp8"],
                     help="fp8: the decode workloads with E4M3 weights and per-row scales")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -645,6 +652,9 @@ def main(argv=None):
                 continue
             print(f"bench: config row {name}", file=sys.stderr, flush=True)
             rows.append(config_row(name, dev, stream, torch, F))
+        for name, path in CONFIG_PATH_ROWS:
+            print(f"bench: config row {name} ({path} path)", file=sys.stderr, flush=True)
+            rows.append(config_row(name, dev, stream, torch, F, path=path))
         out["configs"] = rows
     print(json.dumps(out), flush=True)
     return 0

@@ -82,7 +82,7 @@ __all__ = [
 ]
 
 ACT = {"none": 0, "gelu_erf": 1, "gelu_tanh": 2, "relu": 3, "silu": 4}
-PATHS = {"auto": 0, "decode": 1, "gemm": 2, "small": 3}
+PATHS = {"auto": 0, "decode": 1, "gemm": 2, "small": 3, "fused": 4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -218,7 +218,8 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
 
 @contextlib.contextmanager
 def force_path(path: str):
-    """Force the calling thread's mlp2/geglu path: "auto", "decode", "gemm", "small"."""
+    """Force the calling thread's mlp2/glu path: "auto", "decode", "gemm", "small" (mlp2 only) or
+    "fused" (the gated block in one launch, D <= 1024)."""
     L = lib()
     _check(L.fmlp_set_path(PATHS[path]))
     try:

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfmlp.so")
-SOURCES = ["abi.cpp", "gemm.hip", "decode.hip", "decode_w8.hip", "small_mlp.hip", "moe.hip", "transpose.hip", "noalloc.hip"]
+SOURCES = ["abi.cpp", "gemm.hip", "decode.hip", "decode_w8.hip", "small_mlp.hip", "moe.hip", "transpose.hip", "noalloc.hip",
+           "glu_fused.hip"]
 ARCH = "gfx950"
 # Per-source flags.  The GEMM main loop is written in issue order (fragment
 # reads of the next stage ahead of the MFMAs they hide behind); the pre-RA

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -19,9 +20,9 @@ using namespace fmlp;
 namespace {
 
 thread_local std::string g_last_error;
-thread_local int g_path = 0;   // 0 auto, 1 decode, 2 two-GEMM, 3 small fused
+thread_local int g_path = 0;   // 0 auto, 1 decode, 2 two-GEMM, 3 small fused, 4 fused gated block
 
-constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3;
+constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3, kPathFused = 4;
 constexpr int64_t kDecodeMaxM = 16;
 constexpr int64_t kSmallMaxDim = 128;
 constexpr int64_t kMaxDim = int64_t(1) << 31;   // bound on a token count
@@ -195,7 +196,7 @@ fmlp_status record_error(fmlp_status s, const char* msg) { return fail(s, "%s", 
 
 extern "C" {
 
-int fmlp_version(void) { return 103; }
+int fmlp_version(void) { return 104; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {
@@ -214,7 +215,7 @@ const char* fmlp_status_string(fmlp_status s) {
 const char* fmlp_last_error(void) { return g_last_error.c_str(); }
 
 fmlp_status fmlp_set_path(int path) {
-  if (path < kPathAuto || path > kPathSmall) return fail(FMLP_E_ARG, "path=%d is not 0..3", path);
+  if (path < kPathAuto || path > kPathFused) return fail(FMLP_E_ARG, "path=%d is not 0..4", path);
   g_path = path;
   return ok();
 }
@@ -275,6 +276,7 @@ fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* 
   const bool small_ok = K <= kSmallMaxDim && H <= kSmallMaxDim && N <= kSmallMaxDim;
   int path = g_path;
   if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : (small_ok ? kPathSmall : kPathGemm);
+  if (path == kPathFused) return fail(FMLP_E_ARG, "the fused gated-block path is glu-only");
   if (path == kPathDecode && M > kDecodeMaxM)
     return fail(FMLP_E_ARG, "decode path needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   if (path == kPathSmall && !small_ok)
@@ -306,9 +308,10 @@ fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* 
 }
 
 size_t fmlp_geglu_workspace_size(int64_t M, int64_t D, int64_t H) {
-  (void)D;
   if (M < 0 || H <= 0) return 0;
-  return kHeader + hidden_bytes(M, H);
+  size_t body = hidden_bytes(M, H);                 // m of the two-launch and decode paths
+  if (D > 0 && D <= kGluFusedMaxD) body = std::max(body, glu_fused_workspace_bytes(M, D, H));
+  return kHeader + body;
 }
 
 size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H) { return fmlp_geglu_workspace_size(M, D, H); }
@@ -334,6 +337,10 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
   int path = g_path;
   if (path == kPathAuto) path = (M <= kDecodeMaxM) ? kPathDecode : kPathGemm;
   if (path == kPathSmall) return fail(FMLP_E_ARG, "the small fused path is mlp2-only");
+  if (path == kPathFused && D > kGluFusedMaxD)
+    return fail(FMLP_E_ARG, "the fused gated block needs D <= %lld (D=%lld)", (long long)kGluFusedMaxD, (long long)D);
+  if (path == kPathFused && H > kGluFusedMaxH)
+    return fail(FMLP_E_ARG, "the fused gated block needs H <= %lld (H=%lld)", (long long)kGluFusedMaxH, (long long)H);
   if (path == kPathDecode && M > kDecodeMaxM)
     return fail(FMLP_E_ARG, "decode path needs M <= %lld (M=%lld)", (long long)kDecodeMaxM, (long long)M);
   const size_t need = fmlp_geglu_workspace_size(M, D, H);
@@ -352,6 +359,9 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
     return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
                     "geglu (decode, persistent) launch");
   }
+  if (path == kPathFused)
+    return launched(launch_glu_fused(x, Wg, Wu, Wd, gate_act, M, D, H, y, m, next_launch_salt(), s),
+                    "gated block (fused, one launch)");
   hipError_t e = gemm_glu_gateup(x, Wg, Wu, gate_act, M, D, H, m, cus, s);
   if (e != hipSuccess) return launched(e, "geglu gate+up launch");
   return launched(gemm_linear(m, Wd, nullptr, FMLP_ACT_NONE, M, H, D, y, cus, s), "geglu down launch");

@@ -748,9 +748,6 @@ Occ occ() {
   return o;
 }
 
-// A salt per launch: a process-wide counter through a bijective mix, seeded
-// from the clock and the process id, so every launch of this process gets a
-// different value (for 2^32 launches) and other processes most likely others.
 uint32_t mix32(uint32_t v) {
   v ^= v >> 16;
   v *= 0x85EBCA6Bu;
@@ -759,12 +756,20 @@ uint32_t mix32(uint32_t v) {
   v ^= v >> 16;
   return v;
 }
-uint32_t next_salt() {
+
+}  // namespace
+
+// A salt per launch: a process-wide counter through a bijective mix, seeded
+// from the clock and the process id, so every launch of this process gets a
+// different value (for 2^32 launches) and other processes most likely others.
+uint32_t next_launch_salt() {
   static const uint32_t seed = mix32((uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() ^
                                      (uint32_t)getpid() * 0x9E3779B1u);
   static std::atomic<uint32_t> counter{0};
   return mix32(seed ^ counter.fetch_add(1u, std::memory_order_relaxed) * 0x27D4EB2Du);
 }
+
+namespace {
 
 // One kernel variant on `grid` blocks.  The two-layer form waits for every
 // block at its barrier; the grid is capped at one block per CU (the LDS ring
@@ -777,7 +782,7 @@ uint32_t next_salt() {
 template <bool DUAL1, bool TWO, int MC, bool LL>
 hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
                           hipStream_t s) {
-  const uint32_t salt = TWO ? next_salt() : 0u;
+  const uint32_t salt = TWO ? next_launch_salt() : 0u;
   hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync, salt);
   return hipGetLastError();
 }

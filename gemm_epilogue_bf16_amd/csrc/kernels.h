@@ -116,6 +116,51 @@ static_assert(kDecodeMaxBlocks % 4 == 0, "flags are read 4 at a time");
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M,
                                    uint32_t* sync, hipStream_t s);
 
+// A 32-bit tag per launch, different for every launch of this process (for
+// 2^32 launches) and most likely for other processes: the epoch salt of the
+// one-launch decode and of the fused gated block's arrival words.
+uint32_t next_launch_salt();
+
+// ---------------------------------------------------------------------------
+// The gated block in one launch with m kept on chip (glu_fused.hip), for
+// D <= kGluFusedMaxD: y = (act(x Wg^T) * (x Wu^T)) Wd^T.  ws holds
+// glu_fused_workspace_bytes(M, D, H) bytes (no initialisation needed).
+// ---------------------------------------------------------------------------
+constexpr int64_t kGluFusedMaxD = 1024;
+constexpr int64_t kGluFusedMaxH = 1 << 22;   // 32-bit byte offsets of a 256-row Wd stage
+constexpr int kGluFusedRows = 64;      // token rows per block
+constexpr int kGluFusedSub = 128;      // hidden units per sub-chunk
+constexpr int kGluFusedMaxParts = 8;
+// The hidden range splits into S parts of hc units (a multiple of 128), S
+// chosen so that the m_tiles * S blocks fill a 256-CU device, with no empty
+// part.  With S > 1 the workspace holds S fp32 partials of y.
+struct GluFusedShape {
+  int64_t m_tiles;
+  int S, hc;
+};
+inline GluFusedShape glu_fused_shape(int64_t M, int64_t H) {
+  GluFusedShape f;
+  f.m_tiles = (M + kGluFusedRows - 1) / kGluFusedRows;
+  const int64_t subs = (H + kGluFusedSub - 1) / kGluFusedSub;
+  int64_t S = f.m_tiles > 0 ? (256 + f.m_tiles - 1) / f.m_tiles : 1;
+  S = S < kGluFusedMaxParts ? S : kGluFusedMaxParts;
+  S = S < subs ? S : subs;
+  S = S > 1 ? S : 1;
+  const int64_t per = (subs + S - 1) / S;   // sub-chunks per part
+  f.hc = (int)(per * kGluFusedSub);
+  f.S = (int)((subs + per - 1) / per);
+  return f;
+}
+inline size_t glu_fused_arrive_bytes(int64_t m_tiles) { return ((size_t)m_tiles * 8 + 255) / 256 * 256; }
+inline size_t glu_fused_workspace_bytes(int64_t M, int64_t D, int64_t H) {
+  if (M <= 0 || D <= 0 || H <= 0) return 0;
+  const GluFusedShape f = glu_fused_shape(M, H);
+  const size_t parts = f.S > 1 ? (size_t)f.S * (size_t)f.m_tiles * kGluFusedRows * (size_t)D * 4 : 0;
+  return glu_fused_arrive_bytes(f.m_tiles) + parts;
+}
+hipError_t launch_glu_fused(const uint16_t* x, const uint16_t* Wg, const uint16_t* Wu, const uint16_t* Wd, int act,
+                            int64_t M, int64_t D, int64_t H, uint16_t* y, void* ws, uint32_t salt, hipStream_t s);
+
 // ---------------------------------------------------------------------------
 // Small fused MLP: K, H, N <= 128, any M; one launch.
 // ---------------------------------------------------------------------------

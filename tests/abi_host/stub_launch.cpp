@@ -47,4 +47,9 @@ hipError_t launch_rowsum(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, 
   reached("launch_rowsum");
 }
 hipError_t launch_fill_zero(uint16_t*, int64_t, hipStream_t) { reached("launch_fill_zero"); }
+hipError_t launch_glu_fused(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, int, int64_t, int64_t,
+                            int64_t, uint16_t*, void*, uint32_t, hipStream_t) {
+  reached("launch_glu_fused");
+}
+uint32_t next_launch_salt() { return 1u; }
 }  // namespace fmlp

@@ -114,7 +114,10 @@ def test_mlp2_validation(L):
 
 def test_geglu_validation(L):
     need = L.fmlp_geglu_workspace_size(8192, 768, 3072)
-    assert need == 8192 + 8192 * 3072 * 2
+    # the larger of m (two launches) and the one-launch form's arrival words +
+    # two fp32 partials of y (128 token tiles of 64 rows, 2 parts of the hidden range)
+    assert need == 8192 + max(8192 * 3072 * 2, 128 * 8 + 2 * 8192 * 768 * 4)
+    assert L.fmlp_geglu_workspace_size(8192, 4096, 3072) == 8192 + 8192 * 3072 * 2   # D > 1024: no fused form
     assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, None, 0, None) == E_WS
     assert L.fmlp_geglu(X, W, W, W, 16, 64, 128, Y, WS + 8, 1 << 20, None) == E_ALIGN
     assert L.fmlp_geglu(X, W, None, W, 16, 64, 128, Y, WS, 1 << 20, None) == E_NULL
@@ -125,6 +128,14 @@ def test_geglu_validation(L):
     finally:
         L.fmlp_set_path(0)
     assert L.fmlp_geglu(X, W, W, W, 0, 64, 128, Y, WS, 1 << 20, None) == OK
+    assert L.fmlp_set_path(4) == OK   # the one-launch gated block: D <= 1024, glu only
+    try:
+        assert L.fmlp_geglu(X, W, W, W, 16, 1032, 128, Y, WS, 1 << 30, None) == E_ARG
+        assert "D <= 1024" in _err(L)
+        assert L.fmlp_mlp2(X, W, None, W, None, 2, 16, 64, 128, 64, Y, WS, 1 << 20, None) == E_ARG
+    finally:
+        L.fmlp_set_path(0)
+    assert L.fmlp_set_path(5) == E_ARG
 
 
 def test_glu_validation(L):
