@@ -524,8 +524,41 @@ constexpr int64_t kBwdMaxTokens = kMaxInner;
 size_t ws_bf16(int64_t rows, int64_t cols) { return round_up((size_t)rows * (size_t)cols * 2, 256); }
 int64_t pad8(int64_t v) { return (v + 7) / 8 * 8; }
 
+// Weight gradients contract over the tokens: C[R, Cc] = A[R, T] . B[Cc, T]^T
+// with both operands transposed to token-contiguous rows (T = tokens padded
+// to 8).  Few output tiles over a long token range leave most CUs idle (the
+// 3072 x 768 gradient of the 768/3072 block: 36 tiles of 256 x 256 over 8192
+// tokens), so when the 256 x 256 tiles do not fill a 256-CU device the token
+// range is split in P parts, as many as fit one round (at most 8, at least
+// 8 stages of 64 tokens each; parts may differ by one stage): each part writes
+// an fp32 copy of C into the workspace and a fixed-order sum rounds once
+// (deterministic).  P does not depend on the device, so the workspace size is
+// known without one.
+int wgrad_split(int64_t R, int64_t T, int64_t Cc) {
+  const int64_t tiles = ((R + 255) / 256) * ((Cc + 255) / 256);
+  if (tiles >= 256) return 1;
+  const int64_t nk = (T + 63) / 64;
+  const int64_t P = std::min<int64_t>({256 / tiles, 8, nk / 8});
+  return P > 1 ? (int)P : 1;
+}
+size_t wgrad_parts_bytes(int64_t R, int64_t T, int64_t Cc) {
+  const int P = wgrad_split(R, T, Cc);
+  return P > 1 ? round_up((size_t)P * (size_t)R * (size_t)Cc * 4, 256) : 0;
+}
+hipError_t gemm_wgrad(const uint16_t* A, const uint16_t* B, int64_t R, int64_t T, int64_t Cc, uint16_t* C,
+                      float* parts, int cus, hipStream_t s) {
+  const int P = wgrad_split(R, T, Cc);
+  if (P == 1) return gemm_linear(A, B, nullptr, FMLP_ACT_NONE, R, T, Cc, C, cus, s);
+  GemmParams p = dense_params(A, T, B, nullptr, nullptr, parts, Cc, R, Cc, T, FMLP_ACT_NONE, cus);
+  p.ksplit = P;
+  p.c_kstride = R * Cc;
+  const hipError_t e = launch_gemm(GEMM_OUT_F32_SCALED, false, false, TILE_256x256, p, s);
+  if (e != hipSuccess) return e;
+  return launch_sum_parts(parts, P, R * Cc, R * Cc, C, s);
+}
+
 struct LinearBwdLayout {
-  size_t dz, wt, dzt, xt, total;
+  size_t dz, wt, dzt, xt, parts, total;
 };
 LinearBwdLayout linear_bwd_layout(int64_t M, int64_t K, int64_t N) {
   const int64_t Mp = pad8(M);
@@ -535,12 +568,13 @@ LinearBwdLayout linear_bwd_layout(int64_t M, int64_t K, int64_t N) {
   L.wt = o;  o += ws_bf16(K, N);
   L.dzt = o; o += ws_bf16(N, Mp);
   L.xt = o;  o += ws_bf16(K, Mp);
+  L.parts = o; o += wgrad_parts_bytes(N, Mp, K);
   L.total = o;
   return L;
 }
 
 struct GluBwdLayout {
-  size_t wdt, dm, m, dgdu, wgut, dyt, mt, dgdut, xt, total;
+  size_t wdt, dm, m, dgdu, wgut, dyt, mt, dgdut, xt, parts, total;
 };
 GluBwdLayout glu_bwd_layout(int64_t M, int64_t D, int64_t H) {
   const int64_t Mp = pad8(M);
@@ -555,6 +589,7 @@ GluBwdLayout glu_bwd_layout(int64_t M, int64_t D, int64_t H) {
   L.mt = o;    o += ws_bf16(H, Mp);
   L.dgdut = o; o += ws_bf16(2 * H, Mp);
   L.xt = o;    o += ws_bf16(D, Mp);
+  L.parts = o; o += std::max(wgrad_parts_bytes(D, Mp, H), wgrad_parts_bytes(H, Mp, D));
   L.total = o;
   return L;
 }
@@ -627,7 +662,7 @@ fmlp_status fmlp_linear_bwd(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_b
   // dW = dz^T x and db = sum over tokens: both contract over the token rows
   HIP_TRY(launch_transpose(dz, M, N, N, dzt, Mp, Mp, s), "linear_bwd transpose dz");
   HIP_TRY(launch_transpose(x, M, K, K, xt, Mp, Mp, s), "linear_bwd transpose x");
-  HIP_TRY(gemm_linear(dzt, xt, nullptr, FMLP_ACT_NONE, N, Mp, K, dW, cus, s), "linear_bwd dW launch");
+  HIP_TRY(gemm_wgrad(dzt, xt, N, Mp, K, dW, reinterpret_cast<float*>(ws + L.parts), cus, s), "linear_bwd dW launch");
   if (db) HIP_TRY(launch_rowsum(dzt, N, Mp, Mp, db, s), "linear_bwd db launch");
   return ok();
 }
@@ -690,10 +725,10 @@ fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf1
   HIP_TRY(launch_transpose(at(L.m), M, H, H, at(L.mt), Mp, Mp, s), "glu_bwd transpose m");
   HIP_TRY(launch_transpose(at(L.dgdu), M, 2 * H, 2 * H, at(L.dgdut), Mp, Mp, s), "glu_bwd transpose dg|du");
   HIP_TRY(launch_transpose(x, M, D, D, at(L.xt), Mp, Mp, s), "glu_bwd transpose x");
-  HIP_TRY(gemm_linear(at(L.dyt), at(L.mt), nullptr, FMLP_ACT_NONE, D, Mp, H, dWd, cus, s), "glu_bwd dWd launch");
-  HIP_TRY(gemm_linear(at(L.dgdut), at(L.xt), nullptr, FMLP_ACT_NONE, H, Mp, D, dWg, cus, s), "glu_bwd dWg launch");
-  HIP_TRY(gemm_linear(at(L.dgdut) + H * Mp, at(L.xt), nullptr, FMLP_ACT_NONE, H, Mp, D, dWu, cus, s),
-          "glu_bwd dWu launch");
+  float* parts = reinterpret_cast<float*>(ws + L.parts);
+  HIP_TRY(gemm_wgrad(at(L.dyt), at(L.mt), D, Mp, H, dWd, parts, cus, s), "glu_bwd dWd launch");
+  HIP_TRY(gemm_wgrad(at(L.dgdut), at(L.xt), H, Mp, D, dWg, parts, cus, s), "glu_bwd dWg launch");
+  HIP_TRY(gemm_wgrad(at(L.dgdut) + H * Mp, at(L.xt), H, Mp, D, dWu, parts, cus, s), "glu_bwd dWu launch");
   return ok();
 }
 

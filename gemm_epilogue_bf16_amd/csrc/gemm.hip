@@ -14,9 +14,11 @@
 //                        m = act(g) * u, act = tanh GELU for GeGLU (section
 //                        "The fused Triton kernel": the intermediate never
 //                        makes an HBM round trip) or another gate activation
-//   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights),
-//                        optionally split over K into parts that each write
-//                        their own copy (summed in order by the caller)
+//   GEMM_OUT_F32_SCALED  fp32 output scaled per row (expert combine weights;
+//                        no scale: 1), optionally split over K into parts
+//                        that each write their own copy (summed in order by
+//                        the caller: the MoE combine, or the backward's
+//                        weight gradients)
 //   GEMM_OUT_DACT        backward of a Linear + activation: the forward GEMM
 //                        recomputes z = x W^T + b in registers and writes only
 //                        dz = dy * act'(z)
@@ -343,15 +345,20 @@ gemm_bf16_kernel(GemmParams p) {
   // sets alternate), so with one k-step per stage an odd count gets one
   // all-zero stage more, which adds nothing.  The block's stream is its
   // tiles' stages back to back: stream stage q is stage q % NS of tile q / NS.
-  // stages per tile: a split-K part's share (the caller splits only when the
-  // stage count divides evenly and stays even for one k-step per stage)
+  // Split over K: part kp of a tile takes stages [kp nk / KSP, (kp + 1) nk /
+  // KSP) (shares that differ by at most one stage; with one k-step per stage
+  // the caller keeps every share even).
   const int nk = (Kc + BK - 1) / BK;
-  const int NS = KSP > 1 ? nk / KSP : (KS % 2 == 0 ? nk : (nk + 1) & ~1);
+  const int NS = KSP > 1 ? nk / KSP : (KS % 2 == 0 ? nk : (nk + 1) & ~1);   // stages of an unsplit tile
+  auto part_first = [&](int kp) { return (int)((int64_t)kp * nk / KSP); };
+  auto part_stages = [&](int kp) { return SPLITK ? part_first(kp + 1) - part_first(kp) : NS; };
   int iss_kp = 0;   // K part of the tile whose stages are being issued
+  int iss_ns = NS;  // and its stage count
   {
     const Tile t0 = tile_at(0);
     issue_tile(t0);
     iss_kp = t0.kp;
+    iss_ns = part_stages(t0.kp);
   }
 
   // How this wave loads the next stage of its stream (stages are issued once
@@ -370,11 +377,12 @@ gemm_bf16_kernel(GemmParams p) {
       const Tile nt = tile_at(iss_t);
       issue_tile(nt);
       iss_kp = nt.kp;
+      iss_ns = part_stages(nt.kp);
     }
-    const int ks0 = __builtin_amdgcn_readfirstlane(live ? iss_kp * NS + iss_s : 0);   // stage index within K
+    const int ks0 = __builtin_amdgcn_readfirstlane(live ? (SPLITK ? part_first(iss_kp) : 0) + iss_s : 0);   // stage index within K
     const int k0 = live ? ks0 * BK : Kc;
     const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, (uint32_t)ks0 * (BK * 2)};
-    if (++iss_s == NS) {
+    if (++iss_s == iss_ns) {
       iss_s = 0;
       ++iss_t;
     }
@@ -539,7 +547,7 @@ gemm_bf16_kernel(GemmParams p) {
           run_vals(i, q, 0, v);
           if (!(row_ok && n < N)) continue;
           if constexpr (OUT == GEMM_OUT_F32_SCALED) {
-            const float sc = p.row_scale[lrow];
+            const float sc = p.row_scale ? p.row_scale[lrow] : 1.f;
             float* dst = static_cast<float*>(p.C) + (int64_t)t.kp * p.c_kstride + lrow * p.ldc + n;
             u32x4_t lo, hi;
 #pragma unroll
@@ -706,14 +714,15 @@ gemm_bf16_kernel(GemmParams p) {
   using K0 = std::integral_constant<int, 0>;
   int slot = 0;
   for (int ti = 0; ti < nmine; ++ti) {
+    const int ns = SPLITK ? part_stages(tile_at(ti).kp) : NS;
     if constexpr (KS >= 2) {
-      for (int q = 0; q < NS - 1; ++q) {
+      for (int q = 0; q < ns - 1; ++q) {
         stage(slot, Mid{});
         slot = next_slot(slot);
       }
       stage(slot, Last{});
     } else {
-      for (int q = 0; q < NS - 2; q += 2) {   // NS is even
+      for (int q = 0; q < ns - 2; q += 2) {   // ns is even
         kstep(K0{}, slot, Set0{}, Mid{});
         slot = next_slot(slot);
         kstep(K0{}, slot, Set1{}, Mid{});
@@ -800,6 +809,8 @@ hipError_t launch_gemm(int out_kind, bool gather, bool grouped, int tile, GemmPa
   if (out_kind == GEMM_OUT_GEGLU && !gather && !grouped) return launch_tile<GEMM_OUT_GEGLU, false, false>(tile, p, s);
   if (out_kind == GEMM_OUT_GEGLU && gather && grouped) return launch_tile<GEMM_OUT_GEGLU, true, true>(tile, p, s);
   if (out_kind == GEMM_OUT_F32_SCALED && !gather && grouped) return launch_tile<GEMM_OUT_F32_SCALED, false, true>(tile, p, s);
+  if (out_kind == GEMM_OUT_F32_SCALED && !gather && !grouped && tile == TILE_256x256)
+    return launch_tile<GEMM_OUT_F32_SCALED, false, false>(tile, p, s);
   if (out_kind == GEMM_OUT_DACT && !gather && !grouped && tile != TILE_128x192)
     return launch_tile<GEMM_OUT_DACT, false, false>(tile, p, s);
   if (out_kind == GEMM_OUT_DGLU && !gather && !grouped) return launch_tile<GEMM_OUT_DGLU, false, false>(tile, p, s);

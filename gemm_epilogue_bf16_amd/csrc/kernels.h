@@ -36,7 +36,7 @@ struct GemmParams {
   const int32_t* group_off;  // grouped: [groups+1] logical row offsets
   const int32_t* tile_off;   // grouped: [groups+1] prefix of m-tiles per group
   int groups;
-  const float* row_scale;    // GEMM_OUT_F32_SCALED: per logical row
+  const float* row_scale;    // GEMM_OUT_F32_SCALED: per logical row, or nullptr (1)
   int ksplit;                // GEMM_OUT_F32_SCALED: K split into this many equal parts (0 or 1: none);
                              // part j of a tile writes C + j * c_kstride
   int64_t c_kstride;
@@ -63,6 +63,11 @@ hipError_t launch_rowsum(const uint16_t* in, int64_t R, int64_t C, int64_t ld, u
 
 // out[0, n) = 0 (bf16): the weight gradients of a call with no tokens.
 hipError_t launch_fill_zero(uint16_t* out, int64_t n, hipStream_t s);
+
+// out[i] = bf16(parts[0][i] + parts[1][i] + ... + parts[P-1][i]) for i < n
+// (fp32 parts of a GEMM split over K, stride `stride` floats apart, added in
+// part order: deterministic); n % 8 == 0.
+hipError_t launch_sum_parts(const float* parts, int P, int64_t stride, int64_t n, uint16_t* out, hipStream_t s);
 
 // Tile configurations compiled in.
 enum GemmTile : int {

@@ -18,6 +18,8 @@
 //   rowsum_kernel     one wave per row: 16-byte loads, fp32 partial sums per
 //                     lane in a fixed order, then a fixed butterfly across the
 //                     wave (deterministic), rounded to bf16 once.
+//   sum_parts_kernel  the parts of a weight-gradient GEMM split over the
+//                     tokens, added in part order in fp32 and rounded once.
 #include <algorithm>
 
 #include "common.h"
@@ -94,7 +96,29 @@ __global__ void __launch_bounds__(256) fill_zero_kernel(uint16_t* __restrict__ o
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) out[i] = 0;
 }
 
+__global__ void __launch_bounds__(256) sum_parts_kernel(const float* __restrict__ parts, int P, int64_t stride,
+                                                        int64_t n, uint16_t* __restrict__ out) {
+  for (int64_t i = 8 * ((int64_t)blockIdx.x * 256 + threadIdx.x); i < n; i += 8 * (int64_t)gridDim.x * 256) {
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < P; ++p) {   // part order
+      const float4 a = *reinterpret_cast<const float4*>(parts + p * stride + i);
+      const float4 b = *reinterpret_cast<const float4*>(parts + p * stride + i + 4);
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    }
+    st16(out + i, pack_bf16x8(v));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_sum_parts(const float* parts, int P, int64_t stride, int64_t n, uint16_t* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (P < 1 || n % 8 != 0 || stride < n || stride % 4 != 0) return hipErrorInvalidValue;
+  const int64_t g = std::min<int64_t>((n / 8 + 255) / 256, 8192);
+  hipLaunchKernelGGL(sum_parts_kernel, dim3((unsigned)g), dim3(256), 0, s, parts, P, stride, n, out);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(uint16_t* out, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

@@ -95,7 +95,9 @@ def test_glu_bwd_random(M, D, H, act):
 
 
 def test_glu_bwd_geglu768_full():
-    """The 8192-token 768/3072 GeGLU workload's backward, every gradient in full."""
+    """The 8192-token 768/3072 GeGLU workload's backward, every gradient in full
+    (its weight gradients run split over the tokens in 7 parts of 18 or 19
+    stages)."""
     w = datagen.workload("geglu768")
     t = datagen.make_inputs(w, seed=0)
     dy = datagen.normal_bf16(datagen.rng_for(0, w.family, "dy"), (w.M, w.N))
@@ -172,3 +174,45 @@ def test_bwd_determinism():
     torch.cuda.synchronize()
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+def _wgrad_split(R, T, C):
+    """The token split the library takes for a weight gradient (R x C over T
+    padded tokens): mirrors its documented rule, to know which cases run split."""
+    tiles = (-(-R // 256)) * (-(-C // 256))
+    if tiles >= 256:
+        return 1
+    return max(1, min(256 // tiles, 8, (-(-T // 64)) // 8))
+
+
+@pytest.mark.parametrize("M,K,N,act,parts", [(8190, 264, 520, "gelu_tanh", 8), (2043, 1024, 1032, "silu", 4),
+                                             (5000, 712, 600, "relu", 8), (1000, 264, 2056, "gelu_erf", 2)])
+def test_linear_bwd_token_split(M, K, N, act, parts):
+    """Weight gradients split over the tokens (fp32 parts summed in part
+    order): 4 and 8 parts, parts of unequal length (79 stages of 64 tokens in
+    8 parts, with a token tail), ragged token counts, and bitwise equal on a
+    second call."""
+    assert _wgrad_split(N, -(-M // 8) * 8, K) == parts
+    x, W, b, dy = _linear_case(M * 3 + K, M, K, N, act, True)
+    print(f"case linear_bwd token split M={M} K={K} N={N} act={act} parts={parts}", flush=True)
+    d = [to_dev(a) for a in (x, W, b, dy)]
+    dx, dW, db = F.fmlp_linear_bwd(d[0], d[1], d[2], act, d[3])
+    dW2 = F.fmlp_linear_bwd(d[0], d[1], d[2], act, d[3])[1]
+    torch.cuda.synchronize()
+    rx, rW, rb = oracle.linear_bwd(f64_of_bits(x), f64_of_bits(W), f64_of_bits(b), act, f64_of_bits(dy))
+    assert_parity(dx, rx, f"dx {M}x{K}x{N} {act}")
+    assert_parity(dW, rW, f"dW {M}x{K}x{N} {act} ({parts} parts)")
+    assert_parity(db, rb, f"db {M}x{K}x{N} {act}")
+    assert np.array_equal(bits_of(dW), bits_of(dW2))
+
+
+def test_glu_bwd_token_split():
+    M, D, H = 4096, 256, 640
+    assert _wgrad_split(H, M, D) == 8 and _wgrad_split(D, M, H) == 8
+    x, Wg, Wu, Wd, dy = _glu_case(17, M, D, H, "gelu_tanh")
+    print(f"case glu_bwd token split M={M} D={D} H={H}", flush=True)
+    got = F.fmlp_glu_bwd(*(to_dev(a) for a in (x, Wg, Wu, Wd)), "gelu_tanh", to_dev(dy))
+    torch.cuda.synchronize()
+    ref = oracle.glu_bwd(*(f64_of_bits(a) for a in (x, Wg, Wu, Wd)), "gelu_tanh", f64_of_bits(dy))
+    for g, r, n in zip(got, ref, ("dx", "dWg", "dWu", "dWd")):
+        assert_parity(g, r, f"{n} {M}x{D}x{H} (8 parts)")
