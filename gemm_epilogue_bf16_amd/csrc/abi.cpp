@@ -196,7 +196,7 @@ fmlp_status record_error(fmlp_status s, const char* msg) { return fail(s, "%s", 
 
 extern "C" {
 
-int fmlp_version(void) { return 104; }
+int fmlp_version(void) { return 105; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {
@@ -739,7 +739,10 @@ fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf1
 // ---------------------------------------------------------------------------
 extern "C" size_t fmlp_w8_workspace_size(int64_t M, int64_t H) {
   if (M <= 0 || H <= 0) return 0;
-  return kHeader + round_up((size_t)M * (size_t)H * 2, 256);
+  // h after the decode header: M x H bf16, or at one token H / 2 words of
+  // 8 bytes {bf16 pair, epoch} for the one-launch form
+  const size_t h = std::max((size_t)M * (size_t)H * 2, M == 1 ? (size_t)H * 4 : (size_t)0);
+  return kHeader + round_up(h, 256);
 }
 
 namespace {
@@ -821,11 +824,15 @@ fmlp_status fmlp_mlp2_w8(const fmlp_bf16* x, const fmlp_fp8* W1q, const float* s
   TOKEN_PTR(y, M);
   TRY(check_w8_workspace(M, H, workspace, workspace_bytes));
   if (M == 0) return ok();
-  TRY(check_device());
+  int cus = 0;
+  TRY(check_device(&cus));
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
   W8Layer L1{x, W1q, s1, nullptr, nullptr, b1, h, K, H, act};
   W8Layer L2{h, W2q, s2, nullptr, nullptr, b2, y, H, N, FMLP_ACT_NONE};
+  if (g_path != kPathGemm && decode_w8_two_applies((int)M, L1, L2, cus))
+    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s),
+                    "mlp2 (fp8 weights, one launch)");
   hipError_t e = launch_decode_w8(L1, (int)M, s);
   if (e != hipSuccess) return launched(e, "mlp2 (fp8 weights) layer-1 launch");
   return launched(launch_decode_w8(L2, (int)M, s), "mlp2 (fp8 weights) layer-2 launch");
@@ -849,11 +856,15 @@ fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg
   TOKEN_PTR(y, M);
   TRY(check_w8_workspace(M, H, workspace, workspace_bytes));
   if (M == 0) return ok();
-  TRY(check_device());
+  int cus = 0;
+  TRY(check_device(&cus));
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint16_t* m = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kHeader);
   W8Layer L1{x, Wgq, sg, Wuq, su, nullptr, m, D, H, gate_act};
   W8Layer L2{m, Wdq, sd, nullptr, nullptr, nullptr, y, H, D, FMLP_ACT_NONE};
+  if (g_path != kPathGemm && decode_w8_two_applies((int)M, L1, L2, cus))
+    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s),
+                    "glu (fp8 weights, one launch)");
   hipError_t e = launch_decode_w8(L1, (int)M, s);
   if (e != hipSuccess) return launched(e, "glu (fp8 weights) gate+up launch");
   return launched(launch_decode_w8(L2, (int)M, s), "glu (fp8 weights) down launch");

@@ -25,4 +25,12 @@ struct W8Layer {
 
 hipError_t launch_decode_w8(const W8Layer& L, int M, hipStream_t s);
 
+// Both layers of a one-token forward in one persistent launch (L1.y is the
+// workspace area for h as H / 2 words of 8 bytes {bf16 pair, epoch}; sync is
+// the workspace's decode header).  Applies to M == 1, H = L1.N <= 4096 with
+// H % 16 == 0, L2.K == H, 2 * L1.K <= 64 KB and a device of at most
+// kDecodeMaxBlocks compute units.
+bool decode_w8_two_applies(int M, const W8Layer& L1, const W8Layer& L2, int cus);
+hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s);
+
 }  // namespace fmlp

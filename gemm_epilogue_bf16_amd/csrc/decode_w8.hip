@@ -33,8 +33,12 @@
 //
 // The 8 partial 16 x 16 tiles are summed in a fixed order (bitwise
 // deterministic) by wave 0, which applies the epilogue and stores.
+#include <algorithm>
+
 #include "common.h"
 #include "decode_w8.h"
+#include "exchange.h"
+#include "kernels.h"
 
 namespace fmlp {
 
@@ -270,7 +274,215 @@ hipError_t launch_w8(const W8Layer& L, int M, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Both layers of a one-token FP8 forward in ONE launch (the bf16 engine's
+// word-flag exchange, decode.hip): a persistent grid of at most one block per
+// CU; each block streams its layer-1 tiles (16 output rows over the whole k
+// range, as above, x staged once in LDS), publishes its h values as 8-byte
+// words {bf16 pair, epoch} with device-coherent stores, gathers every block's
+// words into LDS (polling until each carries this call's epoch, bounded and
+// counted), then streams its layer-2 tiles against h in LDS.  Every block
+// owns a layer-1 tile, so block 0 seeing every word means every block has
+// read the generation: only then does block 0 advance it.
+// ---------------------------------------------------------------------------
+
+// The weight descriptors of a 16-row tile and the lane's row offset.
+struct W8Tile {
+  __amdgpu_buffer_rsrc_t d0, d1;
+  uint32_t wrow;
+};
+template <bool DUAL>
+__device__ __forceinline__ W8Tile w8_tile_at(const W8Layer& L, int64_t tile) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = (int)L.K;
+  const int64_t n0 = tile * 16;
+  const int rows = (int)min<int64_t>(16, L.N - n0);
+  W8Tile t;
+  t.d0 = w8_desc(L.W0 + n0 * L.K, (uint32_t)(rows * K));
+  t.d1 = w8_desc(DUAL ? L.W1 + n0 * L.K : L.W0, (uint32_t)(rows * K));
+  t.wrow = (uint32_t)(r * K + g * 16);
+  return t;
+}
+
+// One 16-row tile over the whole k range with the activation row staged in
+// LDS at xs (one token); wave 0 returns the summed accumulators.  A holds the
+// first register batch (issued here).
+template <bool DUAL, int U>
+__device__ __forceinline__ void w8_tile_one_token(const W8Layer& L, int64_t tile, const uint8_t* xs,
+                                                  f32x4_t (*red)[kW8Waves][64], f32x4_t& s0, f32x4_t& s1,
+                                                  W8Batch<DUAL, U>& A) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int K = (int)L.K;
+  const W8Tile tl = w8_tile_at<DUAL>(L, tile);
+  const __amdgpu_buffer_rsrc_t d0 = tl.d0, d1 = tl.d1;
+  const uint32_t wrow = tl.wrow;
+  const uint8_t* xl = xs + g * 32;   // the one token's row; lanes of other tokens drop their value
+  const bool xrow_ok = r == 0;
+  const int chunks = (K + 63) / 64;
+  const int nb = (chunks + kW8Waves * U - 1) / (kW8Waves * U);
+  W8Batch<DUAL, U> B;
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc1 = {0.f, 0.f, 0.f, 0.f};
+  w8_issue<DUAL, U, 1>(A, 0, wave, g, K, d0, d1, d0, wrow, 0u);
+  int b = 0;
+  for (; b + 2 < nb; b += 2) {
+    w8_issue<DUAL, U, 1>(B, b + 1, wave, g, K, d0, d1, d0, wrow, 0u);
+    w8_hold<DUAL, U, 1>(A);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_issue<DUAL, U, 1>(A, b + 2, wave, g, K, d0, d1, d0, wrow, 0u);
+    w8_hold<DUAL, U, 1>(B);
+    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+  }
+  if (b + 1 < nb) {
+    w8_issue<DUAL, U, 1>(B, b + 1, wave, g, K, d0, d1, d0, wrow, 0u);
+    w8_hold<DUAL, U, 1>(A);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_hold<DUAL, U, 1>(B);
+    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+  } else {
+    w8_hold<DUAL, U, 1>(A);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+  }
+  red[0][wave][lane] = acc0;
+  if constexpr (DUAL) red[1][wave][lane] = acc1;
+  __syncthreads();
+  if (wave == 0) {
+    s0 = red[0][0][lane];
+    s1 = red[DUAL ? 1 : 0][0][lane];
+#pragma unroll
+    for (int w = 1; w < kW8Waves; ++w) {
+      s0 += red[0][w][lane];
+      if constexpr (DUAL) s1 += red[1][w][lane];
+    }
+  }
+  __syncthreads();   // red is free for the next tile
+}
+
+constexpr int kW8TwoMaxH = 4096;   // h words gathered per block: 4 H bytes
+
+template <bool DUAL1>
+__global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W8Layer L2, uint32_t* sync,
+                                                                   uint32_t salt) {
+  __shared__ f32x4_t red[2][kW8Waves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kXSmall];   // x, then h: one bf16 row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int G = (int)gridDim.x, blk = (int)blockIdx.x;
+  const uint32_t gen_next = ld_coherent(sync + kSyncGenWord) + 1u;
+  const uint32_t target = epoch_of(gen_next, salt);
+  const int K1 = (int)L1.K, H = (int)L1.N;
+
+  // the input row into LDS
+  for (int i = tid; i < K1 / 8; i += kW8Threads)
+    *reinterpret_cast<u32x4_t*>(xs + i * 16) = ld16(L1.x + (int64_t)i * 8);
+  __syncthreads();
+
+  // layer 1; wave 0's lanes of token 0 (r == 0) hold rows 4g .. 4g + 3 of a tile
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(L1.y, (uint32_t)H * 4u);   // H / 2 words of 8 bytes
+  const int64_t tiles1 = (L1.N + 15) / 16, tiles2 = (L2.N + 15) / 16;
+  for (int64_t t = blk; t < tiles1; t += G) {
+    f32x4_t s0, s1;
+    W8Batch<DUAL1, DUAL1 ? 4 : 8> A1;
+    w8_tile_one_token<DUAL1, DUAL1 ? 4 : 8>(L1, t, xs, red, s0, s1, A1);
+    if (wave == 0 && r == 0) {
+      const int64_t n = t * 16 + 4 * g;   // H % 16 == 0: all four rows exist
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DUAL1) {
+          v[i] = apply_act(s0[i] * L1.s0[n + i], L1.act) * (s1[i] * L1.s1[n + i]);
+        } else {
+          float z = s0[i] * L1.s0[n + i];
+          if (L1.bias) z += bf16_to_f32(L1.bias[n + i]);
+          v[i] = apply_act(z, L1.act);
+        }
+      }
+      st_coherent_b128(rh, (uint32_t)n * 4u, u32x4_t{pack_bf16x2(v[0], v[1]), target, pack_bf16x2(v[2], v[3]), target});
+    }
+  }
+
+  // (Issuing the first layer-2 weight batch here, to stream while h is
+  // gathered, measured slower: 16.4 against 15.2 us for the 4096^3 forward,
+  // since the gather's device-coherent polls then wait behind those loads.)
+  // every block's h: 16-byte pieces of two words, each lane's pieces in flight
+  // together, until both words carry this call's epoch
+  {
+    constexpr int kPer = kW8TwoMaxH / 4 / kW8Threads;   // pieces per thread
+    const int pieces = H / 4;
+    uint32_t pend = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (tid + kW8Threads * i < pieces) pend |= 1u << i;
+    for (uint32_t spins = 0;; ++spins) {
+      u32x4_t v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (pend & (1u << i))
+          v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rh, (uint32_t)(tid + kW8Threads * i) * 16u, 0, 16 /* sc1 */));
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if ((pend & (1u << i)) && v[i][1] == target && v[i][3] == target) {
+          *reinterpret_cast<u32x2_t*>(xs + (tid + kW8Threads * i) * 8) = u32x2_t{v[i][0], v[i][2]};
+          pend &= ~(1u << i);
+        }
+      }
+      if (__syncthreads_or(pend != 0) == 0) break;
+      if (spins >= (1u << 20)) {
+        if (tid == 0)
+          __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (blk == 0 && tid == 0) st_coherent(sync + kSyncGenWord, gen_next);
+  }
+
+  // layer 2 against h in LDS
+  for (int64_t t = blk; t < tiles2; t += G) {
+    f32x4_t s0, s1;
+    W8Batch<false, 8> A2;
+    w8_tile_one_token<false, 8>(L2, t, xs, red, s0, s1, A2);
+    if (wave == 0 && r == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = t * 16 + 4 * g + i;
+        if (n >= L2.N) break;
+        float z = s0[i] * L2.s0[n];
+        if (L2.bias) z += bf16_to_f32(L2.bias[n]);
+        const __bf16 o = (__bf16)z;
+        L2.y[n] = __builtin_bit_cast(uint16_t, o);
+      }
+    }
+  }
+}
+
 }  // namespace
+
+bool decode_w8_two_applies(int M, const W8Layer& L1, const W8Layer& L2, int cus) {
+  const int64_t tiles1 = (L1.N + 15) / 16;
+  return M == 1 && L1.N <= kW8TwoMaxH && L1.N % 16 == 0 && L2.K == L1.N && 2 * L1.K <= kXSmall &&
+         cus > 0 && cus <= kDecodeMaxBlocks && tiles1 >= 1;
+}
+
+hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s) {
+  if (!decode_w8_two_applies(1, L1, L2, cus)) return hipErrorInvalidValue;
+  if (L1.K % 16 != 0 || L2.N <= 0) return hipErrorInvalidValue;
+  const int64_t tiles1 = (L1.N + 15) / 16;
+  // every block owns a layer-1 tile and all are resident at once: at most one per CU
+  const unsigned grid = (unsigned)std::min<int64_t>(tiles1, cus);
+  const uint32_t salt = next_launch_salt();
+  if (L1.W1)
+    hipLaunchKernelGGL((decode_w8_two_kernel<true>), dim3(grid), dim3(kW8Threads), 0, s, L1, L2, sync, salt);
+  else
+    hipLaunchKernelGGL((decode_w8_two_kernel<false>), dim3(grid), dim3(kW8Threads), 0, s, L1, L2, sync, salt);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_w8(const W8Layer& L, int M, hipStream_t s) {
   if (M <= 0 || M > 16 || L.K <= 0 || L.K % 16 != 0 || L.N <= 0) return hipErrorInvalidValue;

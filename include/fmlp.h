@@ -107,8 +107,10 @@ fmlp_status fmlp_linear(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_bf16*
  * mixed from the next generation and a per-launch salt, so neither a header
  * zeroed again between calls, nor recycled memory, nor words left by an
  * earlier call are ever taken for this call's h.  The same workspace may be
- * shared, in stream order, by every call of this header (the FP8 calls and
- * fmlp_geglu/fmlp_glu keep their data after the 8192-byte header too).
+ * shared, in stream order, by every call of this header (the FP8 calls,
+ * fmlp_geglu/fmlp_glu and the backward calls keep their data after the
+ * 8192-byte header too; the one-token FP8 two-layer launch advances the same
+ * generation).
  * The one-launch decode form needs every block resident at once: its grid is
  * at most one block per CU, so on a device not shared with long-running work
  * it always is.  A barrier wait that gives up (after 2^20 polls of the flags)
@@ -251,12 +253,17 @@ fmlp_status fmlp_glu_noalloc(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp
  * Besides the shared rules: M <= 16 (larger M is FMLP_E_ARG; M == 0 is a
  * no-op), every dimension a layer contracts over (K, H, D) a multiple of 16
  * (FMLP_E_ALIGN; an output-only N keeps the multiple of 8), code arrays
- * 16-byte aligned, scale arrays [N] fp32, 4-byte aligned and finite.  One
- * launch per layer: the two-layer forms write h or m [M, H] bf16 to the
- * workspace after its first 8192 bytes, which they never touch (so one
- * workspace can also serve fmlp_mlp2 / fmlp_glu calls in between);
- * fmlp_w8_workspace_size bytes, no initialisation needed; two launches on the
- * stream.
+ * 16-byte aligned, scale arrays [N] fp32, 4-byte aligned and finite.
+ * Launches: at one token with H <= 4096 (and 2 K <= 65536) the two-layer forms
+ * run as ONE persistent launch with the one-launch decode's protocol (ainews,
+ * section "technical deep dive": the fused MLP is one kernel): h is published
+ * as epoch-tagged words after the workspace's 8192-byte header, every block
+ * gathers it, and the header's generation advances by one and its timeout
+ * count works as described for fmlp_mlp2 (same header, same residency
+ * assumption).  Otherwise one launch per layer, writing h or m [M, H] bf16
+ * after the header and never touching the header.  fmlp_set_path(2) forces
+ * the launch-per-layer form.  The workspace: fmlp_w8_workspace_size bytes;
+ * zero its header once, as for fmlp_mlp2.
  */
 typedef uint8_t fmlp_fp8;  /* OCP FP8 E4M3 ("e4m3fn") code */
 
@@ -279,8 +286,9 @@ fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg
                         int gate_act, int64_t M, int64_t D, int64_t H, fmlp_bf16* y,
                         void* workspace, size_t workspace_bytes, fmlp_stream stream);
 
-/* bytes of workspace the two-layer FP8 calls need: an untouched 8192-byte
- * header, then h or m, M x H bf16 (0 for M == 0) */
+/* bytes of workspace the two-layer FP8 calls need: the 8192-byte decode
+ * header, then h or m, M x H bf16, or at one token H / 2 words of 8 bytes,
+ * whichever is larger (0 for M == 0) */
 size_t fmlp_w8_workspace_size(int64_t M, int64_t H);
 
 /*

@@ -40,6 +40,10 @@ hipError_t launch_moe_router(const uint16_t*, const uint16_t*, int64_t, int, int
   reached("launch_moe_router");
 }
 hipError_t launch_decode_w8(const W8Layer&, int, hipStream_t) { reached("launch_decode_w8"); }
+bool decode_w8_two_applies(int, const W8Layer&, const W8Layer&, int) { reached("decode_w8_two_applies"); }
+hipError_t launch_decode_w8_two(const W8Layer&, const W8Layer&, uint32_t*, int, hipStream_t) {
+  reached("launch_decode_w8_two");
+}
 hipError_t launch_transpose(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, int64_t, int64_t, hipStream_t) {
   reached("launch_transpose");
 }

@@ -207,6 +207,7 @@ def test_w8_validation(L):
     S = 0x90000   # a 4-byte aligned stand-in for a scale array (never dereferenced)
     # h after the untouched 8 KB decode header (a workspace shared with the bf16 calls)
     assert L.fmlp_w8_workspace_size(16, 4096) == 8192 + 16 * 4096 * 2
+    assert L.fmlp_w8_workspace_size(1, 4096) == 8192 + 4096 * 4   # one token: H / 2 words of 8 bytes
     assert L.fmlp_w8_workspace_size(0, 4096) == 0
     assert L.fmlp_linear_w8(X, W, S, None, 0, 0, 64, 32, Y, None) == OK          # M == 0: no-op
     assert L.fmlp_linear_w8(X, W, S, None, 0, 17, 64, 32, Y, None) == E_ARG

@@ -2,7 +2,10 @@
 one layer, the two-layer MLP and the gated block at 1..16 tokens, ragged
 inner sizes (multiples of 16 that are not multiples of 64), several row
 tiles and a partial last tile, every activation, and the special codes
-(subnormals, signed zeros, the largest finite value)."""
+(subnormals, signed zeros, the largest finite value).  At one token with a
+hidden size up to 4096 the two layers run in one launch (h exchanged as
+epoch-tagged words); that form is checked bitwise against the two-launch
+form and across back-to-back calls."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +39,8 @@ def test_linear_w8(M, K, N, act):
         assert_parity(y, ref, f"linear_w8 {M}x{K}x{N} {act}")
 
 
-@pytest.mark.parametrize("M,K,H,N", [(1, 4096, 4096, 4096), (16, 4096, 4096, 4096), (5, 1040, 336, 272)])
+@pytest.mark.parametrize("M,K,H,N", [(1, 4096, 4096, 4096), (16, 4096, 4096, 4096), (5, 1040, 336, 272),
+                                     (1, 1040, 336, 272), (1, 8192, 16, 4096), (1, 16, 4096, 16)])
 def test_mlp2_w8(M, K, H, N):
     rng = np.random.default_rng(M + K + H + N)
     x = rand_bf16(rng, (M, K))
@@ -52,7 +56,7 @@ def test_mlp2_w8(M, K, H, N):
 
 
 @pytest.mark.parametrize("M,D,H", [(1, 8192, 28672), (16, 8192, 28672), (4, 1040, 2064), (16, 768, 3072),
-                                   (16, 4096, 1040), (9, 4096, 2048)])
+                                   (16, 4096, 1040), (9, 4096, 2048), (1, 768, 3072), (1, 4096, 1040)])
 @pytest.mark.parametrize("gate_act", ["gelu_tanh", "silu"])
 def test_glu_w8(M, D, H, gate_act):
     if (D, H) == (8192, 28672) and gate_act != "gelu_tanh":
@@ -110,3 +114,39 @@ def test_w8_float8_dtype_and_errors():
         F.fmlp_linear_w8(to_dev(rand_bf16(rng, (2, 24))), torch.zeros(32, 24, dtype=torch.uint8, device=DEV), sd)
     empty = F.fmlp_linear_w8(torch.empty(0, 64, dtype=torch.bfloat16, device=DEV), qd, sd)
     assert empty.shape == (0, 32)
+
+
+@pytest.mark.parametrize("form", ["mlp2", "glu"])
+def test_w8_one_launch_equals_two_launches(form):
+    """At one token the one-launch form computes exactly what the two launches
+    do (same per-tile order, h rounded to bf16 once): bitwise equal, over 20
+    back-to-back calls that alternate two inputs on one workspace, with no
+    barrier wait given up and the decode generation moving once per call."""
+    K, H, N = 4096, 4096, 4096
+    rng = np.random.default_rng(77)
+    xs = [to_dev(rand_bf16(rng, (1, K))) for _ in range(2)]
+    if form == "mlp2":
+        q1, s1, q1d, s1d = _codes(rng, H, K, 1 / 64)
+        q2, s2, q2d, s2d = _codes(rng, N, H, 1 / 64)
+        b1, b2 = to_dev(rand_bf16(rng, (H,), 1 / 64, "uniform")), to_dev(rand_bf16(rng, (N,), 1 / 64, "uniform"))
+        ws = F.workspace_for(DEV, int(F.lib().fmlp_w8_workspace_size(1, H)))
+        call = lambda x, out: F.fmlp_mlp2_w8(x, q1d, s1d, b1, q2d, s2d, b2, "gelu_erf", out=out)  # noqa: E731
+    else:
+        qg, sg, qgd, sgd = _codes(rng, H, K, K ** -0.5)
+        qu, su, qud, sud = _codes(rng, H, K, K ** -0.5)
+        qdn, sdn, qdd, sdd = _codes(rng, K, H, H ** -0.5)
+        ws = F.workspace_for(DEV, int(F.lib().fmlp_w8_workspace_size(1, H)))
+        call = lambda x, out: F.fmlp_glu_w8(x, qgd, sgd, qud, sud, qdd, sdd, "silu", out=out)  # noqa: E731
+    print(f"case fp8 {form} one launch vs two launches", flush=True)
+    with F.force_path("gemm"):
+        want = [call(x, None) for x in xs]
+    torch.cuda.synchronize()
+    gen0, tmo0 = F.decode_generation(ws), F.barrier_timeouts(ws)
+    outs = [torch.empty(1, N, dtype=torch.bfloat16, device=DEV) for _ in range(20)]
+    for i in range(20):
+        call(xs[i % 2], outs[i])
+    torch.cuda.synchronize()
+    for i in range(20):
+        assert torch.equal(outs[i].view(torch.int16), want[i % 2].view(torch.int16)), f"call {i}"
+    assert F.decode_generation(ws) == (gen0 + 20) & 0xFFFFFFFF
+    assert F.barrier_timeouts(ws) == tmo0

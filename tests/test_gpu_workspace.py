@@ -25,9 +25,11 @@ def _ref(x, t, act):
 
 def test_fp8_call_between_decode_calls_on_the_default_workspace():
     """A one-token bf16 decode call (word-flag publish: H = 4096), then a
-    two-layer FP8 call with ReLU at H = 4096 on the same cached workspace, then
-    the bf16 call again with a new x.  The FP8 call keeps its h after the
-    header, so the generation and the flags are untouched by it."""
+    one-token two-layer FP8 call with ReLU at H = 4096 on the same cached
+    workspace (one launch: it advances the same generation with the same
+    word protocol), then the bf16 call again with a new x; then the FP8 call
+    forced to its two-launch form, which keeps its h after the header and
+    leaves the generation alone."""
     rng = np.random.default_rng(4096)
     K, H, N = 256, 4096, 512
     t = _mlp2_inputs(rng, K, H, N)
@@ -49,11 +51,17 @@ def test_fp8_call_between_decode_calls_on_the_default_workspace():
     torch.cuda.synchronize()
     ref8 = oracle.mlp2_w8(f64_of_bits(xs[1]), q1, s1, f64_of_bits(t["b1"]), q2, s2, f64_of_bits(t["b2"]), "relu")
     assert_parity(y8, ref8, "fp8 mlp2 relu")
-    assert F.decode_generation(ws) == (gen0 + 1) & 0xFFFFFFFF, "the FP8 call wrote the decode header"
+    assert F.decode_generation(ws) == (gen0 + 2) & 0xFFFFFFFF
     y1 = F.fmlp_mlp2(to_dev(xs[1]), d["W1"], d["b1"], d["W2"], d["b2"], "gelu_erf", workspace=ws)
     torch.cuda.synchronize()
     assert_parity(y1, _ref(xs[1], t, "gelu_erf"), "bf16 decode, second x")
-    assert F.decode_generation(ws) == (gen0 + 2) & 0xFFFFFFFF
+    assert F.decode_generation(ws) == (gen0 + 3) & 0xFFFFFFFF
+    with F.force_path("gemm"):
+        y8 = F.fmlp_mlp2_w8(to_dev(xs[0]), dq[0], dq[1], d["b1"], dq[2], dq[3], d["b2"], "relu")
+    torch.cuda.synchronize()
+    ref8 = oracle.mlp2_w8(f64_of_bits(xs[0]), q1, s1, f64_of_bits(t["b1"]), q2, s2, f64_of_bits(t["b2"]), "relu")
+    assert_parity(y8, ref8, "fp8 mlp2 relu, two launches")
+    assert F.decode_generation(ws) == (gen0 + 3) & 0xFFFFFFFF, "the two-launch FP8 form wrote the decode header"
     assert F.barrier_timeouts(ws) == tmo0
 
 
