@@ -86,6 +86,7 @@ class Case:
         self.oracle_fn = oracle_fn    # () -> None, runs the oracle on the sample
         self.oracle_sample = oracle_sample  # (description, fraction of one step's flops)
         self.unfused = None           # per weight copy: the same forward as separate launches
+        self.unfused_form = ("fmlp_linear (GEMM + bias + activation), then fmlp_linear (GEMM + bias)", 2)
         self.bytes = w.bytes          # algorithmic HBM bytes of one forward
         self.weights = "bf16"
 
@@ -264,6 +265,18 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
                 kernel, launches, p = "decode_kernel", 1, "persistent decode (1 launch)"
             else:
                 kernel, launches, p = "gemm_bf16_kernel", 2, "fused gate+up GEMM + down GEMM (2 launches)"
+            unfused = None
+            if w.M > 16 and gate_act is None and path in ("auto", "gemm"):
+                # unfused: the page's eager GeGLU with our own GEMMs: g = gelu(x Wg^T) and
+                # u = x Wu^T as two Linear launches, m = g * u as torch's elementwise
+                # multiply (context: a library kernel), then the down projection
+                g_un = torch.empty(w.M, w.H, dtype=torch.bfloat16, device=dev)
+                u_un = torch.empty_like(g_un)
+                m_un = torch.empty_like(g_un)
+                unfused = [(F.bind_linear(x, s_["Wg"], None, "gelu_tanh", out=g_un),
+                            F.bind_linear(x, s_["Wu"], None, "none", out=u_un),
+                            (lambda: torch.mul(g_un, u_un, out=m_un)),
+                            F.bind_linear(m_un, s_["Wd"], None, "none", out=y)) for s_ in sets]
             import oracle
 
             rows = min(w.M, 64 if w.K * w.H > 1e8 else 1024)
@@ -279,6 +292,10 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
             sample = (f"{rows} of {w.M} token rows, full weights", rows / w.M)
         case = Case(w, calls, kernel, launches, p, R, fn, sample)
         case.workspace = ws
+        if unfused is not None:
+            case.unfused = unfused
+            case.unfused_form = ("fmlp_linear (gate GEMM + tanh GELU), fmlp_linear (up GEMM), torch.mul, "
+                                 "fmlp_linear (down GEMM)", 4)
         return case
 
     if w.op == "glu_bwd":
@@ -637,8 +654,8 @@ def main(argv=None):
         "us_per_forward": round(wall_s * 1e6, 3),
         "us_per_forward_device": round(dev_s * 1e6, 3),
         "roofline": roof,
-        "unfused": ({"launches": 2, "us_per_forward": round(unfused_s * 1e6, 3),
-                     "form": "fmlp_linear (GEMM + bias + activation), then fmlp_linear (GEMM + bias)"}
+        "unfused": ({"launches": case.unfused_form[1], "us_per_forward": round(unfused_s * 1e6, 3),
+                     "form": case.unfused_form[0]}
                     if unfused_s is not None else None),
         "baseline_note": ("vs_baseline = value / the page's H100 fused figure (8.1 us, same workload); "
                           "another machine, context only") if vs is not None else None,
