@@ -64,6 +64,7 @@ __all__ = [
     "fmlp_geglu_workspace_size",
     "fmlp_moe_workspace_size",
     "force_path",
+    "cooperative_decode",
     "workspace_for",
     "barrier_timeouts",
     "decode_generation",
@@ -136,7 +137,7 @@ def lib() -> ctypes.CDLL:
             getattr(L, f).argtypes = [_i64] * n
             getattr(L, f).restype = _sz
         for f in ("fmlp_linear", "fmlp_mlp2", "fmlp_geglu", "fmlp_glu", "fmlp_moe_geglu", "fmlp_moe_glu",
-                  "fmlp_moe_route", "fmlp_set_path"):
+                  "fmlp_moe_route", "fmlp_set_path", "fmlp_set_cooperative_decode"):
             getattr(L, f).restype = ctypes.c_int
         L.fmlp_linear_w8.argtypes = [_p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _p, _p]
         L.fmlp_mlp2_w8.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_int, _i64, _i64, _i64, _i64, _p, _p,
@@ -145,6 +146,7 @@ def lib() -> ctypes.CDLL:
         L.fmlp_w8_workspace_size.argtypes = [_i64, _i64]
         L.fmlp_w8_workspace_size.restype = _sz
         L.fmlp_set_path.argtypes = [ctypes.c_int]
+        L.fmlp_set_cooperative_decode.argtypes = [ctypes.c_int]
         L.fmlp_mlp2_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
         L.fmlp_mlp2_workspace_size.restype = _sz
         L.fmlp_geglu_workspace_size.argtypes = [_i64, _i64, _i64]
@@ -214,6 +216,18 @@ def workspace_for(device: torch.device, nbytes: int) -> torch.Tensor:
             ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
             _ws_cache[key] = ws
         return ws
+
+
+@contextlib.contextmanager
+def cooperative_decode():
+    """The calling thread's one-launch decode calls use a cooperative launch
+    (a grid that cannot be resident at once is refused instead of timing out)."""
+    L = lib()
+    _check(L.fmlp_set_cooperative_decode(1))
+    try:
+        yield
+    finally:
+        L.fmlp_set_cooperative_decode(0)
 
 
 @contextlib.contextmanager

@@ -21,6 +21,7 @@ namespace {
 
 thread_local std::string g_last_error;
 thread_local int g_path = 0;   // 0 auto, 1 decode, 2 two-GEMM, 3 small fused, 4 fused gated block
+thread_local bool g_coop = false;   // cooperative launch of the one-launch decode forms
 
 constexpr int kPathAuto = 0, kPathDecode = 1, kPathGemm = 2, kPathSmall = 3, kPathFused = 4;
 constexpr int64_t kDecodeMaxM = 16;
@@ -196,7 +197,7 @@ fmlp_status record_error(fmlp_status s, const char* msg) { return fail(s, "%s", 
 
 extern "C" {
 
-int fmlp_version(void) { return 105; }
+int fmlp_version(void) { return 106; }
 
 const char* fmlp_status_string(fmlp_status s) {
   switch (s) {
@@ -213,6 +214,12 @@ const char* fmlp_status_string(fmlp_status s) {
 }
 
 const char* fmlp_last_error(void) { return g_last_error.c_str(); }
+
+fmlp_status fmlp_set_cooperative_decode(int on) {
+  if (on != 0 && on != 1) return fail(FMLP_E_ARG, "on=%d is not 0 or 1", on);
+  g_coop = on != 0;
+  return ok();
+}
 
 fmlp_status fmlp_set_path(int path) {
   if (path < kPathAuto || path > kPathFused) return fail(FMLP_E_ARG, "path=%d is not 0..4", path);
@@ -299,7 +306,7 @@ fmlp_status fmlp_mlp2(const fmlp_bf16* x, const fmlp_bf16* W1, const fmlp_bf16* 
   if (path == kPathDecode) {
     GemvLayer L1{x, W1, nullptr, b1, h, K, H, act, 0};
     GemvLayer L2{h, W2, nullptr, b2, y, H, N, FMLP_ACT_NONE, 0};
-    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
+    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s, g_coop),
                     "mlp2 (decode, persistent) launch");
   }
   hipError_t e = gemm_linear(x, W1, b1, act, M, K, H, h, cus, s);
@@ -356,7 +363,7 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
   if (path == kPathDecode) {
     GemvLayer L1{x, Wg, Wu, nullptr, m, D, H, gate_act, 1};
     GemvLayer L2{m, Wd, nullptr, nullptr, y, H, D, FMLP_ACT_NONE, 0};
-    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s),
+    return launched(launch_gemv2_persistent(L1, L2, (int)M, static_cast<uint32_t*>(workspace), s, g_coop),
                     "geglu (decode, persistent) launch");
   }
   if (path == kPathFused)
@@ -831,7 +838,7 @@ fmlp_status fmlp_mlp2_w8(const fmlp_bf16* x, const fmlp_fp8* W1q, const float* s
   W8Layer L1{x, W1q, s1, nullptr, nullptr, b1, h, K, H, act};
   W8Layer L2{h, W2q, s2, nullptr, nullptr, b2, y, H, N, FMLP_ACT_NONE};
   if (g_path != kPathGemm && decode_w8_two_applies((int)M, L1, L2, cus))
-    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s),
+    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s, g_coop),
                     "mlp2 (fp8 weights, one launch)");
   hipError_t e = launch_decode_w8(L1, (int)M, s);
   if (e != hipSuccess) return launched(e, "mlp2 (fp8 weights) layer-1 launch");
@@ -863,7 +870,7 @@ fmlp_status fmlp_glu_w8(const fmlp_bf16* x, const fmlp_fp8* Wgq, const float* sg
   W8Layer L1{x, Wgq, sg, Wuq, su, nullptr, m, D, H, gate_act};
   W8Layer L2{m, Wdq, sd, nullptr, nullptr, nullptr, y, H, D, FMLP_ACT_NONE};
   if (g_path != kPathGemm && decode_w8_two_applies((int)M, L1, L2, cus))
-    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s),
+    return launched(launch_decode_w8_two(L1, L2, static_cast<uint32_t*>(workspace), cus, s, g_coop),
                     "glu (fp8 weights, one launch)");
   hipError_t e = launch_decode_w8(L1, (int)M, s);
   if (e != hipSuccess) return launched(e, "glu (fp8 weights) gate+up launch");

@@ -744,15 +744,24 @@ namespace {
 // One kernel variant on `grid` blocks.  The two-layer form waits for every
 // block at its barrier; the grid is capped at one block per CU (the LDS ring
 // admits one), so on an otherwise idle device every block is resident.  A
-// cooperative launch would also refuse a grid that cannot be co-resident, but
-// it was measured to add about 18 us to every call (the 4096^3 two-layer
-// forward at one token: 36 us against 18 us), twice the whole forward's
-// roofline time; the plain launch is kept, and a barrier wait that gives up is
-// counted in the workspace header for the caller to check.
+// cooperative launch also refuses a grid that cannot be co-resident, but it
+// was measured to add about 18 us to every call (the 4096^3 two-layer forward
+// at one token: 36 us against 18 us), twice the whole forward's roofline
+// time; so it is opt-in, the plain launch is the default, and a barrier wait
+// that gives up is counted in the workspace header for the caller to check.
+// With `coop` the launch is cooperative (opt-in, fmlp_set_cooperative_decode):
+// the runtime refuses a grid that cannot be resident at once instead of
+// letting the barrier time out.
 template <bool DUAL1, bool TWO, int MC, bool LL>
 hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
-                          hipStream_t s) {
-  const uint32_t salt = TWO ? next_launch_salt() : 0u;
+                          hipStream_t s, bool coop) {
+  uint32_t salt = TWO ? next_launch_salt() : 0u;
+  if (coop) {
+    GemvLayer a = L1, b = L2;
+    void* args[] = {&a, &b, &M, &sync, &salt};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid),
+                                      dim3(kThreads), args, 0, s);
+  }
   hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync, salt);
   return hipGetLastError();
 }
@@ -760,14 +769,14 @@ hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L
 // activation-row class of M: the rows an LDS stage holds
 template <bool DUAL1, bool TWO>
 hipError_t launch_mc(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
-                     hipStream_t s) {
+                     hipStream_t s, bool coop = false) {
   // word-flag publish of h: one token, h fits h_lds, and every block owns a
   // layer-1 tile (so every block writes words before block 0 can see them all)
   const bool ll = TWO && M == 1 && L2.K <= kLLMaxH && (int64_t)grid <= (L1.N + 15) / 16;
-  if (M <= 1 && ll) return launch_variant<DUAL1, TWO, 1, TWO>(grid, L1, L2, M, sync, s);
-  if (M <= 1) return launch_variant<DUAL1, TWO, 1, false>(grid, L1, L2, M, sync, s);
-  if (M <= 4) return launch_variant<DUAL1, TWO, 4, false>(grid, L1, L2, M, sync, s);
-  return launch_variant<DUAL1, TWO, 16, false>(grid, L1, L2, M, sync, s);
+  if (M <= 1 && ll) return launch_variant<DUAL1, TWO, 1, TWO>(grid, L1, L2, M, sync, s, coop);
+  if (M <= 1) return launch_variant<DUAL1, TWO, 1, false>(grid, L1, L2, M, sync, s, coop);
+  if (M <= 4) return launch_variant<DUAL1, TWO, 4, false>(grid, L1, L2, M, sync, s, coop);
+  return launch_variant<DUAL1, TWO, 16, false>(grid, L1, L2, M, sync, s, coop);
 }
 
 }  // namespace
@@ -785,7 +794,7 @@ hipError_t launch_gemv(const GemvLayer& L, int M, hipStream_t s) {
 }
 
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
-                                   hipStream_t s) {
+                                   hipStream_t s, bool cooperative) {
   if (M <= 0) return hipSuccess;
   if (M > 16) return hipErrorInvalidValue;
   const Occ o = occ();
@@ -797,8 +806,8 @@ hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int
   const int64_t cap = std::min<int64_t>((int64_t)o.cus, kDecodeMaxBlocks);
   const unsigned grid = (unsigned)std::min<int64_t>(cap, std::max(tiles1, tiles2));
   if (grid == 0) return hipSuccess;
-  if (L1.geglu) return launch_mc<true, true>(grid, L1, L2, M, sync, s);
-  return launch_mc<false, true>(grid, L1, L2, M, sync, s);
+  if (L1.geglu) return launch_mc<true, true>(grid, L1, L2, M, sync, s, cooperative);
+  return launch_mc<false, true>(grid, L1, L2, M, sync, s, cooperative);
 }
 
 }  // namespace fmlp

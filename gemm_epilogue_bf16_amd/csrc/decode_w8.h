@@ -31,6 +31,7 @@ hipError_t launch_decode_w8(const W8Layer& L, int M, hipStream_t s);
 // H % 16 == 0, L2.K == H, 2 * L1.K <= 64 KB and a device of at most
 // kDecodeMaxBlocks compute units.
 bool decode_w8_two_applies(int M, const W8Layer& L1, const W8Layer& L2, int cus);
-hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s);
+hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s,
+                                bool cooperative = false);
 
 }  // namespace fmlp

@@ -470,13 +470,21 @@ bool decode_w8_two_applies(int M, const W8Layer& L1, const W8Layer& L2, int cus)
          cus > 0 && cus <= kDecodeMaxBlocks && tiles1 >= 1;
 }
 
-hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s) {
+hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* sync, int cus, hipStream_t s,
+                                bool cooperative) {
   if (!decode_w8_two_applies(1, L1, L2, cus)) return hipErrorInvalidValue;
   if (L1.K % 16 != 0 || L2.N <= 0) return hipErrorInvalidValue;
   const int64_t tiles1 = (L1.N + 15) / 16;
   // every block owns a layer-1 tile and all are resident at once: at most one per CU
   const unsigned grid = (unsigned)std::min<int64_t>(tiles1, cus);
-  const uint32_t salt = next_launch_salt();
+  uint32_t salt = next_launch_salt();
+  if (cooperative) {   // opt-in: the runtime refuses a grid that cannot be resident at once
+    W8Layer a = L1, b = L2;
+    void* args[] = {&a, &b, &sync, &salt};
+    const void* f = L1.W1 ? reinterpret_cast<const void*>(&decode_w8_two_kernel<true>)
+                          : reinterpret_cast<const void*>(&decode_w8_two_kernel<false>);
+    return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kW8Threads), args, 0, s);
+  }
   if (L1.W1)
     hipLaunchKernelGGL((decode_w8_two_kernel<true>), dim3(grid), dim3(kW8Threads), 0, s, L1, L2, sync, salt);
   else

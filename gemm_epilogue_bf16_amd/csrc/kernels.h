@@ -119,7 +119,7 @@ static_assert(kDecodeMaxBlocks % 4 == 0, "flags are read 4 at a time");
 // outputs are published through device-coherent stores and a flag barrier,
 // layer-2 weights stream across the barrier.  sync = the workspace header.
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M,
-                                   uint32_t* sync, hipStream_t s);
+                                   uint32_t* sync, hipStream_t s, bool cooperative = false);
 
 // A 32-bit tag per launch, different for every launch of this process (for
 // 2^32 launches) and most likely for other processes: the epoch salt of the

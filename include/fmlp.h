@@ -363,6 +363,18 @@ size_t fmlp_decode_generation_offset(void);
  */
 fmlp_status fmlp_set_path(int path);
 
+/*
+ * Cooperative launch of the one-launch decode forms (thread-local; applies to
+ * the calling thread's later fmlp_mlp2 / fmlp_geglu / fmlp_glu decode calls and
+ * the one-token FP8 two-layer calls).  on = 1: those kernels go through
+ * hipLaunchCooperativeKernel, so a grid that cannot be resident at once is
+ * refused (FMLP_E_HIP) instead of a barrier wait timing out with y wrong;
+ * measured to add about 18 us per call on MI355X.  on = 0 (default): the
+ * plain launch, with the timeout count in the workspace header.  Other values
+ * are FMLP_E_ARG.
+ */
+fmlp_status fmlp_set_cooperative_decode(int on);
+
 const char* fmlp_status_string(fmlp_status s);
 const char* fmlp_last_error(void);
 int fmlp_version(void);  /* major*10000 + minor*100 + patch */

@@ -20,7 +20,7 @@ int gemm_tile_bm(int tile) { return tile == TILE_256x256 ? 256 : 128; }
 int gemm_tile_bn(int tile) { return tile == TILE_256x256 ? 256 : tile == TILE_128x192 ? 192 : 128; }
 hipError_t launch_gemm(int, bool, bool, int, GemmParams, hipStream_t) { reached("launch_gemm"); }
 hipError_t launch_gemv(const GemvLayer&, int, hipStream_t) { reached("launch_gemv"); }
-hipError_t launch_gemv2_persistent(const GemvLayer&, const GemvLayer&, int, uint32_t*, hipStream_t) {
+hipError_t launch_gemv2_persistent(const GemvLayer&, const GemvLayer&, int, uint32_t*, hipStream_t, bool) {
   reached("launch_gemv2_persistent");
 }
 hipError_t launch_small_mlp2(const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*, const uint16_t*,
@@ -41,7 +41,7 @@ hipError_t launch_moe_router(const uint16_t*, const uint16_t*, int64_t, int, int
 }
 hipError_t launch_decode_w8(const W8Layer&, int, hipStream_t) { reached("launch_decode_w8"); }
 bool decode_w8_two_applies(int, const W8Layer&, const W8Layer&, int) { reached("decode_w8_two_applies"); }
-hipError_t launch_decode_w8_two(const W8Layer&, const W8Layer&, uint32_t*, int, hipStream_t) {
+hipError_t launch_decode_w8_two(const W8Layer&, const W8Layer&, uint32_t*, int, hipStream_t, bool) {
   reached("launch_decode_w8_two");
 }
 hipError_t launch_transpose(const uint16_t*, int64_t, int64_t, int64_t, uint16_t*, int64_t, int64_t, hipStream_t) {

@@ -136,6 +136,9 @@ def test_geglu_validation(L):
     finally:
         L.fmlp_set_path(0)
     assert L.fmlp_set_path(5) == E_ARG
+    assert L.fmlp_set_cooperative_decode(2) == E_ARG
+    assert L.fmlp_set_cooperative_decode(1) == OK
+    assert L.fmlp_set_cooperative_decode(0) == OK
 
 
 def test_glu_validation(L):

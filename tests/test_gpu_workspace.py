@@ -141,3 +141,38 @@ def test_backward_calls_leave_the_decode_header_alone():
     assert_parity(y, _ref(x, t, "gelu_erf"), "decode after a backward call")
     assert F.decode_generation(ws) == (gen0 + 2) & 0xFFFFFFFF
     assert F.barrier_timeouts(ws) == tmo0
+
+
+@pytest.mark.parametrize("M,K,H,N", [(1, 512, 4096, 256), (16, 512, 2048, 1024), (1, 256, 4104, 512)])
+def test_cooperative_decode_launch(M, K, H, N):
+    """The opt-in cooperative launch of the one-launch decode: same results as
+    the plain launch (bitwise), the generation moves once per call and no
+    wait gives up; and the one-token FP8 two-layer launch the same way."""
+    rng = np.random.default_rng(M * 5 + H)
+    t = _mlp2_inputs(rng, K, H, N)
+    d = {k: to_dev(v) for k, v in t.items()}
+    x = rand_bf16(rng, (M, K))
+    ws = torch.zeros(max(F.fmlp_mlp2_workspace_size(M, K, H, N), int(F.lib().fmlp_w8_workspace_size(M, H))),
+                     dtype=torch.uint8, device=DEV)
+    print(f"case cooperative decode M={M} K={K} H={H} N={N}", flush=True)
+    plain = F.fmlp_mlp2(to_dev(x), d["W1"], d["b1"], d["W2"], d["b2"], "gelu_erf", workspace=ws)
+    torch.cuda.synchronize()
+    gen0 = F.decode_generation(ws)
+    with F.cooperative_decode():
+        coop = F.fmlp_mlp2(to_dev(x), d["W1"], d["b1"], d["W2"], d["b2"], "gelu_erf", workspace=ws)
+    torch.cuda.synchronize()
+    assert_parity(coop, _ref(x, t, "gelu_erf"), "cooperative launch")
+    assert np.array_equal(bits_of(coop), bits_of(plain))
+    assert F.decode_generation(ws) == (gen0 + 1) & 0xFFFFFFFF
+    assert F.barrier_timeouts(ws) == 0
+    if M == 1 and H % 16 == 0 and H <= 4096:
+        q1, s1 = datagen.e4m3_weights(rng, H, K, K ** -0.5)
+        q2, s2 = datagen.e4m3_weights(rng, N, H, H ** -0.5)
+        dq = [torch.from_numpy(a).to(DEV) for a in (q1, s1, q2, s2)]
+        y8 = F.fmlp_mlp2_w8(to_dev(x), dq[0], dq[1], d["b1"], dq[2], dq[3], d["b2"], "silu", workspace=ws)
+        with F.cooperative_decode():
+            y8c = F.fmlp_mlp2_w8(to_dev(x), dq[0], dq[1], d["b1"], dq[2], dq[3], d["b2"], "silu", workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(y8c), bits_of(y8))
+        assert F.decode_generation(ws) == (gen0 + 3) & 0xFFFFFFFF
+        assert F.barrier_timeouts(ws) == 0
