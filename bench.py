@@ -382,7 +382,8 @@ def setup_case(name: str, cold: bool, dev, path: str, act=None, w8: bool = False
         fn = lambda: oracle.moe_geglu(xs, ids[:toks], gw[:toks], get)  # noqa: E731
     else:
         fn = lambda: oracle.moe_glu(xs, ids[:toks], gw[:toks], get, gate_act)  # noqa: E731
-    return Case(w, calls, "gemm_bf16_kernel", 4, "route + grouped gate+up + grouped down + combine",
+    return Case(w, calls, "gemm_bf16_kernel", 6,
+                "route (count, scan, place) + grouped gate+up + grouped down + combine",
                 1, fn, (f"{toks} of {w.M} tokens (their experts' weights pre-converted)", toks / w.M))
 
 

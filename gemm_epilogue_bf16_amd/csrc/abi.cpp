@@ -377,7 +377,7 @@ fmlp_status fmlp_glu(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf16* W
 // ---- mixture of experts --------------------------------------------------------
 namespace {
 struct MoeLayout {
-  size_t tok_of, scale_of, pos_of, group_off, tile_off, m, ytilde, total;
+  size_t tok_of, scale_of, pos_of, group_off, tile_off, counts, m, ytilde, total;
 };
 // Split-K of the MoE down projection (K = H): two halves when the 64-k stage
 // count is even and long (the tail m-tile of every expert then costs half a
@@ -396,6 +396,7 @@ MoeLayout moe_layout(int64_t T, int64_t D, int64_t H, int32_t E, int32_t top_k) 
   L.pos_of = o;    o += round_up(P * 4, 256);
   L.group_off = o; o += round_up(((size_t)E + 1) * 4, 256);
   L.tile_off = o;  o += round_up(((size_t)E + 1) * 4, 256);
+  L.counts = o;    o += round_up(moe_route_counts_bytes((int64_t)P, E), 256);
   L.m = o;         o += round_up(P * (size_t)H * 2, 256);
   L.ytilde = o;    o += round_up(P * (size_t)D * 4, 256) * (size_t)moe_down_ksplit(H);
   L.total = o;
@@ -430,7 +431,7 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
   TRY(check_rows("T", T));
   TRY(check_inner("D", D));
   TRY(check_inner("H", H));
-  if (E < 1 || E > 1024) return fail(FMLP_E_ARG, "E=%d must be in [1, 1024]", E);
+  if (E < 1 || E > kMoeRouteMaxExperts) return fail(FMLP_E_ARG, "E=%d must be in [1, %d]", E, kMoeRouteMaxExperts);
   if (top_k < 1 || top_k > 8) return fail(FMLP_E_ARG, "top_k=%d must be in [1, 8]", top_k);
   if ((int64_t)T * top_k >= (int64_t(1) << 31))
     return fail(FMLP_E_SHAPE, "T*top_k=%lld is too large", (long long)T * top_k);
@@ -465,7 +466,8 @@ fmlp_status fmlp_moe_glu(const fmlp_bf16* x, const int32_t* expert_ids, const fl
   const int bm = gemm_tile_bm(kMoeTile);
   const int64_t P = T * top_k;
 
-  hipError_t e = launch_moe_route(expert_ids, gate_w, T, top_k, E, bm, r, s);
+  hipError_t e = launch_moe_route(expert_ids, gate_w, T, top_k, E, bm, r,
+                                  reinterpret_cast<int32_t*>(ws + L.counts), s);
   if (e != hipSuccess) return launched(e, "moe route launch");
 
   GemmParams g = dense_params(x, D, Wg, Wu, nullptr, m, H, P, H, D, gate_act, cus);

@@ -184,8 +184,16 @@ struct MoeRouteOut {
   int32_t* tile_off;    // [E+1] prefix of ceil(count/BM)
   int32_t* err;         // invalid-id count
 };
+// The route runs over blocks of kMoeRoutePairsPerBlock pairs; `counts` is a
+// device scratch array of moe_route_counts_bytes(T * top_k, E) bytes (the
+// blocks' per-expert counts, then their prefixes).
+constexpr int kMoeRoutePairsPerBlock = 512;
+constexpr int kMoeRouteMaxExperts = 1024;
+inline size_t moe_route_counts_bytes(int64_t P, int E) {
+  return (size_t)((P + kMoeRoutePairsPerBlock - 1) / kMoeRoutePairsPerBlock) * (size_t)(E + 1) * 4;
+}
 hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, int top_k, int E,
-                            int bm, const MoeRouteOut& o, hipStream_t s);
+                            int bm, const MoeRouteOut& o, int32_t* counts, hipStream_t s);
 hipError_t launch_moe_combine(const float* ytilde, const int32_t* pos_of, int64_t T, int top_k,
                               int64_t D, int ksplit, int64_t kstride, uint16_t* y, hipStream_t s);
 // Router: logits = x[T,D] . Wr[E,D]^T (fp32), top_k ids per token (ties to the

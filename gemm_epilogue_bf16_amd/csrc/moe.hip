@@ -9,10 +9,11 @@
 //   route:   (token, slot) pairs are bucketed per expert, stable in pair order,
 //            giving each expert one contiguous segment of rows; the grouped
 //            GEMMs then run every expert over its segment with the token rows
-//            gathered on the fly.  Integer work only: counts, an exclusive scan,
-//            and a scatter, in a single block so the order is fixed; each
-//            thread keeps its contiguous run of pairs in registers and the
-//            experts are counted four at a time per block scan.
+//            gathered on the fly.  Integer work only, in three launches over
+//            blocks of 512 pairs: per-block expert counts, their exclusive
+//            scans (over the blocks per expert, then over the experts), and the
+//            scatter, each pair ranked within its block by wave ballots.  The
+//            place of every pair is fixed by pair order alone.
 //   combine: y[t] = sum_j ytilde[pos(t, j)] in slot order j = 0, 1, ... in fp32
 //            (the gate weight was applied in the down-projection epilogue; with
 //            the down projection split over K, the parts of each row are added
@@ -33,130 +34,123 @@ namespace fmlp {
 
 namespace {
 
-constexpr int kRouteThreads = 512;    // 8 waves
+constexpr int kRouteThreads = kMoeRoutePairsPerBlock;   // one pair per thread
 constexpr int kRouteWaves = kRouteThreads / 64;
-constexpr int kRouteCache = 16;       // pairs per thread held in registers
-constexpr int kRouteBatch = 4;        // experts counted per block scan
+constexpr int kRouteScanThreads = 1024;
 
-typedef int i32x4v __attribute__((ext_vector_type(4)));
-
-// Exclusive scan of a 4-vector over the block, in thread order: a wave-level
-// shuffle scan, then each wave adds the totals of the waves before it.
-// Returns the exclusive prefix; *total gets the block total.
-__device__ i32x4v block_exclusive_scan4(i32x4v v, i32x4v* wave_tot, i32x4v* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  i32x4v incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    i32x4v up;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) up[c] = __shfl_up(incl[c], off, 64);
-    if (lane >= off) incl += up;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
+// count: the per-expert histogram of this block's pairs (invalid ids in column
+// E), written as row blockIdx.x of cnt [G][E+1].
+__global__ void __launch_bounds__(kRouteThreads)
+moe_route_count_kernel(const int32_t* __restrict__ ids, int64_t P, int E, int32_t* __restrict__ cnt) {
+  __shared__ int hist[kMoeRouteMaxExperts + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kRouteThreads) hist[e] = 0;
   __syncthreads();
-  i32x4v before = {0, 0, 0, 0}, all = {0, 0, 0, 0};
-  for (int w = 0; w < kRouteWaves; ++w) {
-    const i32x4v t = wave_tot[w];
-    if (w < wave) before += t;
-    all += t;
+  const int64_t p = (int64_t)blockIdx.x * kRouteThreads + tid;
+  if (p < P) {
+    const int e = ids[p];
+    atomicAdd(&hist[(e < 0 || e >= E) ? E : e], 1);
   }
-  __syncthreads();   // wave_tot is reused by the next scan
-  *total = all;
-  return before + incl - v;
+  __syncthreads();
+  int32_t* row = cnt + (int64_t)blockIdx.x * (E + 1);
+  for (int e = tid; e <= E; e += kRouteThreads) row[e] = hist[e];
 }
 
-__global__ void __launch_bounds__(kRouteThreads)
-moe_route_kernel(const int32_t* __restrict__ ids, const float* __restrict__ gate_w, int64_t P,
-                 int top_k, int E, int bm, MoeRouteOut o) {
-  __shared__ i32x4v wave_tot[kRouteWaves];
+// scan: each column of cnt becomes the exclusive prefix over the blocks (the
+// first place, within its expert's segment, of each block's pairs); then the
+// expert totals give group_off and tile_off (exclusive scans over the
+// experts), and column E the invalid-id total.
+__global__ void __launch_bounds__(kRouteScanThreads)
+moe_route_scan_kernel(int32_t* __restrict__ cnt, int G, int E, int bm, MoeRouteOut o) {
+  __shared__ int tot[kMoeRouteMaxExperts + 1];
   const int tid = threadIdx.x;
-  // thread tid owns the contiguous pairs [p0, p0 + n) (P < 2^31), the first
-  // kRouteCache of them in registers
-  const int chunk = (int)((P + kRouteThreads - 1) / kRouteThreads);
-  const int p0 = (int)min(P, (int64_t)tid * chunk);
-  const int n = (int)min((int64_t)chunk, P - p0);
-  const int32_t* my_ids = ids + p0;
-  const float* my_gw = gate_w + p0;
-  int32_t* my_pos = o.pos_of + p0;
-  int mine[kRouteCache];
-  int bad = 0;
+  constexpr int U = 16;   // blocks whose counts are requested together
+  for (int e = tid; e <= E; e += kRouteScanThreads) {
+    int run = 0;
+    for (int b0 = 0; b0 < G; b0 += U) {
+      int v[U];
 #pragma unroll
-  for (int j = 0; j < kRouteCache; ++j) {
-    mine[j] = j < n ? my_ids[j] : 0;
-    if (j < n && (mine[j] < 0 || mine[j] >= E)) {
-      my_pos[j] = -1;
-      ++bad;
-    }
-    if (j >= n) mine[j] = -1;   // never matches an expert
-  }
-  for (int j = kRouteCache; j < n; ++j) {
-    const int e = my_ids[j];
-    if (e < 0 || e >= E) {
-      my_pos[j] = -1;
-      ++bad;
-    }
-  }
-
-  i32x4v tot;
-  (void)block_exclusive_scan4(i32x4v{bad, 0, 0, 0}, wave_tot, &tot);
-  if (tid == 0) o.err[0] = tot[0];
-
-  // places pair j (expert e0 + d, d in [0, kRouteBatch)) at the next slot of
-  // its expert
-  auto place = [&](int j, int d, i32x4v& pos) {
-    int at = 0;
+      for (int j = 0; j < U; ++j) v[j] = b0 + j < G ? cnt[(int64_t)(b0 + j) * (E + 1) + e] : 0;
 #pragma unroll
-    for (int c = 0; c < kRouteBatch; ++c)
-      if (d == c) at = pos[c]++;
-    o.tok_of[at] = (p0 + j) / top_k;
-    o.scale_of[at] = my_gw[j];
-    my_pos[j] = at;
-  };
-  int running = 0, running_tiles = 0;
-  for (int e0 = 0; e0 < E; e0 += kRouteBatch) {
-    const int nb = min(kRouteBatch, E - e0);
-    i32x4v cnt = {0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < kRouteCache; ++j) {
-      const int d = mine[j] - e0;
-#pragma unroll
-      for (int c = 0; c < kRouteBatch; ++c) cnt[c] += (d == c && c < nb) ? 1 : 0;
-    }
-    for (int j = kRouteCache; j < n; ++j) {
-      const int d = my_ids[j] - e0;
-#pragma unroll
-      for (int c = 0; c < kRouteBatch; ++c) cnt[c] += (d == c && c < nb) ? 1 : 0;
-    }
-    const i32x4v base = block_exclusive_scan4(cnt, wave_tot, &tot);
-    i32x4v pos;
-    int acc = running;
-#pragma unroll
-    for (int c = 0; c < kRouteBatch; ++c) {
-      pos[c] = acc + base[c];
-      acc += tot[c];
-    }
-#pragma unroll
-    for (int j = 0; j < kRouteCache; ++j) {
-      const int d = mine[j] - e0;
-      if (d >= 0 && d < nb) place(j, d, pos);
-    }
-    for (int j = kRouteCache; j < n; ++j) {
-      const int d = my_ids[j] - e0;
-      if (d >= 0 && d < nb) place(j, d, pos);
-    }
-    for (int c = 0; c < nb; ++c) {
-      if (tid == 0) {
-        o.group_off[e0 + c] = running;
-        o.tile_off[e0 + c] = running_tiles;
+      for (int j = 0; j < U; ++j) {
+        if (b0 + j < G) {
+          cnt[(int64_t)(b0 + j) * (E + 1) + e] = run;
+          run += v[j];
+        }
       }
-      running += tot[c];
-      running_tiles += (tot[c] + bm - 1) / bm;
     }
+    tot[e] = run;
   }
-  if (tid == 0) {
-    o.group_off[E] = running;
-    o.tile_off[E] = running_tiles;
+  __syncthreads();
+  if (tid >= 64) return;
+  // wave 0: the experts 64 at a time, a shuffle scan of counts and tiles each
+  const int lane = tid;
+  int base = 0, tbase = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int c = e < E ? tot[e] : 0;
+    const int t = (c + bm - 1) / bm;
+    int ic = c, it = t;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int uc = __shfl_up(ic, off, 64), ut = __shfl_up(it, off, 64);
+      if (lane >= off) {
+        ic += uc;
+        it += ut;
+      }
+    }
+    if (e < E) {
+      o.group_off[e] = base + ic - c;
+      o.tile_off[e] = tbase + it - t;
+    }
+    base += __shfl(ic, 63, 64);
+    tbase += __shfl(it, 63, 64);
+  }
+  if (lane == 0) {
+    o.group_off[E] = base;
+    o.tile_off[E] = tbase;
+    o.err[0] = tot[E];
+  }
+}
+
+// place: pair p of expert e goes to group_off[e] + (its block's first place
+// in e) + (pairs of e in earlier waves of the block) + (pairs of e in earlier
+// lanes of its wave), which keeps pair order within every expert.  A wave
+// ranks its lanes one expert at a time: the lowest unranked lane names the
+// expert, a ballot finds every lane with it.
+__global__ void __launch_bounds__(kRouteThreads)
+moe_route_place_kernel(const int32_t* __restrict__ ids, const float* __restrict__ gate_w, int64_t P, int top_k,
+                       int E, const int32_t* __restrict__ cnt, MoeRouteOut o) {
+  __shared__ int wcnt[kRouteWaves * kMoeRouteMaxExperts];   // [wave][expert]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t p = (int64_t)blockIdx.x * kRouteThreads + tid;
+  const bool have = p < P;
+  const int e = have ? ids[p] : -1;
+  const float w = have ? gate_w[p] : 0.f;
+  const bool valid = have && e >= 0 && e < E;
+  for (int i = tid; i < kRouteWaves * E; i += kRouteThreads) wcnt[i] = 0;
+  __syncthreads();
+  const uint64_t below = lane == 0 ? 0ull : ~0ull >> (64 - lane);   // the lanes before this one
+  int rank = 0;
+  uint64_t pending = __builtin_amdgcn_ballot_w64(valid);
+  while (pending != 0) {   // wave-uniform
+    const int leader = __builtin_ctzll(pending);
+    const int ec = __shfl(e, leader, 64);
+    const bool mine = valid && e == ec;
+    const uint64_t same = __builtin_amdgcn_ballot_w64(mine);
+    if (mine) rank = __popcll(same & below);
+    if (lane == leader) wcnt[wave * E + ec] = __popcll(same);
+    pending &= ~same;
+  }
+  __syncthreads();
+  if (valid) {
+    int at = o.group_off[e] + cnt[(int64_t)blockIdx.x * (E + 1) + e] + rank;
+    for (int v = 0; v < wave; ++v) at += wcnt[v * E + e];
+    o.tok_of[at] = (int32_t)(p / top_k);
+    o.scale_of[at] = w;
+    o.pos_of[p] = at;
+  } else if (have) {
+    o.pos_of[p] = -1;
   }
 }
 
@@ -470,9 +464,21 @@ hipError_t launch_moe_router(const uint16_t* x, const uint16_t* Wr, int64_t T, i
 }
 
 hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, int top_k, int E,
-                            int bm, const MoeRouteOut& o, hipStream_t s) {
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, s, ids, gate_w,
-                     T * (int64_t)top_k, top_k, E, bm, o);
+                            int bm, const MoeRouteOut& o, int32_t* counts, hipStream_t s) {
+  if (E < 1 || E > kMoeRouteMaxExperts || top_k < 1 || T < 0 || bm < 1) return hipErrorInvalidValue;
+  const int64_t P = T * (int64_t)top_k;
+  const int64_t G = (P + kRouteThreads - 1) / kRouteThreads;
+  if (P >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  if (G > 0) {
+    hipLaunchKernelGGL(moe_route_count_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, s, ids, P, E, counts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(moe_route_scan_kernel, dim3(1), dim3(kRouteScanThreads), 0, s, counts, (int)G, E, bm, o);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || G == 0) return e;
+  hipLaunchKernelGGL(moe_route_place_kernel, dim3((unsigned)G), dim3(kRouteThreads), 0, s, ids, gate_w, P, top_k, E,
+                     counts, o);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ hipError_t launch_small_mlp2(const uint16_t*, const uint16_t*, const uint16_t*, 
                              int, int64_t, int, int, int, uint16_t*, hipStream_t) {
   reached("launch_small_mlp2");
 }
-hipError_t launch_moe_route(const int32_t*, const float*, int64_t, int, int, int, const MoeRouteOut&,
+hipError_t launch_moe_route(const int32_t*, const float*, int64_t, int, int, int, const MoeRouteOut&, int32_t*,
                             hipStream_t) {
   reached("launch_moe_route");
 }

@@ -120,6 +120,71 @@ def test_moe_many_pairs_and_partial_expert_batch():
     assert_parity(y, _oracle(x, ok_ids, gw0, Wg, Wu, Wd), "moe many pairs")
 
 
+def _route_tables(ws, T, E, k):
+    """The route tables in an fmlp_moe_geglu workspace, at the offsets the
+    library lays them out: after the 8 KB header, tok_of, scale_of and pos_of
+    ([T*k] each), then group_off and tile_off ([E+1] each), every array
+    starting on a 256-byte boundary."""
+    P = T * k
+    ru = lambda n: -(-n // 256) * 256
+    o = 8192
+    out = {}
+    for name, n, dt in (("tok_of", P, torch.int32), ("scale_of", P, torch.float32), ("pos_of", P, torch.int32),
+                        ("group_off", E + 1, torch.int32), ("tile_off", E + 1, torch.int32)):
+        out[name] = ws[o:o + 4 * n].view(dt).cpu().numpy()
+        o += ru(4 * n)
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,case", [
+    (1, 1, 1, "random"), (257, 64, 3, "random"), (700, 8, 2, "skewed"), (5000, 6, 2, "invalid"),
+    (3000, 1000, 8, "random"), (4096, 8, 2, "workload"), (2048, 3, 1, "one expert"),
+])
+def test_moe_route_tables_exact(T, E, k, case):
+    """The bucketing itself, exactly: every valid (token, slot) pair p = t*k + j
+    sits in its expert's segment in pair order (a stable sort by expert), with
+    its token and gate weight; pos_of maps each pair to its row (-1 if its id
+    is invalid); group_off and tile_off are the prefix sums of the expert
+    sizes and of their 256-row tile counts.  Blocks of the routing kernels
+    hold 512 pairs, so these cases span one to 47 of them, partial last ones
+    and up to 1000 experts."""
+    rng = np.random.default_rng(T + E + k)
+    if case == "workload":
+        ids, gw = datagen.make_routes(T, E, k, seed=0)
+    else:
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        gw = rng.random((T, k)).astype(np.float32)
+    if case == "skewed":
+        ids = np.where(rng.random((T, k)) < 0.9, 5, 2).astype(np.int32)
+        ids[:3] = [[0, 7], [7, 7], [0, 0]]
+    if case == "invalid":
+        ids[0, 0], ids[2503, 1], ids[4999, 1], ids[1000, 0] = -1, E, 77, -5
+    if case == "one expert":
+        ids[:] = 1
+    D = H = 64
+    Wg, Wu, Wd = (np.zeros((E, H, D), np.uint16), np.zeros((E, H, D), np.uint16), np.zeros((E, D, H), np.uint16))
+    ws = F.workspace_for(DEV, F.fmlp_moe_workspace_size(T, D, H, E, k))
+    x = rand_bf16(rng, (T, D))
+    print(f"case moe route tables T={T} E={E} k={k} {case}", flush=True)
+    _run(x, ids, gw, Wg, Wu, Wd, ws)
+    got = _route_tables(ws, T, E, k)
+    flat, wflat = ids.reshape(-1), gw.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    vp = np.nonzero(valid)[0]
+    order = vp[np.argsort(flat[vp], kind="stable")]
+    n = len(order)
+    assert F.moe_invalid_ids(ws) == len(flat) - n
+    assert np.array_equal(got["tok_of"][:n], (order // k).astype(np.int32))
+    assert np.array_equal(got["scale_of"][:n].view(np.int32), wflat[order].view(np.int32))
+    pos = np.full(len(flat), -1, np.int32)
+    pos[order] = np.arange(n, dtype=np.int32)
+    assert np.array_equal(got["pos_of"], pos)
+    counts = np.bincount(flat[vp], minlength=E)
+    assert np.array_equal(got["group_off"], np.concatenate([[0], np.cumsum(counts)]).astype(np.int32))
+    tiles = -(-counts // 256)
+    assert np.array_equal(got["tile_off"], np.concatenate([[0], np.cumsum(tiles)]).astype(np.int32))
+
+
 def test_moe_determinism():
     rng = np.random.default_rng(4)
     T, D, H, E, k = 513, 256, 384, 8, 2
