@@ -207,7 +207,10 @@ __device__ __forceinline__ Seg seg_first(const Stream& st) {
   return q;
 }
 
-template <bool DUAL1, bool TWO, int MC, bool LL>
+// ACT: the activation of the first (or only) layer, fixed at compile time (a
+// runtime choice inlines every activation into the epilogue); a second layer
+// has none.
+template <bool DUAL1, bool TWO, int MC, bool LL, int ACT>
 __global__ void __launch_bounds__(kThreads)
 decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync, uint32_t salt) {
   static_assert(!LL || (TWO && MC == 1), "word-flag publish: two layers, one token");
@@ -524,7 +527,6 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync, uint32_t salt) 
   uint16_t* const y1 = in_sgpr(L1.y);
   uint16_t* const y2 = in_sgpr(L2.y);
   const int N1 = in_sgpr((int)L1.N), N2 = in_sgpr((int)L2.N);
-  const int act1 = in_sgpr(L1.act), act2 = in_sgpr(L2.act);
   // The bias of the next tile is requested one tile ahead, straight into LDS.
   auto ctrl_fetch_bias = [&](int bslot, const Seg& q) {
     const bool l2 = TWO && q.kind == SEG_L2;
@@ -541,7 +543,6 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync, uint32_t salt) 
     const bool l2 = TWO && q.kind == SEG_L2;
     const bool dual = DUAL1 && q.kind == SEG_L1;
     const int N = pick(l2, N2, N1);
-    const int act = pick(l2, act2, act1);
     uint16_t* const y = pick(l2, y2, y1);
     float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
     for (int v = 0; v < kWorkers; ++v) {
@@ -561,7 +562,7 @@ decode_kernel(GemvLayer L1, GemvLayer L2, int M, uint32_t* sync, uint32_t salt) 
       const float b[4] = {bf16_lo(bias.x), bf16_hi(bias.x), bf16_lo(bias.y), bf16_hi(bias.y)};
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        v[r] = dual ? apply_act(g[r], act) * u[r] : apply_act(g[r] + b[r], act);   // b = 0 without a bias
+        v[r] = dual ? act_of<ACT>(g[r]) * u[r] : (l2 ? g[r] + b[r] : act_of<ACT>(g[r] + b[r]));   // b = 0 without a bias
       const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
       if (LL && !l2) {    // h as two words {bf16 pair, epoch}: the data is its own flag
         const __amdgpu_buffer_rsrc_t rh = make_rsrc(y, (uint32_t)N * 4u);
@@ -711,7 +712,7 @@ Occ occ() {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return o;
     o.cus = prop.multiProcessorCount;
     const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                        &o.per_cu, reinterpret_cast<const void*>(&decode_kernel<true, true, 1, false>), kThreads,
+                        &o.per_cu, reinterpret_cast<const void*>(&decode_kernel<true, true, 1, false, ACT_GELU_TANH>), kThreads,
                         0) == hipSuccess;
     o.ok = ok && o.cus > 0 && o.per_cu > 0;
   }
@@ -752,18 +753,31 @@ namespace {
 // With `coop` the launch is cooperative (opt-in, fmlp_set_cooperative_decode):
 // the runtime refuses a grid that cannot be resident at once instead of
 // letting the barrier time out.
-template <bool DUAL1, bool TWO, int MC, bool LL>
-hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
-                          hipStream_t s, bool coop) {
+template <bool DUAL1, bool TWO, int MC, bool LL, int ACT>
+hipError_t launch_act(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
+                      hipStream_t s, bool coop) {
   uint32_t salt = TWO ? next_launch_salt() : 0u;
   if (coop) {
     GemvLayer a = L1, b = L2;
     void* args[] = {&a, &b, &M, &sync, &salt};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid),
-                                      dim3(kThreads), args, 0, s);
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&decode_kernel<DUAL1, TWO, MC, LL, ACT>),
+                                      dim3(grid), dim3(kThreads), args, 0, s);
   }
-  hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, MC, LL>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync, salt);
+  hipLaunchKernelGGL((decode_kernel<DUAL1, TWO, MC, LL, ACT>), dim3(grid), dim3(kThreads), 0, s, L1, L2, M, sync,
+                     salt);
   return hipGetLastError();
+}
+template <bool DUAL1, bool TWO, int MC, bool LL>
+hipError_t launch_variant(unsigned grid, const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
+                          hipStream_t s, bool coop) {
+  switch (L1.act) {
+    case ACT_NONE: return launch_act<DUAL1, TWO, MC, LL, ACT_NONE>(grid, L1, L2, M, sync, s, coop);
+    case ACT_GELU_ERF: return launch_act<DUAL1, TWO, MC, LL, ACT_GELU_ERF>(grid, L1, L2, M, sync, s, coop);
+    case ACT_GELU_TANH: return launch_act<DUAL1, TWO, MC, LL, ACT_GELU_TANH>(grid, L1, L2, M, sync, s, coop);
+    case ACT_RELU: return launch_act<DUAL1, TWO, MC, LL, ACT_RELU>(grid, L1, L2, M, sync, s, coop);
+    case ACT_SILU: return launch_act<DUAL1, TWO, MC, LL, ACT_SILU>(grid, L1, L2, M, sync, s, coop);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // activation-row class of M: the rows an LDS stage holds
@@ -796,7 +810,7 @@ hipError_t launch_gemv(const GemvLayer& L, int M, hipStream_t s) {
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M, uint32_t* sync,
                                    hipStream_t s, bool cooperative) {
   if (M <= 0) return hipSuccess;
-  if (M > 16) return hipErrorInvalidValue;
+  if (M > 16 || L2.act != ACT_NONE) return hipErrorInvalidValue;   // the second layer has no activation
   const Occ o = occ();
   if (!o.ok) return hipErrorInvalidDevice;
   const int64_t tiles1 = (L1.N + 15) / 16, tiles2 = (L2.N + 15) / 16;

@@ -118,6 +118,7 @@ static_assert(kDecodeMaxBlocks % 4 == 0, "flags are read 4 at a time");
 // Two dependent layers in ONE launch: every block is resident at once, layer-1
 // outputs are published through device-coherent stores and a flag barrier,
 // layer-2 weights stream across the barrier.  sync = the workspace header.
+// The second layer has no activation (L2.act must be ACT_NONE).
 hipError_t launch_gemv2_persistent(const GemvLayer& L1, const GemvLayer& L2, int M,
                                    uint32_t* sync, hipStream_t s, bool cooperative = false);
 
