@@ -55,12 +55,14 @@ def test_mlp2_w8(M, K, H, N):
     assert_parity(y, ref, f"mlp2_w8 {M}x{K}x{H}x{N}")
 
 
-@pytest.mark.parametrize("M,D,H", [(1, 8192, 28672), (16, 8192, 28672), (4, 1040, 2064), (16, 768, 3072),
-                                   (16, 4096, 1040), (9, 4096, 2048), (1, 768, 3072), (1, 4096, 1040)])
-@pytest.mark.parametrize("gate_act", ["gelu_tanh", "silu"])
+# the full-size shapes once, with the GeGLU gate; the others with both gates
+_GLU_W8_CASES = [(M, 8192, 28672, "gelu_tanh") for M in (1, 16)] + [
+    (M, D, H, act) for (M, D, H) in [(4, 1040, 2064), (16, 768, 3072), (16, 4096, 1040), (9, 4096, 2048),
+                                     (1, 768, 3072), (1, 4096, 1040)] for act in ("gelu_tanh", "silu")]
+
+
+@pytest.mark.parametrize("M,D,H,gate_act", _GLU_W8_CASES)
 def test_glu_w8(M, D, H, gate_act):
-    if (D, H) == (8192, 28672) and gate_act != "gelu_tanh":
-        pytest.skip("full-size case once, with the GeGLU gate")
     rng = np.random.default_rng(M * 3 + D + H)
     x = rand_bf16(rng, (M, D))
     qg, sg, qgd, sgd = _codes(rng, H, D, D ** -0.5)
