@@ -759,6 +759,9 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
                         ((OUT == GEMM_OUT_F32_SCALED && p.ksplit > 1) ? p.ksplit : 1);
   if (tiles <= 0) return hipSuccess;
   if (tiles > 0x7fffffff || p.cus <= 0) return hipErrorInvalidValue;
+  // A 32-k stage tile consumes its stages two at a time, so it needs an even
+  // stage count per tile; the parts of a split K range can be odd.
+  if (OUT == GEMM_OUT_F32_SCALED && BK < 64 && p.ksplit > 1) return hipErrorInvalidValue;
   // persistent: as many blocks as fit on the chip at once, each looping over
   // its tiles
   auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT, M32>;
