@@ -194,11 +194,21 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   // the first weight batch is in flight while the activations are staged
   w8_issue<DUAL, U, XB>(A, 0, wave, g, K, d0, d1, dx, wrow, xrow);
   if constexpr (XB > 0) {
-    const int per_row = K / 8;   // 16-byte pieces
-    for (int i = threadIdx.x; i < M * per_row; i += kW8Threads) {
-      const int m = i / per_row, c = i - m * per_row;
-      *reinterpret_cast<u32x4_t*>(xs + m * xstride + c * 16) = ld16(L.x + (int64_t)m * K + c * 8);
+    // Loads that write LDS, 1 KB of one activation row each (lanes past the
+    // row's end masked off), all in flight before the one wait: a load into
+    // registers and then LDS per 16-byte piece cost a round trip each (16 per
+    // thread at 16 tokens).
+    const int per_row = K / 8;                 // 16-byte pieces per row
+    const int ipr = (per_row + 63) / 64;       // load instructions per row
+    const i32x4_t xd = make_desc(reinterpret_cast<uint64_t>(L.x), (uint32_t)(M * K) * 2u);
+    const uint32_t xs_lds = lds_addr(xs);
+    for (int t = wave; t < M * ipr; t += kW8Waves) {   // wave-uniform
+      const int m = t / ipr, q = t - m * ipr;
+      const int c = q * 64 + lane;
+      if (c < per_row)
+        asm_load_lds(xd, uniform32(xs_lds + (uint32_t)(m * xstride + q * 1024)), (uint32_t)(m * K + c * 8) * 2u);
     }
+    wait_vm<0>();
     __syncthreads();
   }
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
