@@ -51,7 +51,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode.hip"],
     "gemm_bf16_kernel": ["common.h", "kernels.h", "lds_dma.h", "gemm.hip", "moe.hip"],
     "small_mlp2_kernel": ["common.h", "kernels.h", "small_mlp.hip"],
-    "moe_router_mfma_kernel": ["common.h", "kernels.h", "moe.hip"],
+    "moe_router_mfma_kernel": ["common.h", "kernels.h", "lds_dma.h", "moe.hip"],
     "decode_w8_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode_w8.h", "decode_w8.hip"],
     "decode_w8_two_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode_w8.h", "decode_w8.hip"],
     "glu_fused_kernel": ["common.h", "kernels.h", "lds_dma.h", "glu_fused.hip"],

@@ -29,6 +29,7 @@
 //            (E * D * 2 <= 64 KB), else read through the caches.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 namespace fmlp {
 
@@ -362,11 +363,21 @@ moe_router_lds_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict
                       float* __restrict__ logits) {
   __shared__ u32x4_t wlds[kRouterLdsBytes / 16];
   const int nch = D / 8;
-  for (int i = threadIdx.x; i < E * nch; i += kRouterLdsThreads)
-    wlds[i] = ld16(Wr + (int64_t)i * 8);
-  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  {
+    // Wr into LDS by loads that write LDS, 1 KB each (lanes past the end
+    // masked off), all in flight before one wait
+    const int nchunks = E * nch;
+    const i32x4_t wd = make_desc(reinterpret_cast<uint64_t>(Wr), (uint32_t)nchunks * 16u);
+    const uint32_t wl = lds_addr(&wlds[0]);
+    for (int j = wave; j < (nchunks + 63) / 64; j += kRouterLdsThreads / 64) {   // wave-uniform
+      const int c = 64 * j + lane;
+      if (c < nchunks) asm_load_lds(wd, uniform32(wl + 1024u * (uint32_t)j), (uint32_t)c * 16u);
+    }
+    wait_vm<0>();
+    __syncthreads();
+  }
   const int64_t t0 = ((int64_t)blockIdx.x * (kRouterLdsThreads / 64) + wave) * TW;
   if (t0 >= T) return;
   float acc[TW][EC];
