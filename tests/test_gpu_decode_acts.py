@@ -1,4 +1,4 @@
-"""The decode kernel (1-16 tokens) for every activation on every form, against
+"""The decode kernel (1-16 tokens) and the small MLP for every activation, against
 the fp64 oracle (oracle.linear, oracle.mlp2, oracle.glu): one layer, the
 two-layer MLP and the gated block in one launch, at 1, 3 and 16 tokens (the
 kernel's three activation-row classes).  The one-token two-layer shapes have
@@ -64,3 +64,21 @@ def test_decode_glu_acts(act, M):
         y = F.fmlp_glu(*(to_dev(a) for a in (x, Wg, Wu, Wd)), act)
     torch.cuda.synchronize()
     assert_parity(y, oracle.glu(*(f64_of_bits(a) for a in (x, Wg, Wu, Wd)), act), f"glu {act} M={M}")
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_small_mlp2_acts(act):
+    """The single-launch small MLP (K, H, N <= 128), also one kernel per
+    activation, with a ragged last block of token rows."""
+    rng = np.random.default_rng(17 + ACTS.index(act))
+    M, K, H, N = 100, 32, 72, 40
+    t = {"x": rand_bf16(rng, (M, K)), "W1": rand_bf16(rng, (H, K), K ** -0.5, "uniform"),
+         "b1": rand_bf16(rng, (H,), 0.3, "uniform"), "W2": rand_bf16(rng, (N, H), H ** -0.5, "uniform"),
+         "b2": rand_bf16(rng, (N,), 0.3, "uniform")}
+    print(f"case small mlp2 {act}", flush=True)
+    d = {k: to_dev(v) for k, v in t.items()}
+    with F.force_path("small"):
+        y = F.fmlp_mlp2(d["x"], d["W1"], d["b1"], d["W2"], d["b2"], act)
+    torch.cuda.synchronize()
+    ref = oracle.mlp2(*(f64_of_bits(t[k]) for k in ("x", "W1", "b1", "W2", "b2")), act)
+    assert_parity(y, ref, f"small mlp2 {act}")
