@@ -140,6 +140,7 @@ def _route_tables(ws, T, E, k):
     (1, 1, 1, "random"), (257, 64, 3, "random"), (700, 8, 2, "skewed"), (5000, 6, 2, "invalid"),
     (3000, 1000, 8, "random"), (4096, 8, 2, "workload"), (2048, 3, 1, "one expert"),
     (600, 1024, 2, "random"),   # the most experts a call takes
+    (65536, 16, 4, "random"),   # 512 blocks of pairs: the scan reads many batches of block counts
 ])
 def test_moe_route_tables_exact(T, E, k, case):
     """The bucketing itself, exactly: every valid (token, slot) pair p = t*k + j
@@ -147,7 +148,7 @@ def test_moe_route_tables_exact(T, E, k, case):
     its token and gate weight; pos_of maps each pair to its row (-1 if its id
     is invalid); group_off and tile_off are the prefix sums of the expert
     sizes and of their 256-row tile counts.  Blocks of the routing kernels
-    hold 512 pairs, so these cases span one to 47 of them, partial last ones
+    hold 512 pairs, so these cases span one to 512 of them, partial last ones
     and up to 1024 experts."""
     rng = np.random.default_rng(T + E + k)
     if case == "workload":
