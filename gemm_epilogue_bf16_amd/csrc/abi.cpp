@@ -514,8 +514,9 @@ fmlp_status fmlp_moe_route(const fmlp_bf16* x, const fmlp_bf16* Wr, int64_t T, i
        reinterpret_cast<uintptr_t>(logits)) & 3u)
     return fail(FMLP_E_ALIGN, "expert_ids, gate_w and logits must be 4-byte aligned");
   if (T == 0) return ok();
-  TRY(check_device());
-  return launched(launch_moe_router(x, Wr, T, (int)D, E, top_k, expert_ids, gate_w, logits,
+  int cus = 0;
+  TRY(check_device(&cus));
+  return launched(launch_moe_router(x, Wr, T, (int)D, E, top_k, expert_ids, gate_w, logits, cus,
                                     static_cast<hipStream_t>(stream)),
                   "moe router launch");
 }

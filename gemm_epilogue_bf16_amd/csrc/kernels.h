@@ -198,9 +198,10 @@ hipError_t launch_moe_route(const int32_t* ids, const float* gate_w, int64_t T, 
 hipError_t launch_moe_combine(const float* ytilde, const int32_t* pos_of, int64_t T, int top_k,
                               int64_t D, int ksplit, int64_t kstride, uint16_t* y, hipStream_t s);
 // Router: logits = x[T,D] . Wr[E,D]^T (fp32), top_k ids per token (ties to the
-// lower id) and softmax gate weights over them; logits may be nullptr.
+// lower id) and softmax gate weights over them; logits may be nullptr.  cus:
+// the device's compute units (picks the load batching of the <= 16-expert form).
 constexpr int kRouterMaxExperts = 64;
 hipError_t launch_moe_router(const uint16_t* x, const uint16_t* Wr, int64_t T, int D, int E, int top_k,
-                             int32_t* ids, float* gate_w, float* logits, hipStream_t s);
+                             int32_t* ids, float* gate_w, float* logits, int cus, hipStream_t s);
 
 }  // namespace fmlp

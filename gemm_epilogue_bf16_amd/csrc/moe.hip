@@ -296,8 +296,13 @@ moe_router_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ W
 // with the router weights as the row operand (experts past E read as zero)
 // and 16 tokens as the column operand.  Wave w takes the 32-k steps w, w + 8,
 // ...; the 8 partial tiles go through LDS and wave 0 sums them in wave order.
+// U k steps of a wave have their loads in flight together: 16 when the grid
+// has at most one block per CU (about 200 VGPRs, so one 8-wave block fits a
+// CU), 8 otherwise (about 100 VGPRs, two blocks per CU).  U changes only how
+// many loads are issued before the MFMAs, not the order of the sums.
 constexpr int kRouterMfmaWaves = 8;
 
+template <int U>
 __global__ void __launch_bounds__(kRouterMfmaWaves * 64)
 moe_router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ Wr, int64_t T, int D, int E,
                        int top_k, int32_t* __restrict__ ids, float* __restrict__ gate_w,
@@ -314,7 +319,6 @@ moe_router_mfma_kernel(const uint16_t* __restrict__ x, const uint16_t* __restric
   const uint16_t* xrow = x + (col_ok ? t0 + li : 0) * (int64_t)D;
   const int steps = (D + 31) / 32;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 16;                    // k steps whose loads are in flight together
   for (int s0 = wave; s0 < steps; s0 += kRouterMfmaWaves * U) {
     u32x4_t a[U], b[U];
 #pragma unroll
@@ -455,15 +459,19 @@ hipError_t launch_router_cfg(const uint16_t* x, const uint16_t* Wr, int64_t T, i
 }  // namespace
 
 hipError_t launch_moe_router(const uint16_t* x, const uint16_t* Wr, int64_t T, int D, int E, int top_k,
-                             int32_t* ids, float* gate_w, float* logits, hipStream_t s) {
+                             int32_t* ids, float* gate_w, float* logits, int cus, hipStream_t s) {
   if (E < 1 || E > kRouterMaxExperts || top_k < 1 || top_k > 8 || top_k > E || D % 8 != 0)
     return hipErrorInvalidValue;
   if (E <= 16) {
     const int64_t blocks = (T + 15) / 16;
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(moe_router_mfma_kernel, dim3((unsigned)blocks), dim3(kRouterMfmaWaves * 64), 0, s, x, Wr, T,
-                       D, E, top_k, ids, gate_w, logits);
+    if (blocks <= cus)
+      hipLaunchKernelGGL(moe_router_mfma_kernel<16>, dim3((unsigned)blocks), dim3(kRouterMfmaWaves * 64), 0, s, x,
+                         Wr, T, D, E, top_k, ids, gate_w, logits);
+    else
+      hipLaunchKernelGGL(moe_router_mfma_kernel<8>, dim3((unsigned)blocks), dim3(kRouterMfmaWaves * 64), 0, s, x,
+                         Wr, T, D, E, top_k, ids, gate_w, logits);
     return hipGetLastError();
   }
   if ((int64_t)E * D * 2 <= kRouterLdsBytes) {

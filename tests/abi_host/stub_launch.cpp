@@ -35,7 +35,7 @@ hipError_t launch_moe_combine(const float*, const int32_t*, int64_t, int, int64_
                               hipStream_t) {
   reached("launch_moe_combine");
 }
-hipError_t launch_moe_router(const uint16_t*, const uint16_t*, int64_t, int, int, int, int32_t*, float*, float*,
+hipError_t launch_moe_router(const uint16_t*, const uint16_t*, int64_t, int, int, int, int32_t*, float*, float*, int,
                              hipStream_t) {
   reached("launch_moe_router");
 }
