@@ -45,8 +45,9 @@ def _check(x, Wr, k, what):
     # up to 16 experts on the matrix cores (k tails: D not a multiple of 32);
     # past 16 with the router weights past 64 KB: read through the caches
     (33, 8192, 8, 2), (200, 4104, 16, 2), (17, 40, 16, 8), (70, 1536, 32, 3), (50, 2048, 64, 4),
-    # more 16-token tiles than CUs
-    (4200, 264, 8, 2), (5000, 4104, 16, 3),
+    # more 16-token tiles than CUs (the 8-step load batches, two blocks per CU),
+    # the last at the workload's width with twice its tokens
+    (4200, 264, 8, 2), (5000, 4104, 16, 3), (8192, 4096, 8, 2),
 ])
 def test_router_random(T, D, E, k):
     rng = np.random.default_rng(T + D + E + k)
