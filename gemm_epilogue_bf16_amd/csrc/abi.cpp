@@ -567,6 +567,45 @@ hipError_t gemm_wgrad(const uint16_t* A, const uint16_t* B, int64_t R, int64_t T
   return launch_sum_parts(parts, P, R * Cc, R * Cc, C, s);
 }
 
+// k-major operands (no transpose copies; the GEMM reads row-major [K, ld]
+// operands with transposing LDS reads).  Only the 256x256 tile has this form,
+// so a GEMM that would run on smaller tiles keeps the transposes.
+bool kmajor_fits(int64_t rows, int64_t ld) { return rows * ld * 2 < (int64_t(1) << 31); }
+// C[M, N] = A[M, K] . B[K, N] with B row-major [K, ldb]; with kb_split > 0
+// (a multiple of 64) rows [0, kb_split) of B are B0's and the rest B1's.
+bool gemm_bkmajor_ok(int64_t M, int64_t N, int64_t K, int64_t kb_split, int cus) {
+  const int64_t rows = kb_split > 0 ? std::max(kb_split, K - kb_split) : K;
+  return choose_tile_linear(M, N, cus) == TILE_256x256 && kmajor_fits(rows, N) && kb_split % 64 == 0;
+}
+hipError_t gemm_bkmajor(const uint16_t* A, const uint16_t* B0, const uint16_t* B1, int64_t kb_split, int64_t M,
+                        int64_t N, int64_t K, uint16_t* C, int cus, hipStream_t s) {
+  GemmParams p = dense_params(A, K, B0, B1, nullptr, C, N, M, N, K, FMLP_ACT_NONE, cus);
+  p.kmajor = 2;
+  p.ldb = N;
+  p.kb_split = kb_split;
+  return launch_gemm(GEMM_OUT_BF16, false, false, TILE_256x256, p, s);
+}
+// C[R, Cc] = A^T B over T token rows, A row-major [T, lda] (columns 0 .. R-1),
+// B row-major [T, ldb] (columns 0 .. Cc-1): a weight gradient without copies
+bool wgrad_kmajor_ok(int64_t R, int64_t T, int64_t Cc, int64_t lda, int64_t ldb, int cus) {
+  const bool tile_ok = wgrad_split(R, T, Cc) > 1 || choose_tile_linear(R, Cc, cus) == TILE_256x256;
+  return tile_ok && kmajor_fits(T, lda) && kmajor_fits(T, ldb);
+}
+hipError_t gemm_wgrad_kmajor(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t R, int64_t T,
+                             int64_t Cc, uint16_t* C, float* parts, int cus, hipStream_t s) {
+  const int P = wgrad_split(R, T, Cc);
+  GemmParams p = dense_params(A, lda, B, nullptr, nullptr, P > 1 ? static_cast<void*>(parts) : C, Cc, R, Cc, T,
+                              FMLP_ACT_NONE, cus);
+  p.kmajor = 3;
+  p.ldb = ldb;
+  if (P == 1) return launch_gemm(GEMM_OUT_BF16, false, false, TILE_256x256, p, s);
+  p.ksplit = P;
+  p.c_kstride = R * Cc;
+  const hipError_t e = launch_gemm(GEMM_OUT_F32_SCALED, false, false, TILE_256x256, p, s);
+  if (e != hipSuccess) return e;
+  return launch_sum_parts(parts, P, R * Cc, R * Cc, C, s);
+}
+
 struct LinearBwdLayout {
   size_t dz, wt, dzt, xt, parts, total;
 };
@@ -715,9 +754,14 @@ fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf1
   char* ws = static_cast<char*>(workspace);
   auto at = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
   const int64_t Mp = pad8(M);
-  // dm = dy Wd (contraction over Wd's rows: Wd read transposed)
-  HIP_TRY(launch_transpose(Wd, D, H, H, at(L.wdt), D, D, s), "glu_bwd transpose Wd");
-  HIP_TRY(gemm_linear(dy, at(L.wdt), nullptr, FMLP_ACT_NONE, M, D, H, at(L.dm), cus, s), "glu_bwd dm launch");
+  // dm = dy Wd: the contraction runs over Wd's rows (Wd read k-major, or
+  // transposed first where the GEMM runs on smaller tiles)
+  if (gemm_bkmajor_ok(M, H, D, 0, cus)) {
+    HIP_TRY(gemm_bkmajor(dy, Wd, nullptr, 0, M, H, D, at(L.dm), cus, s), "glu_bwd dm launch");
+  } else {
+    HIP_TRY(launch_transpose(Wd, D, H, H, at(L.wdt), D, D, s), "glu_bwd transpose Wd");
+    HIP_TRY(gemm_linear(dy, at(L.wdt), nullptr, FMLP_ACT_NONE, M, D, H, at(L.dm), cus, s), "glu_bwd dm launch");
+  }
   // the gate+up GEMM again, with the derivative epilogue: m, and [dg | du]
   GemmParams p = dense_params(x, D, Wg, Wu, nullptr, at(L.m), H, M, H, D, gate_act, cus);
   p.E = at(L.dm);
@@ -726,19 +770,35 @@ fmlp_status fmlp_glu_bwd(const fmlp_bf16* x, const fmlp_bf16* Wg, const fmlp_bf1
   p.ldc2 = 2 * H;
   HIP_TRY(launch_gemm(GEMM_OUT_DGLU, false, false, choose_tile(M, (H + 127) / 128, cus), p, s),
           "glu_bwd gate+up launch");
-  // dx = dg Wg + du Wu = [dg | du] [Wg ; Wu]: one GEMM over 2H
-  HIP_TRY(launch_transpose(Wg, H, D, D, at(L.wgut), 2 * H, H, s), "glu_bwd transpose Wg");
-  HIP_TRY(launch_transpose(Wu, H, D, D, at(L.wgut) + H, 2 * H, H, s), "glu_bwd transpose Wu");
-  HIP_TRY(gemm_linear(at(L.dgdu), at(L.wgut), nullptr, FMLP_ACT_NONE, M, 2 * H, D, dx, cus, s), "glu_bwd dx launch");
-  // weight gradients: contractions over the token rows
-  HIP_TRY(launch_transpose(dy, M, D, D, at(L.dyt), Mp, Mp, s), "glu_bwd transpose dy");
-  HIP_TRY(launch_transpose(at(L.m), M, H, H, at(L.mt), Mp, Mp, s), "glu_bwd transpose m");
-  HIP_TRY(launch_transpose(at(L.dgdu), M, 2 * H, 2 * H, at(L.dgdut), Mp, Mp, s), "glu_bwd transpose dg|du");
-  HIP_TRY(launch_transpose(x, M, D, D, at(L.xt), Mp, Mp, s), "glu_bwd transpose x");
+  // dx = dg Wg + du Wu = [dg | du] [Wg ; Wu]: one GEMM over 2H (the weights
+  // read k-major, B switching from Wg to Wu at row H, or transposed first)
+  if (H % 64 == 0 && gemm_bkmajor_ok(M, D, 2 * H, H, cus)) {
+    HIP_TRY(gemm_bkmajor(at(L.dgdu), Wg, Wu, H, M, D, 2 * H, dx, cus, s), "glu_bwd dx launch");
+  } else {
+    HIP_TRY(launch_transpose(Wg, H, D, D, at(L.wgut), 2 * H, H, s), "glu_bwd transpose Wg");
+    HIP_TRY(launch_transpose(Wu, H, D, D, at(L.wgut) + H, 2 * H, H, s), "glu_bwd transpose Wu");
+    HIP_TRY(gemm_linear(at(L.dgdu), at(L.wgut), nullptr, FMLP_ACT_NONE, M, 2 * H, D, dx, cus, s),
+            "glu_bwd dx launch");
+  }
+  // weight gradients: contractions over the token rows (both operands read
+  // k-major, or transposed first)
   float* parts = reinterpret_cast<float*>(ws + L.parts);
-  HIP_TRY(gemm_wgrad(at(L.dyt), at(L.mt), D, Mp, H, dWd, parts, cus, s), "glu_bwd dWd launch");
-  HIP_TRY(gemm_wgrad(at(L.dgdut), at(L.xt), H, Mp, D, dWg, parts, cus, s), "glu_bwd dWg launch");
-  HIP_TRY(gemm_wgrad(at(L.dgdut) + H * Mp, at(L.xt), H, Mp, D, dWu, parts, cus, s), "glu_bwd dWu launch");
+  if (wgrad_kmajor_ok(D, M, H, D, H, cus)) {
+    HIP_TRY(gemm_wgrad_kmajor(dy, D, at(L.m), H, D, M, H, dWd, parts, cus, s), "glu_bwd dWd launch");
+  } else {
+    HIP_TRY(launch_transpose(dy, M, D, D, at(L.dyt), Mp, Mp, s), "glu_bwd transpose dy");
+    HIP_TRY(launch_transpose(at(L.m), M, H, H, at(L.mt), Mp, Mp, s), "glu_bwd transpose m");
+    HIP_TRY(gemm_wgrad(at(L.dyt), at(L.mt), D, Mp, H, dWd, parts, cus, s), "glu_bwd dWd launch");
+  }
+  if (wgrad_kmajor_ok(H, M, D, 2 * H, D, cus)) {
+    HIP_TRY(gemm_wgrad_kmajor(at(L.dgdu), 2 * H, x, D, H, M, D, dWg, parts, cus, s), "glu_bwd dWg launch");
+    HIP_TRY(gemm_wgrad_kmajor(at(L.dgdu) + H, 2 * H, x, D, H, M, D, dWu, parts, cus, s), "glu_bwd dWu launch");
+  } else {
+    HIP_TRY(launch_transpose(at(L.dgdu), M, 2 * H, 2 * H, at(L.dgdut), Mp, Mp, s), "glu_bwd transpose dg|du");
+    HIP_TRY(launch_transpose(x, M, D, D, at(L.xt), Mp, Mp, s), "glu_bwd transpose x");
+    HIP_TRY(gemm_wgrad(at(L.dgdut), at(L.xt), H, Mp, D, dWg, parts, cus, s), "glu_bwd dWg launch");
+    HIP_TRY(gemm_wgrad(at(L.dgdut) + H * Mp, at(L.xt), H, Mp, D, dWu, parts, cus, s), "glu_bwd dWu launch");
+  }
   return ok();
 }
 

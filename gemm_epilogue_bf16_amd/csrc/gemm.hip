@@ -154,6 +154,34 @@ constexpr bool m32_reads_conflict_free(bool weights) {
 static_assert(m32_reads_conflict_free<8>(false) && m32_reads_conflict_free<8>(true),
               "32-row fragment reads of 128-byte rows");
 
+// k-major operand tiles (the backward's contractions over the rows of both
+// operands, read without a transpose copy).  A stage holds 64 k-rows of the
+// tile's 256 columns: rows of 512 bytes, 32 chunks of 16 B, chunk c of row k
+// at slot c ^ kswz(k).  A fragment (16 columns x 32 k) is two transposing
+// reads (ds_read_b64_tr_b16): within each 16-lane group, lane 4 r + q points
+// at 4 consecutive columns of k-row kbase + r, and lane j gets column group
+// j / 4, element j % 4 of all four rows, i.e. 4 consecutive k of one column;
+// kbase = 32 ks + 8 (lane / 16) and + 4 give a lane the 8 consecutive k of the
+// 16x16x32 operand, in the order the row-major reads give them.  kswz moves
+// chunk bits 1-3: the 8 k-rows of a half-wave's read land on 8 distinct chunk
+// pairs (an activation fragment's 16 columns are one chunk pair per row).  A
+// weight fragment's 16 columns are 4 half chunks (the column permutation that
+// gives each lane runs of 8 output columns), all in the same half, so its
+// reads take two passes.
+__host__ __device__ constexpr int kswz(int k) { return 2 * ((k & 7) ^ (((k >> 3) & 1) << 2)); }
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t lds_read_tr_pair(uint32_t addr0, uint32_t addr1) {
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4;
+  const v4i16_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(uintptr_t)addr0);
+  const v4i16_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4*)(uintptr_t)addr1);
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 0, 1));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 2, 3));
+  return r;
+}
+
 // The main loop interleaves MFMAs with loads and LDS reads in a fixed order.
 // Instruction selection moves an MFMA builtin freely (it touches no memory),
 // so the loop issues them as volatile asm, which keeps its place among the
@@ -198,8 +226,9 @@ __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 7\
 // M32: the wave tile runs on v_mfma_f32_32x32x16_bf16 (32x32 fragments, 16 k
 // per MFMA) instead of v_mfma_f32_16x16x32_bf16: half the MFMA instructions
 // and half the operand register reads per flop, the same LDS bytes.
+// KM: bit 0 A, bit 1 B stored k-major (GemmParams::kmajor).
 template <int BM, int BN, int WAVES_M, int WAVES_N, int BK, int R, int OUT, bool GATHER, bool GROUPED,
-          int GACT = ACT_NONE, bool M32 = false>
+          int GACT = ACT_NONE, bool M32 = false, int KM = 0>
 __global__ void __launch_bounds__(WAVES_M * WAVES_N * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N;
@@ -229,6 +258,10 @@ gemm_bf16_kernel(GemmParams p) {
   static_assert(!DUAL || HALF >= 1, "gate and up fragments");
   static_assert(KS == 1 || KS % 2 == 0, "k-steps per stage");
   static_assert(R >= 2 && LOADS * (R - 2) < 64, "ring depth");
+  constexpr bool KMA = (KM & 1) != 0, KMB = (KM & 2) != 0;
+  static_assert(KM == 0 || (!DUAL && !GATHER && !GROUPED && !M32 && BM == 256 && BN == 256 && BK == 64 &&
+                            WAVES_M == 2 && WAVES_N == 4),
+                "k-major operands: 256x256 tiles of 8 waves, 16x16x32 MFMAs, one weight set");
 
   __shared__ u32x4_t ring[R * SLOT];
 
@@ -319,15 +352,39 @@ gemm_bf16_kernel(GemmParams p) {
   // offsets of the lane's load 0 within a tile (load i adds a constant number of rows)
   const uint32_t a_lane = (uint32_t)ra * lda2 + (uint32_t)a_k * 2u;
   const uint32_t b_lane = (uint32_t)ra * K2 + (uint32_t)b_k * 2u;
+  // k-major: load i of this wave fills k-rows 16 i + 2 wave + lane / 32 of
+  // the stage (2 rows of 512 B per instruction), the lane's slot lane % 32 of
+  // its row holding chunk slot ^ kswz(row) (kswz reads row bits 0-3, the same
+  // for every i)
+  const int kr0 = 2 * wave + (lane >> 5);
+  const uint32_t km_chunk = (uint32_t)(((lane & 31) ^ kswz(kr0)) * 16);
+  const uint32_t ldb2 = (uint32_t)(KMB ? p.ldb : 0) * 2u;
+  const uint32_t a_lane_km = (uint32_t)kr0 * lda2 + km_chunk;
+  const uint32_t b_lane_km = (uint32_t)kr0 * ldb2 + km_chunk;
   i32x4_t da, db0, db1;
   uint32_t a_gat[GATHER ? A_INS : 1];   // gather: the lane's source-row offsets in this tile
   auto issue_tile = [&](const Tile& t) {
     const int a_rows_here = (int)(t.row_end - t.row_begin);
-    da = GATHER ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
-                : make_desc(reinterpret_cast<uint64_t>(p.A + t.row_begin * p.lda), (uint32_t)a_rows_here * lda2);
+    // k-major descriptors end at the operand's last element ((K - 1) ld +
+    // width): columns past the width read the next row's (in the operand, and
+    // only into accumulators that are never stored), past the last row zeros
+    if constexpr (KMA)   // the tile's rows are columns row_begin .. of A [K, lda], p.M wide
+      da = make_desc(reinterpret_cast<uint64_t>(p.A + t.row_begin),
+                     (uint32_t)((((int64_t)Kc - 1) * p.lda + p.M - t.row_begin) * 2));
+    else
+      da = GATHER ? make_desc(reinterpret_cast<uint64_t>(p.A), (uint32_t)(p.a_src_rows * p.lda * 2))
+                  : make_desc(reinterpret_cast<uint64_t>(p.A + t.row_begin * p.lda), (uint32_t)a_rows_here * lda2);
     const int n_here = (int)min((int64_t)OUT_N, N - t.n0);   // weight rows of each set in this tile
-    db0 = make_desc(reinterpret_cast<uint64_t>(t.b0 + t.n0 * K), (uint32_t)n_here * K2);
-    db1 = DUAL ? make_desc(reinterpret_cast<uint64_t>(t.b1 + t.n0 * K), (uint32_t)n_here * K2) : db0;
+    if constexpr (KMB) {   // the tile's columns are columns n0 .. of B0 [K0, ldb] (and B1 [K - K0, ldb]), N wide
+      const int64_t k0rows = p.kb_split > 0 ? p.kb_split : (int64_t)Kc;
+      db0 = make_desc(reinterpret_cast<uint64_t>(t.b0 + t.n0), (uint32_t)(((k0rows - 1) * p.ldb + N - t.n0) * 2));
+      db1 = p.kb_split > 0 ? make_desc(reinterpret_cast<uint64_t>(t.b1 + t.n0),
+                                       (uint32_t)((((int64_t)Kc - p.kb_split - 1) * p.ldb + N - t.n0) * 2))
+                           : db0;
+    } else {
+      db0 = make_desc(reinterpret_cast<uint64_t>(t.b0 + t.n0 * K), (uint32_t)n_here * K2);
+      db1 = DUAL ? make_desc(reinterpret_cast<uint64_t>(t.b1 + t.n0 * K), (uint32_t)n_here * K2) : db0;
+    }
     if constexpr (GATHER) {
       const int rt = RPI * wave + opaque(lane) / CH;
       const int ak = 8 * ((opaque(lane) % CH) ^ swz_a<CH>(rt));
@@ -369,7 +426,11 @@ gemm_bf16_kernel(GemmParams p) {
   int iss_t = 0, iss_s = 0;   // tile and stage within the tile of the next stage issued
   struct StageIssue {
     bool a_in, b_in;
-    uint32_t kb;
+    uint32_t kb;      // soffset of the stage's k range: row-major operands
+    uint32_t kb_a;    // A's (its rows past a k-major stage's first)
+    uint32_t kb_b;    // B's
+    int k0;           // the stage's first k (K when past the end)
+    bool b1;          // k-major B: the stage's rows come from B1
   };
   auto stage_begin = [&]() -> StageIssue {
     const bool live = iss_t < nmine;   // block-uniform
@@ -381,7 +442,11 @@ gemm_bf16_kernel(GemmParams p) {
     }
     const int ks0 = __builtin_amdgcn_readfirstlane(live ? (SPLITK ? part_first(iss_kp) : 0) + iss_s : 0);   // stage index within K
     const int k0 = live ? ks0 * BK : Kc;
-    const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, (uint32_t)ks0 * (BK * 2)};
+    const uint32_t kb = (uint32_t)ks0 * (BK * 2);
+    const bool b1 = KMB && p.kb_split > 0 && k0 >= p.kb_split;   // block-uniform
+    const StageIssue st{k0 + a_k < Kc, k0 + b_k < Kc, kb,
+                        KMA ? (uint32_t)(ks0 * BK) * lda2 : kb,
+                        KMB ? (uint32_t)(ks0 * BK - (b1 ? (int)p.kb_split : 0)) * ldb2 : kb, k0, b1};
     if (++iss_s == iss_ns) {
       iss_s = 0;
       ++iss_t;
@@ -391,14 +456,25 @@ gemm_bf16_kernel(GemmParams p) {
   // load i (of LOADS) of a stage into the slot at LDS byte address `base`
   auto dma = [&](int i, uint32_t base, const StageIssue& st) {
     if (i < A_INS) {
-      const uint32_t off = GATHER ? a_gat[GATHER ? i : 0] : a_lane + (uint32_t)(RPI * i * NW) * lda2;
-      asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, st.a_in ? off : kOutOfRange, st.kb);
+      if constexpr (KMA) {   // k-rows past K load zeros
+        const uint32_t off = a_lane_km + (uint32_t)(16 * i) * lda2;
+        asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, st.k0 + kr0 + 16 * i < Kc ? off : kOutOfRange, st.kb_a);
+      } else {
+        const uint32_t off = GATHER ? a_gat[GATHER ? i : 0] : a_lane + (uint32_t)(RPI * i * NW) * lda2;
+        asm_load_lds(da, base + (uint32_t)(i * NW) * 1024u, st.a_in ? off : kOutOfRange, st.kb_a);
+      }
     } else {
       const int b = i - A_INS;
-      const bool up = DUAL && RPI * (b * NW) >= BN / 2;   // compile-time per i
-      const uint32_t off = b_lane + (uint32_t)((RPI * b * NW) % (DUAL ? BN / 2 : BN)) * K2;
-      asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024),
-                   st.b_in ? off : kOutOfRange, st.kb);
+      if constexpr (KMB) {
+        const uint32_t off = b_lane_km + (uint32_t)(16 * b) * ldb2;
+        asm_load_lds(st.b1 ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024),
+                     st.k0 + kr0 + 16 * b < Kc ? off : kOutOfRange, st.kb_b);
+      } else {
+        const bool up = DUAL && RPI * (b * NW) >= BN / 2;   // compile-time per i
+        const uint32_t off = b_lane + (uint32_t)((RPI * b * NW) % (DUAL ? BN / 2 : BN)) * K2;
+        asm_load_lds(up ? db1 : db0, base + (uint32_t)(BM * CH * 16 + b * NW * 1024),
+                     st.b_in ? off : kOutOfRange, st.kb_b);
+      }
     }
   };
   auto issue_all = [&](int slot) {
@@ -441,14 +517,47 @@ gemm_bf16_kernel(GemmParams p) {
   // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order its MFMAs consume them.
   constexpr int NREADS = FM + FN;
   u32x4_t xf[2][FM], wf[2][FN];
+  // k-major: per k-step and half (k-rows kbase and kbase + 4) the lane's
+  // byte offset in the operand's region for fragment 0; fragment f XORs chunk
+  // bits the lane's own part leaves zero (activation: 2 f; weight: 4 (f / 2),
+  // plus the half chunk f % 2)
+  uint32_t km_x[KM ? KS : 1][2], km_w[KM ? KS : 1][2];
+  if constexpr (KM != 0) {
+    const int kq = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = ks * 32 + 8 * kq + (s16 >> 2) + 4 * h;
+        km_x[ks][h] = (uint32_t)(row * 512 + (((wm * 16 + ((s16 & 3) >> 1)) ^ kswz(row)) << 4) + ((s16 & 1) << 3));
+        km_w[ks][h] = (uint32_t)(BM * CH * 16 + row * 512 + (((wn * 8 + (s16 & 3)) ^ kswz(row)) << 4));
+      }
+  }
+  auto frag_x = [&](const u32x4_t* sl, int ks, int f) -> u32x4_t {
+    if constexpr (KMA) {
+      const uint32_t b = lds_addr(sl);
+      return lds_read_tr_pair(b + (km_x[ks][0] ^ (uint32_t)(32 * f)), b + (km_x[ks][1] ^ (uint32_t)(32 * f)));
+    } else {
+      return sl[x_idx[ks] + f * MR * CH];
+    }
+  };
+  auto frag_w = [&](const u32x4_t* sl, int ks, int f) -> u32x4_t {
+    if constexpr (KMB) {
+      const uint32_t b = lds_addr(sl) + (uint32_t)(8 * (f & 1));
+      return lds_read_tr_pair(b + (km_w[ks][0] ^ (uint32_t)(64 * (f >> 1))),
+                              b + (km_w[ks][1] ^ (uint32_t)(64 * (f >> 1))));
+    } else {
+      return sl[w_idx[ks] + w_delta(f, FN, BN, DUAL, M32) * CH];
+    }
+  };
   auto frag_read = [&](int n, const u32x4_t* sl, int ks, auto set_c) {
     constexpr int set = decltype(set_c)::value;
     if (n == 0) {
-      xf[set][0] = sl[x_idx[ks]];
+      xf[set][0] = frag_x(sl, ks, 0);
     } else if (n <= FN) {
-      wf[set][n - 1] = sl[w_idx[ks] + w_delta(n - 1, FN, BN, DUAL, M32) * CH];
+      wf[set][n - 1] = frag_w(sl, ks, n - 1);
     } else {
-      xf[set][n - FN] = sl[x_idx[ks] + (n - FN) * MR * CH];
+      xf[set][n - FN] = frag_x(sl, ks, n - FN);
     }
   };
   auto mfma_t = [&](int t, auto set_c) {   // MFMA t of a k-step: row t / FN, column t % FN
@@ -749,7 +858,7 @@ gemm_bf16_kernel(GemmParams p) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int R, int OUT, bool GATHER, bool GROUPED, int GACT,
-          bool M32 = false>
+          bool M32 = false, int KM = 0>
 hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   constexpr int OUT_N = (OUT == GEMM_OUT_GEGLU || OUT == GEMM_OUT_DGLU) ? BN / 2 : BN;
   if (!GROUPED) p.tiles_m = (int)((p.M + BM - 1) / BM);
@@ -762,9 +871,21 @@ hipError_t launch_cfg(GemmParams p, hipStream_t s) {
   // A 32-k stage tile consumes its stages two at a time, so it needs an even
   // stage count per tile; the parts of a split K range can be odd.
   if (OUT == GEMM_OUT_F32_SCALED && BK < 64 && p.ksplit > 1) return hipErrorInvalidValue;
+  if (KM != p.kmajor) return hipErrorInvalidValue;
+  if constexpr (KM != 0) {   // the byte spans of k-major operands fit the 31-bit offsets
+    if ((KM & 1) && p.K * p.lda * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    if (KM & 2) {
+      if (p.kb_split < 0 || p.kb_split >= p.K || p.kb_split % BK != 0) return hipErrorInvalidValue;
+      if (p.kb_split > 0 && p.B1 == nullptr) return hipErrorInvalidValue;
+      const int64_t rows = p.kb_split > 0 ? std::max(p.kb_split, p.K - p.kb_split) : p.K;
+      if (rows * p.ldb * 2 >= (int64_t(1) << 31) || p.ldb < p.N) return hipErrorInvalidValue;
+    }
+  } else if (p.kb_split != 0) {
+    return hipErrorInvalidValue;
+  }
   // persistent: as many blocks as fit on the chip at once, each looping over
   // its tiles
-  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT, M32>;
+  auto kernel = gemm_bf16_kernel<BM, BN, WM, WN, BK, R, OUT, GATHER, GROUPED, GACT, M32, KM>;
   static const int per_cu = [&] {
     int o = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kernel, WM * WN * 64, 0) != hipSuccess) o = 1;
@@ -798,6 +919,19 @@ hipError_t launch_tile(int tile, const GemmParams& p, hipStream_t s) {
       case ACT_NONE: break;
       default: return hipErrorInvalidValue;
     }
+  }
+  if constexpr ((OUT == GEMM_OUT_BF16 || OUT == GEMM_OUT_F32_SCALED) && !GATHER && !GROUPED) {
+    if (p.kmajor != 0) {   // k-major operands: 256x256 tiles only
+      if (tile != TILE_256x256) return hipErrorInvalidValue;
+      switch (p.kmajor) {
+        case 1: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, false, false, GACT, false, 1>(p, s);
+        case 2: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, false, false, GACT, false, 2>(p, s);
+        case 3: return launch_cfg<256, 256, 2, 4, 64, 2, OUT, false, false, GACT, false, 3>(p, s);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  } else {
+    if (p.kmajor != 0) return hipErrorInvalidValue;
   }
   switch (tile) {
     case TILE_128x128: return launch_cfg<128, 128, 2, 2, 32, 4, OUT, GATHER, GROUPED, GACT>(p, s);

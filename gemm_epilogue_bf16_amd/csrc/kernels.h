@@ -44,6 +44,15 @@ struct GemmParams {
   int64_t lde;               //   (bf16, row stride lde)
   void* C2;                  // GEMM_OUT_DGLU: dg | du output, bf16, row stride ldc2
   int64_t ldc2;
+  // k-major operands (the backward's contractions over rows, read without a
+  // transpose copy; 256x256 tiles, plain bf16 or split fp32 output only):
+  // bit 0: A is stored [K, lda] (the tile's rows are columns of A); bit 1: B is
+  // stored [K, ldb] (the tile's columns are columns of B).  kb_split > 0 (a
+  // multiple of 64, B k-major): k rows [0, kb_split) come from B0 and
+  // [kb_split, K) from B1, both with row stride ldb.
+  int kmajor;
+  int64_t ldb;
+  int64_t kb_split;
   int cus;                   // compute units: the persistent grid's size cap
   // launch geometry, filled by launch_gemm
   int tiles_m, tiles_n, group_m;

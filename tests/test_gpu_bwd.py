@@ -145,6 +145,28 @@ def test_glu_bwd_large_sampled():
         assert torch.isfinite(g.float()).all()
 
 
+def test_glu_bwd_kmajor_ragged_sampled():
+    """A shape whose backward GEMMs all read their row-contracted operands
+    k-major (256x256 tiles fill the chip): dm over Wd's rows, dx over [Wg; Wu]
+    with the weights switching at row H, and the three weight gradients over
+    the tokens (split in 3 parts).  Ragged everywhere: 8200 tokens (a partial
+    last 64-row stage), and widths that are not multiples of a tile.  Sampled
+    as the large workload's backward: token rows of dx over all columns, whole
+    rows of dWg, dWu and whole columns of dWd."""
+    M, D, H = 8200, 2056, 2112
+    x, Wg, Wu, Wd, dy = _glu_case(29, M, D, H, "gelu_tanh")
+    print(f"case glu_bwd k-major M={M} D={D} H={H}", flush=True)
+    dx, dWg, dWu, dWd = F.fmlp_glu_bwd(*(to_dev(a) for a in (x, Wg, Wu, Wd)), "gelu_tanh", to_dev(dy))
+    torch.cuda.synchronize()
+    rows, hid = bwd_sample(M, H)
+    ref = oracle.glu_bwd_sampled(*(f64_of_bits(a) for a in (x, Wg, Wu, Wd)), "gelu_tanh", f64_of_bits(dy), rows, hid)
+    r_t, h_t = torch.from_numpy(rows).to(DEV), torch.from_numpy(hid).to(DEV)
+    assert_parity(dx[r_t], ref[0], "k-major dx rows")
+    assert_parity(dWg[h_t], ref[1], "k-major dWg rows")
+    assert_parity(dWu[h_t], ref[2], "k-major dWu rows")
+    assert_parity(dWd[:, h_t], ref[3], "k-major dWd columns")
+
+
 def test_bwd_zero_tokens_gives_zero_weight_gradients():
     K, N = 64, 48
     W = to_dev(rand_bf16(np.random.default_rng(0), (N, K), 0.1, "uniform"))
