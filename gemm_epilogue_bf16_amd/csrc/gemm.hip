@@ -164,10 +164,13 @@ static_assert(m32_reads_conflict_free<8>(false) && m32_reads_conflict_free<8>(tr
 // kbase = 32 ks + 8 (lane / 16) and + 4 give a lane the 8 consecutive k of the
 // 16x16x32 operand, in the order the row-major reads give them.  kswz moves
 // chunk bits 1-3: the 8 k-rows of a half-wave's read land on 8 distinct chunk
-// pairs (an activation fragment's 16 columns are one chunk pair per row).  A
-// weight fragment's 16 columns are 4 half chunks (the column permutation that
-// gives each lane runs of 8 output columns), all in the same half, so its
-// reads take two passes.
+// pairs (an activation fragment's 16 consecutive columns are one chunk pair
+// per row), so those reads are conflict free.  A weight fragment keeps the
+// pair permutation that gives each lane runs of 8 output columns (16-byte
+// stores): its 16 columns are 4 half chunks, all in the same half, so its
+// reads take two passes.  (Weight columns kept in order instead, 4-column
+// runs with 8-byte stores and conflict-free reads, measured 1 % slower on the
+// large backward.)
 __host__ __device__ constexpr int kswz(int k) { return 2 * ((k & 7) ^ (((k >> 3) & 1) << 2)); }
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4_t lds_read_tr_pair(uint32_t addr0, uint32_t addr1) {
@@ -517,35 +520,34 @@ gemm_bf16_kernel(GemmParams p) {
   // is x0, w0 .. w(FN-1), x1 .. x(FM-1): the order its MFMAs consume them.
   constexpr int NREADS = FM + FN;
   u32x4_t xf[2][FM], wf[2][FN];
-  // k-major: per k-step and half (k-rows kbase and kbase + 4) the lane's
-  // byte offset in the operand's region for fragment 0; fragment f XORs chunk
-  // bits the lane's own part leaves zero (activation: 2 f; weight: 4 (f / 2),
-  // plus the half chunk f % 2)
-  uint32_t km_x[KM ? KS : 1][2], km_w[KM ? KS : 1][2];
+  // k-major: the lane's byte offset in the operand's region for k-step 0,
+  // half 0 (k-row 8 (lane / 16) + (lane % 16) / 4) and fragment 0.  The rest
+  // are compile-time: k-step 1 is 32 rows on (the swizzle reads row bits 0-3:
+  // + 16384 bytes), half 1 is 4 rows on (row bit 2 set: swizzle bit 3 flips,
+  // XOR 128, then + 2048), and a fragment XORs chunk bits the lane's own part
+  // leaves zero (activation f: 2 f; weight f: 4 (f / 2), plus half chunk
+  // f % 2).  One register per operand.
+  uint32_t km_x = 0, km_w = 0;
   if constexpr (KM != 0) {
     const int kq = lane >> 4, s16 = lane & 15;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = ks * 32 + 8 * kq + (s16 >> 2) + 4 * h;
-        km_x[ks][h] = (uint32_t)(row * 512 + (((wm * 16 + ((s16 & 3) >> 1)) ^ kswz(row)) << 4) + ((s16 & 1) << 3));
-        km_w[ks][h] = (uint32_t)(BM * CH * 16 + row * 512 + (((wn * 8 + (s16 & 3)) ^ kswz(row)) << 4));
-      }
+    const int row = 8 * kq + (s16 >> 2);
+    km_x = (uint32_t)(row * 512 + (((wm * 16 + ((s16 & 3) >> 1)) ^ kswz(row)) << 4) + ((s16 & 1) << 3));
+    km_w = (uint32_t)(BM * CH * 16 + row * 512 + (((wn * 8 + (s16 & 3)) ^ kswz(row)) << 4));
   }
+  auto km_pair = [&](const u32x4_t* sl, uint32_t a0, int ks, uint32_t half) -> u32x4_t {
+    const uint32_t b = lds_addr(sl) + (uint32_t)(16384 * ks) + half;
+    return lds_read_tr_pair(b + a0, b + ((a0 ^ 128u) + 2048u));
+  };
   auto frag_x = [&](const u32x4_t* sl, int ks, int f) -> u32x4_t {
     if constexpr (KMA) {
-      const uint32_t b = lds_addr(sl);
-      return lds_read_tr_pair(b + (km_x[ks][0] ^ (uint32_t)(32 * f)), b + (km_x[ks][1] ^ (uint32_t)(32 * f)));
+      return km_pair(sl, km_x ^ (uint32_t)(32 * f), ks, 0u);
     } else {
       return sl[x_idx[ks] + f * MR * CH];
     }
   };
   auto frag_w = [&](const u32x4_t* sl, int ks, int f) -> u32x4_t {
-    if constexpr (KMB) {
-      const uint32_t b = lds_addr(sl) + (uint32_t)(8 * (f & 1));
-      return lds_read_tr_pair(b + (km_w[ks][0] ^ (uint32_t)(64 * (f >> 1))),
-                              b + (km_w[ks][1] ^ (uint32_t)(64 * (f >> 1))));
+    if constexpr (KMB) {   // the pair permutation: columns 32 (f / 2) + 8 g + 4 (f % 2) .. + 3, g = 0..3
+      return km_pair(sl, km_w ^ (uint32_t)(64 * (f >> 1)), ks, (uint32_t)(8 * (f & 1)));
     } else {
       return sl[w_idx[ks] + w_delta(f, FN, BN, DUAL, M32) * CH];
     }

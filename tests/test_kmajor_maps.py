@@ -55,12 +55,16 @@ def frag_addrs(kind, wave, ks, f, h):
     for lane in range(64):
         kq, s16 = lane >> 4, lane & 15
         row = ks * 32 + 8 * kq + (s16 >> 2) + 4 * h
+        row0 = 8 * kq + (s16 >> 2)            # k-step 0, half 0: the one per-lane register
         if kind == "x":
-            base = row * 512 + (((wm * 16 + ((s16 & 3) >> 1)) ^ kswz(row)) << 4) + ((s16 & 1) << 3)
-            addrs.append(base ^ (32 * f))
+            a0 = (row0 * 512 + (((wm * 16 + ((s16 & 3) >> 1)) ^ kswz(row0)) << 4) + ((s16 & 1) << 3)) ^ (32 * f)
+            half = 0
         else:
-            base = row * 512 + (((wn * 8 + (s16 & 3)) ^ kswz(row)) << 4)
-            addrs.append((base ^ (64 * (f >> 1))) + 8 * (f & 1))
+            a0 = (row0 * 512 + (((wn * 8 + (s16 & 3)) ^ kswz(row0)) << 4)) ^ (64 * (f >> 1))
+            half = 8 * (f & 1)
+        # k-step ks: + 16384; half h = 1: (a0 ^ 128) + 2048
+        addrs.append(16384 * ks + half + (a0 if h == 0 else (a0 ^ 128) + 2048))
+        assert row == row0 + 32 * ks + 4 * h
     return addrs
 
 
