@@ -705,14 +705,30 @@ fmlp_status fmlp_linear_bwd(const fmlp_bf16* x, const fmlp_bf16* W, const fmlp_b
             "linear_bwd dz launch");
     dz = dzw;
   }
-  // dx = dz W: the contraction runs over W's rows, so W is read transposed
-  HIP_TRY(launch_transpose(W, N, K, K, wt, N, N, s), "linear_bwd transpose W");
-  HIP_TRY(gemm_linear(dz, wt, nullptr, FMLP_ACT_NONE, M, N, K, dx, cus, s), "linear_bwd dx launch");
+  // dx = dz W: the contraction runs over W's rows (W read k-major, or
+  // transposed first where the GEMM runs on smaller tiles)
+  if (gemm_bkmajor_ok(M, K, N, 0, cus)) {
+    HIP_TRY(gemm_bkmajor(dz, W, nullptr, 0, M, K, N, dx, cus, s), "linear_bwd dx launch");
+  } else {
+    HIP_TRY(launch_transpose(W, N, K, K, wt, N, N, s), "linear_bwd transpose W");
+    HIP_TRY(gemm_linear(dz, wt, nullptr, FMLP_ACT_NONE, M, N, K, dx, cus, s), "linear_bwd dx launch");
+  }
   // dW = dz^T x and db = sum over tokens: both contract over the token rows
-  HIP_TRY(launch_transpose(dz, M, N, N, dzt, Mp, Mp, s), "linear_bwd transpose dz");
-  HIP_TRY(launch_transpose(x, M, K, K, xt, Mp, Mp, s), "linear_bwd transpose x");
-  HIP_TRY(gemm_wgrad(dzt, xt, N, Mp, K, dW, reinterpret_cast<float*>(ws + L.parts), cus, s), "linear_bwd dW launch");
-  if (db) HIP_TRY(launch_rowsum(dzt, N, Mp, Mp, db, s), "linear_bwd db launch");
+  // (dz and x read k-major; dz transposed for the row sum of db)
+  bool have_dzt = false;
+  float* parts = reinterpret_cast<float*>(ws + L.parts);
+  if (wgrad_kmajor_ok(N, M, K, N, K, cus)) {
+    HIP_TRY(gemm_wgrad_kmajor(dz, N, x, K, N, M, K, dW, parts, cus, s), "linear_bwd dW launch");
+  } else {
+    HIP_TRY(launch_transpose(dz, M, N, N, dzt, Mp, Mp, s), "linear_bwd transpose dz");
+    HIP_TRY(launch_transpose(x, M, K, K, xt, Mp, Mp, s), "linear_bwd transpose x");
+    HIP_TRY(gemm_wgrad(dzt, xt, N, Mp, K, dW, parts, cus, s), "linear_bwd dW launch");
+    have_dzt = true;
+  }
+  if (db) {
+    if (!have_dzt) HIP_TRY(launch_transpose(dz, M, N, N, dzt, Mp, Mp, s), "linear_bwd transpose dz");
+    HIP_TRY(launch_rowsum(dzt, N, Mp, Mp, db, s), "linear_bwd db launch");
+  }
   return ok();
 }
 

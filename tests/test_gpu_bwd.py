@@ -167,6 +167,27 @@ def test_glu_bwd_kmajor_ragged_sampled():
     assert_parity(dWd[:, h_t], ref[3], "k-major dWd columns")
 
 
+@pytest.mark.parametrize("with_bias", [True, False])
+def test_linear_bwd_kmajor_ragged(with_bias):
+    """The linear backward with dx over W's rows read k-major (256x256 tiles
+    fill the chip) and dW over the tokens read k-major (dz and x as they lie);
+    ragged token count and widths.  Without a bias, dz is not transposed at all."""
+    M, K, N = 8200, 2056, 520
+    rng = np.random.default_rng(31 + with_bias)
+    x, W = rand_bf16(rng, (M, K)), rand_bf16(rng, (N, K), K ** -0.5, "uniform")
+    b = rand_bf16(rng, (N,), 0.3, "uniform") if with_bias else None
+    dy = rand_bf16(rng, (M, N))
+    print(f"case linear_bwd k-major M={M} K={K} N={N} bias={with_bias}", flush=True)
+    dx, dW, db = F.fmlp_linear_bwd(to_dev(x), to_dev(W), to_dev(b) if with_bias else None, "gelu_tanh", to_dev(dy))
+    torch.cuda.synchronize()
+    rdx, rdW, rdb = oracle.linear_bwd(f64_of_bits(x), f64_of_bits(W), f64_of_bits(b) if with_bias else None,
+                                      "gelu_tanh", f64_of_bits(dy))
+    assert_parity(dx, rdx, "k-major linear dx")
+    assert_parity(dW, rdW, "k-major linear dW")
+    if with_bias:
+        assert_parity(db, rdb, "k-major linear db")
+
+
 def test_bwd_zero_tokens_gives_zero_weight_gradients():
     K, N = 64, 48
     W = to_dev(rand_bf16(np.random.default_rng(0), (N, K), 0.1, "uniform"))
