@@ -185,8 +185,10 @@ size_t fmlp_glu_workspace_size(int64_t M, int64_t D, int64_t H);
  * in fp32 and written as bf16 once; the intermediate dz (or dm, m, dg, du) is
  * rounded to bf16 once before the GEMM that consumes it, as eager PyTorch
  * stores it.  Results are bitwise deterministic.  Operands that a backward
- * GEMM contracts over their rows are first written transposed into the
- * workspace.  Outputs are caller-owned bf16, must not alias inputs, and
+ * GEMM contracts over their rows are read in place (k-major, through LDS
+ * transpose reads) where the GEMM runs on 256x256 tiles, and otherwise first
+ * written transposed into the workspace, as is dz for the bias gradient's row
+ * sum.  Outputs are caller-owned bf16, must not alias inputs, and
  * M < 2^22; with M == 0 the weight and bias gradients are written as zeros.
  * Workspace: the *_bwd_workspace_size bytes, no initialisation needed; the
  * first 8192 bytes (the decode header of fmlp_mlp2 / fmlp_glu) are never
