@@ -24,7 +24,9 @@ def _codes(rng, rows, cols, bound):
 
 
 @pytest.mark.parametrize("M,K,N", [(1, 16, 16), (1, 4096, 4096), (16, 4096, 4096), (3, 1040, 200),
-                                   (7, 528, 24), (16, 8192, 48), (2, 28672, 32)])
+                                   (7, 528, 24), (16, 8192, 48), (2, 28672, 32),
+                                   # activations too wide to stage, several tokens, a partial last tile
+                                   (16, 8192, 8200), (9, 8208, 8216)])
 @pytest.mark.parametrize("act", ["none", "gelu_erf", "silu"])
 def test_linear_w8(M, K, N, act):
     rng = np.random.default_rng(M * 131 + K + N)
