@@ -63,12 +63,13 @@ __device__ __forceinline__ u32x4_t w8_load_stream(__amdgpu_buffer_rsrc_t d, uint
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(d, (int)off, 0, 2));
 }
 
-// 2 E4M3 codes (bytes 0, 1 of q, or 2, 3 with HI) -> 2 bf16 in one word, exact
+// 2 E4M3 codes (bytes 0, 1 of q, or 2, 3 with HI) -> 2 bf16 in one word, exact:
+// gfx950's scaled conversion with scale 1 (one instruction; an in-bounds check
+// of all 65536 code pairs in both halves matched the fp32 conversion followed
+// by taking the upper 16 bits, NaN codes included)
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16(uint32_t q) {
-  typedef float f32x2_t __attribute__((ext_vector_type(2)));
-  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, HI);
-  return (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xFFFF0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q, 1.0f, HI));
 }
 
 // 16 codes (k 0..15 in byte order) -> the two 8-element bf16 MFMA operands
@@ -133,25 +134,34 @@ __device__ __forceinline__ void w8_hold(W8Batch<DUAL, U>& B) {
   }
 }
 
+// The activation operand of load j: from registers, or from the LDS row at xl
+// (XB > 0), where tokens past M and k past K read the 32 zero bytes at xz
+// instead (the padding is never read as data).
+template <bool DUAL, int U, int XB>
+__device__ __forceinline__ void w8_x(const W8Batch<DUAL, U>& B, int b, int j, int wave, int g, int K,
+                                     bool xrow_ok, const uint8_t* xl, const uint8_t* xz, u32x4_t& x0,
+                                     u32x4_t& x1) {
+  if constexpr (XB == 0) {
+    x0 = B.x[j][0];
+    x1 = B.x[j][1];
+  } else {
+    const int c = w8_chunk(b, U, j, wave);
+    const uint8_t* src = (xrow_ok && c * 64 + g * 16 < K) ? xl + c * 128 : xz;
+    x0 = *reinterpret_cast<const u32x4_t*>(src);
+    x1 = *reinterpret_cast<const u32x4_t*>(src + 16);
+  }
+}
+
+// jmax < U: loads j >= jmax of the batch are not multiplied (wave-uniform)
 template <bool DUAL, int U, int XB>
 __device__ __forceinline__ void w8_consume(const W8Batch<DUAL, U>& B, int b, int wave, int g, int K,
-                                           bool xrow_ok, const uint8_t* xl, f32x4_t& acc0,
-                                           f32x4_t& acc1) {
+                                           bool xrow_ok, const uint8_t* xl, const uint8_t* xz,
+                                           f32x4_t& acc0, f32x4_t& acc1, int jmax = U) {
 #pragma unroll
   for (int j = 0; j < U; ++j) {
+    if (j >= jmax) break;
     u32x4_t x0, x1;
-    if constexpr (XB == 0) {
-      x0 = B.x[j][0];
-      x1 = B.x[j][1];
-    } else {
-      // zero for tokens past M and k past K (the padding is never read as data)
-      const int c = w8_chunk(b, U, j, wave);
-      const bool ok = xrow_ok && c * 64 + g * 16 < K;
-      const int off = ok ? c * 128 : 0;
-      x0 = *reinterpret_cast<const u32x4_t*>(xl + off);
-      x1 = *reinterpret_cast<const u32x4_t*>(xl + off + 16);
-      if (!ok) x0 = x1 = zero4();
-    }
+    w8_x<DUAL, U, XB>(B, b, j, wave, g, K, xrow_ok, xl, xz, x0, x1);
     u32x4_t a0, a1;
     e4m3x16_to_bf16(B.w0[j], a0, a1);
     acc0 = mfma_16x16x32(a0, x0, acc0);
@@ -164,13 +174,85 @@ __device__ __forceinline__ void w8_consume(const W8Batch<DUAL, U>& B, int b, int
   }
 }
 
+// Two batches of one wave (the k chunks of waves wa and wb of the one-role
+// form) into their own accumulators, interleaved so that consecutive MFMAs
+// never depend on each other; each accumulator sums in the one-role order.
+template <bool DUAL>
+__device__ __forceinline__ void w8_consume_two(const W8Batch<DUAL, 8>& A, const W8Batch<DUAL, 8>& B, int wa,
+                                               int wb, int g, int K, bool xrow_ok, const uint8_t* xl,
+                                               const uint8_t* xz, f32x4_t& a0, f32x4_t& a1, f32x4_t& b0,
+                                               f32x4_t& b1, int jmax) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= jmax) break;
+    u32x4_t xa0, xa1, xb0, xb1, wa0, wa1, wb0, wb1;
+    w8_x<DUAL, 8, 1>(A, 0, j, wa, g, K, xrow_ok, xl, xz, xa0, xa1);
+    w8_x<DUAL, 8, 1>(B, 0, j, wb, g, K, xrow_ok, xl, xz, xb0, xb1);
+    e4m3x16_to_bf16(A.w0[j], wa0, wa1);
+    e4m3x16_to_bf16(B.w0[j], wb0, wb1);
+    a0 = mfma_16x16x32(wa0, xa0, a0);
+    b0 = mfma_16x16x32(wb0, xb0, b0);
+    a0 = mfma_16x16x32(wa1, xa1, a0);
+    b0 = mfma_16x16x32(wb1, xb1, b0);
+    if constexpr (DUAL) {
+      e4m3x16_to_bf16(A.w1[j], wa0, wa1);
+      e4m3x16_to_bf16(B.w1[j], wb0, wb1);
+      a1 = mfma_16x16x32(wa0, xa0, a1);
+      b1 = mfma_16x16x32(wb0, xb0, b1);
+      a1 = mfma_16x16x32(wa1, xa1, a1);
+      b1 = mfma_16x16x32(wb1, xb1, b1);
+    }
+  }
+}
+
+// The epilogue's per-row values of rows n .. n + 3 (the rows of lane group g
+// in a tile): the scales and the bias, requested together at the start of the
+// tile, so they cost no round trip of their own at the end.  A row past N
+// reads row N - 1 (its value is never used); without a bias nothing is read
+// (an empty buffer descriptor reads as zero).  The bias stays in its bf16
+// bits until the epilogue: converting it where it is loaded would wait for the
+// load there (the empty asm keeps the conversion from being hoisted).
+template <bool DUAL>
+struct W8Rows {
+  float s0[4], s1[4];
+  uint32_t b[4];
+  __device__ __forceinline__ float bias(int i) const {
+    uint32_t v = b[i];
+    asm volatile("" : "+v"(v));
+    return __uint_as_float(v << 16);
+  }
+};
+template <bool DUAL>
+__device__ __forceinline__ W8Rows<DUAL> w8_rows(const W8Layer& L, int64_t n) {
+  W8Rows<DUAL> R;
+  const __amdgpu_buffer_rsrc_t d0 = w8_desc(L.s0, (uint32_t)L.N * 4u);
+  const __amdgpu_buffer_rsrc_t d1 = w8_desc(DUAL ? L.s1 : L.s0, (uint32_t)L.N * 4u);
+  const __amdgpu_buffer_rsrc_t db = w8_desc(L.bias ? (const void*)L.bias : (const void*)L.s0,
+                                            L.bias ? (uint32_t)L.N * 2u : 0u);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t row = (uint32_t)min<int64_t>(n + i, L.N - 1);
+    R.s0[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d0, (int)(row * 4u), 0, 0));
+    if constexpr (DUAL)
+      R.s1[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d1, (int)(row * 4u), 0, 0));
+    else
+      R.s1[i] = 0.f;
+    R.b[i] = __builtin_amdgcn_raw_buffer_load_b16(db, (int)(row * 2u), 0, 0);
+  }
+  return R;
+}
+
 // XB: bytes of LDS for the activations, M rows of 2K + 16 bytes (the 16-byte
-// pad puts the 16 token rows of a fragment read in different banks); 0: the
-// activations are loaded from memory beside the weights.
+// pad puts the 16 token rows of a fragment read in different banks) and 32
+// zero bytes; 0: the activations are loaded from memory beside the weights.
 template <bool DUAL, int U, int XB>
 __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M) {
   __shared__ f32x4_t red[DUAL ? 2 : 1][kW8Waves][64];
   __shared__ __attribute__((aligned(16))) uint8_t xs[XB > 0 ? XB : 16];
+  // the activation operand of masked loads: the last 32 bytes of xs, past the
+  // staged rows (a separate array would take the gated form's 80 KB past half
+  // the CU's LDS, and two blocks would no longer fit)
+  const uint8_t* xz = xs + (XB > 0 ? XB - 32 : 0);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15;   // weight row in the tile; token for the activation operand
@@ -191,6 +273,7 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   const int chunks = (K + 63) / 64;
   const int nb = (chunks + kW8Waves * U - 1) / (kW8Waves * U);
   W8Batch<DUAL, U> A, B;
+  const W8Rows<DUAL> R = w8_rows<DUAL>(L, n0 + 4 * g);
   // the first weight batch is in flight while the activations are staged
   w8_issue<DUAL, U, XB>(A, 0, wave, g, K, d0, d1, dx, wrow, xrow);
   if constexpr (XB > 0) {
@@ -202,6 +285,7 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
     const int ipr = (per_row + 63) / 64;       // load instructions per row
     const i32x4_t xd = make_desc(reinterpret_cast<uint64_t>(L.x), (uint32_t)(M * K) * 2u);
     const uint32_t xs_lds = lds_addr(xs);
+    if (threadIdx.x < 2) *reinterpret_cast<u32x4_t*>(xs + XB - 32 + 16 * threadIdx.x) = zero4();
     for (int t = wave; t < M * ipr; t += kW8Waves) {   // wave-uniform
       const int m = t / ipr, q = t - m * ipr;
       const int c = q * 64 + lane;
@@ -221,20 +305,20 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   for (; b + 2 < nb; b += 2) {
     w8_issue<DUAL, U, XB>(B, b + 1, wave, g, K, d0, d1, dx, wrow, xrow);
     w8_hold<DUAL, U, XB>(A);
-    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
     w8_issue<DUAL, U, XB>(A, b + 2, wave, g, K, d0, d1, dx, wrow, xrow);
     w8_hold<DUAL, U, XB>(B);
-    w8_consume<DUAL, U, XB>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, XB>(B, b + 1, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   }
   if (b + 1 < nb) {
     w8_issue<DUAL, U, XB>(B, b + 1, wave, g, K, d0, d1, dx, wrow, xrow);
     w8_hold<DUAL, U, XB>(A);
-    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
     w8_hold<DUAL, U, XB>(B);
-    w8_consume<DUAL, U, XB>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, XB>(B, b + 1, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   } else {
     w8_hold<DUAL, U, XB>(A);
-    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, XB>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   }
 
   red[0][wave][lane] = acc0;
@@ -258,10 +342,10 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
     const int64_t n = n0 + row;
     float z;
     if constexpr (DUAL) {
-      z = apply_act(s0[v] * L.s0[n], L.act) * (s1[v] * L.s1[n]);
+      z = apply_act(s0[v] * R.s0[v], L.act) * (s1[v] * R.s1[v]);
     } else {
-      z = s0[v] * L.s0[n];
-      if (L.bias) z += bf16_to_f32(L.bias[n]);
+      z = s0[v] * R.s0[v];
+      if (L.bias) z += R.bias(v);
       z = apply_act(z, L.act);
     }
     const __bf16 o = (__bf16)z;
@@ -269,12 +353,12 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   }
 }
 
-constexpr int kXSmall = 64 * 1024;    // one token up to K = 32760
-constexpr int kXLarge = 136 * 1024;   // 16 tokens up to K = 4348
+constexpr int kXSmall = 64 * 1024;    // one token up to K = 32736
+constexpr int kXLarge = 136 * 1024;   // 16 tokens up to K = 4336
 
 template <bool DUAL, int U>
 hipError_t launch_w8(const W8Layer& L, int M, dim3 grid, hipStream_t s) {
-  const int64_t xneed = (int64_t)M * (2 * L.K + 16);
+  const int64_t xneed = (int64_t)M * (2 * L.K + 16) + 32;   // rows and the zero pad
   if (xneed <= kXSmall)
     hipLaunchKernelGGL((decode_w8_kernel<DUAL, U, kXSmall>), grid, dim3(kW8Threads), 0, s, L, M);
   else if (xneed <= kXLarge)
@@ -320,8 +404,8 @@ __device__ __forceinline__ W8Tile w8_tile_at(const W8Layer& L, int64_t tile) {
 // first register batch (issued here).
 template <bool DUAL, int U>
 __device__ __forceinline__ void w8_tile_one_token(const W8Layer& L, int64_t tile, const uint8_t* xs,
-                                                  f32x4_t (*red)[kW8Waves][64], f32x4_t& s0, f32x4_t& s1,
-                                                  W8Batch<DUAL, U>& A) {
+                                                  const uint8_t* xz, f32x4_t (*red)[kW8Waves][64], f32x4_t& s0,
+                                                  f32x4_t& s1, W8Batch<DUAL, U>& A) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -341,20 +425,20 @@ __device__ __forceinline__ void w8_tile_one_token(const W8Layer& L, int64_t tile
   for (; b + 2 < nb; b += 2) {
     w8_issue<DUAL, U, 1>(B, b + 1, wave, g, K, d0, d1, d0, wrow, 0u);
     w8_hold<DUAL, U, 1>(A);
-    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
     w8_issue<DUAL, U, 1>(A, b + 2, wave, g, K, d0, d1, d0, wrow, 0u);
     w8_hold<DUAL, U, 1>(B);
-    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   }
   if (b + 1 < nb) {
     w8_issue<DUAL, U, 1>(B, b + 1, wave, g, K, d0, d1, d0, wrow, 0u);
     w8_hold<DUAL, U, 1>(A);
-    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
     w8_hold<DUAL, U, 1>(B);
-    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, 1>(B, b + 1, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   } else {
     w8_hold<DUAL, U, 1>(A);
-    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, acc0, acc1);
+    w8_consume<DUAL, U, 1>(A, b, wave, g, K, xrow_ok, xl, xz, acc0, acc1);
   }
   red[0][wave][lane] = acc0;
   if constexpr (DUAL) red[1][wave][lane] = acc1;
@@ -378,6 +462,8 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
                                                                    uint32_t salt) {
   __shared__ f32x4_t red[2][kW8Waves][64];
   __shared__ __attribute__((aligned(16))) uint8_t xs[kXSmall];   // x, then h: one bf16 row
+  __shared__ u32x4_t xzero[2];   // the activation operand of masked loads
+  const uint8_t* xz = reinterpret_cast<const uint8_t*>(xzero);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -388,6 +474,7 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
   const int K1 = (int)L1.K, H = (int)L1.N;
 
   // the input row into LDS
+  if (tid < 2) xzero[tid] = zero4();
   for (int i = tid; i < K1 / 8; i += kW8Threads)
     *reinterpret_cast<u32x4_t*>(xs + i * 16) = ld16(L1.x + (int64_t)i * 8);
   __syncthreads();
@@ -398,17 +485,18 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
   for (int64_t t = blk; t < tiles1; t += G) {
     f32x4_t s0, s1;
     W8Batch<DUAL1, DUAL1 ? 4 : 8> A1;
-    w8_tile_one_token<DUAL1, DUAL1 ? 4 : 8>(L1, t, xs, red, s0, s1, A1);
+    const int64_t n = t * 16 + 4 * g;   // H % 16 == 0: all four rows exist
+    const W8Rows<DUAL1> R = w8_rows<DUAL1>(L1, n);
+    w8_tile_one_token<DUAL1, DUAL1 ? 4 : 8>(L1, t, xs, xz, red, s0, s1, A1);
     if (wave == 0 && r == 0) {
-      const int64_t n = t * 16 + 4 * g;   // H % 16 == 0: all four rows exist
       float v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if constexpr (DUAL1) {
-          v[i] = apply_act(s0[i] * L1.s0[n + i], L1.act) * (s1[i] * L1.s1[n + i]);
+          v[i] = apply_act(s0[i] * R.s0[i], L1.act) * (s1[i] * R.s1[i]);
         } else {
-          float z = s0[i] * L1.s0[n + i];
-          if (L1.bias) z += bf16_to_f32(L1.bias[n + i]);
+          float z = s0[i] * R.s0[i];
+          if (L1.bias) z += R.bias(i);
           v[i] = apply_act(z, L1.act);
         }
       }
@@ -457,14 +545,231 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
   for (int64_t t = blk; t < tiles2; t += G) {
     f32x4_t s0, s1;
     W8Batch<false, 8> A2;
-    w8_tile_one_token<false, 8>(L2, t, xs, red, s0, s1, A2);
+    const W8Rows<false> R = w8_rows<false>(L2, t * 16 + 4 * g);
+    w8_tile_one_token<false, 8>(L2, t, xs, xz, red, s0, s1, A2);
     if (wave == 0 && r == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t n = t * 16 + 4 * g + i;
         if (n >= L2.N) break;
-        float z = s0[i] * L2.s0[n];
-        if (L2.bias) z += bf16_to_f32(L2.bias[n]);
+        float z = s0[i] * R.s0[i];
+        if (L2.bias) z += R.bias(i);
+        const __bf16 o = (__bf16)z;
+        L2.y[n] = __builtin_bit_cast(uint16_t, o);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The same two-layer forward with the block's waves in two roles, for rows of
+// at most 4096 codes in both layers and one layer-1 tile per block.  A wave's
+// loads return in the order it issued them, so in the one-role form a layer-2
+// request made before the exchange delays the exchange's polls behind it.
+// Here waves 4-7 stream the layer-1 tile, publish h and gather it, while
+// waves 0-3 hold the block's first layer-2 tile (16 rows over every k) in
+// registers, requested once layer 1's weights have landed: no poll waits
+// behind a layer-2 load, and layer 2 starts from registers as soon as h is in
+// LDS.  Wave p of a role does the work of waves
+// p and p + 4 of the one-role form (their k chunks, in their order, into
+// separate accumulators), and the 8 partial tiles are summed in the same
+// order, so the result is bitwise that of the one-role form.
+// ---------------------------------------------------------------------------
+constexpr int kW8SplitMaxK = kW8Waves * 8 * 64;   // one 8-load batch of 8 waves
+constexpr int kW8Role = kW8Waves / 2;
+
+template <bool DUAL1>
+__global__ __launch_bounds__(kW8Threads) void decode_w8_split_kernel(W8Layer L1, W8Layer L2, uint32_t* sync,
+                                                                     uint32_t salt) {
+  __shared__ f32x4_t red[2][kW8Waves][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[2 * kW8SplitMaxK];   // x, then h
+  __shared__ uint32_t busy[2][kW8Waves];
+  __shared__ u32x4_t xzero[2];   // the activation operand of masked loads
+  const uint8_t* xz = reinterpret_cast<const uint8_t*>(xzero);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int G = (int)gridDim.x, blk = (int)blockIdx.x;
+  const bool streamer = wave >= kW8Role;   // layer 1 and the exchange; waves below hold layer 2
+  const int p = wave & (kW8Role - 1);
+  const int K1 = (int)L1.K, H = (int)L1.N, K2 = (int)L2.K;
+  const int64_t tiles2 = (L2.N + 15) / 16;
+  const bool has2 = blk < tiles2;
+  const uint8_t* xl = xs + g * 32;   // the one token's row; lanes of other tokens drop their value
+  const bool xrow_ok = r == 0;
+
+  W8Batch<false, 8> P0, P1;   // layer 2: the k chunks of waves p and p + 4
+  W8Rows<false> R2;
+  // layer 1: the one-role form multiplies 8 loads per wave, or 4 when one
+  // gated batch of 4 covers k
+  const int j1 = (DUAL1 && (K1 + 63) / 64 <= kW8Waves * 4) ? 4 : 8;
+  W8Batch<DUAL1, 8> A0, A1;
+  // The generation is read by the streaming waves only, between their weight
+  // and activation loads, and its uses are pinned inside their branch: a use
+  // on the path the holding waves share would make them wait for their own
+  // layer-2 loads (wait counts are merged over both roles' paths).
+  uint32_t gen_next = 0, target = 0;
+  W8Rows<DUAL1> R1;
+  if (streamer) {
+    R1 = w8_rows<DUAL1>(L1, (int64_t)blk * 16 + 4 * g);
+    const W8Tile t1 = w8_tile_at<DUAL1>(L1, blk);
+    w8_issue<DUAL1, 8, 1>(A0, 0, p, g, K1, t1.d0, t1.d1, t1.d0, t1.wrow, 0u);
+    w8_issue<DUAL1, 8, 1>(A1, 0, p + kW8Role, g, K1, t1.d0, t1.d1, t1.d0, t1.wrow, 0u);
+    gen_next = ld_coherent(sync + kSyncGenWord) + 1u;
+    // the input row, all pieces in flight together (pieces past K1 read as
+    // zero and land in LDS that is never read as data)
+    constexpr int kXPer = 2 * kW8SplitMaxK / 16 / (kW8Role * 64);
+    const __amdgpu_buffer_rsrc_t rx = w8_desc(L1.x, (uint32_t)K1 * 2u);
+    const int st = tid - kW8Role * 64;
+    if (st < 2) xzero[st] = zero4();
+    u32x4_t xv[kXPer];
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) xv[k] = w8_load(rx, (uint32_t)(st + kW8Role * 64 * k) * 16u);
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) *reinterpret_cast<u32x4_t*>(xs + (st + kW8Role * 64 * k) * 16) = xv[k];
+    target = epoch_of(gen_next, salt);
+    asm volatile("" : "+v"(gen_next), "+v"(target));
+  }
+  lds_barrier();   // x is in LDS, so layer 1's weights have landed
+  // Only now the layer-2 request: made at kernel start it shares the memory
+  // with layer 1's and delays layer 1 (and so the exchange) by as much as it
+  // gains (15.3 against 13.5 us for the 4096^3 MLP); made here it streams
+  // while layer 1 is multiplied and h is exchanged.
+  if (!streamer && has2) {
+    R2 = w8_rows<false>(L2, (int64_t)blk * 16 + 4 * g);
+    const W8Tile t2 = w8_tile_at<false>(L2, blk);
+    w8_issue<false, 8, 1>(P0, 0, p, g, K2, t2.d0, t2.d0, t2.d0, t2.wrow, 0u);
+    w8_issue<false, 8, 1>(P1, 0, p + kW8Role, g, K2, t2.d0, t2.d0, t2.d0, t2.wrow, 0u);
+  }
+  if (streamer) {
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0, b0 = a0, b1 = a0;
+    w8_hold<DUAL1, 8, 1>(A0);
+    w8_hold<DUAL1, 8, 1>(A1);
+    w8_consume_two<DUAL1>(A0, A1, p, p + kW8Role, g, K1, xrow_ok, xl, xz, a0, a1, b0, b1, j1);
+    red[0][p][lane] = a0;
+    red[0][p + kW8Role][lane] = b0;
+    if constexpr (DUAL1) {
+      red[1][p][lane] = a1;
+      red[1][p + kW8Role][lane] = b1;
+    }
+  }
+  lds_barrier();
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(L1.y, (uint32_t)H * 4u);   // H / 2 words of 8 bytes
+  if (wave == kW8Role) {
+    f32x4_t s0 = red[0][0][lane];
+    f32x4_t s1 = red[DUAL1 ? 1 : 0][0][lane];
+#pragma unroll
+    for (int w = 1; w < kW8Waves; ++w) {
+      s0 += red[0][w][lane];
+      if constexpr (DUAL1) s1 += red[1][w][lane];
+    }
+    if (r == 0) {
+      const int64_t n = (int64_t)blk * 16 + 4 * g;   // H % 16 == 0: all four rows exist
+      float v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (DUAL1) {
+          v[i] = apply_act(s0[i] * R1.s0[i], L1.act) * (s1[i] * R1.s1[i]);
+        } else {
+          float z = s0[i] * R1.s0[i];
+          if (L1.bias) z += R1.bias(i);
+          v[i] = apply_act(z, L1.act);
+        }
+      }
+      st_coherent_b128(rh, (uint32_t)n * 4u, u32x4_t{pack_bf16x2(v[0], v[1]), target, pack_bf16x2(v[2], v[3]), target});
+    }
+  }
+
+  // every block's h into LDS, gathered by the streaming waves (16-byte pieces
+  // of two words, each thread's in flight together) until both words of every
+  // piece carry this call's epoch; the holding waves only meet the barriers
+  {
+    constexpr int kPer = kW8TwoMaxH / 4 / (kW8Role * 64);   // pieces per thread
+    const int pieces = H / 4;
+    const int st = tid - kW8Role * 64;
+    uint32_t pend = 0;
+    if (streamer) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (st + kW8Role * 64 * i < pieces) pend |= 1u << i;
+    }
+    for (uint32_t spins = 0;; ++spins) {
+      if (streamer) {
+        u32x4_t v[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i)
+          if (pend & (1u << i))
+            v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rh, (uint32_t)(st + kW8Role * 64 * i) * 16u, 0, 16 /* sc1 */));
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          if ((pend & (1u << i)) && v[i][1] == target && v[i][3] == target) {
+            *reinterpret_cast<u32x2_t*>(xs + (st + kW8Role * 64 * i) * 8) = u32x2_t{v[i][0], v[i][2]};
+            pend &= ~(1u << i);
+          }
+        }
+        const bool more = __builtin_amdgcn_ballot_w64(pend != 0) != 0;
+        if (lane == 0) busy[spins & 1][wave] = more ? 1u : 0u;
+      }
+      // a barrier without a vector-memory wait: the holders' loads stay in flight.
+      // busy[spins & 1] is written again two passes on, after every wave has read it.
+      lds_barrier();
+      uint32_t more = 0;
+#pragma unroll
+      for (int w = kW8Role; w < kW8Waves; ++w) more |= busy[spins & 1][w];
+      if (more == 0) break;
+      if (spins >= (1u << 20)) {
+        if (tid == kW8Role * 64)
+          __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (blk == 0 && tid == kW8Role * 64) st_coherent(sync + kSyncGenWord, gen_next);
+  }
+
+  // layer 2: the first tile from registers, any further ones streamed by all waves
+  if (has2) {
+    if (!streamer) {
+      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, unused0 = c0, unused1 = c0;
+      w8_hold<false, 8, 1>(P0);
+      w8_hold<false, 8, 1>(P1);
+      w8_consume_two<false>(P0, P1, p, p + kW8Role, g, K2, xrow_ok, xl, xz, c0, unused0, c1, unused1, 8);
+      red[0][p][lane] = c0;
+      red[0][p + kW8Role][lane] = c1;
+    }
+    lds_barrier();
+    f32x4_t s0 = red[0][0][lane];
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < kW8Waves; ++w) s0 += red[0][w][lane];
+    }
+    lds_barrier();   // red is free for the next tile
+    if (wave == 0 && r == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = (int64_t)blk * 16 + 4 * g + i;
+        if (n >= L2.N) break;
+        float z = s0[i] * R2.s0[i];
+        if (L2.bias) z += R2.bias(i);
+        const __bf16 o = (__bf16)z;
+        L2.y[n] = __builtin_bit_cast(uint16_t, o);
+      }
+    }
+  }
+  for (int64_t t = blk + G; t < tiles2; t += G) {
+    f32x4_t s0, s1;
+    W8Batch<false, 8> A2;
+    const W8Rows<false> R = w8_rows<false>(L2, t * 16 + 4 * g);
+    w8_tile_one_token<false, 8>(L2, t, xs, xz, red, s0, s1, A2);
+    if (wave == 0 && r == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = t * 16 + 4 * g + i;
+        if (n >= L2.N) break;
+        float z = s0[i] * R.s0[i];
+        if (L2.bias) z += R.bias(i);
         const __bf16 o = (__bf16)z;
         L2.y[n] = __builtin_bit_cast(uint16_t, o);
       }
@@ -487,19 +792,21 @@ hipError_t launch_decode_w8_two(const W8Layer& L1, const W8Layer& L2, uint32_t* 
   const int64_t tiles1 = (L1.N + 15) / 16;
   // every block owns a layer-1 tile and all are resident at once: at most one per CU
   const unsigned grid = (unsigned)std::min<int64_t>(tiles1, cus);
+  // the two-role form: one layer-1 tile per block, and both layers' rows read in one batch
+  const bool split = tiles1 <= cus && L1.K <= kW8SplitMaxK;
   uint32_t salt = next_launch_salt();
-  if (cooperative) {   // opt-in: the runtime refuses a grid that cannot be resident at once
-    W8Layer a = L1, b = L2;
-    void* args[] = {&a, &b, &sync, &salt};
-    const void* f = L1.W1 ? reinterpret_cast<const void*>(&decode_w8_two_kernel<true>)
-                          : reinterpret_cast<const void*>(&decode_w8_two_kernel<false>);
-    return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kW8Threads), args, 0, s);
-  }
-  if (L1.W1)
-    hipLaunchKernelGGL((decode_w8_two_kernel<true>), dim3(grid), dim3(kW8Threads), 0, s, L1, L2, sync, salt);
+  const void* f;
+  if (split)
+    f = L1.W1 ? reinterpret_cast<const void*>(&decode_w8_split_kernel<true>)
+              : reinterpret_cast<const void*>(&decode_w8_split_kernel<false>);
   else
-    hipLaunchKernelGGL((decode_w8_two_kernel<false>), dim3(grid), dim3(kW8Threads), 0, s, L1, L2, sync, salt);
-  return hipGetLastError();
+    f = L1.W1 ? reinterpret_cast<const void*>(&decode_w8_two_kernel<true>)
+              : reinterpret_cast<const void*>(&decode_w8_two_kernel<false>);
+  W8Layer a = L1, b = L2;
+  void* args[] = {&a, &b, &sync, &salt};
+  // cooperative (opt-in): the runtime refuses a grid that cannot be resident at once
+  if (cooperative) return hipLaunchCooperativeKernel(f, dim3(grid), dim3(kW8Threads), args, 0, s);
+  return hipLaunchKernel(f, dim3(grid), dim3(kW8Threads), args, 0, s);
 }
 
 hipError_t launch_decode_w8(const W8Layer& L, int M, hipStream_t s) {

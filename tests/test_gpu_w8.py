@@ -120,14 +120,21 @@ def test_w8_float8_dtype_and_errors():
     assert empty.shape == (0, 32)
 
 
-@pytest.mark.parametrize("form", ["mlp2", "glu"])
-def test_w8_one_launch_equals_two_launches(form):
+# (form, K, H, N): rows of at most 4096 codes with one layer-1 tile per block
+# take the two-role kernel (a gated layer 1 of one or two load batches, blocks
+# without a layer-2 tile, blocks with several); K = 8192 takes the one-role kernel
+_ONE_LAUNCH_CASES = [("mlp2", 4096, 4096, 4096), ("glu", 4096, 4096, 4096), ("mlp2", 1040, 336, 272),
+                     ("glu", 768, 3072, 768), ("glu", 2112, 1040, 2112), ("mlp2", 1040, 64, 272),
+                     ("mlp2", 8192, 1024, 1040), ("glu", 8192, 2048, 8192)]
+
+
+@pytest.mark.parametrize("form,K,H,N", _ONE_LAUNCH_CASES)
+def test_w8_one_launch_equals_two_launches(form, K, H, N):
     """At one token the one-launch form computes exactly what the two launches
     do (same per-tile order, h rounded to bf16 once): bitwise equal, over 20
     back-to-back calls that alternate two inputs on one workspace, with no
     barrier wait given up and the decode generation moving once per call."""
-    K, H, N = 4096, 4096, 4096
-    rng = np.random.default_rng(77)
+    rng = np.random.default_rng(77 + K + H + N)
     xs = [to_dev(rand_bf16(rng, (1, K))) for _ in range(2)]
     if form == "mlp2":
         q1, s1, q1d, s1d = _codes(rng, H, K, 1 / 64)
@@ -141,7 +148,7 @@ def test_w8_one_launch_equals_two_launches(form):
         qdn, sdn, qdd, sdd = _codes(rng, K, H, H ** -0.5)
         ws = F.workspace_for(DEV, int(F.lib().fmlp_w8_workspace_size(1, H)))
         call = lambda x, out: F.fmlp_glu_w8(x, qgd, sgd, qud, sud, qdd, sdd, "silu", out=out)  # noqa: E731
-    print(f"case fp8 {form} one launch vs two launches", flush=True)
+    print(f"case fp8 {form} K={K} H={H} N={N} one launch vs two launches", flush=True)
     with F.force_path("gemm"):
         want = [call(x, None) for x in xs]
     torch.cuda.synchronize()
