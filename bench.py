@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "moe_router_mfma_kernel": ["common.h", "kernels.h", "lds_dma.h", "moe.hip"],
     "decode_w8_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode_w8.h", "decode_w8.hip"],
     "decode_w8_two_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode_w8.h", "decode_w8.hip"],
+    "decode_w8_split_kernel": ["common.h", "kernels.h", "lds_dma.h", "exchange.h", "decode_w8.h", "decode_w8.hip"],
     "glu_fused_kernel": ["common.h", "kernels.h", "lds_dma.h", "glu_fused.hip"],
 }
 
@@ -185,7 +186,9 @@ def _setup_w8(w, cold: bool, dev, gate_act):
                 cache.update({k: f64(v) for k, v in t.items()})
             return oracle.glu_w8(cache["x"], *host["Wg"], *host["Wu"], *host["Wd"], act)
     if w.M == 1 and w.H <= 4096:   # both layers in one launch (h exchanged as epoch-tagged words)
-        kernel, launches, p = "decode_w8_two_kernel", 1, "FP8-weight decode, both layers in one launch"
+        # rows of at most 4096 codes: the two-role form (layer 2 held in registers during the exchange)
+        kernel = "decode_w8_split_kernel" if w.K <= 4096 else "decode_w8_two_kernel"
+        launches, p = 1, "FP8-weight decode, both layers in one launch"
     else:
         kernel, launches, p = "decode_w8_kernel", 2, "FP8-weight decode (one launch per layer)"
     case = Case(w, calls, kernel, launches, p, R, fn, (f"{rows} of {w.M} token rows, full weights", 1.0))
@@ -524,7 +527,7 @@ def roofline_of(case: Case, kernel_s: float) -> dict:
 def decode_timeouts(case: Case, F):
     """Barrier waits that gave up in the one-launch decode kernel (0 expected)."""
     ws = getattr(case, "workspace", None)
-    if case.kernel not in ("decode_kernel", "decode_w8_two_kernel") or ws is None:
+    if case.kernel not in ("decode_kernel", "decode_w8_two_kernel", "decode_w8_split_kernel") or ws is None:
         return None
     return F.barrier_timeouts(ws)
 
