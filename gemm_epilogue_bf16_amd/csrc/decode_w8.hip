@@ -568,9 +568,10 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
 // request made before the exchange delays the exchange's polls behind it.
 // Here waves 4-7 stream the layer-1 tile, publish h and gather it, while
 // waves 0-3 hold the block's first layer-2 tile (16 rows over every k) in
-// registers, requested once layer 1's weights have landed: no poll waits
-// behind a layer-2 load, and layer 2 starts from registers as soon as h is in
-// LDS.  Wave p of a role does the work of waves
+// registers, requested once layer 1's weights have landed and turned into
+// bf16 operands during the exchange: no poll waits behind a layer-2 load, and
+// once h is in LDS layer 2 is only multiplies.  (All 8 waves multiplying layer
+// 1, 8 loads each, measured slower: 12.8 against 12.3 us for the 4096^3 MLP.)  Wave p of a role does the work of waves
 // p and p + 4 of the one-role form (their k chunks, in their order, into
 // separate accumulators), and the 8 partial tiles are summed in the same
 // order, so the result is bitwise that of the one-role form.
@@ -583,7 +584,6 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_split_kernel(W8Layer L1,
                                                                      uint32_t salt) {
   __shared__ f32x4_t red[2][kW8Waves][64];
   __shared__ __attribute__((aligned(16))) uint8_t xs[2 * kW8SplitMaxK];   // x, then h
-  __shared__ uint32_t busy[2][kW8Waves];
   __shared__ u32x4_t xzero[2];   // the activation operand of masked loads
   const uint8_t* xz = reinterpret_cast<const uint8_t*>(xzero);
   const int tid = threadIdx.x;
@@ -681,61 +681,69 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_split_kernel(W8Layer L1,
     }
   }
 
-  // every block's h into LDS, gathered by the streaming waves (16-byte pieces
-  // of two words, each thread's in flight together) until both words of every
-  // piece carry this call's epoch; the holding waves only meet the barriers
-  {
+  // every block's h into LDS: each streaming wave gathers its own pieces
+  // (16-byte pieces of two words, a thread's in flight together) until both
+  // words of every piece carry this call's epoch, with no barrier between its
+  // polls.  Meanwhile the holding waves turn their layer-2 codes into bf16
+  // operands, so that once h is in LDS only the multiplies remain.
+  u32x4_t q0[8][2], q1[8][2];   // layer 2's operands: the chunks of waves p and p + 4
+  if (streamer) {
     constexpr int kPer = kW8TwoMaxH / 4 / (kW8Role * 64);   // pieces per thread
     const int pieces = H / 4;
     const int st = tid - kW8Role * 64;
     uint32_t pend = 0;
-    if (streamer) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+      if (st + kW8Role * 64 * i < pieces) pend |= 1u << i;
+    for (uint32_t spins = 0;; ++spins) {
+      u32x4_t v[kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
-        if (st + kW8Role * 64 * i < pieces) pend |= 1u << i;
-    }
-    for (uint32_t spins = 0;; ++spins) {
-      if (streamer) {
-        u32x4_t v[kPer];
+        if (pend & (1u << i))
+          v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rh, (uint32_t)(st + kW8Role * 64 * i) * 16u, 0, 16 /* sc1 */));
 #pragma unroll
-        for (int i = 0; i < kPer; ++i)
-          if (pend & (1u << i))
-            v[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rh, (uint32_t)(st + kW8Role * 64 * i) * 16u, 0, 16 /* sc1 */));
-#pragma unroll
-        for (int i = 0; i < kPer; ++i) {
-          if ((pend & (1u << i)) && v[i][1] == target && v[i][3] == target) {
-            *reinterpret_cast<u32x2_t*>(xs + (st + kW8Role * 64 * i) * 8) = u32x2_t{v[i][0], v[i][2]};
-            pend &= ~(1u << i);
-          }
+      for (int i = 0; i < kPer; ++i) {
+        if ((pend & (1u << i)) && v[i][1] == target && v[i][3] == target) {
+          *reinterpret_cast<u32x2_t*>(xs + (st + kW8Role * 64 * i) * 8) = u32x2_t{v[i][0], v[i][2]};
+          pend &= ~(1u << i);
         }
-        const bool more = __builtin_amdgcn_ballot_w64(pend != 0) != 0;
-        if (lane == 0) busy[spins & 1][wave] = more ? 1u : 0u;
       }
-      // a barrier without a vector-memory wait: the holders' loads stay in flight.
-      // busy[spins & 1] is written again two passes on, after every wave has read it.
-      lds_barrier();
-      uint32_t more = 0;
-#pragma unroll
-      for (int w = kW8Role; w < kW8Waves; ++w) more |= busy[spins & 1][w];
-      if (more == 0) break;
+      if (__builtin_amdgcn_ballot_w64(pend != 0) == 0) break;   // wave-uniform
       if (spins >= (1u << 20)) {
-        if (tid == kW8Role * 64)
+        if (lane == 0)
           __hip_atomic_fetch_add(sync + kSyncTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (blk == 0 && tid == kW8Role * 64) st_coherent(sync + kSyncGenWord, gen_next);
+  } else if (has2) {
+    w8_hold<false, 8, 1>(P0);
+    w8_hold<false, 8, 1>(P1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      e4m3x16_to_bf16(P0.w0[j], q0[j][0], q0[j][1]);
+      e4m3x16_to_bf16(P1.w0[j], q1[j][0], q1[j][1]);
+    }
   }
+  lds_barrier();   // h is in LDS: block 0 has seen every block's words
+  if (blk == 0 && tid == kW8Role * 64) st_coherent(sync + kSyncGenWord, gen_next);
 
   // layer 2: the first tile from registers, any further ones streamed by all waves
   if (has2) {
     if (!streamer) {
-      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, unused0 = c0, unused1 = c0;
-      w8_hold<false, 8, 1>(P0);
-      w8_hold<false, 8, 1>(P1);
-      w8_consume_two<false>(P0, P1, p, p + kW8Role, g, K2, xrow_ok, xl, xz, c0, unused0, c1, unused1, 8);
+      // each accumulator sums in the one-role order; consecutive MFMAs are independent
+      f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4_t xa0, xa1, xb0, xb1;
+        w8_x<false, 8, 1>(P0, 0, j, p, g, K2, xrow_ok, xl, xz, xa0, xa1);
+        w8_x<false, 8, 1>(P1, 0, j, p + kW8Role, g, K2, xrow_ok, xl, xz, xb0, xb1);
+        c0 = mfma_16x16x32(q0[j][0], xa0, c0);
+        c1 = mfma_16x16x32(q1[j][0], xb0, c1);
+        c0 = mfma_16x16x32(q0[j][1], xa1, c0);
+        c1 = mfma_16x16x32(q1[j][1], xb1, c1);
+      }
       red[0][p][lane] = c0;
       red[0][p + kW8Role][lane] = c1;
     }
