@@ -570,11 +570,12 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_two_kernel(W8Layer L1, W
 // waves 0-3 hold the block's first layer-2 tile (16 rows over every k) in
 // registers, requested once layer 1's weights have landed and turned into
 // bf16 operands during the exchange: no poll waits behind a layer-2 load, and
-// once h is in LDS layer 2 is only multiplies.  (All 8 waves multiplying layer
-// 1, 8 loads each, measured slower: 12.8 against 12.3 us for the 4096^3 MLP.)  Wave p of a role does the work of waves
-// p and p + 4 of the one-role form (their k chunks, in their order, into
-// separate accumulators), and the 8 partial tiles are summed in the same
-// order, so the result is bitwise that of the one-role form.
+// once h is in LDS layer 2 is only multiplies.  (All 8 waves multiplying
+// layer 1, 8 loads each, measured slower: 12.8 against 12.3 us for the 4096^3
+// MLP.)  Wave p of a role does the work of waves p and p + 4 of the one-role
+// form (their k chunks, in their order, into separate accumulators), and the
+// 8 partial tiles are summed in the same order, so the result is bitwise that
+// of the one-role form.
 // ---------------------------------------------------------------------------
 constexpr int kW8SplitMaxK = kW8Waves * 8 * 64;   // one 8-load batch of 8 waves
 constexpr int kW8Role = kW8Waves / 2;
