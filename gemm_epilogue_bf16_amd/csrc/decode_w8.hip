@@ -276,8 +276,12 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
   const int nb = (chunks + kW8Waves * U - 1) / (kW8Waves * U);
   W8Batch<DUAL, U> A, B;
   const W8Rows<DUAL> R = w8_rows<DUAL>(L, n0 + 4 * g);
-  // the first weight batch is in flight while the activations are staged
-  w8_issue<DUAL, U, XB>(A, 0, wave, g, K, d0, d1, dx, wrow, xrow);
+  // The first weight batch is in flight while the activations are staged.  A
+  // wave's loads return in issue order: with the larger staging (up to 16
+  // token rows, several times the batch's bytes, from L2) the activations are
+  // requested first, so that they do not land only after the batch.
+  constexpr bool kXFirst = XB > 64 * 1024;
+  if constexpr (!kXFirst) w8_issue<DUAL, U, XB>(A, 0, wave, g, K, d0, d1, dx, wrow, xrow);
   if constexpr (XB > 0) {
     // Loads that write LDS, 1 KB of one activation row each (lanes past the
     // row's end masked off), all in flight before the one wait: a load into
@@ -294,7 +298,12 @@ __global__ __launch_bounds__(kW8Threads) void decode_w8_kernel(W8Layer L, int M)
       if (c < per_row)
         asm_load_lds(xd, uniform32(xs_lds + (uint32_t)(m * xstride + q * 1024)), (uint32_t)(m * K + c * 8) * 2u);
     }
-    wait_vm<0>();
+    if constexpr (kXFirst) {
+      w8_issue<DUAL, U, XB>(A, 0, wave, g, K, d0, d1, dx, wrow, xrow);
+      wait_vm<(DUAL ? 2 : 1) * U>();   // everything but the batch: the rows' values and the activations
+    } else {
+      wait_vm<0>();
+    }
     __syncthreads();
   }
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f};
